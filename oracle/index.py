@@ -1,0 +1,186 @@
+"""Index oracle: zigzag split, Ulysses layout, ring schedule, tile classes.
+
+Test infrastructure only (see the package docstring).  Integer and copy work:
+results here are exact, so GPU parity against them is bit-exact.
+
+Notation: S global sequence length, rd (= cp) ring degree, ud Ulysses degree,
+c = S / (2 rd) the zigzag chunk length.  Arrays use the user-facing layout
+[batch, seq_len, num_heads, head_dim] of [YunChang] (quickstart section).
+"""
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# Algorithm 2 ([USP review] section 三, "Algorithm 2: 负载均衡序列分段")
+# --------------------------------------------------------------------------
+
+def _chunk(seq, n):
+    """``seq.chunk(n)`` for a length divisible by n (sizes that do not divide
+    are rejected, as no page says how to pad)."""
+    if len(seq) % n != 0:
+        raise ValueError(f"length {len(seq)} does not split into {n} equal chunks")
+    return np.split(seq, n)
+
+
+def zigzag_local_positions(S, rd, ud, ring_rank, ulysses_rank):
+    """Global token positions held by ring rank ``ring_rank`` / Ulysses rank
+    ``ulysses_rank``, in local order.
+
+    Follows Algorithm 2 step by step on the position sequence 0..S-1:
+    split into 2*rd chunks, concatenate chunk r with chunk 2*rd-1-r, split that
+    into ud equal parts and keep part u.
+    """
+    seq = np.arange(S, dtype=np.int64)
+    seq_chunks = _chunk(seq, 2 * rd)
+    reorder_seq = np.concatenate([seq_chunks[ring_rank], seq_chunks[2 * rd - ring_rank - 1]])
+    return _chunk(reorder_seq, ud)[ulysses_rank]
+
+
+def zigzag_share_positions(S, rd, ring_rank):
+    """Positions of a ring rank's whole share (Algorithm 2 with ud = 1)."""
+    return zigzag_local_positions(S, rd, 1, ring_rank, 0)
+
+
+def zigzag_extract(x, rd, ud, ring_rank, ulysses_rank):
+    """Local shard of (B, S, H, D) array ``x`` for rank (r, u): (B, 2c/ud, H, D)."""
+    pos = zigzag_local_positions(x.shape[1], rd, ud, ring_rank, ulysses_rank)
+    return x[:, pos].copy()
+
+
+def zigzag_extract_all(x, rd, ud):
+    """Every rank's shard, stacked rank-major: (rd, ud, B, 2c/ud, H, D)."""
+    return np.stack([np.stack([zigzag_extract(x, rd, ud, r, u) for u in range(ud)])
+                     for r in range(rd)])
+
+
+def zigzag_scatter_all(shards, S):
+    """Inverse of :func:`zigzag_extract_all`: put every shard back at its
+    global positions.  ``shards``: (rd, ud, B, L, H, D)."""
+    rd, ud, B, L, H, D = shards.shape
+    out = np.zeros((B, S, H, D), dtype=shards.dtype)
+    for r in range(rd):
+        for u in range(ud):
+            out[:, zigzag_local_positions(S, rd, ud, r, u)] = shards[r, u]
+    return out
+
+
+def chunk_owner(chunk, rd):
+    """Ring rank that holds zigzag chunk ``chunk`` (0 <= chunk < 2 rd)."""
+    return chunk if chunk < rd else 2 * rd - 1 - chunk
+
+
+# --------------------------------------------------------------------------
+# Ulysses 4D all-to-all as a layout ([USP review] section 三, the AllToAll4D
+# box: (bs, L/N, hc, hd) -> (hc/N, bs, L, hd); Algorithm 1 steps 1-3 and 5)
+# --------------------------------------------------------------------------
+
+def ulysses_fwd(shards, ulysses_rank):
+    """What Ulysses rank u holds after the forward all-to-all.
+
+    ``shards``: the N sequence shards of the group, each (bs, L/N, hc, hd), in
+    Ulysses-rank order.  Rank u receives head block u (hc/N contiguous heads)
+    from every peer; the sequence is gathered in peer order.  Result:
+    (hc/N, bs, L, hd).
+    """
+    N = len(shards)
+    hc = shards[0].shape[2]
+    if hc % N != 0:
+        raise ValueError("head count must divide by the Ulysses degree")
+    hb = hc // N
+    gathered = np.concatenate([s[:, :, ulysses_rank * hb:(ulysses_rank + 1) * hb, :] for s in shards],
+                              axis=1)                       # (bs, L, hc/N, hd)
+    return np.ascontiguousarray(np.transpose(gathered, (2, 0, 1, 3)))
+
+
+def ulysses_inv(head_shards, ulysses_rank):
+    """Algorithm 1 step 5 for Ulysses rank u: the inverse all-to-all.
+
+    ``head_shards``: the N head-major tensors of the group, each
+    (hc/N, bs, L, hd).  Rank u gets back its sequence slice u (L/N tokens) with
+    all hc heads, head block u' coming from peer u'.  Result: (bs, L/N, hc, hd).
+    """
+    N = len(head_shards)
+    L = head_shards[0].shape[2]
+    if L % N != 0:
+        raise ValueError("sequence length must divide by the Ulysses degree")
+    ls = L // N
+    parts = [np.transpose(h[:, :, ulysses_rank * ls:(ulysses_rank + 1) * ls, :], (1, 2, 0, 3))
+             for h in head_shards]                          # each (bs, L/N, hc/N, hd)
+    return np.ascontiguousarray(np.concatenate(parts, axis=2))
+
+
+# --------------------------------------------------------------------------
+# Ring schedule ([CP vs Ulysses] concepts section and Figure 1)
+# --------------------------------------------------------------------------
+
+def ring_kv_block(ring_rank, step, cp):
+    """KV block held by rank r at step t: the KV moves one rank forward per
+    step, so after t steps rank r holds the block that started on rank r - t."""
+    return (ring_rank - step) % cp
+
+
+# --------------------------------------------------------------------------
+# Causal tile classes and load accounting ([CP vs Ulysses] Figure 2 and the
+# section "为什么要一头一尾配对"; [USP review] section 二 on the 7x imbalance)
+# --------------------------------------------------------------------------
+
+FULL, DIAGONAL, SKIP = "full", "diagonal", "skip"
+
+
+def tile_class(q_chunk, kv_chunk):
+    """Class of the (query chunk, key chunk) cell of the causal mask."""
+    if q_chunk > kv_chunk:
+        return FULL
+    if q_chunk == kv_chunk:
+        return DIAGONAL
+    return SKIP
+
+
+_WEIGHT = {FULL: 1.0, DIAGONAL: 0.5, SKIP: 0.0}   # a diagonal cell counts half
+
+
+def zigzag_chunks(ring_rank, rd):
+    """The two zigzag chunks of ring rank r, in local order."""
+    return (ring_rank, 2 * rd - 1 - ring_rank)
+
+
+def step_units(ring_rank, step, cp):
+    """Causal work of rank r at ring step t, in units of one chunk-pair cell."""
+    j = ring_kv_block(ring_rank, step, cp)
+    return sum(_WEIGHT[tile_class(a, b)]
+               for a in zigzag_chunks(ring_rank, cp) for b in zigzag_chunks(j, cp))
+
+
+def zigzag_rank_units(ring_rank, cp):
+    """Total causal work of a zigzag rank over its cp steps (small cells)."""
+    return sum(step_units(ring_rank, t, cp) for t in range(cp))
+
+
+def sequential_rank_units(rank, cp):
+    """Causal work of rank ``rank`` when the sequence is cut into cp blocks in
+    order (the "basic" split), in units of one big block cell."""
+    return sum(_WEIGHT[tile_class(rank, b)] for b in range(cp))
+
+
+def visible_pairs(q_pos, k_pos, seg_start=None):
+    """Exact number of visible (query, key) pairs: key position <= query
+    position (and, with packed samples, key in the query's sample)."""
+    q_pos = np.asarray(q_pos)
+    k_sorted = np.sort(np.asarray(k_pos))
+    hi = np.searchsorted(k_sorted, q_pos, side="right")
+    if seg_start is None:
+        return int(hi.sum())
+    lo = np.searchsorted(k_sorted, np.asarray(seg_start), side="left")
+    return int(np.maximum(hi - lo, 0).sum())
+
+
+# --------------------------------------------------------------------------
+# Packed samples ([ByteScale notes], motivation: short samples packed into one
+# long sequence).  cu_seqlens holds n+1 boundaries 0 = b_0 < ... < b_n = S.
+# --------------------------------------------------------------------------
+
+def segment_start(cu_seqlens, pos):
+    """First global position of the sample that holds each position."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    seg = np.searchsorted(cu, np.asarray(pos), side="right") - 1
+    return cu[seg]

@@ -1,0 +1,101 @@
+"""USP-Attention composed over a virtual (ud x rd) grid, in float64.
+
+Test infrastructure only (see the package docstring).
+
+[USP review] section 三: Algorithm 2 gives every (ring rank r, Ulysses rank u)
+its local tokens; Algorithm 1 then runs AllToAll4D on Q, K and V over the
+Ulysses group, LoadBalance-RingAttention over the ring group, and the inverse
+AllToAll4D on O.  [CP vs Ulysses] (concepts section) defines the ring: each
+rank keeps its queries, the KV blocks travel one rank per step, each step
+yields (o_j, lse_j), and the partials are merged with the LSE rule.
+
+Here every rank is a loop index; nothing is shared between ranks except what
+the steps above pass.
+"""
+import numpy as np
+
+from . import index as ix
+from .attention import masked_attention
+from .merge import lse_merge_many
+
+
+def _seg_start(cu_seqlens, pos):
+    return None if cu_seqlens is None else ix.segment_start(cu_seqlens, pos)
+
+
+def ring_attention_rank(q_local, q_pos, k_blocks, v_blocks, k_pos_blocks, ring_rank, scale,
+                        causal=True, cu_seqlens=None, return_partials=False):
+    """LoadBalance-RingAttention as seen by one ring rank.
+
+    q_local: (B, L, H, D) with global positions ``q_pos``; ``k_blocks`` /
+    ``v_blocks``: the cp KV blocks (B, L, Hkv, D) indexed by the rank that
+    holds them at step 0, with positions ``k_pos_blocks``.  At step t the rank
+    computes against block (r - t) mod cp; partials are merged in that order.
+
+    Returns (o (B, L, H, D), lse (H, B, L)) and, if asked, the list of step
+    partials in ring order, each as (o_j (H, B, L, D), lse_j (H, B, L)): rows
+    are merged head-major so that o_j and lse_j share their leading indices.
+    """
+    cp = len(k_blocks)
+    seg = _seg_start(cu_seqlens, q_pos)
+    partials = []
+    for t in range(cp):
+        j = ix.ring_kv_block(ring_rank, t, cp)
+        o_j, lse_j = masked_attention(q_local, k_blocks[j], v_blocks[j], scale,
+                                      q_pos, k_pos_blocks[j], causal, seg)
+        partials.append((np.transpose(o_j, (2, 0, 1, 3)), lse_j))
+    o, lse = lse_merge_many(partials)
+    o = np.ascontiguousarray(np.transpose(o, (1, 2, 0, 3)))
+    return (o, lse, partials) if return_partials else (o, lse)
+
+
+def usp_attention(Q, K, V, rd, ud, scale, causal=True, cu_seqlens=None):
+    """Algorithm 1 with Algorithm 2's split, on all rd*ud virtual ranks.
+
+    Q: (B, S, H, D); K, V: (B, S, Hkv, D) in global token order.  Returns
+    o: (B, S, H, D) in global order and lse: (H, B, S).
+    """
+    B, S, H, D = Q.shape
+    Hkv = K.shape[2]
+    if H % ud or Hkv % ud:
+        raise ValueError("head counts must divide by the Ulysses degree")
+
+    # Algorithm 2: every rank's local tokens.
+    def shards(X):
+        return [[ix.zigzag_extract(X, rd, ud, r, u) for u in range(ud)] for r in range(rd)]
+    Qs, Ks, Vs = shards(Q), shards(K), shards(V)
+
+    # Algorithm 1 steps 1-3: AllToAll4D over each Ulysses group (fixed r).
+    def a2a(Xs):
+        return [[ulysses_to_seq_major(ix.ulysses_fwd(Xs[r], u)) for u in range(ud)]
+                for r in range(rd)]
+    Qh, Kh, Vh = a2a(Qs), a2a(Ks), a2a(Vs)
+
+    # Positions after the gather: peer shards concatenated in Ulysses order.
+    share_pos = [np.concatenate([ix.zigzag_local_positions(S, rd, ud, r, u) for u in range(ud)])
+                 for r in range(rd)]
+
+    # Algorithm 1 step 4: the ring, per (r, u).
+    Oh = [[None] * ud for _ in range(rd)]
+    lse = np.full((H, B, S), -np.inf)
+    hb = H // ud
+    for r in range(rd):
+        for u in range(ud):
+            o_ru, lse_ru = ring_attention_rank(
+                Qh[r][u], share_pos[r], [Kh[j][u] for j in range(rd)],
+                [Vh[j][u] for j in range(rd)], share_pos, r, scale, causal, cu_seqlens)
+            Oh[r][u] = np.ascontiguousarray(np.transpose(o_ru, (2, 0, 1, 3)))   # head-major
+            lse[u * hb:(u + 1) * hb][:, :, share_pos[r]] = lse_ru
+
+    # Algorithm 1 step 5: inverse AllToAll4D, then back to global order.
+    O = np.zeros((B, S, H, D))
+    for r in range(rd):
+        for u in range(ud):
+            O[:, ix.zigzag_local_positions(S, rd, ud, r, u)] = ix.ulysses_inv(Oh[r], u)
+    return O, lse
+
+
+def ulysses_to_seq_major(x):
+    """(hc/N, bs, L, hd) -> (bs, L, hc/N, hd): a view change for the attention
+    routine, which takes the [batch, seq, head, dim] layout."""
+    return np.ascontiguousarray(np.transpose(x, (1, 2, 0, 3)))
