@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""Benchmark: one GPU's share of USP-Attention at the 128K-token hybrid
+workload (S = 131072, 32 query heads, 8 KV heads, head dim 128, bf16, ring
+degree 4 x Ulysses degree 2), on one MI355X.
+
+A step is the per-GPU hot path (OneGpuShare.step): zigzag extract of Q, K, V,
+Ulysses layout of Q, K, V, the fused ring walk over 4 KV blocks (attention
++ LSE merge + bf16 epilogue) and the inverse layout of O.  Inputs are seeded
+synthetic tensors already resident in HBM; the peers' pieces (other ring
+ranks' KV blocks, the other Ulysses rank's shards and output) are produced
+once before timing.
+
+Prints one JSON line.  ``value`` is causal-effective attention TFLOP/s over
+the whole step; ``roofline`` rates the dominant kernel (the ring walk)
+against the bf16 dense MFMA peak using HIP-event times of that kernel alone;
+``kernels`` rates each kernel of the step; ``cpu_baseline`` is the fp64
+oracle on a bounded row sample of the same workload, timed on the host.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD = "usp_hybrid_s128k_ud2_rd4"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+WALK_KERNEL = "attn_bf16_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_walk_usp_hybrid_s128k.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--ring-rank", type=int, default=0)
+    p.add_argument("--ulysses-rank", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=96, help="query rows of the oracle sample")
+    return p.parse_args()
+
+
+def kernel_source_hash():
+    path = os.path.join(ROOT, "sequence_ring_attention_amd", "csrc", "attn_bf16.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per walk launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, r, u, n_rows):
+    """The oracle as it stands on a bounded sample: n_rows query rows of this
+    share (all its heads) against the whole sequence, fp64 on the host."""
+    import numpy as np
+    import torch
+    from oracle import attention as oa
+    from oracle import index as ix
+    from sequence_ring_attention_amd import inputs
+    q, k, v = inputs.workload_qkv(w)
+    hb = w.H // w.ud
+    qn = q[:, :, u * hb:(u + 1) * hb].to(torch.float64).numpy()
+    kv_lo, kv_hi = u * (w.Hkv // w.ud), (u + 1) * (w.Hkv // w.ud)
+    kn = k[:, :, kv_lo:kv_hi].to(torch.float64).numpy()
+    vn = v[:, :, kv_lo:kv_hi].to(torch.float64).numpy()
+    pos = ix.zigzag_share_positions(w.S, w.rd, r)
+    rng = np.random.default_rng(1234)
+    rows = np.sort(rng.choice(len(pos), size=n_rows, replace=False))
+    qp = pos[rows]
+    t0 = time.perf_counter()
+    oa.masked_attention(qn[:, qp], kn, vn, w.scale, q_pos=qp)
+    dt = time.perf_counter() - t0
+    pairs = int((qp + 1).sum())                       # causal: position p sees p + 1 keys
+    flops = 4.0 * w.D * hb * w.B * pairs
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_rows} random query rows of share (r={r}, u={u}) x {hb} heads vs all "
+                      f"{w.S} keys, fp64 numpy, {dt:.2f} s, {flops / 1e9:.1f} GFLOP causal-effective",
+            "seconds": dt, "host_cpu_count": os.cpu_count(),
+            "affinity_cores": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share on a single MI355X; --gpus {args.gpus} is not "
+              "supported (no multi-GPU path in this build).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sequence_ring_attention_amd import inputs
+    from sequence_ring_attention_amd.pipeline import OneGpuShare
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    w = inputs.WORKLOADS[WORKLOAD]
+    r, u = args.ring_rank, args.ulysses_rank
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {WORKLOAD} inputs", file=sys.stderr, flush=True)
+    q, k, v = inputs.workload_qkv(w)
+    Q, K, V = q.to(dev), k.to(dev), v.to(dev)
+    del q, k, v
+    share = OneGpuShare(Q, K, V, w.rd, w.ud, r, u)
+    share.prepare_peers()
+    torch.cuda.synchronize()
+    print("[bench] peers prepared; warmup", file=sys.stderr, flush=True)
+
+    # algorithmic work per step
+    hb = w.H // w.ud
+    c = w.chunk
+    units = 2 * w.rd                                 # 2 chunk-pair cells per ring step
+    flops = 4.0 * w.D * hb * w.B * units * c * c      # half-diagonal convention
+    flops_exact = 4.0 * w.D * hb * w.B * (units * c * c + c)
+    zig_bytes, fwd_bytes, inv_bytes = share.copy_bytes()
+
+    for _ in range(args.warmup):
+        share.step()
+    torch.cuda.synchronize()
+
+    # timed region: whole steps, with per-phase events on the same stream
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    marks = [[ev() for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start, t_end = ev(), ev()
+    t_start.record(stream)
+    wall0 = time.perf_counter()
+    for s in range(args.steps):
+        share.step(marks[s])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    seg = lambda i, j: sum(marks[s][i].elapsed_time(marks[s][j]) for s in range(args.steps)) / args.steps
+    zig_ms, fwd_ms, walk_ms, inv_ms = seg(0, 1), seg(1, 2), seg(2, 3), seg(3, 4)
+
+    walk_tflops = flops / (walk_ms * 1e-3) / 1e12
+    traffic = measured_traffic()
+    result = {
+        "metric": "ring-step attention causal TFLOP/s + % bf16 MFMA peak; layout GB/s, 1 GPU",
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "seq_len": w.S, "num_q_heads": w.H, "num_kv_heads": w.Hkv,
+                   "head_dim": w.D, "batch": w.B, "ring_degree": w.rd, "ulysses_degree": w.ud,
+                   "share": {"ring_rank": r, "ulysses_rank": u},
+                   "share_tokens": w.S // w.rd, "heads_per_gpu": hb},
+        "roofline": {"bound": "mfma", "achieved": walk_tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": walk_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": traffic, "kernel": WALK_KERNEL,
+                     "work_per_launch_tflop": flops / 1e12,
+                     "work_per_launch_tflop_exact_pairs": flops_exact / 1e12,
+                     "avg_launch_ms": walk_ms},
+        "kernels": {
+            "zigzag_extract_qkv": {"ms": zig_ms, "bytes": zig_bytes,
+                                   "GB/s": zig_bytes / (zig_ms * 1e-3) / 1e9,
+                                   "frac_hbm": zig_bytes / (zig_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+            "ulysses_layout_fwd_qkv": {"ms": fwd_ms, "bytes": fwd_bytes,
+                                       "GB/s": fwd_bytes / (fwd_ms * 1e-3) / 1e9,
+                                       "frac_hbm": fwd_bytes / (fwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+            "ring_walk_attention": {"ms": walk_ms, "TFLOP/s": walk_tflops,
+                                    "frac_mfma": walk_tflops / PEAK_BF16_TFLOPS},
+            "ulysses_layout_inv_o": {"ms": inv_ms, "bytes": inv_bytes,
+                                     "GB/s": inv_bytes / (inv_ms * 1e-3) / 1e9,
+                                     "frac_hbm": inv_bytes / (inv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        },
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, r, u, args.cpu_rows)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

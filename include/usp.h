@@ -1,0 +1,208 @@
+/*
+ * usp.h -- C ABI of libusp.so: one GPU's share of the USP attention forward
+ * pass (Ulysses all-to-all layout + zigzag Ring-Attention) on AMD MI355X
+ * (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [USP review]    "USP: 统一序列并行方法用于长上下文生成式AI" (xllm-io paper
+ *                   review of Fang & Zhao, USP), section 三: the AllToAll4D
+ *                   layout (bs, L/N, hc, hd) -> (hc/N, bs, L, hd), Algorithm 1
+ *                   (USP-Attention) and Algorithm 2 (load-balanced split).
+ *   [CP vs Ulysses] "Context Parallel 与 Ulysses" (ml-interview blog): the
+ *                   ring schedule and the LSE merge (concepts section,
+ *                   Figure 1), the causal balance of the 2*cp split (Figure 2).
+ *   [YunChang]      the YunChang README translation: the user-facing layout
+ *                   [batch, seq_len, num_heads, head_dim] and the attention
+ *                   call's options (dropout, window, softcap, ALiBi ...).
+ *
+ * Conventions shared by every entry point:
+ *   - Every buffer is device memory owned by the caller.  The library
+ *     allocates nothing, keeps no device state between calls and never
+ *     synchronises: work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     default stream) and results are valid once that stream has completed.
+ *   - Element strides count elements, not bytes; head_dim is always the
+ *     contiguous (stride 1) dimension.
+ *   - Validation is synchronous and happens before any launch.  A non-OK
+ *     status means nothing was enqueued (except USP_ERR_HIP, which reports a
+ *     launch error).  usp_last_error_detail() gives a message for the last
+ *     non-OK status of the calling thread.
+ *   - Calls are thread-safe; calls that write the same buffers race.
+ *   - Positions: S is the global sequence length, rd (= cp) the ring degree,
+ *     ud the Ulysses degree, c = S / (2 rd) the zigzag chunk length.  Ring
+ *     rank r holds chunks r and 2 rd - 1 - r (in that order), i.e. a "share"
+ *     of 2c tokens whose global positions are r*c + i for i < c and
+ *     (2 rd - 1 - r)*c + (i - c) for c <= i < 2c.
+ */
+#ifndef USP_H
+#define USP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define USP_ABI_VERSION 1
+
+typedef enum {
+  USP_OK = 0,
+  USP_ERR_INVALID_ARG = 1, /* a null/misaligned pointer, a bad size, rank or step */
+  USP_ERR_UNSUPPORTED = 2, /* a valid request this library does not implement */
+  USP_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+} usp_status;
+
+typedef enum { USP_DTYPE_BF16 = 0, USP_DTYPE_FP32 = 1 } usp_dtype;
+
+/* Element strides of a 4D [batch, seq, head, head_dim] tensor. */
+typedef struct {
+  int64_t b, s, h;
+} usp_strides;
+
+/*
+ * Problem description shared by the attention entry points.
+ *
+ * Q is one ring rank's share (2c rows per batch and head) in `dtype`; K and V
+ * are the cp KV blocks as they would arrive over the ring: block j is ring
+ * rank j's share and starts `kv_block_stride` elements after block j - 1.
+ * With strides, both the sequence-major layout (B, 2c, H, D) and the
+ * head-major layout after the Ulysses all-to-all (H, B, 2c, D) are accepted
+ * without copies.
+ */
+typedef struct {
+  int64_t batch;          /* B >= 1                                             */
+  int64_t seq_len;        /* S, global; must divide by 2 * cp                   */
+  int64_t num_q_heads;    /* Hq (the heads this GPU holds)                      */
+  int64_t num_kv_heads;   /* Hkv; Hq % Hkv == 0, query head h reads KV head
+                             h / (Hq / Hkv) (contiguous groups)                 */
+  int64_t head_dim;       /* D: 64 or 128                                       */
+  usp_dtype dtype;        /* of Q, K, V and the final O; partials and lse are
+                             always fp32                                        */
+  float softmax_scale;    /* multiplies Q K^T; usually 1 / sqrt(D)              */
+  int32_t causal;         /* 1: key visible iff its global position <= the
+                             query's (token itself included); 0: no mask        */
+  int32_t cp;             /* ring degree (number of virtual ring ranks) >= 1    */
+  usp_strides q, k, v, o; /* element strides; o is used by usp_attn_fwd only    */
+  int64_t kv_block_stride;/* elements from KV block j to block j + 1            */
+  int64_t q_rank_stride;  /* usp_attn_fwd with ring_rank = -1: elements from
+                             rank r's query share to rank r + 1's               */
+  int64_t o_rank_stride;  /* same, for the output O                            */
+  const int32_t *cu_seqlens; /* device; num_seqs + 1 increasing global
+                             boundaries from 0 to S of packed samples (a key is
+                             visible only inside its query's sample; needs
+                             causal = 1).  NULL = one sequence.                 */
+  int32_t num_seqs;
+} usp_attn_desc;
+
+/*
+ * Zigzag split -- [USP review] section 三, Algorithm 2: cut the sequence into
+ * 2 rd chunks, give ring rank r chunks r and 2 rd - 1 - r, and give Ulysses
+ * rank u the u-th of ud equal parts of that share.
+ *
+ * Shapes (dtype elements, all contiguous):
+ *   x / out "global":  (B, S, H, D)
+ *   shard:             (B, S / (rd ud), H, D)
+ * Forward (inverse = 0), x global ->
+ *   ring_rank >= 0, ulysses_rank >= 0: out = that rank's shard;
+ *   ring_rank >= 0, ulysses_rank = -1: out = (ud, shard) of ring group r;
+ *   ring_rank = -1, ulysses_rank = -1: out = (rd, ud, shard) of every rank
+ *     (for B = 1 this is the whole sequence in zigzag order).
+ * Inverse (inverse = 1) swaps the roles: x holds the shard(s) in the layout
+ *   above and out is global; only the positions of the selected rank(s) are
+ *   written.
+ * Errors: USP_ERR_INVALID_ARG for null or 16-byte-misaligned pointers, x ==
+ *   out, sizes < 1, S % (2 rd ud) != 0, ranks out of range or
+ *   (ring_rank = -1, ulysses_rank >= 0).
+ */
+usp_status usp_zigzag_extract(const void *x, void *out, usp_dtype dtype, int64_t batch,
+                              int64_t seq_len, int64_t heads, int64_t head_dim, int32_t rd,
+                              int32_t ud, int32_t ring_rank, int32_t ulysses_rank,
+                              int32_t inverse, void *stream);
+
+/*
+ * Ulysses AllToAll4D as a single-GPU permutation -- [USP review] section 三:
+ * (bs, L/N, hc, hd) -> (hc/N, bs, L, hd) (the page writes "hs" for hc) and
+ * Algorithm 1, steps 1-3 (forward) and 5 (inverse).  Rank u takes head block
+ * u (hc/N contiguous heads) from every peer u', and peers' sequence pieces
+ * are gathered in u' order:
+ *     Y_u[h', b, u' (L/N) + t, :] = X_u'[b, t, u (hc/N) + h', :].
+ *
+ * Forward (inverse = 0): in = the N peers' shards, (N, bs, L/N, hc, hd);
+ *   out = (hc/N, bs, L, hd) for ulysses_rank = u >= 0, or
+ *   (N, hc/N, bs, L, hd) for every rank when ulysses_rank = -1.
+ * Inverse (inverse = 1): in = the N head-major tensors (N, hc/N, bs, L, hd);
+ *   out = rank u's (bs, L/N, hc, hd), or (N, bs, L/N, hc, hd) for -1.
+ * seq_len is L, the sequence length the Ulysses group holds together.
+ * Errors: USP_ERR_INVALID_ARG for null or 16-byte-misaligned pointers,
+ *   in == out, sizes < 1, hc % N != 0, L % N != 0, rank out of range.
+ */
+usp_status usp_ulysses_a2a_layout(const void *in, void *out, usp_dtype dtype, int64_t batch,
+                                  int64_t seq_len, int64_t heads, int64_t head_dim,
+                                  int32_t ulysses_degree, int32_t ulysses_rank, int32_t inverse,
+                                  void *stream);
+
+/*
+ * One ring step -- [CP vs Ulysses], concepts section and Figure 1: at step t
+ * ring rank r holds KV block j = (r - t) mod cp and computes its queries
+ * against it.  Output is the step's partial result: o_step = softmax-weighted
+ * sum of the visible values of block j, normalised over block j only, and
+ * lse_step = natural-log log-sum-exp of the scaled logits over those keys.  A
+ * query that sees no key of block j gets o = 0 and lse = -inf.
+ *
+ *   q:        rank r's share, strides desc->q, 2c rows
+ *   k_all, v_all: the cp KV blocks (desc->k, desc->v, desc->kv_block_stride)
+ *   o_step:   fp32 (Hq, B, 2c, D), contiguous
+ *   lse_step: fp32 (Hq, B, 2c), contiguous
+ * Errors: USP_ERR_INVALID_ARG for a bad descriptor (see usp_attn_desc), null
+ *   or misaligned pointers, ring_rank or step outside [0, cp);
+ *   USP_ERR_UNSUPPORTED for head_dim other than 64/128, or cu_seqlens with
+ *   causal = 0.
+ */
+usp_status usp_ring_attn_step_fwd(const void *q, const void *k_all, const void *v_all,
+                                  float *o_step, float *lse_step, const usp_attn_desc *desc,
+                                  int32_t ring_rank, int32_t step, void *stream);
+
+/*
+ * LSE merge, in place on the accumulator -- [CP vs Ulysses], concepts
+ * section: lse = log(e^lse1 + e^lse2), o = e^(lse1 - lse) o1 + e^(lse2 - lse)
+ * o2, evaluated as M + log(e^(lse1-M) + e^(lse2-M)) with M = max(lse1, lse2).
+ * A partial with lse = -inf (no visible key) is the identity; two such
+ * partials give (0, -inf).
+ *   o_acc (rows, head_dim), lse_acc (rows): fp32, updated in place
+ *   o_step (rows, head_dim), lse_step (rows): fp32, read only
+ * Errors: USP_ERR_INVALID_ARG for null or 16-byte-misaligned pointers, rows <
+ *   0, head_dim < 1 or head_dim % 4 != 0.  rows = 0 is a no-op.
+ */
+usp_status usp_lse_merge(float *o_acc, float *lse_acc, const float *o_step,
+                         const float *lse_step, int64_t rows, int64_t head_dim, void *stream);
+
+/*
+ * The whole ring for one rank in a single launch -- LoadBalance-RingAttention
+ * of [USP review] Algorithm 1 step 4 with the ring of [CP vs Ulysses]: the
+ * rank walks KV blocks (r - t) mod cp for t = 0 .. cp-1, which already sit in
+ * HBM, and folds each step into a running (max, sum, output) per query row;
+ * that running fold is the LSE merge applied step after step.  The epilogue
+ * writes the final O in `dtype` (bf16: round to nearest even) with strides
+ * desc->o, and lse (fp32, natural log) as (Hq, B, 2c).
+ *
+ * ring_rank = -1 runs every rank in one launch: rank r's query share starts
+ * r * desc->q_rank_stride elements after q, its output r * desc->o_rank_stride
+ * after o, and lse becomes (cp, Hq, B, 2c).
+ * Errors: as usp_ring_attn_step_fwd, and ring_rank outside [-1, cp).
+ */
+usp_status usp_attn_fwd(const void *q, const void *k_all, const void *v_all, void *o,
+                        float *lse, const usp_attn_desc *desc, int32_t ring_rank, void *stream);
+
+/* Name of a status code (static storage). */
+const char *usp_status_string(usp_status status);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char *usp_last_error_detail(void);
+
+/* USP_ABI_VERSION of the loaded library. */
+int32_t usp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* USP_H */

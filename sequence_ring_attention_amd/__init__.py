@@ -1,0 +1,16 @@
+"""USP (Ulysses + zigzag Ring-Attention) forward hot path for AMD MI355X.
+
+The compute lives in ``libusp.so`` (hand-written HIP kernels for gfx950,
+C ABI in ``include/usp.h``); ``binding`` marshals torch tensors into it and
+``inputs`` draws the seeded synthetic workloads.  The binding is loaded on
+first use, so ``inputs`` can be imported on machines without the library.
+"""
+_BINDING_NAMES = {"usp_zigzag_extract", "usp_ulysses_a2a_layout", "usp_ring_attn_step_fwd",
+                  "usp_lse_merge", "usp_attn_fwd", "attn_desc", "UspError", "UspAttnDesc", "lib"}
+
+
+def __getattr__(name):
+    if name in _BINDING_NAMES:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

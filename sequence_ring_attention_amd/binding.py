@@ -1,0 +1,228 @@
+"""ctypes binding of libusp.so: one Python function per C entry point, same
+names, argument marshalling only.  Every step of the path runs in the HIP
+library; nothing here computes.
+
+Tensors are torch tensors used as device buffers; the stream defaults to
+torch's current stream.  A non-OK status raises ``UspError``.  If the library
+is not built the first call raises ``RuntimeError``: there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libusp.so")
+
+USP_OK, USP_ERR_INVALID_ARG, USP_ERR_UNSUPPORTED, USP_ERR_HIP = 0, 1, 2, 3
+USP_DTYPE_BF16, USP_DTYPE_FP32 = 0, 1
+
+EXPORTED = ["usp_zigzag_extract", "usp_ulysses_a2a_layout", "usp_ring_attn_step_fwd",
+            "usp_lse_merge", "usp_attn_fwd", "usp_status_string", "usp_last_error_detail",
+            "usp_abi_version"]
+
+
+class UspError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__(f"{_STATUS.get(status, status)}: {detail}")
+
+
+_STATUS = {0: "USP_OK", 1: "USP_ERR_INVALID_ARG", 2: "USP_ERR_UNSUPPORTED", 3: "USP_ERR_HIP"}
+
+
+class UspStrides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("s", ctypes.c_int64), ("h", ctypes.c_int64)]
+
+
+class UspAttnDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seq_len", ctypes.c_int64),
+                ("num_q_heads", ctypes.c_int64), ("num_kv_heads", ctypes.c_int64),
+                ("head_dim", ctypes.c_int64), ("dtype", ctypes.c_int), ("softmax_scale", ctypes.c_float),
+                ("causal", ctypes.c_int32), ("cp", ctypes.c_int32),
+                ("q", UspStrides), ("k", UspStrides), ("v", UspStrides), ("o", UspStrides),
+                ("kv_block_stride", ctypes.c_int64), ("q_rank_stride", ctypes.c_int64),
+                ("o_rank_stride", ctypes.c_int64), ("cu_seqlens", ctypes.c_void_p),
+                ("num_seqs", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libusp.so (once)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int
+        L.usp_zigzag_extract.argtypes = [vp, vp, st, i64, i64, i64, i64, i32, i32, i32, i32, i32, vp]
+        L.usp_ulysses_a2a_layout.argtypes = [vp, vp, st, i64, i64, i64, i64, i32, i32, i32, vp]
+        L.usp_ring_attn_step_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, i32, vp]
+        L.usp_lse_merge.argtypes = [vp, vp, vp, vp, i64, i64, vp]
+        L.usp_attn_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, vp]
+        for f in ("usp_zigzag_extract", "usp_ulysses_a2a_layout", "usp_ring_attn_step_fwd",
+                  "usp_lse_merge", "usp_attn_fwd"):
+            getattr(L, f).restype = st
+        L.usp_status_string.argtypes = [st]
+        L.usp_status_string.restype = ctypes.c_char_p
+        L.usp_last_error_detail.argtypes = []
+        L.usp_last_error_detail.restype = ctypes.c_char_p
+        L.usp_abi_version.argtypes = []
+        L.usp_abi_version.restype = i32
+        _lib = L
+    return _lib
+
+
+def check(status):
+    if status != USP_OK:
+        raise UspError(status, lib().usp_last_error_detail().decode())
+
+
+def _dtype(t):
+    if t.dtype == torch.bfloat16:
+        return USP_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return USP_DTYPE_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live in GPU memory")
+
+
+def _contig(*ts):
+    for t in ts:
+        if not t.is_contiguous():
+            raise ValueError("tensor must be contiguous")
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(stream)
+
+
+def usp_zigzag_extract(x, out, rd, ud, ring_rank, ulysses_rank, inverse=False, stream=None):
+    """Forward: x global (B, S, H, D) -> out shard(s).  Inverse: x shard(s) ->
+    out global.  Shapes as in include/usp.h."""
+    _dev(x, out)
+    _contig(x, out)
+    B, S, H, D = (out if inverse else x).shape
+    groups = rd * ud if ring_rank < 0 else (ud if ulysses_rank < 0 else 1)
+    shard_elems = groups * B * (S // (rd * ud)) * H * D
+    if (x if inverse else out).numel() != shard_elems:
+        raise ValueError(f"shard buffer must hold {shard_elems} elements")
+    check(lib().usp_zigzag_extract(x.data_ptr(), out.data_ptr(), _dtype(x), B, S, H, D, rd, ud,
+                                   ring_rank, ulysses_rank, int(inverse), _stream(stream)))
+    return out
+
+
+def usp_ulysses_a2a_layout(inp, out, degree, rank, inverse=False, stream=None):
+    """Forward: inp (N, bs, L/N, hc, hd) -> out (hc/N, bs, L, hd) [rank u] or
+    (N, ...) [rank -1].  Inverse: inp (N, hc/N, bs, L, hd) -> (bs, L/N, hc, hd)
+    [or (N, ...)]."""
+    _dev(inp, out)
+    _contig(inp, out)
+    if not inverse:
+        N, bs, ls, hc, hd = inp.shape
+        L = ls * N
+    else:
+        N, hb, bs, L, hd = inp.shape
+        hc = hb * N
+    if N != degree:
+        raise ValueError("leading dimension of inp must equal the Ulysses degree")
+    if out.numel() != (degree if rank < 0 else 1) * bs * L * (hc // degree) * hd:
+        raise ValueError("out has the wrong number of elements")
+    check(lib().usp_ulysses_a2a_layout(inp.data_ptr(), out.data_ptr(), _dtype(inp), bs, L, hc, hd,
+                                       degree, rank, int(inverse), _stream(stream)))
+    return out
+
+
+def _check_attn(k_all, v_all, lse, desc, n_ranks):
+    if k_all.shape[0] != desc.cp or v_all.shape[0] != desc.cp:
+        raise ValueError("k_all / v_all need a leading dim of cp blocks")
+    L = desc.seq_len // desc.cp
+    if lse.dtype != torch.float32 or lse.numel() != n_ranks * desc.num_q_heads * desc.batch * L:
+        raise ValueError("lse must be fp32 with (ranks, Hq, B, 2c) elements")
+
+
+def usp_ring_attn_step_fwd(q, k_all, v_all, o_step, lse_step, desc, ring_rank, step, stream=None):
+    _dev(q, k_all, v_all, o_step, lse_step)
+    _check_attn(k_all, v_all, lse_step, desc, 1)
+    if o_step.dtype != torch.float32 or not o_step.is_contiguous() or \
+            o_step.numel() != lse_step.numel() * desc.head_dim:
+        raise ValueError("o_step must be contiguous fp32 (Hq, B, 2c, D)")
+    check(lib().usp_ring_attn_step_fwd(q.data_ptr(), k_all.data_ptr(), v_all.data_ptr(),
+                                       o_step.data_ptr(), lse_step.data_ptr(), ctypes.byref(desc),
+                                       ring_rank, step, _stream(stream)))
+    return o_step, lse_step
+
+
+def usp_lse_merge(o_acc, lse_acc, o_step, lse_step, stream=None):
+    """In place on (o_acc, lse_acc); o tensors (..., D) fp32, lse (...) fp32."""
+    _dev(o_acc, lse_acc, o_step, lse_step)
+    _contig(o_acc, lse_acc, o_step, lse_step)
+    D = o_acc.shape[-1]
+    rows = lse_acc.numel()
+    if o_acc.numel() != rows * D or o_step.numel() != rows * D or lse_step.numel() != rows:
+        raise ValueError("o (rows, D) and lse (rows) shapes disagree")
+    check(lib().usp_lse_merge(o_acc.data_ptr(), lse_acc.data_ptr(), o_step.data_ptr(),
+                              lse_step.data_ptr(), rows, D, _stream(stream)))
+    return o_acc, lse_acc
+
+
+def usp_attn_fwd(q, k_all, v_all, o, lse, desc, ring_rank, stream=None):
+    _dev(q, k_all, v_all, o, lse)
+    _check_attn(k_all, v_all, lse, desc, desc.cp if ring_rank < 0 else 1)
+    check(lib().usp_attn_fwd(q.data_ptr(), k_all.data_ptr(), v_all.data_ptr(), o.data_ptr(),
+                             lse.data_ptr(), ctypes.byref(desc), ring_rank, _stream(stream)))
+    return o, lse
+
+
+def attn_desc(seq_len, cp, q, k_all, v_all, o=None, layout="bshd", causal=True, softmax_scale=None,
+              cu_seqlens=None, all_ranks=False):
+    """Build a ``UspAttnDesc`` from tensors.
+
+    ``layout`` names the order of the last four dims of every tensor: "bshd"
+    (sequence-major, [batch, seq, head, dim]) or "hbsd" (head-major, after the
+    Ulysses layout).  ``k_all``/``v_all`` have a leading cp (block) dim; with
+    ``all_ranks`` so do ``q`` and ``o``.
+    """
+    pos = {"bshd": (0, 1, 2), "hbsd": (1, 2, 0)}[layout]
+
+    def strides(t, lead):
+        st = t.stride()[lead:]
+        if st[3] != 1:
+            raise ValueError("head_dim must be the contiguous dim")
+        return UspStrides(st[pos[0]], st[pos[1]], st[pos[2]])
+
+    ql = 1 if all_ranks else 0
+    shp = q.shape[ql:]
+    B, Hq, D = shp[pos[0]], shp[pos[2]], shp[3]
+    Hkv = k_all.shape[1:][pos[2]]
+    d = UspAttnDesc()
+    d.batch, d.seq_len, d.num_q_heads, d.num_kv_heads, d.head_dim = B, seq_len, Hq, Hkv, D
+    d.dtype = _dtype(q)
+    d.softmax_scale = (D ** -0.5) if softmax_scale is None else softmax_scale
+    d.causal = int(causal)
+    d.cp = cp
+    d.q = strides(q, ql)
+    d.k = strides(k_all, 1)
+    d.v = strides(v_all, 1)
+    if v_all.stride(0) != k_all.stride(0):
+        raise ValueError("k_all and v_all must share the block stride")
+    d.kv_block_stride = k_all.stride(0)
+    if o is not None:
+        d.o = strides(o, ql)
+        d.o_rank_stride = o.stride(0) if all_ranks else 0
+    d.q_rank_stride = q.stride(0) if all_ranks else 0
+    if cu_seqlens is not None:
+        d.cu_seqlens = cu_seqlens.data_ptr()
+        d.num_seqs = cu_seqlens.numel() - 1
+    return d

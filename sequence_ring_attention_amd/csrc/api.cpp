@@ -1,0 +1,302 @@
+// C ABI of libusp.so (declared in include/usp.h): argument validation, grid
+// planning and dispatch to the HIP kernels.  Every check runs on the host
+// before anything is enqueued; no entry point allocates or synchronises.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/usp.h"
+#include "usp_internal.h"
+
+namespace {
+
+thread_local char g_detail[512] = "";
+
+usp_status fail(usp_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+usp_status ok() {
+  g_detail[0] = '\0';
+  return USP_OK;
+}
+
+usp_status hip_result(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(USP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t elem_bytes(usp_dtype dt) { return dt == USP_DTYPE_BF16 ? 2 : 4; }
+
+bool dtype_ok(usp_dtype dt) { return dt == USP_DTYPE_BF16 || dt == USP_DTYPE_FP32; }
+
+uint32_t log2_exact(uint64_t v) {
+  if (v == 0 || (v & (v - 1))) return 31;
+  uint32_t s = 0;
+  while ((1ull << s) < v) ++s;
+  return s;
+}
+
+// Fill the piece fields of a copy plan: pieces of about 64 KiB.
+void plan_pieces(usp::CopyPlan &p) {
+  uint64_t rows = 65536 / p.row_bytes;
+  if (rows < 1) rows = 1;
+  if (rows > p.rows_per_item) rows = p.rows_per_item;
+  p.rows_per_piece = (uint32_t)rows;
+  p.pieces_per_item = (uint32_t)((p.rows_per_item + rows - 1) / rows);
+  p.row_vecs = (uint32_t)(p.row_bytes / 16);
+  p.row_vecs_shift = log2_exact(p.row_vecs);
+}
+
+constexpr int64_t kMaxIndex = (int64_t)1 << 31;
+
+}  // namespace
+
+extern "C" {
+
+const char *usp_status_string(usp_status s) {
+  switch (s) {
+    case USP_OK: return "USP_OK";
+    case USP_ERR_INVALID_ARG: return "USP_ERR_INVALID_ARG";
+    case USP_ERR_UNSUPPORTED: return "USP_ERR_UNSUPPORTED";
+    case USP_ERR_HIP: return "USP_ERR_HIP";
+  }
+  return "USP_ERR_UNKNOWN";
+}
+
+const char *usp_last_error_detail(void) { return g_detail; }
+
+int32_t usp_abi_version(void) { return USP_ABI_VERSION; }
+
+usp_status usp_zigzag_extract(const void *x, void *out, usp_dtype dtype, int64_t batch,
+                              int64_t seq_len, int64_t heads, int64_t head_dim, int32_t rd,
+                              int32_t ud, int32_t ring_rank, int32_t ulysses_rank,
+                              int32_t inverse, void *stream) {
+  if (!x || !out) return fail(USP_ERR_INVALID_ARG, "zigzag_extract: null pointer");
+  if (!aligned16(x) || !aligned16(out))
+    return fail(USP_ERR_INVALID_ARG, "zigzag_extract: pointers must be 16-byte aligned");
+  if (x == out) return fail(USP_ERR_INVALID_ARG, "zigzag_extract: x and out must differ");
+  if (!dtype_ok(dtype)) return fail(USP_ERR_INVALID_ARG, "zigzag_extract: unknown dtype %d", (int)dtype);
+  if (batch < 1 || seq_len < 1 || heads < 1 || head_dim < 1 || rd < 1 || ud < 1)
+    return fail(USP_ERR_INVALID_ARG, "zigzag_extract: sizes and degrees must be >= 1");
+  if (inverse != 0 && inverse != 1) return fail(USP_ERR_INVALID_ARG, "zigzag_extract: inverse must be 0 or 1");
+  if (seq_len % (2 * (int64_t)rd * ud) != 0)
+    return fail(USP_ERR_INVALID_ARG, "zigzag_extract: seq_len %lld not divisible by 2*rd*ud = %lld",
+                (long long)seq_len, (long long)(2 * (int64_t)rd * ud));
+  if (ring_rank < -1 || ring_rank >= rd || ulysses_rank < -1 || ulysses_rank >= ud)
+    return fail(USP_ERR_INVALID_ARG, "zigzag_extract: rank out of range");
+  if (ring_rank == -1 && ulysses_rank != -1)
+    return fail(USP_ERR_INVALID_ARG, "zigzag_extract: ring_rank = -1 needs ulysses_rank = -1");
+  const int64_t row_bytes = heads * head_dim * elem_bytes(dtype);
+  if (row_bytes % 16 != 0)
+    return fail(USP_ERR_UNSUPPORTED, "zigzag_extract: heads*head_dim*element size must be a multiple of 16 bytes");
+  if (batch * seq_len >= kMaxIndex) return fail(USP_ERR_UNSUPPORTED, "zigzag_extract: too many rows");
+
+  usp::CopyPlan p{};
+  p.src = static_cast<const char *>(x);
+  p.dst = static_cast<char *>(out);
+  p.kind = inverse ? usp::kZigzagInv : usp::kZigzagFwd;
+  const int64_t groups = ring_rank < 0 ? (int64_t)rd * ud : (ulysses_rank < 0 ? ud : 1);
+  p.n_items = (uint32_t)(groups * batch);
+  p.rows_per_item = (uint32_t)(seq_len / ((int64_t)rd * ud));
+  p.row_bytes = (uint64_t)row_bytes;
+  p.p[0] = batch;
+  p.p[1] = seq_len;
+  p.p[2] = seq_len / (2 * (int64_t)rd);
+  p.p[3] = rd;
+  p.p[4] = ud;
+  p.p[5] = p.rows_per_item;
+  p.p[6] = ring_rank;
+  p.p[7] = ulysses_rank;
+  plan_pieces(p);
+  return hip_result(usp::launch_copy(p, static_cast<hipStream_t>(stream)), "zigzag_extract launch");
+}
+
+usp_status usp_ulysses_a2a_layout(const void *in, void *out, usp_dtype dtype, int64_t batch,
+                                  int64_t seq_len, int64_t heads, int64_t head_dim,
+                                  int32_t ulysses_degree, int32_t ulysses_rank, int32_t inverse,
+                                  void *stream) {
+  if (!in || !out) return fail(USP_ERR_INVALID_ARG, "ulysses_a2a_layout: null pointer");
+  if (!aligned16(in) || !aligned16(out))
+    return fail(USP_ERR_INVALID_ARG, "ulysses_a2a_layout: pointers must be 16-byte aligned");
+  if (in == out) return fail(USP_ERR_INVALID_ARG, "ulysses_a2a_layout: in and out must differ");
+  if (!dtype_ok(dtype)) return fail(USP_ERR_INVALID_ARG, "ulysses_a2a_layout: unknown dtype %d", (int)dtype);
+  if (batch < 1 || seq_len < 1 || heads < 1 || head_dim < 1 || ulysses_degree < 1)
+    return fail(USP_ERR_INVALID_ARG, "ulysses_a2a_layout: sizes and degree must be >= 1");
+  if (inverse != 0 && inverse != 1) return fail(USP_ERR_INVALID_ARG, "ulysses_a2a_layout: inverse must be 0 or 1");
+  const int64_t N = ulysses_degree;
+  if (heads % N != 0)
+    return fail(USP_ERR_INVALID_ARG, "ulysses_a2a_layout: heads %lld not divisible by degree %lld",
+                (long long)heads, (long long)N);
+  if (seq_len % N != 0)
+    return fail(USP_ERR_INVALID_ARG, "ulysses_a2a_layout: seq_len %lld not divisible by degree %lld",
+                (long long)seq_len, (long long)N);
+  if (ulysses_rank < -1 || ulysses_rank >= ulysses_degree)
+    return fail(USP_ERR_INVALID_ARG, "ulysses_a2a_layout: rank out of range");
+  const int64_t row_bytes = head_dim * elem_bytes(dtype);
+  if (row_bytes % 16 != 0)
+    return fail(USP_ERR_UNSUPPORTED, "ulysses_a2a_layout: head_dim*element size must be a multiple of 16 bytes");
+  if (N * batch * seq_len * heads >= kMaxIndex)
+    return fail(USP_ERR_UNSUPPORTED, "ulysses_a2a_layout: too many rows");
+
+  const int64_t G = ulysses_rank < 0 ? N : 1;
+  const int64_t hb = heads / N, Ls = seq_len / N;
+  usp::CopyPlan p{};
+  p.src = static_cast<const char *>(in);
+  p.dst = static_cast<char *>(out);
+  p.kind = inverse ? usp::kUlyssesInv : usp::kUlyssesFwd;
+  p.n_items = (uint32_t)(G * hb * batch * N);
+  p.rows_per_item = (uint32_t)Ls;
+  p.row_bytes = (uint64_t)row_bytes;
+  p.p[0] = batch;
+  p.p[1] = seq_len;
+  p.p[2] = heads;
+  p.p[3] = N;
+  p.p[4] = hb;
+  p.p[5] = Ls;
+  p.p[6] = ulysses_rank;
+  plan_pieces(p);
+  return hip_result(usp::launch_copy(p, static_cast<hipStream_t>(stream)), "ulysses_a2a_layout launch");
+}
+
+usp_status usp_lse_merge(float *o_acc, float *lse_acc, const float *o_step, const float *lse_step,
+                         int64_t rows, int64_t head_dim, void *stream) {
+  if (rows < 0) return fail(USP_ERR_INVALID_ARG, "lse_merge: rows < 0");
+  if (head_dim < 1 || head_dim % 4 != 0)
+    return fail(USP_ERR_INVALID_ARG, "lse_merge: head_dim must be a positive multiple of 4");
+  if (rows == 0) return ok();
+  if (!o_acc || !lse_acc || !o_step || !lse_step) return fail(USP_ERR_INVALID_ARG, "lse_merge: null pointer");
+  if (!aligned16(o_acc) || !aligned16(o_step))
+    return fail(USP_ERR_INVALID_ARG, "lse_merge: o buffers must be 16-byte aligned");
+  return hip_result(usp::launch_lse_merge(o_acc, lse_acc, o_step, lse_step, rows, head_dim,
+                                          static_cast<hipStream_t>(stream)),
+                    "lse_merge launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared checks of the attention descriptor; fills the kernel arguments.
+usp_status attn_prepare(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                        const usp_attn_desc *d, int32_t ring_rank, bool all_ranks_ok,
+                        usp::AttnArgs &a, const char *who) {
+  if (!d) return fail(USP_ERR_INVALID_ARG, "%s: null descriptor", who);
+  if (!q || !k || !v || !o || !lse) return fail(USP_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(USP_ERR_INVALID_ARG, "%s: q, k, v, o must be 16-byte aligned", who);
+  if (!dtype_ok(d->dtype)) return fail(USP_ERR_INVALID_ARG, "%s: unknown dtype %d", who, (int)d->dtype);
+  if (d->batch < 1 || d->seq_len < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->cp < 1)
+    return fail(USP_ERR_INVALID_ARG, "%s: sizes and cp must be >= 1", who);
+  if (d->num_q_heads % d->num_kv_heads != 0)
+    return fail(USP_ERR_INVALID_ARG, "%s: num_q_heads must be a multiple of num_kv_heads", who);
+  if (d->seq_len % (2 * (int64_t)d->cp) != 0)
+    return fail(USP_ERR_INVALID_ARG, "%s: seq_len %lld not divisible by 2*cp = %lld", who,
+                (long long)d->seq_len, (long long)(2 * (int64_t)d->cp));
+  if (!(d->softmax_scale > 0.0f) || !std::isfinite(d->softmax_scale))
+    return fail(USP_ERR_INVALID_ARG, "%s: softmax_scale must be finite and > 0", who);
+  if (d->causal != 0 && d->causal != 1) return fail(USP_ERR_INVALID_ARG, "%s: causal must be 0 or 1", who);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(USP_ERR_UNSUPPORTED, "%s: head_dim %lld (supported: 64, 128)", who, (long long)d->head_dim);
+  if (d->cu_seqlens && !d->causal)
+    return fail(USP_ERR_UNSUPPORTED, "%s: packed samples (cu_seqlens) need causal = 1", who);
+  if (d->cu_seqlens && d->num_seqs < 1) return fail(USP_ERR_INVALID_ARG, "%s: num_seqs must be >= 1", who);
+  if (ring_rank < (all_ranks_ok ? -1 : 0) || ring_rank >= d->cp)
+    return fail(USP_ERR_INVALID_ARG, "%s: ring_rank %d out of range", who, (int)ring_rank);
+  const int64_t L = d->seq_len / d->cp;
+  if (d->seq_len >= kMaxIndex || d->batch * d->num_q_heads * L * d->cp >= kMaxIndex)
+    return fail(USP_ERR_UNSUPPORTED, "%s: problem too large for 32-bit row indices", who);
+  // every stride the kernels use must keep 16-byte alignment of a head row
+  const int64_t e = elem_bytes(d->dtype);
+  const int64_t strides[] = {d->q.b, d->q.s, d->q.h, d->k.b, d->k.s, d->k.h, d->v.b, d->v.s,
+                             d->v.h, d->kv_block_stride};
+  for (int64_t s : strides)
+    if (s < 0 || (s * e) % 16 != 0)
+      return fail(USP_ERR_INVALID_ARG, "%s: strides must be >= 0 and keep 16-byte alignment", who);
+
+  a = usp::AttnArgs{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = const_cast<void *>(o);
+  a.lse = const_cast<float *>(lse);
+  a.B = (int32_t)d->batch;
+  a.Hq = (int32_t)d->num_q_heads;
+  a.Hkv = (int32_t)d->num_kv_heads;
+  a.G = a.Hq / a.Hkv;
+  a.L = (int32_t)L;
+  a.c = (int32_t)(L / 2);
+  a.cp = d->cp;
+  a.causal = d->causal;
+  a.q_sb = d->q.b; a.q_ss = d->q.s; a.q_sh = d->q.h;
+  a.k_sb = d->k.b; a.k_ss = d->k.s; a.k_sh = d->k.h;
+  a.v_sb = d->v.b; a.v_ss = d->v.s; a.v_sh = d->v.h;
+  a.o_sb = d->o.b; a.o_ss = d->o.s; a.o_sh = d->o.h;
+  a.kv_blk = d->kv_block_stride;
+  a.q_rank = d->q_rank_stride;
+  a.o_rank = d->o_rank_stride;
+  a.scale = d->softmax_scale;
+  a.scale_log2 = (float)((double)d->softmax_scale * 1.4426950408889634074);
+  a.cu = d->cu_seqlens;
+  a.nseq = d->num_seqs;
+  a.ring_rank = ring_rank;
+  a.n_ranks = ring_rank < 0 ? d->cp : 1;
+  a.n_qtiles = (int32_t)((L + 127) / 128);
+  const int64_t groups = (int64_t)a.n_ranks * a.n_qtiles * a.B * a.Hkv;
+  a.xcd_remap = groups % 8 == 0;
+  return USP_OK;
+}
+
+usp_status attn_launch(const usp::AttnArgs &a, const usp_attn_desc *d, void *stream, const char *who) {
+  hipError_t e = d->dtype == USP_DTYPE_BF16
+                     ? usp::launch_attn_bf16(a, (int)d->head_dim, static_cast<hipStream_t>(stream))
+                     : usp::launch_attn_fp32(a, (int)d->head_dim, static_cast<hipStream_t>(stream));
+  return hip_result(e, who);
+}
+
+}  // namespace
+
+extern "C" {
+
+usp_status usp_ring_attn_step_fwd(const void *q, const void *k_all, const void *v_all, float *o_step,
+                                  float *lse_step, const usp_attn_desc *desc, int32_t ring_rank,
+                                  int32_t step, void *stream) {
+  usp::AttnArgs a;
+  usp_status s = attn_prepare(q, k_all, v_all, o_step, lse_step, desc, ring_rank, false, a,
+                              "ring_attn_step_fwd");
+  if (s != USP_OK) return s;
+  if (!aligned16(o_step)) return fail(USP_ERR_INVALID_ARG, "ring_attn_step_fwd: o_step must be 16-byte aligned");
+  if (step < 0 || step >= desc->cp)
+    return fail(USP_ERR_INVALID_ARG, "ring_attn_step_fwd: step %d out of range", (int)step);
+  a.t_lo = step;
+  a.t_hi = step + 1;
+  a.partial = 1;
+  return attn_launch(a, desc, stream, "ring_attn_step_fwd launch");
+}
+
+usp_status usp_attn_fwd(const void *q, const void *k_all, const void *v_all, void *o, float *lse,
+                        const usp_attn_desc *desc, int32_t ring_rank, void *stream) {
+  usp::AttnArgs a;
+  usp_status s = attn_prepare(q, k_all, v_all, o, lse, desc, ring_rank, true, a, "attn_fwd");
+  if (s != USP_OK) return s;
+  const int64_t e = elem_bytes(desc->dtype);
+  const int64_t ostr[] = {desc->o.b, desc->o.s, desc->o.h, desc->q_rank_stride, desc->o_rank_stride};
+  for (int64_t st : ostr)
+    if (st < 0 || (st * e) % 8 != 0)
+      return fail(USP_ERR_INVALID_ARG, "attn_fwd: o and rank strides must be >= 0 and keep 8-byte alignment");
+  if (ring_rank < 0 && (desc->q_rank_stride * e) % 16 != 0)
+    return fail(USP_ERR_INVALID_ARG, "attn_fwd: q_rank_stride must keep 16-byte alignment");
+  a.t_lo = 0;
+  a.t_hi = desc->cp;
+  a.partial = 0;
+  return attn_launch(a, desc, stream, "attn_fwd launch");
+}
+
+}  // extern "C"

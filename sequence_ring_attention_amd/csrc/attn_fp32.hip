@@ -1,0 +1,122 @@
+// Ring-step / ring-walk attention for fp32 inputs (small problems).
+//
+// One wavefront per (rank, query head, batch, query row); the 64 lanes split
+// head_dim.  Logits, the running max/sum and the output accumulator are kept
+// in double: a product of two floats is exact in double, so the only
+// rounding that reaches the fp32 outputs is the final one.
+//
+// Semantics as the bf16 kernel: ring rank r at step t reads KV block
+// (r - t) mod cp ("Context Parallel 与 Ulysses", concepts section and
+// Figure 1); a key is visible iff its global position is <= the query's
+// (causal) and, for packed samples, inside the query's sample.  The fold over
+// steps is the online form of the LSE merge of the same page.
+#include "usp_internal.h"
+
+namespace usp {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ inline int share_pos(int rank, int i, int c, int cp) {
+  return i < c ? rank * c + i : (2 * cp - 1 - rank) * c + (i - c);
+}
+
+__device__ inline int seg_start(const int32_t *cu, int nseq, int pos) {
+  int lo = 0, hi = nseq;  // cu[lo] <= pos < cu[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= pos) lo = mid; else hi = mid;
+  }
+  return cu[lo];
+}
+
+__device__ inline double wave_sum(double x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_fp32_kernel(AttnArgs a) {
+  constexpr int PER = D / 64;  // elements per lane (1 or 2)
+  const int lane = threadIdx.x & 63;
+  const int64_t w = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int64_t rows_per_rank = (int64_t)a.Hq * a.B * a.L;
+  if (w >= rows_per_rank * a.n_ranks) return;  // whole wavefront exits together
+  int64_t rest = w;
+  const int qrow = (int)(rest % a.L);
+  rest /= a.L;
+  const int b = (int)(rest % a.B);
+  rest /= a.B;
+  const int hq = (int)(rest % a.Hq);
+  const int rank = a.ring_rank >= 0 ? a.ring_rank : (int)(rest / a.Hq);
+  const int kvh = hq / a.G;
+  const int qpos = share_pos(rank, qrow, a.c, a.cp);
+  const int sst = a.cu ? seg_start(a.cu, a.nseq, qpos) : 0;
+
+  const float *qp = static_cast<const float *>(a.q) + (a.ring_rank < 0 ? rank * a.q_rank : 0) +
+                    b * a.q_sb + (int64_t)qrow * a.q_ss + hq * a.q_sh;
+  double qv[PER], acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    qv[e] = (double)qp[lane + 64 * e];
+    acc[e] = 0.0;
+  }
+  const double scale = (double)a.scale;
+  double m = -INFINITY, l = 0.0;
+  for (int t = a.t_lo; t < a.t_hi; ++t) {
+    int j = (rank - t) % a.cp;
+    if (j < 0) j += a.cp;
+    const float *kb = static_cast<const float *>(a.k) + j * a.kv_blk + b * a.k_sb + kvh * a.k_sh;
+    const float *vb = static_cast<const float *>(a.v) + j * a.kv_blk + b * a.v_sb + kvh * a.v_sh;
+    for (int kk = 0; kk < a.L; ++kk) {
+      const int kpos = share_pos(j, kk, a.c, a.cp);
+      if (a.causal && kpos > qpos) continue;
+      if (a.cu && kpos < sst) continue;
+      double part = 0.0;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) part += qv[e] * (double)kb[(int64_t)kk * a.k_ss + lane + 64 * e];
+      const double s = wave_sum(part) * scale;
+      const double m_new = s > m ? s : m;
+      const double alpha = exp(m - m_new);  // m = -inf on the first key: alpha = 0
+      const double p = exp(s - m_new);
+      l = l * alpha + p;
+#pragma unroll
+      for (int e = 0; e < PER; ++e)
+        acc[e] = acc[e] * alpha + p * (double)vb[(int64_t)kk * a.v_ss + lane + 64 * e];
+      m = m_new;
+    }
+  }
+  const bool empty = l == 0.0;
+  const double inv = empty ? 0.0 : 1.0 / l;
+  const float lse = empty ? -INFINITY : (float)(m + log(l));
+  if (a.partial) {
+    float *o = static_cast<float *>(a.o) + (((int64_t)hq * a.B + b) * a.L + qrow) * D;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[lane + 64 * e] = (float)(acc[e] * inv);
+  } else {
+    float *o = static_cast<float *>(a.o) + (a.ring_rank < 0 ? rank * a.o_rank : 0) + b * a.o_sb +
+               (int64_t)qrow * a.o_ss + hq * a.o_sh;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[lane + 64 * e] = (float)(acc[e] * inv);
+  }
+  if (lane == 0) {
+    const int64_t li = (((a.ring_rank < 0 ? (int64_t)rank * a.Hq : 0) + hq) * a.B + b) * a.L + qrow;
+    a.lse[li] = lse;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fp32(const AttnArgs &a, int head_dim, hipStream_t stream) {
+  const int64_t waves = (int64_t)a.Hq * a.B * a.L * a.n_ranks;
+  const int64_t blocks = (waves + 3) / 4;
+  if (blocks == 0) return hipSuccess;
+  if (head_dim == 64)
+    hipLaunchKernelGGL(attn_fp32_kernel<64>, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_fp32_kernel<128>, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace usp

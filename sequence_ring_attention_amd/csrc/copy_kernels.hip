@@ -1,0 +1,152 @@
+// Zigzag split and Ulysses all-to-all layout as batched 2D row copies.
+//
+// Both are pure data movement, bound by HBM bandwidth.  Every shape reduces
+// to "items": runs of rows that are contiguous (or evenly strided) on both
+// sides, so each workgroup copies whole 16-byte vectors with one scalar
+// index decode per piece instead of per element.
+//
+// Zigzag ("USP" paper review, section 三, Algorithm 2): the share of ring
+// rank r is chunk r followed by chunk 2rd-1-r; the u-th of ud equal parts of
+// it belongs to Ulysses rank u.  In (B, S, H, D) a token's H*D elements are
+// one contiguous row, so a shard is at most two contiguous runs of rows.
+//
+// Ulysses (same section, the AllToAll4D box (bs, L/N, hc, hd) ->
+// (hc/N, bs, L, hd)): for fixed (head h', batch b, source peer u') the
+// Ls = L/N rows of D elements are strided by hc*D on the sequence-major side
+// and contiguous on the head-major side.
+#include "usp_internal.h"
+
+namespace usp {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+struct RowMap {
+  int64_t src_base, src_stride, dst_base, dst_stride;  // in rows
+  int64_t split, src_jump, dst_jump;                   // rows t >= split add the jumps
+};
+
+__device__ inline RowMap decode(const CopyPlan &P, uint32_t item) {
+  RowMap m;
+  m.split = INT64_MAX;
+  m.src_jump = m.dst_jump = 0;
+  if (P.kind == kZigzagFwd || P.kind == kZigzagInv) {
+    const int64_t B = P.p[0], S = P.p[1], c = P.p[2], rd = P.p[3], ud = P.p[4], T = P.p[5];
+    const int64_t r_fix = P.p[6], u_fix = P.p[7];
+    const int64_t b = item % B, g = item / B;
+    int64_t r, u;
+    if (r_fix < 0) {
+      r = g / ud;
+      u = g % ud;
+    } else if (u_fix < 0) {
+      r = r_fix;
+      u = g;
+    } else {
+      r = r_fix;
+      u = u_fix;
+    }
+    // local index l = u*T + t; position r*c + l for l < c, (2rd-1-r)*c + l - c after.
+    const int64_t global_base = b * S + r * c + u * T;
+    const int64_t split = c - u * T;
+    const int64_t jump = (2 * rd - 1 - r) * c - c - r * c;
+    const int64_t shard_base = (int64_t)item * T;
+    if (P.kind == kZigzagFwd) {
+      m.src_base = global_base;
+      m.dst_base = shard_base;
+      m.src_jump = jump;
+    } else {
+      m.src_base = shard_base;
+      m.dst_base = global_base;
+      m.dst_jump = jump;
+    }
+    m.src_stride = m.dst_stride = 1;
+    m.split = split;
+  } else if (P.kind == kUlyssesFwd) {
+    const int64_t bs = P.p[0], L = P.p[1], hc = P.p[2], N = P.p[3], hb = P.p[4], Ls = P.p[5];
+    const int64_t u_fix = P.p[6];
+    int64_t rest = item;
+    const int64_t up = rest % N;
+    rest /= N;
+    const int64_t b = rest % bs;
+    rest /= bs;
+    const int64_t hp = rest % hb;
+    const int64_t g = rest / hb;
+    const int64_t u = u_fix < 0 ? g : u_fix;
+    m.dst_base = ((g * hb + hp) * bs + b) * L + up * Ls;
+    m.dst_stride = 1;
+    m.src_base = ((up * bs + b) * Ls) * hc + u * hb + hp;
+    m.src_stride = hc;
+  } else {  // kUlyssesInv
+    const int64_t bs = P.p[0], L = P.p[1], hc = P.p[2], N = P.p[3], hb = P.p[4], Ls = P.p[5];
+    const int64_t u_fix = P.p[6];
+    int64_t rest = item;
+    const int64_t hp = rest % hb;
+    rest /= hb;
+    const int64_t up = rest % N;
+    rest /= N;
+    const int64_t b = rest % bs;
+    const int64_t g = rest / bs;
+    const int64_t u = u_fix < 0 ? g : u_fix;
+    m.src_base = ((up * hb + hp) * bs + b) * L + u * Ls;
+    m.src_stride = 1;
+    m.dst_base = ((g * bs + b) * Ls) * hc + up * hb + hp;
+    m.dst_stride = hc;
+  }
+  return m;
+}
+
+__global__ __launch_bounds__(kThreads) void copy_rows_kernel(CopyPlan P) {
+  const uint32_t total = P.n_items * P.pieces_per_item;
+  for (uint32_t piece = blockIdx.x; piece < total; piece += gridDim.x) {
+    const uint32_t item = piece / P.pieces_per_item;
+    const uint32_t row0 = (piece - item * P.pieces_per_item) * P.rows_per_piece;
+    const uint32_t nrows = min(P.rows_per_piece, P.rows_per_item - row0);
+    const RowMap m = decode(P, item);
+    const uint32_t nvec = nrows * P.row_vecs;
+    for (uint32_t v0 = threadIdx.x; v0 < nvec; v0 += kThreads * kUnroll) {
+      u32x4 buf[kUnroll];
+      int64_t doff[kUnroll];
+#pragma unroll
+      for (int k = 0; k < kUnroll; ++k) {
+        const uint32_t idx = v0 + k * kThreads;
+        doff[k] = -1;
+        if (idx < nvec) {
+          uint32_t row, col;
+          if (P.row_vecs_shift < 31) {
+            row = idx >> P.row_vecs_shift;
+            col = idx & (P.row_vecs - 1);
+          } else {
+            row = idx / P.row_vecs;
+            col = idx - row * P.row_vecs;
+          }
+          const int64_t t = (int64_t)row0 + row;
+          const bool second = t >= m.split;
+          const int64_t srow = m.src_base + t * m.src_stride + (second ? m.src_jump : 0);
+          const int64_t drow = m.dst_base + t * m.dst_stride + (second ? m.dst_jump : 0);
+          buf[k] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4 *>(P.src + srow * (int64_t)P.row_bytes) + col);
+          doff[k] = drow * (int64_t)P.row_bytes + (int64_t)col * 16;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kUnroll; ++k) {
+        if (doff[k] >= 0) __builtin_nontemporal_store(buf[k], reinterpret_cast<u32x4 *>(P.dst + doff[k]));
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_copy(const CopyPlan &plan, hipStream_t stream) {
+  const uint64_t total = (uint64_t)plan.n_items * plan.pieces_per_item;
+  if (total == 0) return hipSuccess;
+  const uint32_t grid = (uint32_t)(total < 8192 ? total : 8192);
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(grid), dim3(kThreads), 0, stream, plan);
+  return hipGetLastError();
+}
+
+}  // namespace usp

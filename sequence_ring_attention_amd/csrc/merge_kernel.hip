@@ -1,0 +1,98 @@
+// LSE merge of a step's partial result into an accumulator, in place.
+//
+// "Context Parallel 与 Ulysses" (ml-interview blog), concepts section: two
+// partials combine as lse = log(e^lse1 + e^lse2) and
+// o = e^(lse1 - lse) o1 + e^(lse2 - lse) o2.  Evaluated in the shifted form
+// lse = M + log1p(e^(m - M)) with M the larger and m the smaller input, in
+// double precision, so the fp32 result is rounded once.  A partial with
+// lse = -inf (no visible key) is the identity; two of them give (0, -inf).
+//
+// All lanes that touch one row live in the same wavefront, so every lane has
+// read lse_acc[row] before the row's writer lane stores the new value.
+#include "usp_internal.h"
+
+namespace usp {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void lse_merge_kernel(float *o_acc, float *lse_acc,
+                                                             const float *o_step,
+                                                             const float *lse_step, int64_t rows,
+                                                             int32_t d4, int32_t rows_per_wave,
+                                                             int32_t lanes_per_row) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
+  const int sub = lane / lanes_per_row;  // row within the wave's group
+  const int col0 = lane - sub * lanes_per_row;
+  const bool active_lane = sub < rows_per_wave;
+  for (int64_t group = wave; group * rows_per_wave < rows; group += nwaves) {
+    const int64_t row = group * rows_per_wave + sub;
+    const bool live = active_lane && row < rows;
+    double l1 = -INFINITY, l2 = -INFINITY;
+    if (live) {
+      l1 = (double)lse_acc[row];
+      l2 = (double)lse_step[row];
+    }
+    const bool e1 = l1 == -INFINITY, e2 = l2 == -INFINITY;
+    double a1, a2, lse;
+    if (e1 && e2) {
+      a1 = 0.0;
+      a2 = 0.0;
+      lse = -INFINITY;
+    } else if (e2) {
+      a1 = 1.0;
+      a2 = 0.0;
+      lse = l1;
+    } else if (e1) {
+      a1 = 0.0;
+      a2 = 1.0;
+      lse = l2;
+    } else {
+      const double M = l1 > l2 ? l1 : l2;
+      const double w = exp((l1 > l2 ? l2 : l1) - M);  // in (0, 1]
+      lse = M + log1p(w);
+      const double big = 1.0 / (1.0 + w), small = w / (1.0 + w);
+      a1 = l1 > l2 ? big : small;
+      a2 = l1 > l2 ? small : big;
+    }
+    if (live) {
+      float4 *acc = reinterpret_cast<float4 *>(o_acc + row * (int64_t)d4 * 4);
+      const float4 *stp = reinterpret_cast<const float4 *>(o_step + row * (int64_t)d4 * 4);
+      for (int col = col0; col < d4; col += lanes_per_row) {
+        const float4 x = acc[col], y = stp[col];
+        float4 r;
+        r.x = (float)(a1 * (double)x.x + a2 * (double)y.x);
+        r.y = (float)(a1 * (double)x.y + a2 * (double)y.y);
+        r.z = (float)(a1 * (double)x.z + a2 * (double)y.z);
+        r.w = (float)(a1 * (double)x.w + a2 * (double)y.w);
+        acc[col] = r;
+      }
+    }
+    // every lane of this row read lse_acc[row] above (same wavefront, program order)
+    if (live && col0 == 0) lse_acc[row] = (float)lse;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_lse_merge(float *o_acc, float *lse_acc, const float *o_step,
+                            const float *lse_step, int64_t rows, int64_t head_dim,
+                            hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const int32_t d4 = (int32_t)(head_dim / 4);
+  int32_t rows_per_wave = 1, lanes_per_row = 64;
+  if (d4 <= 64 && 64 % d4 == 0) {
+    rows_per_wave = 64 / d4;
+    lanes_per_row = d4;
+  }
+  const int64_t groups = (rows + rows_per_wave - 1) / rows_per_wave;
+  int64_t blocks = (groups + 3) / 4;  // 4 waves per block
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(lse_merge_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, o_acc,
+                     lse_acc, o_step, lse_step, rows, d4, rows_per_wave, lanes_per_row);
+  return hipGetLastError();
+}
+
+}  // namespace usp

@@ -1,0 +1,82 @@
+// Internal launch interface between the C ABI (api.cpp) and the HIP kernels.
+// Host code validates every argument before calling a launcher; launchers
+// only size grids and enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace usp {
+
+// ---------------------------------------------------------------- copies --
+
+// A batch of 2D row copies.  Item i copies `rows_per_item` rows of
+// `row_bytes` bytes; rows of an item start at base offsets that depend on
+// the copy kind and advance by fixed strides, with at most one jump (the
+// zigzag share is two runs of positions).
+enum CopyKind : int32_t {
+  kZigzagFwd = 0,  // global (B,S,H,D) -> shards
+  kZigzagInv = 1,  // shards -> global
+  kUlyssesFwd = 2, // (N, bs, L/N, hc, hd) -> (G, hc/N, bs, L, hd)
+  kUlyssesInv = 3, // (N, hc/N, bs, L, hd) -> (G, bs, L/N, hc, hd)
+};
+
+struct CopyPlan {
+  const char *src;
+  char *dst;
+  int32_t kind;
+  uint32_t n_items;
+  uint32_t rows_per_item;
+  uint32_t row_vecs;        // 16-byte vectors per row
+  uint32_t row_vecs_shift;  // log2(row_vecs) when a power of two, else 31
+  uint32_t rows_per_piece;  // rows a workgroup copies per piece
+  uint32_t pieces_per_item;
+  uint64_t row_bytes;
+  // zigzag: B, S (rows), chunk c, rd, ud, shard rows T, fixed ranks (or -1)
+  // ulysses: bs, L, hc, N, hb = hc/N, Ls = L/N, fixed rank (or -1)
+  int64_t p[10];
+};
+
+hipError_t launch_copy(const CopyPlan &plan, hipStream_t stream);
+
+// ----------------------------------------------------------------- merge --
+
+hipError_t launch_lse_merge(float *o_acc, float *lse_acc, const float *o_step,
+                            const float *lse_step, int64_t rows, int64_t head_dim,
+                            hipStream_t stream);
+
+// ------------------------------------------------------------- attention --
+
+struct AttnArgs {
+  const void *q;
+  const void *k;
+  const void *v;
+  void *o;       // fp32 partial (Hq,B,L,D) or final in dtype with strides
+  float *lse;    // (Hq,B,L), or (cp,Hq,B,L) for every rank
+  int32_t B, Hq, Hkv, G;
+  int32_t L;     // share length 2c
+  int32_t c;     // chunk length
+  int32_t cp;
+  int32_t causal;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t kv_blk;
+  int64_t q_rank, o_rank;
+  float scale;       // softmax scale
+  float scale_log2;  // softmax scale * log2(e)
+  const int32_t *cu; // packed-sample boundaries or null
+  int32_t nseq;
+  int32_t ring_rank; // >= 0, or -1 for every rank
+  int32_t t_lo, t_hi; // ring steps to walk
+  int32_t partial;    // 1: write fp32 partial (o_step, lse_step)
+  int32_t n_qtiles;   // query tiles per share
+  int32_t n_ranks;    // ranks in this launch (1 or cp)
+  int32_t xcd_remap;  // 1: group blocks sharing a KV head on one XCD
+};
+
+hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t stream);
+hipError_t launch_attn_fp32(const AttnArgs &a, int head_dim, hipStream_t stream);
+
+}  // namespace usp

@@ -1,0 +1,118 @@
+"""One GPU's share of USP-Attention on a virtual (ud x rd) grid.
+
+The share of virtual GPU (ring rank r, Ulysses rank u) is, in the order of
+the "USP" paper review's Algorithms 1 and 2 (section 三):
+
+1. zigzag-extract its own Q, K, V shard from the global tensors;
+2. Ulysses layout (the all-to-all as a permutation) of Q, K, V to head-major
+   (hc/ud, bs, 2c, hd) for its head block u;
+3. the ring walk over the cp KV blocks with the fused LSE merge, writing O
+   (bf16) and lse;
+4. the inverse Ulysses layout of O back to its (bs, 2c/ud, hc, hd) shard.
+
+On a real grid the peers' pieces arrive over the interconnect: the other
+Ulysses ranks' shards and outputs (all-to-all) and the other ring ranks' KV
+blocks (ring P2P).  Here they are produced once by ``prepare_peers`` with
+the same kernels, outside ``step``; ``step`` is exactly the per-GPU work.
+
+This module only allocates buffers and sequences C-ABI calls.
+"""
+import torch
+
+from . import binding as B
+
+
+class OneGpuShare:
+    def __init__(self, Q, K, V, rd, ud, ring_rank, ulysses_rank, causal=True, cu_seqlens=None):
+        """Q (B, S, H, D), K/V (B, S, Hkv, D): global tensors on the GPU."""
+        self.Q, self.K, self.V = Q, K, V
+        self.rd, self.ud, self.r, self.u = rd, ud, ring_rank, ulysses_rank
+        Bn, S, H, D = Q.shape
+        Hkv = K.shape[2]
+        if H % ud or Hkv % ud or S % (2 * rd * ud):
+            raise ValueError("grid does not divide the problem")
+        self.Bn, self.S, self.H, self.Hkv, self.D = Bn, S, H, Hkv, D
+        self.T, self.L = S // (rd * ud), S // rd
+        self.causal, self.cu = causal, cu_seqlens
+        dev, dt = Q.device, Q.dtype
+        T, L = self.T, self.L
+        e = lambda *s: torch.empty(*s, dtype=dt, device=dev)
+        # group shards of ring group r (slot u is ours, the others are the peers')
+        self.qz, self.kz, self.vz = e(ud, Bn, T, H, D), e(ud, Bn, T, Hkv, D), e(ud, Bn, T, Hkv, D)
+        # head-major Q of every Ulysses rank in the group, and the ring's KV
+        # blocks (block j = ring rank j's share) for every head block
+        self.qh = e(ud, H // ud, Bn, L, D)
+        self.kh = e(ud, rd, Hkv // ud, Bn, L, D)
+        self.vh = e(ud, rd, Hkv // ud, Bn, L, D)
+        # outputs of every Ulysses rank of the group, and lse
+        self.oh = e(ud, H // ud, Bn, L, D)
+        self.lse = torch.empty(ud, H // ud, Bn, L, dtype=torch.float32, device=dev)
+        self.out = e(Bn, T, H, D)     # this GPU's output shard after the inverse layout
+        self._descs = {}
+
+    def desc(self, u):
+        if u not in self._descs:
+            self._descs[u] = B.attn_desc(self.S, self.rd, self.qh[u], self.kh[u], self.vh[u], o=self.oh[u],
+                                         layout="hbsd", causal=self.causal, cu_seqlens=self.cu)
+        return self._descs[u]
+
+    # ------------------------------------------------------------ pieces --
+    def _kv_blocks(self, r, u, scratch_k, scratch_v):
+        """Ring rank r's K/V head block u, head-major, into the ring slots."""
+        B.usp_zigzag_extract(self.K, scratch_k, self.rd, self.ud, r, -1)
+        B.usp_zigzag_extract(self.V, scratch_v, self.rd, self.ud, r, -1)
+        B.usp_ulysses_a2a_layout(scratch_k, self.kh[u, r], self.ud, u)
+        B.usp_ulysses_a2a_layout(scratch_v, self.vh[u, r], self.ud, u)
+
+    def _walk(self, u):
+        B.usp_attn_fwd(self.qh[u], self.kh[u], self.vh[u], self.oh[u], self.lse[u], self.desc(u), self.r)
+
+    def prepare_peers(self):
+        """Everything the peers would send: other ring ranks' KV blocks (all
+        head blocks), the group's other shards, and the other Ulysses ranks'
+        outputs."""
+        sk = torch.empty_like(self.kz)
+        sv = torch.empty_like(self.vz)
+        for u in range(self.ud):
+            for r in range(self.rd):
+                self._kv_blocks(r, u, sk, sv)
+        B.usp_zigzag_extract(self.Q, self.qz, self.rd, self.ud, self.r, -1)
+        B.usp_zigzag_extract(self.K, self.kz, self.rd, self.ud, self.r, -1)
+        B.usp_zigzag_extract(self.V, self.vz, self.rd, self.ud, self.r, -1)
+        for u in range(self.ud):
+            if u != self.u:
+                B.usp_ulysses_a2a_layout(self.qz, self.qh[u], self.ud, u)
+                self._walk(u)
+
+    def step(self, marks=None):
+        """The per-GPU hot path: extract, layout, ring walk, inverse layout.
+
+        ``marks``: optional 5 events recorded on the current stream around
+        the four phases (for per-kernel timing)."""
+        r, u, rd, ud = self.r, self.u, self.rd, self.ud
+        mark = (lambda i: marks[i].record()) if marks is not None else (lambda i: None)
+        mark(0)
+        B.usp_zigzag_extract(self.Q, self.qz[u], rd, ud, r, u)
+        B.usp_zigzag_extract(self.K, self.kz[u], rd, ud, r, u)
+        B.usp_zigzag_extract(self.V, self.vz[u], rd, ud, r, u)
+        mark(1)
+        B.usp_ulysses_a2a_layout(self.qz, self.qh[u], ud, u)
+        B.usp_ulysses_a2a_layout(self.kz, self.kh[u, r], ud, u)
+        B.usp_ulysses_a2a_layout(self.vz, self.vh[u, r], ud, u)
+        mark(2)
+        self._walk(u)
+        mark(3)
+        B.usp_ulysses_a2a_layout(self.oh, self.out, ud, u, inverse=True)
+        mark(4)
+        return self.out
+
+    # ------------------------------------------------------- accounting --
+    def copy_bytes(self):
+        """Bytes each copy phase of one step reads plus writes (every element
+        once): zigzag extract of Q, K, V; forward layout of Q, K, V; inverse
+        layout of O.  A shard of Q holds as many elements as one Ulysses head
+        block of the 2c-token share."""
+        e = self.Q.element_size()
+        q = self.T * self.H * self.D * self.Bn * e
+        kv = self.T * self.Hkv * self.D * self.Bn * e
+        return 2 * (q + 2 * kv), 2 * (q + 2 * kv), 2 * q

@@ -1,0 +1,95 @@
+"""Shared helpers of the GPU parity tests: device setup, zigzag shares built
+with the oracle's positions, and the tolerance checks of the parity bar.
+
+Tolerances (floating point): bf16 inputs -- o max-abs <= 1e-2, o mean-abs <=
+1e-3, lse max-abs <= 1e-3; fp32 inputs -- o max-abs <= 2e-5, o mean-abs <=
+1e-6, lse max-abs <= 1e-6.  Rows with no visible key must carry lse = -inf
+on both sides.  Index and layout work must be bit-exact.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import index as ix
+
+TOL = {"bf16": (1e-2, 1e-3, 1e-3), "fp32": (2e-5, 1e-6, 1e-6)}
+
+
+def device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def say(*msg):
+    """Name the case before a GPU step, flushed, so a failing run says where it was."""
+    print("[case]", *msg, flush=True)
+    sys.stdout.flush()
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def bits(t):
+    """Raw bits of a CPU/GPU tensor as a numpy integer array (bf16 -> int16)."""
+    t = t.detach().cpu()
+    return t.view(torch.int16).numpy() if t.dtype == torch.bfloat16 else t.view(torch.int32).numpy()
+
+
+def share_positions(S, rd):
+    return [ix.zigzag_share_positions(S, rd, r) for r in range(rd)]
+
+
+def shares(X, rd):
+    """(B, S, H, D) -> (rd, B, S/rd, H, D): every ring rank's zigzag share,
+    gathered with the oracle's positions (a library gather, no method math)."""
+    S = X.shape[1]
+    idx = torch.from_numpy(np.concatenate(share_positions(S, rd))).to(X.device)
+    g = X.index_select(1, idx)
+    return g.view(X.shape[0], rd, S // rd, *X.shape[2:]).transpose(0, 1).contiguous()
+
+
+def check_close(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what=""):
+    """o arrays in the same layout; lse arrays in the same layout."""
+    omax_tol, omean_tol, lse_tol = TOL[dtype]
+    o_gpu = np.asarray(o_gpu, dtype=np.float64)
+    o_ref = np.asarray(o_ref, dtype=np.float64)
+    lse_gpu = np.asarray(lse_gpu, dtype=np.float64)
+    lse_ref = np.asarray(lse_ref, dtype=np.float64)
+    assert o_gpu.shape == o_ref.shape and lse_gpu.shape == lse_ref.shape
+    assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite o"
+    ninf_g, ninf_r = np.isneginf(lse_gpu), np.isneginf(lse_ref)
+    assert np.array_equal(ninf_g, ninf_r), f"{what}: -inf rows differ"
+    assert not np.any(np.isnan(lse_gpu)), f"{what}: NaN lse"
+    d = np.abs(o_gpu - o_ref)
+    dl = np.abs(np.where(ninf_r, 0.0, lse_gpu - np.where(ninf_r, 0.0, lse_ref)))
+    stats = dict(o_max=float(d.max()), o_mean=float(d.mean()), lse_max=float(dl.max()) if dl.size else 0.0)
+    assert stats["o_max"] <= omax_tol, f"{what}: {stats}"
+    assert stats["o_mean"] <= omean_tol, f"{what}: {stats}"
+    assert stats["lse_max"] <= lse_tol, f"{what}: {stats}"
+    return stats
+
+
+def guarded(shape, dtype, dev, fill=0):
+    """A tensor followed by a canary tail; returns (view, check_fn)."""
+    n = int(np.prod(shape))
+    tail = 4096
+    buf = torch.full((n + tail,), fill, dtype=dtype, device=dev)
+    canary = torch.full((tail,), -7, dtype=dtype, device=dev)
+    buf[n:] = canary
+
+    def intact():
+        return bool(torch.equal(buf[n:], canary))
+    return buf[:n].view(shape), intact
+
+
+def sample_rows(L, c, n_random, seed, extra=()):
+    """Local row indices: the edges of both chunks, optional extra rows and a
+    seeded random set."""
+    rng = np.random.default_rng(seed)
+    base = {0, 1, c - 1, c, c + 1, L - 2, L - 1, *extra}
+    base |= set(rng.choice(L, size=min(n_random, L), replace=False).tolist())
+    return np.array(sorted(i for i in base if 0 <= i < L))

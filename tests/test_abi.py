@@ -1,0 +1,148 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+and the host-side validation rejects bad arguments before any launch.
+
+Error-path calls pass fake (but aligned) addresses that validation must
+reject; they are skipped where a GPU is visible so that a validation bug can
+never turn into a launch on real hardware.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from sequence_ring_attention_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "usp.h")
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="fake-pointer error paths run on CPU only")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:usp_status|const char \*|int32_t)\s*(usp_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert len(names) == 8, names
+    lib = B.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(B.EXPORTED)
+
+
+def test_abi_version_and_status_strings():
+    lib = B.lib()
+    assert lib.usp_abi_version() == 1
+    assert lib.usp_status_string(0) == b"USP_OK"
+    assert lib.usp_status_string(2) == b"USP_ERR_UNSUPPORTED"
+    assert lib.usp_status_string(99) == b"USP_ERR_UNKNOWN"
+
+
+FAKE = 0x10000      # aligned, never dereferenced: validation must reject first
+FAKE2 = 0x20000
+FAKE3 = 0x30000
+
+
+def _zz(**kw):
+    a = dict(x=FAKE, out=FAKE2, dtype=0, B=1, S=64, H=2, D=64, rd=4, ud=1, r=0, u=0, inv=0)
+    a.update(kw)
+    return B.lib().usp_zigzag_extract(a["x"], a["out"], a["dtype"], a["B"], a["S"], a["H"], a["D"],
+                                      a["rd"], a["ud"], a["r"], a["u"], a["inv"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(x=FAKE + 2), 1), (dict(out=FAKE), 1), (dict(dtype=7), 1),
+    (dict(S=60), 1), (dict(rd=0), 1), (dict(r=4), 1), (dict(u=1), 1), (dict(r=-1, u=0), 1),
+    (dict(inv=2), 1), (dict(H=1, D=2, dtype=0), 2), (dict(B=0), 1),
+])
+def test_zigzag_rejects(kw, status):
+    assert _zz(**kw) == status
+    assert B.lib().usp_last_error_detail()
+
+
+def _uly(**kw):
+    a = dict(i=FAKE, o=FAKE2, dtype=0, B=1, L=64, H=4, D=64, N=2, u=0, inv=0)
+    a.update(kw)
+    return B.lib().usp_ulysses_a2a_layout(a["i"], a["o"], a["dtype"], a["B"], a["L"], a["H"], a["D"],
+                                          a["N"], a["u"], a["inv"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(i=None), 1), (dict(o=FAKE + 8), 1), (dict(o=FAKE), 1), (dict(H=3), 1), (dict(L=63), 1),
+    (dict(u=2), 1), (dict(u=-2), 1), (dict(N=0), 1), (dict(D=4), 2), (dict(inv=-1), 1),
+])
+def test_ulysses_rejects(kw, status):
+    assert _uly(**kw) == status
+
+
+@no_gpu
+def test_merge_rejects():
+    lib = B.lib()
+    assert lib.usp_lse_merge(FAKE, FAKE2, FAKE3, FAKE, -1, 64, None) == 1
+    assert lib.usp_lse_merge(FAKE, FAKE2, FAKE3, FAKE, 4, 6, None) == 1
+    assert lib.usp_lse_merge(None, FAKE2, FAKE3, FAKE, 4, 64, None) == 1
+    assert lib.usp_lse_merge(FAKE + 4, FAKE2, FAKE3, FAKE, 4, 64, None) == 1
+    assert lib.usp_lse_merge(None, None, None, None, 0, 64, None) == 0    # rows = 0: no-op
+
+
+def _desc(**kw):
+    d = B.UspAttnDesc()
+    d.batch, d.seq_len, d.num_q_heads, d.num_kv_heads, d.head_dim = 1, 256, 4, 2, 128
+    d.dtype, d.softmax_scale, d.causal, d.cp = 0, 128 ** -0.5, 1, 4
+    d.q = B.UspStrides(64 * 4 * 128, 4 * 128, 128)
+    d.k = B.UspStrides(64 * 2 * 128, 2 * 128, 128)
+    d.v = B.UspStrides(64 * 2 * 128, 2 * 128, 128)
+    d.o = B.UspStrides(64 * 4 * 128, 4 * 128, 128)
+    d.kv_block_stride = 64 * 2 * 128
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(seq_len=250), 1), (dict(num_q_heads=3), 1), (dict(head_dim=96), 2), (dict(head_dim=32), 2),
+    (dict(softmax_scale=0.0), 1), (dict(softmax_scale=float("inf")), 1), (dict(cp=0), 1),
+    (dict(causal=2), 1), (dict(dtype=5), 1), (dict(cu_seqlens=FAKE, num_seqs=2, causal=0), 2),
+    (dict(cu_seqlens=FAKE, num_seqs=0), 1), (dict(kv_block_stride=3), 1),
+    (dict(q=B.UspStrides(1, 4 * 128, 128)), 1), (dict(batch=0), 1),
+])
+def test_attention_descriptor_rejects(kw, status):
+    lib = B.lib()
+    d = _desc(**kw)
+    assert lib.usp_ring_attn_step_fwd(FAKE, FAKE2, FAKE3, FAKE, FAKE2, ctypes.byref(d), 0, 0, None) == status
+    assert lib.usp_attn_fwd(FAKE, FAKE2, FAKE3, FAKE, FAKE2, ctypes.byref(d), 0, None) == status
+
+
+@no_gpu
+def test_attention_rank_and_step_ranges():
+    lib = B.lib()
+    d = _desc()
+    step = lambda r, t: lib.usp_ring_attn_step_fwd(FAKE, FAKE2, FAKE3, FAKE, FAKE2, ctypes.byref(d), r, t, None)
+    assert step(4, 0) == 1 and step(-1, 0) == 1 and step(0, 4) == 1 and step(0, -1) == 1
+    walk = lambda r: lib.usp_attn_fwd(FAKE, FAKE2, FAKE3, FAKE, FAKE2, ctypes.byref(d), r, None)
+    assert walk(4) == 1 and walk(-2) == 1
+    assert lib.usp_attn_fwd(FAKE, FAKE2, FAKE3, FAKE, FAKE2, None, 0, None) == 1
+    assert lib.usp_attn_fwd(None, FAKE2, FAKE3, FAKE, FAKE2, ctypes.byref(d), 0, None) == 1
+
+
+@no_gpu
+def test_valid_arguments_reach_the_runtime_and_report_hip_errors():
+    """With no GPU present, a call that passes validation fails at launch with
+    USP_ERR_HIP and a message, never a crash."""
+    lib = B.lib()
+    assert _zz() == 3
+    assert b"launch" in lib.usp_last_error_detail()
+
+
+def test_binding_refuses_host_tensors():
+    x = torch.zeros(1, 64, 2, 64, dtype=torch.bfloat16)
+    out = torch.zeros(1, 16, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        B.usp_zigzag_extract(x, out, 4, 1, 0, 0)
