@@ -41,7 +41,7 @@ def parse():
     p.add_argument("--ring-rank", type=int, default=0)
     p.add_argument("--ulysses-rank", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=96, help="query rows of the oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=384, help="query rows of the oracle sample")
     return p.parse_args()
 
 

@@ -131,7 +131,15 @@ def test_lse_merge(rows, D):
     B.usp_lse_merge(acc, lacc, o2.to(dev), l2.to(dev))
     torch.cuda.synchronize()
     assert ok1() and ok2()
-    check_close(f64(acc), f64(lacc), ro, rl, "fp32", "merge")
+    # The kernel evaluates the merge in double and rounds once to fp32, so each
+    # output is within one fp32 ulp of the exact merge (inputs reach |lse| = 80
+    # here, where an absolute 1e-6 bar would be below half an ulp).
+    go, gl = f64(acc), f64(lacc)
+    assert np.array_equal(np.isneginf(gl), np.isneginf(rl))
+    fin = ~np.isneginf(rl)
+    assert np.all(np.abs(gl[fin] - rl[fin]) <= np.spacing(np.abs(rl[fin]).astype(np.float32)))
+    assert np.all(np.abs(go - ro) <= np.spacing(np.maximum(np.abs(ro), 1e-30).astype(np.float32)) * 1.5)
+    assert np.all(go[np.isneginf(rl)] == 0)
 
 
 # -------------------------------------------------------------- attention --
