@@ -42,7 +42,23 @@ def parse():
     p.add_argument("--ulysses-rank", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=384, help="query rows of the oracle sample")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="only run a plain device copy of this many MiB (for scaling HBM byte counters)")
     return p.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain torch device-to-device copy of known size, three times; its
+    FETCH_SIZE / WRITE_SIZE counters give the factor between counted and
+    moved bytes."""
+    import torch
+    n = mib * 2**20 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}))
 
 
 def kernel_source_hash():
@@ -103,6 +119,9 @@ def main():
         print(f"bench.py measures one GPU's share on a single MI355X; --gpus {args.gpus} is not "
               "supported (no multi-GPU path in this build).", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return
     import torch
     from sequence_ring_attention_amd import inputs
     from sequence_ring_attention_amd.pipeline import OneGpuShare
