@@ -22,12 +22,28 @@
 //     and 16 of its keys per 32-key block, so the row max needs a single
 //     exchange with the partner lane (lane ^ 32), and the rescale of O is a
 //     per-lane scalar;
-//   * O^T += V^T P^T with V^T from LDS (transposed while staging) and P (the
-//     probabilities rounded to bf16) straight from the S^T registers as the
-//     N operand: the K-row order of the first product is permuted so that
-//     each lane's eight bf16 probabilities are eight consecutive keys.
-//   * K and V tiles of 64 keys are staged global -> registers -> LDS; the
-//     next tile's global loads are issued before the current tile's math.
+//   * O^T += V^T P^T with P (the probabilities rounded to bf16) straight
+//     from the S^T registers as the N operand: the K-row order of the first
+//     product is permuted so that each lane's eight bf16 probabilities are
+//     eight consecutive keys.  V stays row-major in LDS and is read
+//     transposed into the M operand with ds_read_b64_tr_b16 (each 16-lane
+//     group turns four 4-lane row reads into one column per lane);
+//   * K and V tiles of 64 keys go global -> LDS directly with buffer loads
+//     (buffer_load_dwordx4 ... lds: each lane's 16 bytes land at the wave's
+//     LDS base + 16 * lane, no registers involved).  A buffer descriptor per
+//     KV block carries the block's exact byte extent, so no load can leave
+//     the block; per-lane offsets are loop invariant and the tile offset is a
+//     scalar.  Two LDS stages: the next tile is in flight while the current
+//     one is computed, each tile costs one barrier, and the loop is unrolled
+//     over the two stages so every LDS operand read uses an immediate offset
+//     on a per-lane base computed once.  The 16-byte chunks of every key row
+//     are XOR-swizzled by the row index, chosen so that the K operand reads
+//     (16 rows, one chunk) and the transposed V reads (4 rows, two chunks)
+//     hit distinct banks;
+//   * the running max is only moved (and O rescaled) when a tile's max
+//     exceeds it by more than 2^8: below that the probabilities are computed
+//     against the stale max, which changes nothing but the reference point of
+//     the final division (o = O / l and lse = m + log l stay exact).
 //
 // Grid order: heaviest query tiles first (the last rows of a share see the
 // most keys), and the Hq / Hkv query heads that read one KV head run back to
@@ -46,14 +62,57 @@ constexpr int BM = 128;  // query rows per workgroup
 constexpr int BN = 64;   // keys per tile
 constexpr int NT = 256;  // threads per workgroup
 
+constexpr float TAU = 8.0f;  // log2 headroom before the running max must move
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int RSRC_WORD3 = 0x00020000;  // raw (untyped) buffer descriptor, gfx9 family
+
+template <int S>
+struct StageTag {
+  static constexpr int value = S;
+};
+
 template <int D>
 struct Lds {
-  static constexpr int K_ROW = D * 2 + 16;   // bytes per key row, padded against bank conflicts
-  static constexpr int V_ROW = BN * 2 + 16;  // bytes per head-dim row of V^T, padded
-  static constexpr int K_BYTES = BN * K_ROW;
-  static constexpr int V_BYTES = D * V_ROW;
-  static constexpr int BYTES = K_BYTES + V_BYTES;
+  static constexpr int ROW = D * 2;               // bytes per key row (K and V alike)
+  static constexpr int CH = D / 8;                // 16-byte chunks per row
+  static constexpr int TILE = BN * ROW;           // one K or V tile
+  static constexpr int STAGE = 2 * TILE;          // K then V
+  static constexpr int BYTES = 2 * STAGE;         // double buffered
+  static constexpr int KEYS_PER_KIB = 1024 / ROW; // rows one wave-wide direct load fills
+  static constexpr int KIB_PER_TILE = TILE / 1024;
 };
+
+// Physical 16-byte chunk of logical chunk `ch` in key row `key`.  The XOR
+// mask is a permutation of the low row bits onto chunk bits.  D = 128
+// (256-byte rows, one bank sweep each): the 16 rows one K read touches get 16
+// distinct masks, and the 4 rows of a transposed V read (row bits 0 and 1)
+// move whole 4-chunk groups (chunk bits 2 and 3), so 32 lanes reading 4 rows
+// x 4 chunks cover 16 distinct chunk slots.  D = 64 (two rows per sweep):
+// the row parity picks the half sweep and row bits 1..3 are permuted, bit 1
+// onto chunk bit 2.
+template <int D>
+__device__ inline int swz(int key, int ch) {
+  if (D == 128) {
+    const int f = ((key & 1) << 2) | ((key & 2) << 2) | ((key >> 2) & 1) | (((key >> 3) & 1) << 1);
+    return ch ^ f;
+  } else {
+    const int f = (((key >> 1) & 1) << 2) | ((key >> 2) & 1) | (((key >> 3) & 1) << 1);
+    return ch ^ f;
+  }
+}
+
+// Lane l and lane l ^ 32 exchange a value (one VALU op, no LDS round trip).
+__device__ inline float partner_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float partner_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Global position of local index i of ring rank `rank`'s share.
 __device__ inline int share_pos(int rank, int i, int c, int cp) {
@@ -77,8 +136,43 @@ __device__ inline int seg_start(const int32_t *cu, int nseq, int pos) {
   return cu[lo];
 }
 
-__device__ inline uint32_t lo16(uint32_t w) { return w & 0xffffu; }
-__device__ inline uint32_t hi16(uint32_t w) { return w >> 16; }
+
+// Issue one K tile and one V tile (64 keys each) from KV block base
+// pointers into an LDS stage with buffer loads straight to LDS.  Wave w fills
+// KiB blocks w, w + 4, ...; lane l of a block writes 16 bytes at block base +
+// 16 l, so its per-lane offset (kvoff / vvoff) names the logical chunk that
+// the swizzle places there.  When the share ends inside the tile, rows past
+// it repeat the last row (their logits are masked, probabilities zero).
+template <int D>
+__device__ inline void issue_kv_tile(char *stage, const char *kblk, const char *vblk, uint32_t k_extent,
+                                     uint32_t v_extent, int64_t kbytes, int64_t vbytes, int k0, int L, int wave,
+                                     int lane, const uint32_t *kvoff, const uint32_t *vvoff) {
+  constexpr int CH = Lds<D>::CH;
+  constexpr int NBLK = Lds<D>::KIB_PER_TILE / 4;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kblk), 0, k_extent, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vblk), 0, v_extent, RSRC_WORD3);
+  char *const sK = stage;
+  char *const sV = stage + Lds<D>::TILE;
+  if (k0 + BN <= L) {
+    const uint32_t ks = (uint32_t)(k0 * kbytes), vs = (uint32_t)(k0 * vbytes);
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(sK + (wave + 4 * i) * 1024), 16, kvoff[i], ks, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(sV + (wave + 4 * i) * 1024), 16, vvoff[i], vs, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i) {
+      const int row = (wave + 4 * i) * Lds<D>::KEYS_PER_KIB + lane / CH;
+      const int lch = swz<D>(row, lane % CH);
+      const int key = min(k0 + row, L - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(sK + (wave + 4 * i) * 1024), 16,
+                                               (uint32_t)(key * kbytes + lch * 16), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(sV + (wave + 4 * i) * 1024), 16,
+                                               (uint32_t)(key * vbytes + lch * 16), 0, 0, 0);
+    }
+  }
+}
 
 // The key range of block j one query tile can see, in 64-key tiles.
 struct StepRange {
@@ -87,9 +181,7 @@ struct StepRange {
 
 template <int D, bool PARTIAL>
 __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[Lds<D>::BYTES];
-  char *const sK = smem;
-  char *const sV = smem + Lds<D>::K_BYTES;
+  __shared__ __attribute__((aligned(1024))) char smem[Lds<D>::BYTES];
 
   // ---------------------------------------------------------- work item --
   const int bid = blockIdx.x;
@@ -116,6 +208,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnArgs a) {
   }
   const int hq = kvh * a.G + g;
   const int c = a.c, cp = a.cp, L = a.L;
+  const bool causal = a.causal != 0, packed = a.cu != nullptr;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -165,58 +258,48 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnArgs a) {
   StepRange cur = step_range(t);
   while (cur.kt >= cur.ke && ++t < a.t_hi) cur = step_range(t);
 
-  // ------------------------------------------------------- staging regs --
-  constexpr int KCH = D / 8;                  // 16-byte chunks per key row
-  constexpr int KROWS = NT / KCH;             // key rows per pass
-  constexpr int KPASS = BN / KROWS;           // passes per tile
-  constexpr int VITEMS = (BN / 4) * KCH;      // (4 keys x 8 dims) items of V
-  uint4 kreg[KPASS];
-  uint4 vreg[4];
+  // ------------------------------------------------ global -> LDS tiles --
+  // per-lane byte offsets (within a tile) of the direct loads; see issue_kv_tile
+  constexpr int CH = Lds<D>::CH;
+  constexpr int NBLK = Lds<D>::KIB_PER_TILE / 4;  // KiB blocks per wave per tile
+  const int64_t kbytes = a.k_ss * 2, vbytes = a.v_ss * 2;
+  uint32_t kvoff[NBLK], vvoff[NBLK];
+#pragma unroll
+  for (int i = 0; i < NBLK; ++i) {
+    const int row = (wave + 4 * i) * Lds<D>::KEYS_PER_KIB + lane / CH;
+    const int lch = swz<D>(row, lane % CH);
+    kvoff[i] = (uint32_t)(row * kbytes + lch * 16);
+    vvoff[i] = (uint32_t)(row * vbytes + lch * 16);
+  }
+  const char *const kbase = static_cast<const char *>(a.k) + 2 * (b * a.k_sb + kvh * a.k_sh);
+  const char *const vbase = static_cast<const char *>(a.v) + 2 * (b * a.v_sb + kvh * a.v_sh);
+  const uint32_t k_extent = (uint32_t)((L - 1) * kbytes + 2 * D);
+  const uint32_t v_extent = (uint32_t)((L - 1) * vbytes + 2 * D);
+  auto issue_tile = [&](int j, int k0, int stg) {
+    issue_kv_tile<D>(smem + stg * Lds<D>::STAGE, kbase + 2 * j * a.kv_blk, vbase + 2 * j * a.kv_blk, k_extent,
+                     v_extent, kbytes, vbytes, k0, L, wave, lane, kvoff, vvoff);
+  };
+  auto wait_tiles = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
-  auto load_tile = [&](int j, int k0) {
-    const __bf16 *kb = static_cast<const __bf16 *>(a.k) + j * a.kv_blk + b * a.k_sb + kvh * a.k_sh;
-    const __bf16 *vb = static_cast<const __bf16 *>(a.v) + j * a.kv_blk + b * a.v_sb + kvh * a.v_sh;
+  // Per-lane LDS byte offsets of the MFMA operand reads, relative to a tile.
+  // K operand: row 32*kb + sig, logical chunk 2*ks + hh (rows sig and 32 + sig
+  // share the swizzle mask).  V operand (transposed reads): lane 16*g + 4*r + q
+  // reads row 16*p + 8*(g/2) + 4*e + r at dims 32*mb + 16*(g%2) + 4q .. +3;
+  // the mask depends on the row mod 16 only, so p moves by whole 16-row blocks.
+  const int sig = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
+  int koff[D / 16];
 #pragma unroll
-    for (int p = 0; p < KPASS; ++p) {
-      const int key = k0 + p * KROWS + tid / KCH;
-      kreg[p] = key < L ? *reinterpret_cast<const uint4 *>(kb + (int64_t)key * a.k_ss + (tid % KCH) * 8)
-                        : uint4{0, 0, 0, 0};
-    }
-    if (tid < VITEMS) {
-      const int kg = tid % (BN / 4), ch = tid / (BN / 4);
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = sig * Lds<D>::ROW + swz<D>(sig, 2 * ks + hh) * 16;
+  const int tg = lane >> 4, tr = (lane >> 2) & 3, tq = lane & 3;
+  int voff[D / 32][2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = k0 + 4 * kg + i;
-        vreg[i] = key < L ? *reinterpret_cast<const uint4 *>(vb + (int64_t)key * a.v_ss + ch * 8)
-                          : uint4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&]() {
+  for (int mb = 0; mb < D / 32; ++mb) {
 #pragma unroll
-    for (int p = 0; p < KPASS; ++p) {
-      const int key = p * KROWS + tid / KCH;
-      *reinterpret_cast<uint4 *>(sK + key * Lds<D>::K_ROW + (tid % KCH) * 16) = kreg[p];
+    for (int e = 0; e < 2; ++e) {
+      const int row = 8 * (tg >> 1) + 4 * e + tr;
+      voff[mb][e] = row * Lds<D>::ROW + swz<D>(row, 4 * mb + 2 * (tg & 1) + (tq >> 1)) * 16 + (tq & 1) * 8;
     }
-    if (tid < VITEMS) {
-      const int kg = tid % (BN / 4), ch = tid / (BN / 4);
-      const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-      const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
-      const uint32_t w2[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
-      const uint32_t w3[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        // dims 2m (low halves) and 2m+1 (high halves) of keys 4kg .. 4kg+3
-        uint2 even, odd;
-        even.x = lo16(w0[m]) | (lo16(w1[m]) << 16);
-        even.y = lo16(w2[m]) | (lo16(w3[m]) << 16);
-        odd.x = hi16(w0[m]) | (hi16(w1[m]) << 16);
-        odd.y = hi16(w2[m]) | (hi16(w3[m]) << 16);
-        *reinterpret_cast<uint2 *>(sV + (ch * 8 + 2 * m) * Lds<D>::V_ROW + kg * 8) = even;
-        *reinterpret_cast<uint2 *>(sV + (ch * 8 + 2 * m + 1) * Lds<D>::V_ROW + kg * 8) = odd;
-      }
-    }
-  };
+  }
 
   // --------------------------------------------------------- main loop --
   f32x16 O[D / 32];
@@ -224,103 +307,117 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnArgs a) {
   for (int mb = 0; mb < D / 32; ++mb) O[mb] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
   const float sl2 = a.scale_log2;
-  // M-row -> key permutation of the K operand (swap bits 2 and 3), so that
-  // accumulator register r of lane half hh holds key 16*(r/8) + 8*hh + r%8.
-  const int sig = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
 
-  if (t < a.t_hi) load_tile(cur.j, cur.kt * BN);
-  while (t < a.t_hi) {
-    // the next tile of the walk (wave-uniform)
-    int nt = t;
+  // next tile of the walk after `x` (workgroup-uniform); `tx` is its step
+  auto advance = [&](int &tx, StepRange &x) {
+    ++x.kt;
+    while (x.kt >= x.ke && ++tx < a.t_hi) x = step_range(tx);
+  };
+
+  // One tile on LDS stage STG (a compile-time constant, so every operand
+  // read below is a per-lane base plus an immediate offset).
+  auto body = [&](auto stage_tag) {
+    constexpr int STG = decltype(stage_tag)::value;
+    // the next tile goes into the other stage while this one is computed
+    int t_nxt = t;
     StepRange nxt = cur;
-    ++nxt.kt;
-    while (nxt.kt >= nxt.ke && ++nt < a.t_hi) nxt = step_range(nt);
+    advance(t_nxt, nxt);
+    if (t_nxt < a.t_hi) issue_tile(nxt.j, nxt.kt * BN, STG ^ 1);
 
-    store_tile();
-    __syncthreads();
-    if (nt < a.t_hi) load_tile(nxt.j, nxt.kt * BN);
-
+    const char *const sK = smem + STG * Lds<D>::STAGE;
+    const char *const sV = sK + Lds<D>::TILE;
     const int j = cur.j;
     const int k0 = cur.kt * BN;
     // tile class: every (query, key) pair of the workgroup visible?
     const int klast = min(k0 + BN, L) - 1;
     const int kpos_min = share_pos(j, k0, c, cp);
     const int kpos_max = share_pos(j, klast, c, cp);
-    bool full = (k0 + BN <= L);
-    if (a.causal) full = full && kpos_max <= qpos_min;
-    if (a.cu) full = full && kpos_min >= sst_max;
+    const bool full = __builtin_amdgcn_readfirstlane(
+        (k0 + BN <= L) & (!causal | (kpos_max <= qpos_min)) & (!packed | (kpos_min >= sst_max)));
 
     // S^T = K Q^T for two 32-key blocks
     f32x16 S0 = f32x16{}, S1 = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(sK + sig * Lds<D>::K_ROW + (16 * ks + 8 * hh) * 2);
-      const bf16x8 kb = *reinterpret_cast<const bf16x8 *>(sK + (32 + sig) * Lds<D>::K_ROW + (16 * ks + 8 * hh) * 2);
+      const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(sK + koff[ks]);
+      const bf16x8 kb = *reinterpret_cast<const bf16x8 *>(sK + koff[ks] + 32 * Lds<D>::ROW);
       S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], S0, 0, 0, 0);
       S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[ks], S1, 0, 0, 0);
     }
 
-    if (!full) {
+    if (!full) {  // diagonal, sample-boundary or ragged tile: elementwise mask
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kl = 16 * (r / 8) + 8 * hh + (r % 8);
         const int kk0 = k0 + kl, kk1 = k0 + 32 + kl;
         const int p0 = share_pos(j, kk0, c, cp), p1 = share_pos(j, kk1, c, cp);
-        bool v0 = kk0 < L, v1 = kk1 < L;
-        if (a.causal) {
-          v0 = v0 && p0 <= my_qpos;
-          v1 = v1 && p1 <= my_qpos;
-        }
-        if (a.cu) {
-          v0 = v0 && p0 >= my_sst;
-          v1 = v1 && p1 >= my_sst;
-        }
-        if (!v0) S0[r] = -INFINITY;
-        if (!v1) S1[r] = -INFINITY;
+        const bool v0 = (kk0 < L) & (!causal | (p0 <= my_qpos)) & (!packed | (p0 >= my_sst));
+        const bool v1 = (kk1 < L) & (!causal | (p1 <= my_qpos)) & (!packed | (p1 >= my_sst));
+        S0[r] = v0 ? S0[r] : -INFINITY;
+        S1[r] = v1 ? S1[r] : -INFINITY;
       }
     }
 
-    // online softmax (base 2, scale folded in)
+    // online softmax (base 2, scale folded in), running max moved lazily
     float mx = S0[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S0[r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S1[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * sl2);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float psum = 0.0f;
+    mx = partner_max(mx) * sl2;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + TAU) != 0) {  // some row's max moved: rescale (wave-uniform)
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb) O[mb] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+    float ps0 = 0.0f, ps1 = 0.0f;
     bf16x8 pf[4];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[r], sl2, -m_use));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[r], sl2, -m_use));
-      psum += p0 + p1;
+      ps0 += p0;
+      ps1 += p1;
       pf[r / 8][r % 8] = (__bf16)p0;
       pf[2 + r / 8][r % 8] = (__bf16)p1;
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) O[mb] *= alpha;
+    l_run += ps0 + ps1;
 
-    // O^T += V^T P^T, 16 keys per MFMA
+    // O^T += V^T P^T, 16 keys per MFMA; V^T read transposed from row-major V
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(sV + (32 * mb + n) * Lds<D>::V_ROW + (16 * p + 8 * hh) * 2);
-        O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[p], O[mb], 0, 0, 0);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(const_cast<char *>(sV) + voff[mb][0] + p * 16 * Lds<D>::ROW));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(const_cast<char *>(sV) + voff[mb][1] + p * 16 * Lds<D>::ROW));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[p], O[mb], 0, 0, 0);
       }
     }
+    wait_tiles();
     __syncthreads();
-    t = nt;
+    t = t_nxt;
     cur = nxt;
+  };
+
+  // prologue: tile 0 into stage 0
+  if (t < a.t_hi) issue_tile(cur.j, cur.kt * BN, 0);
+  wait_tiles();
+  __syncthreads();
+  while (t < a.t_hi) {
+    body(StageTag<0>{});
+    if (t >= a.t_hi) break;
+    body(StageTag<1>{});
   }
 
   // ---------------------------------------------------------- epilogue --
-  const float l = l_run + __shfl_xor(l_run, 32);
+  const float l = partner_sum(l_run);
   const bool empty = !(l > 0.0f);
   const float inv = empty ? 0.0f : 1.0f / l;
   const float lse = empty ? -INFINITY : (m_run + __log2f(l)) * 0.69314718055994530942f;
