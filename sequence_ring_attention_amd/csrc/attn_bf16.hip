@@ -337,6 +337,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnArgs a) {
 
     // S^T = K Q^T for two 32-key blocks
     f32x16 S0 = f32x16{}, S1 = f32x16{};
+    __builtin_amdgcn_s_setprio(1);  // keep the matrix core fed while the SIMD's other wave runs softmax
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(sK + koff[ks]);
@@ -344,6 +345,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnArgs a) {
       S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], S0, 0, 0, 0);
       S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[ks], S1, 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
 
     if (!full) {  // diagonal, sample-boundary or ragged tile: elementwise mask
 #pragma unroll
@@ -388,6 +390,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnArgs a) {
     l_run += ps0 + ps1;
 
     // O^T += V^T P^T, 16 keys per MFMA; V^T read transposed from row-major V
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
 #pragma unroll
@@ -400,6 +403,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnArgs a) {
         O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[p], O[mb], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     wait_tiles();
     __syncthreads();
     t = t_nxt;
