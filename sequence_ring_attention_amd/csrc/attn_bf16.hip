@@ -58,9 +58,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128;  // query rows per workgroup
 constexpr int BN = 64;   // keys per tile
-constexpr int NT = 256;  // threads per workgroup
+// NW wavefronts per workgroup, 32 query rows each: BM = 32 NW query rows and
+// 64 NW threads per workgroup.
 
 constexpr float TAU = 8.0f;  // log2 headroom before the running max must move
 
@@ -137,39 +137,31 @@ __device__ inline int seg_start(const int32_t *cu, int nseq, int pos) {
 }
 
 
-// Issue one K tile and one V tile (64 keys each) from KV block base
-// pointers into an LDS stage with buffer loads straight to LDS.  Wave w fills
-// KiB blocks w, w + 4, ...; lane l of a block writes 16 bytes at block base +
-// 16 l, so its per-lane offset (kvoff / vvoff) names the logical chunk that
-// the swizzle places there.  When the share ends inside the tile, rows past
-// it repeat the last row (their logits are masked, probabilities zero).
-template <int D>
-__device__ inline void issue_kv_tile(char *stage, const char *kblk, const char *vblk, uint32_t k_extent,
-                                     uint32_t v_extent, int64_t kbytes, int64_t vbytes, int k0, int L, int wave,
-                                     int lane, const uint32_t *kvoff, const uint32_t *vvoff) {
+// Issue one 64-key tile of a KV block (K or V) into an LDS tile with buffer
+// loads straight to LDS.  Wave w fills KiB blocks w, w + 4, ...; lane l of a
+// block writes 16 bytes at block base + 16 l, so its per-lane offset `voff`
+// names the logical chunk that the swizzle places there.  The descriptor is
+// bounded to the block's extent.  When the share ends inside the tile, rows
+// past it repeat the last row (their logits are masked, probabilities zero).
+template <int D, int NW>
+__device__ inline void issue_tile_lds(char *tile, const char *blk, uint32_t extent, int64_t rowbytes, int k0,
+                                      int L, int wave, int lane, const uint32_t *voff) {
   constexpr int CH = Lds<D>::CH;
-  constexpr int NBLK = Lds<D>::KIB_PER_TILE / 4;
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kblk), 0, k_extent, RSRC_WORD3);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vblk), 0, v_extent, RSRC_WORD3);
-  char *const sK = stage;
-  char *const sV = stage + Lds<D>::TILE;
+  constexpr int NBLK = Lds<D>::KIB_PER_TILE / NW;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(blk), 0, extent, RSRC_WORD3);
   if (k0 + BN <= L) {
-    const uint32_t ks = (uint32_t)(k0 * kbytes), vs = (uint32_t)(k0 * vbytes);
+    const uint32_t so = (uint32_t)(k0 * rowbytes);
 #pragma unroll
-    for (int i = 0; i < NBLK; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(sK + (wave + 4 * i) * 1024), 16, kvoff[i], ks, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(sV + (wave + 4 * i) * 1024), 16, vvoff[i], vs, 0, 0);
-    }
+    for (int i = 0; i < NBLK; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(tile + (wave + NW * i) * 1024), 16, voff[i], so, 0, 0);
   } else {
 #pragma unroll
     for (int i = 0; i < NBLK; ++i) {
-      const int row = (wave + 4 * i) * Lds<D>::KEYS_PER_KIB + lane / CH;
+      const int row = (wave + NW * i) * Lds<D>::KEYS_PER_KIB + lane / CH;
       const int lch = swz<D>(row, lane % CH);
       const int key = min(k0 + row, L - 1);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(sK + (wave + 4 * i) * 1024), 16,
-                                               (uint32_t)(key * kbytes + lch * 16), 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(sV + (wave + 4 * i) * 1024), 16,
-                                               (uint32_t)(key * vbytes + lch * 16), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(tile + (wave + NW * i) * 1024), 16,
+                                               (uint32_t)(key * rowbytes + lch * 16), 0, 0, 0);
     }
   }
 }
@@ -179,8 +171,9 @@ struct StepRange {
   int j, kt, ke;
 };
 
-template <int D, bool PARTIAL>
-__global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnArgs a) {
+template <int D, bool PARTIAL, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
+  constexpr int BM = 32 * NW;
   __shared__ __attribute__((aligned(1024))) char smem[Lds<D>::BYTES];
 
   // ---------------------------------------------------------- work item --
@@ -261,12 +254,12 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnArgs a) {
   // ------------------------------------------------ global -> LDS tiles --
   // per-lane byte offsets (within a tile) of the direct loads; see issue_kv_tile
   constexpr int CH = Lds<D>::CH;
-  constexpr int NBLK = Lds<D>::KIB_PER_TILE / 4;  // KiB blocks per wave per tile
+  constexpr int NBLK = Lds<D>::KIB_PER_TILE / NW;  // KiB blocks per wave per tile
   const int64_t kbytes = a.k_ss * 2, vbytes = a.v_ss * 2;
   uint32_t kvoff[NBLK], vvoff[NBLK];
 #pragma unroll
   for (int i = 0; i < NBLK; ++i) {
-    const int row = (wave + 4 * i) * Lds<D>::KEYS_PER_KIB + lane / CH;
+    const int row = (wave + NW * i) * Lds<D>::KEYS_PER_KIB + lane / CH;
     const int lch = swz<D>(row, lane % CH);
     kvoff[i] = (uint32_t)(row * kbytes + lch * 16);
     vvoff[i] = (uint32_t)(row * vbytes + lch * 16);
@@ -276,8 +269,9 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnArgs a) {
   const uint32_t k_extent = (uint32_t)((L - 1) * kbytes + 2 * D);
   const uint32_t v_extent = (uint32_t)((L - 1) * vbytes + 2 * D);
   auto issue_tile = [&](int j, int k0, int stg) {
-    issue_kv_tile<D>(smem + stg * Lds<D>::STAGE, kbase + 2 * j * a.kv_blk, vbase + 2 * j * a.kv_blk, k_extent,
-                     v_extent, kbytes, vbytes, k0, L, wave, lane, kvoff, vvoff);
+    char *const st = smem + stg * Lds<D>::STAGE;
+    issue_tile_lds<D, NW>(st, kbase + 2 * j * a.kv_blk, k_extent, kbytes, k0, L, wave, lane, kvoff);
+    issue_tile_lds<D, NW>(st + Lds<D>::TILE, vbase + 2 * j * a.kv_blk, v_extent, vbytes, k0, L, wave, lane, vvoff);
   };
   auto wait_tiles = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
@@ -464,22 +458,33 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnArgs a) {
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t stream) {
-  const int64_t blocks = (int64_t)a.n_ranks * a.n_qtiles * a.B * a.Hq;
+template <int NW>
+hipError_t launch_nw(AttnArgs a, int head_dim, hipStream_t stream) {
+  constexpr int BM = 32 * NW;
+  a.n_qtiles = (a.L + BM - 1) / BM;
+  const int64_t groups = (int64_t)a.n_ranks * a.n_qtiles * a.B * a.Hkv;
+  a.xcd_remap = groups % 8 == 0;
+  const int64_t blocks = groups * a.G;
   if (blocks == 0) return hipSuccess;
-  const dim3 grid((uint32_t)blocks), block(NT);
+  const dim3 grid((uint32_t)blocks), block(64 * NW);
   if (head_dim == 128) {
     if (a.partial)
-      hipLaunchKernelGGL((attn_bf16_kernel<128, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((attn_bf16_kernel<128, true, NW>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((attn_bf16_kernel<128, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((attn_bf16_kernel<128, false, NW>), grid, block, 0, stream, a);
   } else {
     if (a.partial)
-      hipLaunchKernelGGL((attn_bf16_kernel<64, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((attn_bf16_kernel<64, true, NW>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((attn_bf16_kernel<64, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((attn_bf16_kernel<64, false, NW>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
+}
+
+// Four wavefronts (128 query rows) per workgroup: eight measured the same at
+// the 128K-token share, and four gives twice as many workgroups for balance.
+hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t stream) {
+  return launch_nw<4>(a, head_dim, stream);
 }
 
 }  // namespace usp
