@@ -78,6 +78,28 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
+def plain_copy_reference(nbytes):
+    """A plain torch device copy of the size of one layout launch, with a
+    1 GiB buffer written between repetitions so the 256 MB last-level cache
+    does not serve it: the practical ceiling of a read+write stream here."""
+    import torch
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    flush = torch.empty(2**30, dtype=torch.uint8, device="cuda:0")
+    times = []
+    for _ in range(9):
+        flush.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = sorted(times)[len(times) // 2]
+    return {"bytes": 2 * nbytes, "ms": ms, "GB/s": 2 * nbytes / (ms * 1e-3) / 1e9,
+            "frac_hbm": 2 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
 def cpu_baseline(w, r, u, n_rows):
     """The oracle as it stands on a bounded sample: n_rows query rows of this
     share (all its heads) against the whole sequence, fp64 on the host."""
@@ -171,6 +193,7 @@ def main():
     zig_ms, fwd_ms, walk_ms, inv_ms = seg(0, 1), seg(1, 2), seg(2, 3), seg(3, 4)
 
     walk_tflops = flops / (walk_ms * 1e-3) / 1e12
+    copy_ref = plain_copy_reference(inv_bytes // 2)
     traffic = measured_traffic()
     result = {
         "metric": "ring-step attention causal TFLOP/s + % bf16 MFMA peak; layout GB/s, 1 GPU",
@@ -207,6 +230,7 @@ def main():
             "ulysses_layout_inv_o": {"ms": inv_ms, "bytes": inv_bytes,
                                      "GB/s": inv_bytes / (inv_ms * 1e-3) / 1e9,
                                      "frac_hbm": inv_bytes / (inv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+            "plain_device_copy_reference": copy_ref,
         },
         "wall_s_timed": wall,
     }
