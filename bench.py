@@ -41,6 +41,7 @@ def parse():
     p.add_argument("--ring-rank", type=int, default=0)
     p.add_argument("--ulysses-rank", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true", help="skip the other workloads' timings")
     p.add_argument("--cpu-rows", type=int, default=384, help="query rows of the oracle sample")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB (for scaling HBM byte counters)")
@@ -98,6 +99,109 @@ def plain_copy_reference(nbytes):
     ms = sorted(times)[len(times) // 2]
     return {"bytes": 2 * nbytes, "ms": ms, "GB/s": 2 * nbytes / (ms * 1e-3) / 1e9,
             "frac_hbm": 2 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
+def _time(fn, reps=5):
+    """Median HIP-event time (ms) of fn() on the current stream."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b))
+    return sorted(out)[len(out) // 2]
+
+
+def packed_pairs(cu, pos):
+    """Visible (query, key) pairs of queries at `pos` under the causal
+    same-sample mask: a query at p sees p - start(sample of p) + 1 keys."""
+    import numpy as np
+    start = np.asarray(cu)[np.searchsorted(cu, pos, side="right") - 1]
+    return int((np.asarray(pos) - start + 1).sum())
+
+
+def extra_workloads():
+    """The other configurations' launches, each timed on its own: the 8K MHA
+    walk of every rank in one launch, the 32K GQA walk of ranks 0 and 7 (zigzag
+    balance) with its per-step launches and merges, and the packed 32K walk
+    of each rank."""
+    import numpy as np
+    import torch
+    from sequence_ring_attention_amd import binding as B
+    from sequence_ring_attention_amd import inputs
+    dev = torch.device("cuda:0")
+    res = {}
+
+    def zig_shares(x, rd):
+        out = torch.empty((rd, 1) + (x.shape[0], x.shape[1] // rd) + tuple(x.shape[2:]), dtype=x.dtype, device=dev)
+        B.usp_zigzag_extract(x, out, rd, 1, -1, -1)
+        return out[:, 0]                                       # (rd, B, 2c, H, D)
+
+    # 8K causal MHA, cp = 4, every rank in one launch
+    w = inputs.WORKLOADS["causal_mha_s8k_cp4"]
+    q, k, v = (t.to(dev) for t in inputs.workload_qkv(w))
+    qs, ks, vs = zig_shares(q, w.rd), zig_shares(k, w.rd), zig_shares(v, w.rd)
+    o = torch.empty_like(qs)
+    lse = torch.empty(w.rd, w.H, w.B, w.share, dtype=torch.float32, device=dev)
+    d = B.attn_desc(w.S, w.rd, qs, ks, vs, o=o, all_ranks=True)
+    ms = _time(lambda: B.usp_attn_fwd(qs, ks, vs, o, lse, d, -1))
+    fl = 2.0 * w.B * w.H * w.S * w.S * w.D
+    res[w.name] = {"all_ranks_walk_ms": ms, "TFLOP": fl / 1e12, "TFLOP/s": fl / (ms * 1e-3) / 1e12}
+
+    # 32K causal GQA, cp = 8: ranks 0 and 7 (walk), rank 0 step by step + merges
+    w = inputs.WORKLOADS["causal_gqa_s32k_cp8"]
+    q, k, v = (t.to(dev) for t in inputs.workload_qkv(w))
+    qs, ks, vs = zig_shares(q, w.rd), zig_shares(k, w.rd), zig_shares(v, w.rd)
+    fl_rank = 4.0 * w.D * w.H * w.B * 2 * w.rd * w.chunk * w.chunk
+    entry = {"TFLOP_per_rank": fl_rank / 1e12}
+    for r in (0, w.rd - 1):
+        qr = qs[r].contiguous()
+        o = torch.empty_like(qr)
+        lse = torch.empty(w.H, w.B, w.share, dtype=torch.float32, device=dev)
+        d = B.attn_desc(w.S, w.rd, qr, ks, vs, o=o)
+        ms = _time(lambda: B.usp_attn_fwd(qr, ks, vs, o, lse, d, r))
+        entry[f"rank{r}_walk_ms"] = ms
+        entry[f"rank{r}_TFLOP/s"] = fl_rank / (ms * 1e-3) / 1e12
+    qr = qs[0].contiguous()
+    acc = torch.empty(w.H, w.B, w.share, w.D, dtype=torch.float32, device=dev)
+    lacc = torch.empty(w.H, w.B, w.share, dtype=torch.float32, device=dev)
+    ost, lst = torch.empty_like(acc), torch.empty_like(lacc)
+    d = B.attn_desc(w.S, w.rd, qr, ks, vs)
+    step_ms = [_time(lambda t=t: B.usp_ring_attn_step_fwd(qr, ks, vs, ost, lst, d, 0, t)) for t in range(w.rd)]
+    merge_ms = _time(lambda: B.usp_lse_merge(acc, lacc, ost, lst))
+    rows = w.H * w.B * w.share
+    merge_bytes = 3 * rows * w.D * 4 + 3 * rows * 4
+    entry["rank0_step_ms"] = step_ms
+    entry["rank0_step_TFLOP/s"] = [fl_rank / w.rd / (m * 1e-3) / 1e12 for m in step_ms]
+    entry["merge_ms"] = merge_ms
+    entry["merge_GB/s"] = merge_bytes / (merge_ms * 1e-3) / 1e9
+    entry["merge_frac_hbm"] = entry["merge_GB/s"] / PEAK_HBM_GBS
+    res[w.name] = entry
+
+    # packed variable-length 32K, cp = 4: each rank
+    w = inputs.WORKLOADS["packed_varlen_s32k_cp4"]
+    q, k, v = (t.to(dev) for t in inputs.workload_qkv(w))
+    cu = inputs.workload_cu_seqlens(w)
+    cu_t = torch.from_numpy(cu).to(dev)
+    qs, ks, vs = zig_shares(q, w.rd), zig_shares(k, w.rd), zig_shares(v, w.rd)
+    entry = {"num_samples": len(cu) - 1}
+    c = w.chunk
+    for r in range(w.rd):
+        pos = np.concatenate([np.arange(r * c, (r + 1) * c), np.arange((2 * w.rd - 1 - r) * c, (2 * w.rd - r) * c)])
+        fl = 4.0 * w.D * w.H * w.B * packed_pairs(cu, pos)
+        qr = qs[r].contiguous()
+        o = torch.empty_like(qr)
+        lse = torch.empty(w.H, w.B, w.share, dtype=torch.float32, device=dev)
+        d = B.attn_desc(w.S, w.rd, qr, ks, vs, o=o, cu_seqlens=cu_t)
+        ms = _time(lambda: B.usp_attn_fwd(qr, ks, vs, o, lse, d, r))
+        entry[f"rank{r}"] = {"TFLOP": fl / 1e12, "ms": ms, "TFLOP/s": fl / (ms * 1e-3) / 1e12}
+    res[w.name] = entry
+    return res
 
 
 def cpu_baseline(w, r, u, n_rows):
@@ -234,6 +338,11 @@ def main():
         },
         "wall_s_timed": wall,
     }
+    if not args.no_extra:
+        print("[bench] other workloads", file=sys.stderr, flush=True)
+        del share, Q, K, V
+        torch.cuda.empty_cache()
+        result["workloads"] = extra_workloads()
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, r, u, args.cpu_rows)
