@@ -483,8 +483,6 @@ hipError_t launch_nw(AttnArgs a, int head_dim, hipStream_t stream) {
 
 // Four wavefronts (128 query rows) per workgroup: eight measured the same at
 // the 128K-token share, and four gives twice as many workgroups for balance.
-// Four wavefronts (128 query rows) per workgroup: eight measured the same at
-// the 128K-token share, and four gives twice as many workgroups for balance.
 hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t stream) {
   return launch_nw<4>(a, head_dim, stream);
 }
