@@ -52,9 +52,26 @@ def shares(X, rd):
     return g.view(X.shape[0], rd, S // rd, *X.shape[2:]).transpose(0, 1).contiguous()
 
 
-def check_close(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what=""):
-    """o arrays in the same layout; lse arrays in the same layout."""
+def bf16_rounding_floor(o_ref):
+    """Expected |error| of rounding the exact values to bf16: a quarter of
+    the bf16 spacing at each value, averaged.  Rounding alone contributes
+    this much to a mean-abs comparison of a bf16 output with the exact one."""
+    a = np.abs(np.asarray(o_ref, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    ulp = np.where(a > 0, 2.0 ** (e - 7), 0.0)
+    return float((ulp / 4).mean()) if a.size else 0.0
+
+
+def check_close(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what="", out_bf16=False):
+    """o arrays in the same layout; lse arrays in the same layout.
+
+    ``out_bf16``: o was rounded to bf16 by the kernel; the mean-abs bar then
+    adds the expected error of that rounding (negligible where |o| << 1, as
+    in the long-sequence workloads; about 1e-3 where rows average only a few
+    values and |o| ~ 1)."""
     omax_tol, omean_tol, lse_tol = TOL[dtype]
+    if out_bf16:
+        omean_tol = omean_tol + bf16_rounding_floor(o_ref)
     o_gpu = np.asarray(o_gpu, dtype=np.float64)
     o_ref = np.asarray(o_ref, dtype=np.float64)
     lse_gpu = np.asarray(lse_gpu, dtype=np.float64)

@@ -155,6 +155,11 @@ ATTN_CASES = {  # name: B, S, H, Hkv, D, cp, causal, cu_seqlens, dtype, layout
     "bf16_cp1": (1, 384, 2, 2, 64, 1, True, None, "bf16", "bshd"),
     "bf16_d64_mqa": (1, 2048, 4, 1, 64, 2, True, None, "bf16", "hbsd"),
     "bf16_tiny_rows": (1, 16, 2, 2, 128, 4, True, None, "bf16", "bshd"),
+    "bf16_one_token_chunks": (1, 8, 2, 1, 128, 4, True, None, "bf16", "bshd"),
+    "bf16_b2_headmajor_gqa": (2, 768, 8, 2, 128, 3, True, None, "bf16", "hbsd"),
+    "bf16_strided_views": (2, 640, 4, 2, 128, 4, True, None, "bf16", "bshd_padded"),
+    "bf16_packed_chunk_edges": (1, 1024, 4, 4, 64, 4, True, [0, 1, 128, 256, 257, 640, 1023, 1024], "bf16", "bshd"),
+    "fp32_packed_cp3": (1, 96, 2, 2, 64, 3, True, [0, 5, 40, 96], "fp32", "bshd"),
 }
 
 
@@ -166,6 +171,12 @@ def _prepare(name):
     qs, ks, vs = shares(q.to(dev), cp), shares(k.to(dev), cp), shares(v.to(dev), cp)   # (cp,B,L,H,D)
     if layout == "hbsd":
         qs, ks, vs = (t.permute(0, 3, 1, 2, 4).contiguous() for t in (qs, ks, vs))
+    if layout == "bshd_padded":   # views into wider buffers: head and sequence strides are not the dense ones
+        def pad(t):
+            big = torch.full(t.shape[:3] + (t.shape[3] + 3, t.shape[4]), float("nan"), dtype=t.dtype, device=t.device)
+            big[:, :, :, 1:1 + t.shape[3]] = t
+            return big[:, :, :, 1:1 + t.shape[3]]
+        qs, ks, vs = pad(qs), pad(ks), pad(vs)
     cu_t = None if cu is None else torch.tensor(cu, dtype=torch.int32, device=dev)
     pos = [ix.zigzag_share_positions(S, cp, r) for r in range(cp)]
     qn, kn, vn = f64(q), f64(k), f64(v)
@@ -187,11 +198,27 @@ def _to_bshd(P, o):
     return np.transpose(o, (1, 2, 0, 3)) if P["layout"] == "hbsd" else o
 
 
+def _layout(P):
+    return "hbsd" if P["layout"] == "hbsd" else "bshd"
+
+
+def _out(P, shape, dt, dev):
+    """Output buffer (with a canary tail); strided into a wider buffer for the padded layout."""
+    if P["layout"] != "bshd_padded":
+        return guarded(shape, dt, dev)
+    Bn, L, H, D = shape[-4:]
+    big, tail_ok = guarded(shape[:-2] + (H + 3, D), dt, dev)
+
+    def ok():  # canary tail and the padding heads around the view both untouched
+        return tail_ok() and not big[..., 0, :].any() and not big[..., H + 1:, :].any()
+    return big[..., 1:1 + H, :], ok
+
+
 @pytest.mark.parametrize("name", sorted(ATTN_CASES))
 def test_ring_steps_and_merge(name):
     P = _prepare(name)
     dev, cp, H, Bn, L, D = P["dev"], P["cp"], P["H"], P["Bn"], P["L"], P["D"]
-    desc = B.attn_desc(P["S"], cp, P["qs"][0], P["ks"], P["vs"], layout=P["layout"], causal=P["causal"],
+    desc = B.attn_desc(P["S"], cp, P["qs"][0], P["ks"], P["vs"], layout=_layout(P), causal=P["causal"],
                        cu_seqlens=P["cu_t"])
     for r in range(cp):
         o_ref, lse_ref, parts = _oracle_rank(P, r)
@@ -220,28 +247,29 @@ def test_ring_walk_per_rank_and_all_ranks(name):
     dev, cp, H, Bn, L, D = P["dev"], P["cp"], P["H"], P["Bn"], P["L"], P["D"]
     dt = torch.float32 if P["dt"] == "fp32" else torch.bfloat16
     refs = [_oracle_rank(P, r) for r in range(cp)]
-    oshape = (Bn, L, H, D) if P["layout"] == "bshd" else (H, Bn, L, D)
+    oshape = (H, Bn, L, D) if P["layout"] == "hbsd" else (Bn, L, H, D)
     for r in range(cp):
         say("walk", name, "rank", r)
-        o, ok1 = guarded(oshape, dt, dev)
+        o, ok1 = _out(P, oshape, dt, dev)
         lse, ok2 = guarded((H, Bn, L), torch.float32, dev)
-        desc = B.attn_desc(P["S"], cp, P["qs"][r], P["ks"], P["vs"], o=o, layout=P["layout"],
+        desc = B.attn_desc(P["S"], cp, P["qs"][r], P["ks"], P["vs"], o=o, layout=_layout(P),
                            causal=P["causal"], cu_seqlens=P["cu_t"])
         B.usp_attn_fwd(P["qs"][r], P["ks"], P["vs"], o, lse, desc, r)
         torch.cuda.synchronize()
         assert ok1() and ok2()
-        check_close(_to_bshd(P, o), f64(lse), refs[r][0], refs[r][1], P["dt"], f"{name} walk r{r}")
+        check_close(_to_bshd(P, o), f64(lse), refs[r][0], refs[r][1], P["dt"], f"{name} walk r{r}",
+                    out_bf16=P["dt"] == "bf16")
     say("walk all ranks", name)
-    o_all, ok1 = guarded((cp, *oshape), dt, dev)
+    o_all, ok1 = _out(P, (cp, *oshape), dt, dev)
     lse_all, ok2 = guarded((cp, H, Bn, L), torch.float32, dev)
-    desc = B.attn_desc(P["S"], cp, P["qs"], P["ks"], P["vs"], o=o_all, layout=P["layout"],
+    desc = B.attn_desc(P["S"], cp, P["qs"], P["ks"], P["vs"], o=o_all, layout=_layout(P),
                        causal=P["causal"], cu_seqlens=P["cu_t"], all_ranks=True)
     B.usp_attn_fwd(P["qs"], P["ks"], P["vs"], o_all, lse_all, desc, -1)
     torch.cuda.synchronize()
     assert ok1() and ok2()
     for r in range(cp):
         check_close(_to_bshd(P, o_all[r]), f64(lse_all[r]), refs[r][0], refs[r][1], P["dt"],
-                    f"{name} all-ranks r{r}")
+                    f"{name} all-ranks r{r}", out_bf16=P["dt"] == "bf16")
 
 
 def test_first_row_is_exactly_v0():
