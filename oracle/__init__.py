@@ -34,9 +34,12 @@ Modules:
   causal load accounting.
 * ``usp``       -- Algorithms 1 and 2 composed over a virtual (ud x rd) grid.
 * ``comm``      -- the per-GPU communication-volume formulas (design input only).
+* ``backward``  -- gradients of the attention (dQ, dK, dV): of the whole
+  sequence, of one ring step given the forward's lse, and of one ring rank.
 
 Parity status: every function is pinned by the ``-m "not gpu"`` tests against
 facts the pages print or against mathematics (closed forms, brute force, a
-library routine).  The one reading that no page fixes -- zigzag applied to a
+library routine); the backward is pinned to finite differences of the forward
+and to torch autograd of a plain masked softmax.  The one reading that no page fixes -- zigzag applied to a
 packed variable-length stream -- is noted where it is used.
 """
