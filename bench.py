@@ -62,9 +62,15 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}))
 
 
+WALK_SOURCES = ("attn_bf16.hip", "attn_tiles.h")
+
+
 def kernel_source_hash():
-    path = os.path.join(ROOT, "sequence_ring_attention_amd", "csrc", "attn_bf16.hip")
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """sha256 (first 16 hex digits) of the walk kernel's sources, in order."""
+    h = hashlib.sha256()
+    for name in WALK_SOURCES:
+        h.update(open(os.path.join(ROOT, "sequence_ring_attention_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():
