@@ -1,7 +1,7 @@
 /*
  * usp.h -- C ABI of libusp.so: one GPU's share of the USP attention forward
- * pass (Ulysses all-to-all layout + zigzag Ring-Attention) on AMD MI355X
- * (gfx950).
+ * pass (Ulysses all-to-all layout + zigzag Ring-Attention) and its backward
+ * on AMD MI355X (gfx950).
  *
  * Sources, cited by page title and section:
  *   [USP review]    "USP: 统一序列并行方法用于长上下文生成式AI" (xllm-io paper
@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define USP_ABI_VERSION 1
+#define USP_ABI_VERSION 2
 
 typedef enum {
   USP_OK = 0,
@@ -191,6 +191,77 @@ usp_status usp_lse_merge(float *o_acc, float *lse_acc, const float *o_step,
  */
 usp_status usp_attn_fwd(const void *q, const void *k_all, const void *v_all, void *o,
                         float *lse, const usp_attn_desc *desc, int32_t ring_rank, void *stream);
+
+/*
+ * ---------------------------------------------------------------- backward
+ * Gradients of the attention above for training (the pages train with the
+ * method: [YunChang] runs its tests with a backward flag, [USP review]
+ * section 六 trains end to end).  They are the derivative of the forward:
+ * with P the softmax probabilities over all cp blocks and dO the gradient of
+ * the output,
+ *   dV = P^T dO,  dP = dO V^T,  dS = P (dP - delta),  dQ = scale dS K,
+ *   dK = scale dS^T Q,  delta = rowsum(dO * O) per query row,
+ * and a KV head's dK, dV sum the contributions of its query heads.  On the
+ * ring ([CP vs Ulysses], concepts section), P restricted to block j is
+ * exp(scale q k^T - lse) with the forward's final lse, so every step's
+ * contribution stands alone: a rank's dQ sums its cp steps, and block j's
+ * dK, dV sum the steps of every rank against block j.  In a real ring the dK,
+ * dV accumulators travel with their KV block; here the blocks sit in HBM and
+ * the accumulators are the caller's fp32 buffers.
+ *
+ * Buffers shared by the backward entry points (device, caller-owned):
+ *   d_o:   the output gradient, `dtype`, with O's strides (desc->o) and, for
+ *          ring_rank = -1, desc->o_rank_stride between ranks.
+ *   stats: fp32 per-row statistics written by usp_attn_bwd_prep and read by
+ *          the gradient passes: stats[i] = delta of row i and stats[R + i] =
+ *          lse of row i times log2(e) (+inf where lse = -inf), with rows i
+ *          ordered (Hq, B, 2c), or (cp, Hq, B, 2c) for ring_rank = -1, and R
+ *          the number of rows.  2 R floats.
+ *   dk_all, dv_all: fp32 accumulators with K's and V's element strides
+ *          (desc->k, desc->v, desc->kv_block_stride): a zeroed buffer shaped
+ *          like k_all, in fp32, fits.  The gradient passes add into them.
+ * Errors (all backward entry points): as usp_ring_attn_step_fwd, plus
+ *   USP_ERR_INVALID_ARG for O or dO strides that do not keep 16-byte
+ *   alignment or more than 2^29 statistics rows.
+ */
+
+/*
+ * Per-row statistics of the backward: delta = rowsum(dO * O) (computed in
+ * fp32 from `dtype` O and dO) and lse * log2(e), into `stats` (layout above).
+ *   o, d_o: desc->o strides (rank stride desc->o_rank_stride for -1)
+ *   lse:    the forward's fp32 lse, (Hq, B, 2c) or (cp, Hq, B, 2c)
+ */
+usp_status usp_attn_bwd_prep(const void *o, const void *d_o, const float *lse, float *stats,
+                             const usp_attn_desc *desc, int32_t ring_rank, void *stream);
+
+/*
+ * One ring step of the backward: ring rank r at step t against KV block
+ * j = (r - t) mod cp ([CP vs Ulysses], concepts section and Figure 1).
+ * Adds the step's contributions:
+ *   dq_acc (fp32 (Hq, B, 2c, D), contiguous) += scale dS K_j,
+ *   block j of dk_all += scale dS^T Q,  block j of dv_all += P^T dO,
+ * where P = exp(scale q k^T - lse) on block j's visible keys.
+ * `stats` comes from usp_attn_bwd_prep with the same ring_rank.
+ * Errors: as usp_ring_attn_step_fwd.
+ */
+usp_status usp_ring_attn_step_bwd(const void *q, const void *k_all, const void *v_all,
+                                  const void *d_o, const float *stats, float *dq_acc,
+                                  float *dk_all, float *dv_all, const usp_attn_desc *desc,
+                                  int32_t ring_rank, int32_t step, void *stream);
+
+/*
+ * The whole ring backward for one rank (or every rank, ring_rank = -1):
+ * usp_attn_bwd_prep into `stats`, then dQ of the rank's queries over all cp
+ * steps, written in `dtype` with Q's strides (desc->q, desc->q_rank_stride),
+ * and the rank's contributions to every block's dK and dV, added into
+ * dk_all, dv_all.  With ring_rank = -1 the blocks receive the sum over all
+ * ranks, which is the full gradient of K and V.
+ * Errors: as usp_attn_fwd.
+ */
+usp_status usp_attn_bwd(const void *q, const void *k_all, const void *v_all, const void *o,
+                        const void *d_o, const float *lse, void *dq, float *dk_all,
+                        float *dv_all, float *stats, const usp_attn_desc *desc,
+                        int32_t ring_rank, void *stream);
 
 /* Name of a status code (static storage). */
 const char *usp_status_string(usp_status status);

@@ -18,8 +18,8 @@ USP_OK, USP_ERR_INVALID_ARG, USP_ERR_UNSUPPORTED, USP_ERR_HIP = 0, 1, 2, 3
 USP_DTYPE_BF16, USP_DTYPE_FP32 = 0, 1
 
 EXPORTED = ["usp_zigzag_extract", "usp_ulysses_a2a_layout", "usp_ring_attn_step_fwd",
-            "usp_lse_merge", "usp_attn_fwd", "usp_status_string", "usp_last_error_detail",
-            "usp_abi_version"]
+            "usp_lse_merge", "usp_attn_fwd", "usp_attn_bwd_prep", "usp_ring_attn_step_bwd", "usp_attn_bwd",
+            "usp_status_string", "usp_last_error_detail", "usp_abi_version"]
 
 
 class UspError(RuntimeError):
@@ -62,8 +62,13 @@ def lib():
         L.usp_ring_attn_step_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, i32, vp]
         L.usp_lse_merge.argtypes = [vp, vp, vp, vp, i64, i64, vp]
         L.usp_attn_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, vp]
+        L.usp_attn_bwd_prep.argtypes = [vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, vp]
+        L.usp_ring_attn_step_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc),
+                                             i32, i32, vp]
+        L.usp_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, vp]
         for f in ("usp_zigzag_extract", "usp_ulysses_a2a_layout", "usp_ring_attn_step_fwd",
-                  "usp_lse_merge", "usp_attn_fwd"):
+                  "usp_lse_merge", "usp_attn_fwd", "usp_attn_bwd_prep", "usp_ring_attn_step_bwd",
+                  "usp_attn_bwd"):
             getattr(L, f).restype = st
         L.usp_status_string.argtypes = [st]
         L.usp_status_string.restype = ctypes.c_char_p
@@ -183,6 +188,67 @@ def usp_attn_fwd(q, k_all, v_all, o, lse, desc, ring_rank, stream=None):
     check(lib().usp_attn_fwd(q.data_ptr(), k_all.data_ptr(), v_all.data_ptr(), o.data_ptr(),
                              lse.data_ptr(), ctypes.byref(desc), ring_rank, _stream(stream)))
     return o, lse
+
+
+def _stats_rows(desc, n_ranks):
+    return n_ranks * desc.num_q_heads * desc.batch * (desc.seq_len // desc.cp)
+
+
+def _check_stats(stats, desc, n_ranks):
+    if stats.dtype != torch.float32 or not stats.is_contiguous() or stats.numel() != 2 * _stats_rows(desc, n_ranks):
+        raise ValueError("stats must be contiguous fp32 with 2 * (ranks, Hq, B, 2c) elements")
+
+
+def _check_dkv(k_all, v_all, dk_all, dv_all):
+    for g, x in ((dk_all, k_all), (dv_all, v_all)):
+        if g.dtype != torch.float32 or g.shape != x.shape or g.stride() != x.stride():
+            raise ValueError("dk_all / dv_all must be fp32 with the shape and element strides of k_all / v_all")
+
+
+def usp_attn_bwd_prep(o, d_o, lse, stats, desc, ring_rank, stream=None):
+    """stats = [rowsum(dO * O) | lse * log2(e)] per query row (layout in include/usp.h)."""
+    _dev(o, d_o, lse, stats)
+    n = desc.cp if ring_rank < 0 else 1
+    if lse.dtype != torch.float32 or lse.numel() != _stats_rows(desc, n):
+        raise ValueError("lse must be fp32 with (ranks, Hq, B, 2c) elements")
+    _check_stats(stats, desc, n)
+    check(lib().usp_attn_bwd_prep(o.data_ptr(), d_o.data_ptr(), lse.data_ptr(), stats.data_ptr(),
+                                  ctypes.byref(desc), ring_rank, _stream(stream)))
+    return stats
+
+
+def usp_ring_attn_step_bwd(q, k_all, v_all, d_o, stats, dq_acc, dk_all, dv_all, desc, ring_rank, step,
+                           stream=None):
+    """Adds step ``step``'s gradient contributions into dq_acc (fp32 (Hq, B, 2c, D)) and into
+    block (r - step) mod cp of dk_all / dv_all (fp32, k_all's / v_all's strides)."""
+    _dev(q, k_all, v_all, d_o, stats, dq_acc, dk_all, dv_all)
+    _check_stats(stats, desc, 1)
+    _check_dkv(k_all, v_all, dk_all, dv_all)
+    if dq_acc.dtype != torch.float32 or not dq_acc.is_contiguous() or \
+            dq_acc.numel() != _stats_rows(desc, 1) * desc.head_dim:
+        raise ValueError("dq_acc must be contiguous fp32 (Hq, B, 2c, D)")
+    check(lib().usp_ring_attn_step_bwd(q.data_ptr(), k_all.data_ptr(), v_all.data_ptr(), d_o.data_ptr(),
+                                       stats.data_ptr(), dq_acc.data_ptr(), dk_all.data_ptr(), dv_all.data_ptr(),
+                                       ctypes.byref(desc), ring_rank, step, _stream(stream)))
+    return dq_acc, dk_all, dv_all
+
+
+def usp_attn_bwd(q, k_all, v_all, o, d_o, lse, dq, dk_all, dv_all, stats, desc, ring_rank, stream=None):
+    """The ring backward of one rank (or every rank, ring_rank = -1): writes dq (dtype, Q's
+    strides) and adds the rank's contributions into dk_all / dv_all."""
+    _dev(q, k_all, v_all, o, d_o, lse, dq, dk_all, dv_all, stats)
+    n = desc.cp if ring_rank < 0 else 1
+    _check_attn(k_all, v_all, lse, desc, n)
+    _check_stats(stats, desc, n)
+    _check_dkv(k_all, v_all, dk_all, dv_all)
+    if dq.dtype != q.dtype or dq.shape != q.shape or dq.stride() != q.stride():
+        raise ValueError("dq must have q's dtype, shape and strides")
+    if d_o.shape != o.shape or d_o.stride() != o.stride() or d_o.dtype != o.dtype:
+        raise ValueError("d_o must have o's dtype, shape and strides")
+    check(lib().usp_attn_bwd(q.data_ptr(), k_all.data_ptr(), v_all.data_ptr(), o.data_ptr(), d_o.data_ptr(),
+                             lse.data_ptr(), dq.data_ptr(), dk_all.data_ptr(), dv_all.data_ptr(),
+                             stats.data_ptr(), ctypes.byref(desc), ring_rank, _stream(stream)))
+    return dq, dk_all, dv_all
 
 
 def attn_desc(seq_len, cp, q, k_all, v_all, o=None, layout="bshd", causal=True, softmax_scale=None,

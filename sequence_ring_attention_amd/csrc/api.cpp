@@ -261,6 +261,99 @@ usp_status attn_launch(const usp::AttnArgs &a, const usp_attn_desc *d, void *str
   return hip_result(e, who);
 }
 
+// ---------------------------------------------------------------- backward
+
+constexpr int64_t kMaxStatsRows = (int64_t)1 << 29;
+
+// O and dO are read with 16-byte vector loads and 16-byte direct tile loads.
+usp_status o_strides_check(const usp_attn_desc *d, int32_t ring_rank, const char *who) {
+  const int64_t e = elem_bytes(d->dtype);
+  const int64_t st[] = {d->o.b, d->o.s, d->o.h, ring_rank < 0 ? d->o_rank_stride : 0,
+                        ring_rank < 0 ? d->q_rank_stride : 0};
+  for (int64_t s : st)
+    if (s < 0 || (s * e) % 16 != 0)
+      return fail(USP_ERR_INVALID_ARG, "%s: O/dO strides and rank strides must be >= 0 and keep 16-byte alignment",
+                  who);
+  return USP_OK;
+}
+
+int64_t stats_rows(const usp_attn_desc *d, int32_t ring_rank) {
+  return (ring_rank < 0 ? (int64_t)d->cp : 1) * d->num_q_heads * d->batch * (d->seq_len / d->cp);
+}
+
+usp_status bwd_prepare(const void *q, const void *k, const void *v, const void *d_o, const float *stats,
+                       const usp_attn_desc *d, int32_t ring_rank, bool all_ranks_ok, usp::BwdArgs &b,
+                       const char *who) {
+  usp::AttnArgs a;
+  usp_status s = attn_prepare(q, k, v, d_o, stats, d, ring_rank, all_ranks_ok, a, who);
+  if (s != USP_OK) return s;
+  if ((s = o_strides_check(d, ring_rank, who)) != USP_OK) return s;
+  const int64_t rows = stats_rows(d, ring_rank);
+  if (rows >= kMaxStatsRows)
+    return fail(USP_ERR_INVALID_ARG, "%s: %lld statistics rows (limit 2^29)", who, (long long)rows);
+  b = usp::BwdArgs{};
+  b.q = q;
+  b.k = k;
+  b.v = v;
+  b.dout = d_o;
+  b.stats = stats;
+  b.rows = rows;
+  b.B = a.B; b.Hq = a.Hq; b.Hkv = a.Hkv; b.G = a.G;
+  b.L = a.L; b.c = a.c; b.cp = a.cp; b.causal = a.causal;
+  b.q_sb = a.q_sb; b.q_ss = a.q_ss; b.q_sh = a.q_sh;
+  b.k_sb = a.k_sb; b.k_ss = a.k_ss; b.k_sh = a.k_sh;
+  b.v_sb = a.v_sb; b.v_ss = a.v_ss; b.v_sh = a.v_sh;
+  b.do_sb = d->o.b; b.do_ss = d->o.s; b.do_sh = d->o.h;
+  b.kv_blk = a.kv_blk;
+  b.q_rank = a.q_rank;
+  b.do_rank = a.o_rank;
+  b.scale = a.scale;
+  b.scale_log2 = a.scale_log2;
+  b.cu = a.cu;
+  b.nseq = a.nseq;
+  b.ring_rank = ring_rank;
+  b.n_ranks = a.n_ranks;
+  return USP_OK;
+}
+
+usp_status grads_check(const void *dq, const float *dk, const float *dv, const void *q, const void *k,
+                       const void *v, const char *who) {
+  if (!dq || !dk || !dv) return fail(USP_ERR_INVALID_ARG, "%s: null gradient pointer", who);
+  if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(USP_ERR_INVALID_ARG, "%s: gradient buffers must be 16-byte aligned", who);
+  if (dq == q || (const void *)dk == k || (const void *)dv == v || (const void *)dk == v ||
+      (const void *)dv == k || (const void *)dk == (const void *)dv || dq == (const void *)dk ||
+      dq == (const void *)dv)
+    return fail(USP_ERR_INVALID_ARG, "%s: gradient buffers must not alias each other or the inputs", who);
+  return USP_OK;
+}
+
+usp_status prep_launch(const void *o, const void *d_o, const float *lse, float *stats, const usp_attn_desc *d,
+                       int32_t ring_rank, void *stream, const char *who) {
+  usp::PrepArgs p{};
+  p.o = o;
+  p.dout = d_o;
+  p.lse = lse;
+  p.stats = stats;
+  p.rows = stats_rows(d, ring_rank);
+  p.B = (int32_t)d->batch;
+  p.Hq = (int32_t)d->num_q_heads;
+  p.L = (int32_t)(d->seq_len / d->cp);
+  p.o_sb = p.do_sb = d->o.b;
+  p.o_ss = p.do_ss = d->o.s;
+  p.o_sh = p.do_sh = d->o.h;
+  p.o_rank = p.do_rank = ring_rank < 0 ? d->o_rank_stride : 0;
+  return hip_result(usp::launch_bwd_prep(p, (int)d->head_dim, d->dtype == USP_DTYPE_BF16,
+                                         static_cast<hipStream_t>(stream)), who);
+}
+
+usp_status bwd_launch(const usp::BwdArgs &b, const usp_attn_desc *d, void *stream, const char *who) {
+  hipError_t e = d->dtype == USP_DTYPE_BF16
+                     ? usp::launch_attn_bwd_bf16(b, (int)d->head_dim, static_cast<hipStream_t>(stream))
+                     : usp::launch_attn_bwd_fp32(b, (int)d->head_dim, static_cast<hipStream_t>(stream));
+  return hip_result(e, who);
+}
+
 }  // namespace
 
 extern "C" {
@@ -297,6 +390,66 @@ usp_status usp_attn_fwd(const void *q, const void *k_all, const void *v_all, voi
   a.t_hi = desc->cp;
   a.partial = 0;
   return attn_launch(a, desc, stream, "attn_fwd launch");
+}
+
+usp_status usp_attn_bwd_prep(const void *o, const void *d_o, const float *lse, float *stats,
+                             const usp_attn_desc *desc, int32_t ring_rank, void *stream) {
+  const char *who = "attn_bwd_prep";
+  if (!desc) return fail(USP_ERR_INVALID_ARG, "%s: null descriptor", who);
+  if (!o || !d_o || !lse || !stats) return fail(USP_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (!aligned16(o) || !aligned16(d_o))
+    return fail(USP_ERR_INVALID_ARG, "%s: o and d_o must be 16-byte aligned", who);
+  if (o == d_o) return fail(USP_ERR_INVALID_ARG, "%s: o and d_o must be distinct buffers", who);
+  // the descriptor checks of the attention entry points, with O standing in
+  // for the inputs it does not use here
+  usp::AttnArgs a;
+  usp_status s = attn_prepare(o, o, o, d_o, stats, desc, ring_rank, true, a, who);
+  if (s != USP_OK) return s;
+  if ((s = o_strides_check(desc, ring_rank, who)) != USP_OK) return s;
+  const int64_t rows = stats_rows(desc, ring_rank);
+  if (rows >= kMaxStatsRows)
+    return fail(USP_ERR_INVALID_ARG, "%s: %lld statistics rows (limit 2^29)", who, (long long)rows);
+  return prep_launch(o, d_o, lse, stats, desc, ring_rank, stream, "attn_bwd_prep launch");
+}
+
+usp_status usp_ring_attn_step_bwd(const void *q, const void *k_all, const void *v_all, const void *d_o,
+                                  const float *stats, float *dq_acc, float *dk_all, float *dv_all,
+                                  const usp_attn_desc *desc, int32_t ring_rank, int32_t step, void *stream) {
+  const char *who = "ring_attn_step_bwd";
+  usp::BwdArgs b;
+  usp_status s = bwd_prepare(q, k_all, v_all, d_o, stats, desc, ring_rank, false, b, who);
+  if (s != USP_OK) return s;
+  if ((s = grads_check(dq_acc, dk_all, dv_all, q, k_all, v_all, who)) != USP_OK) return s;
+  if (step < 0 || step >= desc->cp) return fail(USP_ERR_INVALID_ARG, "%s: step %d out of range", who, (int)step);
+  b.dq = dq_acc;
+  b.dk = dk_all;
+  b.dv = dv_all;
+  b.t_lo = step;
+  b.t_hi = step + 1;
+  b.dq_acc = 1;
+  return bwd_launch(b, desc, stream, "ring_attn_step_bwd launch");
+}
+
+usp_status usp_attn_bwd(const void *q, const void *k_all, const void *v_all, const void *o, const void *d_o,
+                        const float *lse, void *dq, float *dk_all, float *dv_all, float *stats,
+                        const usp_attn_desc *desc, int32_t ring_rank, void *stream) {
+  const char *who = "attn_bwd";
+  usp::BwdArgs b;
+  usp_status s = bwd_prepare(q, k_all, v_all, d_o, stats, desc, ring_rank, true, b, who);
+  if (s != USP_OK) return s;
+  if ((s = grads_check(dq, dk_all, dv_all, q, k_all, v_all, who)) != USP_OK) return s;
+  if (!o || !lse) return fail(USP_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (!aligned16(o)) return fail(USP_ERR_INVALID_ARG, "%s: o must be 16-byte aligned", who);
+  if (o == d_o || dq == o || dq == d_o)
+    return fail(USP_ERR_INVALID_ARG, "%s: o, d_o and dq must be distinct buffers", who);
+  if ((s = prep_launch(o, d_o, lse, stats, desc, ring_rank, stream, "attn_bwd prep launch")) != USP_OK) return s;
+  b.dq = dq;
+  b.dk = dk_all;
+  b.dv = dv_all;
+  b.t_lo = 0;
+  b.t_hi = desc->cp;
+  b.dq_acc = 0;
+  return bwd_launch(b, desc, stream, "attn_bwd launch");
 }
 
 }  // extern "C"

@@ -1,0 +1,602 @@
+// Ring-step / ring-walk attention backward, bf16 inputs, MFMA on gfx950.
+//
+// What is computed: the derivative of the forward.  With the forward's final
+// lse, P = exp(scale q k^T - lse) on the visible pairs of every KV block
+// ("Context Parallel 与 Ulysses", concepts section: each step's partial of a
+// row is that row's softmax over all blocks, restricted to one block), so
+// each step's gradient contribution stands alone:
+//   dP = dO V^T,  dS = P (dP - delta),  dQ += scale dS K,
+//   dK += scale dS^T Q,  dV += P^T dO,
+// with delta = rowsum(dO O) and lse2 = lse log2(e) read from the statistics
+// buffer.  The causal mask is block-granular as in the forward (Figure 2):
+// tiles above the diagonal are never visited and only tiles that straddle it
+// evaluate the elementwise mask.
+//
+// Two passes, each the single owner of what it writes (no atomics, results
+// independent of scheduling):
+//   * dQ pass -- a workgroup of 4 wavefronts owns 128 query rows of one
+//     (rank, query head, batch), walks the steps' 64-key tiles like the
+//     forward and keeps dQ^T in registers.  S^T = K Q^T and dP^T = V dO^T
+//     take K and V rows from LDS as the M operand (K-row order permuted so
+//     that a lane's probabilities are eight consecutive keys), with the
+//     wave's Q and dO rows in registers; dQ^T += K^T dS^T reads K transposed
+//     from the same row-major LDS tile (ds_read_b64_tr_b16) and takes dS^T
+//     straight from the registers.
+//   * dK/dV pass -- a workgroup of 4 wavefronts owns 128 keys of one (KV
+//     block, KV head, batch); each wavefront holds its 32 keys' K and V rows
+//     in registers and keeps dK^T and dV^T there.  For every rank that
+//     reaches the block and every query head reading the KV head, the visible
+//     64-row query tiles of Q and dO stream through LDS (double buffered,
+//     buffer loads straight to LDS, the forward's swizzle) with the tile's
+//     delta and lse2.  S = Q K^T and dP = dO V^T take Q and dO rows as the M
+//     operand; dV^T += dO^T P and dK^T += Q^T dS read dO and Q transposed.
+// The scale is applied once, to the final dQ and dK.
+#include "attn_tiles.h"
+#include "usp_internal.h"
+
+namespace usp {
+namespace {
+
+using namespace tiles;
+
+constexpr int NW = 4;          // wavefronts per workgroup
+constexpr int BM = 32 * NW;    // query rows per dQ workgroup
+constexpr int BK = 32 * NW;    // keys per dK/dV workgroup
+constexpr int STATS = 512;     // bytes of one tile's delta[64] and lse2[64]
+
+__device__ inline int mod_cp(int x, int cp) {
+  x %= cp;
+  return x < 0 ? x + cp : x;
+}
+
+// Index n of the packed sample holding `pos`: cu[n] <= pos < cu[n + 1].
+__device__ inline int seg_index(const int32_t *cu, int nseq, int pos) {
+  int lo = 0, hi = nseq;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= pos) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Rows of a bf16 matrix as the N operand of v_mfma_f32_32x32x16_bf16: lane
+// (n, hh) holds row n, dims 16 ks + 8 hh .. + 7.
+template <int D>
+__device__ inline void load_row_frags(bf16x8 *f, const __bf16 *row, bool valid, int hh) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    f[ks] = valid ? *reinterpret_cast<const bf16x8 *>(row + 16 * ks + 8 * hh) : bf16x8{};
+}
+
+// Per-lane LDS offsets of the operand reads on a 64-row tile (shared by both
+// passes): row reads as the M operand (rows sig and 32 + sig, chunk 2 ks + hh)
+// and transposed reads (4 rows x 4 dims per 4-lane group).
+template <int D>
+struct TileOffsets {
+  int row[D / 16];
+  int tr[D / 32][2];
+  __device__ inline TileOffsets(int lane) {
+    const int n = lane & 31, hh = lane >> 5;
+    const int sig = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) row[ks] = sig * Lds<D>::ROW + swz<D>(sig, 2 * ks + hh) * 16;
+    const int tg = lane >> 4, trr = (lane >> 2) & 3, tq = lane & 3;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r = 8 * (tg >> 1) + 4 * e + trr;
+        tr[mb][e] = r * Lds<D>::ROW + swz<D>(r, 4 * mb + 2 * (tg & 1) + (tq >> 1)) * 16 + (tq & 1) * 8;
+      }
+    }
+  }
+};
+
+// M operand of 32 d-rows x 16 tile rows, read transposed from a row-major
+// tile: tile rows 16 p .. 16 p + 15, dims 32 mb .. 32 mb + 31.
+template <int D>
+__device__ inline bf16x8 read_tr(const char *tile, const TileOffsets<D> &o, int mb, int p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(const_cast<char *>(tile) + o.tr[mb][0] +
+                                                                         p * 16 * Lds<D>::ROW));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(const_cast<char *>(tile) + o.tr[mb][1] +
+                                                                         p * 16 * Lds<D>::ROW));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Per-lane byte offsets of the direct tile loads (see issue_tile_lds).
+template <int D>
+__device__ inline void tile_load_offsets(uint32_t *voff, int64_t rowbytes, int wave, int lane) {
+  constexpr int CH = Lds<D>::CH;
+#pragma unroll
+  for (int i = 0; i < Lds<D>::KIB_PER_TILE / NW; ++i) {
+    const int row = (wave + NW * i) * Lds<D>::KEYS_PER_KIB + lane / CH;
+    voff[i] = (uint32_t)(row * rowbytes + swz<D>(row, lane % CH) * 16);
+  }
+}
+
+// ================================================================ dQ pass ==
+
+template <int D, bool ACC>
+__global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[Lds<D>::BYTES];
+
+  // work item: as the forward (heaviest query tiles first, the query heads
+  // of one KV head back to back on one XCD)
+  const int bid = blockIdx.x;
+  int gi, g;
+  if (a.xcd_remap) {
+    const int x = bid & 7, i = bid >> 3;
+    gi = (i / a.G) * 8 + x;
+    g = i % a.G;
+  } else {
+    gi = bid / a.G;
+    g = bid % a.G;
+  }
+  const int kvh = gi % a.Hkv;
+  int rest = gi / a.Hkv;
+  const int b = rest % a.B;
+  const int order = rest / a.B;
+  int rank, lt;
+  if (a.ring_rank >= 0) {
+    rank = a.ring_rank;
+    lt = a.n_tiles - 1 - order;
+  } else {
+    rank = order % a.cp;
+    lt = a.n_tiles - 1 - order / a.cp;
+  }
+  const int hq = kvh * a.G + g;
+  const int c = a.c, cp = a.cp, L = a.L;
+  const bool causal = a.causal != 0, packed = a.cu != nullptr;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, hh = lane >> 5;
+  const int q0 = lt * BM;
+  const int qrow = q0 + wave * 32 + n;
+  const bool qvalid = qrow < L;
+  const int qlast = min(q0 + BM, L) - 1;
+  const int qpos_min = share_pos(rank, q0, c, cp);
+  const int qpos_max = share_pos(rank, qlast, c, cp);
+  const int my_qpos = qvalid ? share_pos(rank, qrow, c, cp) : -1;
+  int sst_min = 0, sst_max = 0, my_sst = 0;
+  if (packed) {
+    sst_min = a.cu[seg_index(a.cu, a.nseq, qpos_min)];
+    sst_max = a.cu[seg_index(a.cu, a.nseq, qpos_max)];
+    my_sst = qvalid ? a.cu[seg_index(a.cu, a.nseq, my_qpos)] : 0x7fffffff;
+  }
+  const int rs = a.ring_rank >= 0 ? 0 : rank;
+  const int64_t srow = (((int64_t)rs * a.Hq + hq) * a.B + b) * L + qrow;
+  const float delta = qvalid ? a.stats[srow] : 0.0f;
+  const float lse2 = qvalid ? a.stats[a.rows + srow] : INFINITY;
+
+  bf16x8 qf[D / 16], dof[D / 16];
+  load_row_frags<D>(qf, static_cast<const __bf16 *>(a.q) + (a.ring_rank < 0 ? rank * a.q_rank : 0) + b * a.q_sb +
+                            hq * a.q_sh + (int64_t)qrow * a.q_ss, qvalid, hh);
+  load_row_frags<D>(dof, static_cast<const __bf16 *>(a.dout) + (a.ring_rank < 0 ? rank * a.do_rank : 0) +
+                             b * a.do_sb + hq * a.do_sh + (int64_t)qrow * a.do_ss, qvalid, hh);
+
+  // tile schedule: the key range of each step's block this query tile sees
+  auto step_range = [&](int t) {
+    StepRange r;
+    r.j = mod_cp(rank - t, cp);
+    const int hi = causal ? count_le(r.j, qpos_max, c, cp) : L;
+    const int lo = packed ? count_le(r.j, sst_min - 1, c, cp) : 0;
+    if (hi <= lo) {
+      r.kt = r.ke = 0;
+    } else {
+      r.kt = lo / BN;
+      r.ke = (hi + BN - 1) / BN;
+    }
+    return r;
+  };
+  int t = a.t_lo;
+  StepRange cur = step_range(t);
+  while (cur.kt >= cur.ke && ++t < a.t_hi) cur = step_range(t);
+
+  const int64_t kbytes = a.k_ss * 2, vbytes = a.v_ss * 2;
+  uint32_t kvoff[Lds<D>::KIB_PER_TILE / NW], vvoff[Lds<D>::KIB_PER_TILE / NW];
+  tile_load_offsets<D>(kvoff, kbytes, wave, lane);
+  tile_load_offsets<D>(vvoff, vbytes, wave, lane);
+  const char *const kbase = static_cast<const char *>(a.k) + 2 * (b * a.k_sb + kvh * a.k_sh);
+  const char *const vbase = static_cast<const char *>(a.v) + 2 * (b * a.v_sb + kvh * a.v_sh);
+  const uint32_t k_extent = (uint32_t)((L - 1) * kbytes + 2 * D);
+  const uint32_t v_extent = (uint32_t)((L - 1) * vbytes + 2 * D);
+  auto issue_tile = [&](int j, int k0, int stg) {
+    char *const st = smem + stg * Lds<D>::STAGE;
+    issue_tile_lds<D, NW>(st, kbase + 2 * j * a.kv_blk, k_extent, kbytes, k0, L, wave, lane, kvoff);
+    issue_tile_lds<D, NW>(st + Lds<D>::TILE, vbase + 2 * j * a.kv_blk, v_extent, vbytes, k0, L, wave, lane, vvoff);
+  };
+  auto wait_tiles = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  const TileOffsets<D> off(lane);
+
+  f32x16 dQ[D / 32];
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) dQ[mb] = f32x16{};
+  const float sl2 = a.scale_log2;
+
+  auto advance = [&](int &tx, StepRange &x) {
+    ++x.kt;
+    while (x.kt >= x.ke && ++tx < a.t_hi) x = step_range(tx);
+  };
+
+  auto body = [&](auto stage_tag) {
+    constexpr int STG = decltype(stage_tag)::value;
+    int t_nxt = t;
+    StepRange nxt = cur;
+    advance(t_nxt, nxt);
+    if (t_nxt < a.t_hi) issue_tile(nxt.j, nxt.kt * BN, STG ^ 1);
+
+    const char *const sK = smem + STG * Lds<D>::STAGE;
+    const char *const sV = sK + Lds<D>::TILE;
+    const int j = cur.j;
+    const int k0 = cur.kt * BN;
+    const int klast = min(k0 + BN, L) - 1;
+    const int kpos_min = share_pos(j, k0, c, cp);
+    const int kpos_max = share_pos(j, klast, c, cp);
+    const bool full = __builtin_amdgcn_readfirstlane(
+        (k0 + BN <= L) & (!causal | (kpos_max <= qpos_min)) & (!packed | (kpos_min >= sst_max)));
+
+    // S^T = K Q^T and dP^T = V dO^T, two 32-key blocks each
+    f32x16 S0 = f32x16{}, S1 = f32x16{}, P0 = f32x16{}, P1 = f32x16{};
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(sK + off.row[ks]);
+      const bf16x8 kb = *reinterpret_cast<const bf16x8 *>(sK + off.row[ks] + 32 * Lds<D>::ROW);
+      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], S0, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[ks], S1, 0, 0, 0);
+      const bf16x8 va = *reinterpret_cast<const bf16x8 *>(sV + off.row[ks]);
+      const bf16x8 vb = *reinterpret_cast<const bf16x8 *>(sV + off.row[ks] + 32 * Lds<D>::ROW);
+      P0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dof[ks], P0, 0, 0, 0);
+      P1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, dof[ks], P1, 0, 0, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+
+    if (!full) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kl = 16 * (r / 8) + 8 * hh + (r % 8);
+        const int kk0 = k0 + kl, kk1 = k0 + 32 + kl;
+        const int p0 = share_pos(j, kk0, c, cp), p1 = share_pos(j, kk1, c, cp);
+        const bool v0 = (kk0 < L) & (!causal | (p0 <= my_qpos)) & (!packed | (p0 >= my_sst));
+        const bool v1 = (kk1 < L) & (!causal | (p1 <= my_qpos)) & (!packed | (p1 >= my_sst));
+        S0[r] = v0 ? S0[r] : -INFINITY;
+        S1[r] = v1 ? S1[r] : -INFINITY;
+      }
+    }
+
+    // dS^T = P^T (dP^T - delta), rounded to bf16 as the N operand
+    bf16x8 dsf[4];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[r], sl2, -lse2));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[r], sl2, -lse2));
+      dsf[r / 8][r % 8] = (__bf16)(p0 * (P0[r] - delta));
+      dsf[2 + r / 8][r % 8] = (__bf16)(p1 * (P1[r] - delta));
+    }
+
+    // dQ^T += K^T dS^T, 16 keys per MFMA; K^T read transposed
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) dQ[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(sK, off, mb, p),
+                                                                                 dsf[p], dQ[mb], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    wait_tiles();
+    __syncthreads();
+    t = t_nxt;
+    cur = nxt;
+  };
+
+  if (t < a.t_hi) issue_tile(cur.j, cur.kt * BN, 0);
+  wait_tiles();
+  __syncthreads();
+  while (t < a.t_hi) {
+    body(StageTag<0>{});
+    if (t >= a.t_hi) break;
+    body(StageTag<1>{});
+  }
+
+  if (!qvalid) return;
+  const float scale = a.scale;
+  if (ACC) {
+    float *o = static_cast<float *>(a.dq) + (((int64_t)hq * a.B + b) * L + qrow) * D;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        float4 *dst = reinterpret_cast<float4 *>(o + 32 * mb + 8 * r4 + 4 * hh);
+        float4 val = *dst;
+        val.x += dQ[mb][4 * r4 + 0] * scale;
+        val.y += dQ[mb][4 * r4 + 1] * scale;
+        val.z += dQ[mb][4 * r4 + 2] * scale;
+        val.w += dQ[mb][4 * r4 + 3] * scale;
+        *dst = val;
+      }
+    }
+  } else {
+    __bf16 *o = static_cast<__bf16 *>(a.dq) + (a.ring_rank < 0 ? rank * a.q_rank : 0) + b * a.q_sb +
+                (int64_t)qrow * a.q_ss + hq * a.q_sh;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4 val;
+        val[0] = (__bf16)(dQ[mb][4 * r4 + 0] * scale);
+        val[1] = (__bf16)(dQ[mb][4 * r4 + 1] * scale);
+        val[2] = (__bf16)(dQ[mb][4 * r4 + 2] * scale);
+        val[3] = (__bf16)(dQ[mb][4 * r4 + 3] * scale);
+        *reinterpret_cast<bf16x4 *>(o + 32 * mb + 8 * r4 + 4 * hh) = val;
+      }
+    }
+  }
+}
+
+// =========================================================== dK/dV pass ==
+
+// Query tiles (64 rows) of rank r's share that can see a key tile whose
+// positions span [kpos_min, kpos_max]: causal -- queries at or after
+// kpos_min; packed -- queries before the end of kpos_max's sample.
+struct QRange {
+  int qt, qe;
+};
+
+template <int D>
+__global__ __launch_bounds__(64 * NW, 1) void dkdv_bf16_kernel(BwdArgs a) {
+  constexpr int TILE = Lds<D>::TILE;
+  // stage s: Q tile at 2 s TILE, dO tile at (2 s + 1) TILE; stats of stage s
+  // at 4 TILE + s STATS
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE + 2 * STATS];
+
+  // work item: key tiles in order of local index (the first chunk of a
+  // share holds the earliest positions, which the most queries see)
+  const int n_slots = a.ring_rank >= 0 ? a.t_hi - a.t_lo : a.cp;
+  int rest = blockIdx.x;
+  const int g = rest % a.Hkv;
+  rest /= a.Hkv;
+  const int b = rest % a.B;
+  rest /= a.B;
+  const int slot = rest % n_slots;
+  const int kt = rest / n_slots;
+  const int j = a.ring_rank >= 0 ? mod_cp(a.ring_rank - (a.t_lo + slot), a.cp) : slot;
+  const int r_first = a.ring_rank >= 0 ? a.ring_rank : 0;
+  const int r_last = a.ring_rank >= 0 ? a.ring_rank : a.cp - 1;
+  const int c = a.c, cp = a.cp, L = a.L;
+  const bool causal = a.causal != 0, packed = a.cu != nullptr;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, hh = lane >> 5;
+  const int k0 = kt * BK;
+  const int krow = k0 + 32 * wave + n;
+  const bool kvalid = krow < L;
+  const int klast = min(k0 + BK, L) - 1;
+  const int kpos_min = share_pos(j, k0, c, cp);
+  const int kpos_max = share_pos(j, klast, c, cp);
+  const int my_kpos = kvalid ? share_pos(j, krow, c, cp) : 0x7fffffff;
+  int kend_min = 0x7fffffff, kend_max = 0x7fffffff, my_kend = 0x7fffffff;
+  if (packed) {
+    kend_min = a.cu[seg_index(a.cu, a.nseq, kpos_min) + 1];
+    kend_max = a.cu[seg_index(a.cu, a.nseq, kpos_max) + 1];
+    my_kend = kvalid ? a.cu[seg_index(a.cu, a.nseq, my_kpos) + 1] : 0;
+  }
+
+  auto q_range = [&](int r) {
+    QRange x;
+    const int lo = causal ? count_le(r, kpos_min - 1, c, cp) : 0;
+    const int hi = packed ? count_le(r, kend_max - 1, c, cp) : L;
+    if (hi <= lo) {
+      x.qt = x.qe = 0;
+    } else {
+      x.qt = lo / BN;
+      x.qe = (hi + BN - 1) / BN;
+    }
+    return x;
+  };
+  // iteration state: rank r, query head offset h in the group, tile range
+  int r = r_first, h = 0;
+  QRange cur = q_range(r);
+  auto normalise = [&](int &rx, int &hx, QRange &x) {
+    while (x.qt >= x.qe && rx <= r_last) {
+      if (++hx == a.G) {
+        hx = 0;
+        if (++rx > r_last) break;
+      }
+      x = q_range(rx);
+    }
+  };
+  normalise(r, h, cur);
+  if (r > r_last) return;  // no query sees these keys: nothing to add (uniform)
+
+  bf16x8 kf[D / 16], vf[D / 16];
+  const int64_t kvo = j * a.kv_blk;
+  load_row_frags<D>(kf, static_cast<const __bf16 *>(a.k) + kvo + b * a.k_sb + g * a.k_sh + (int64_t)krow * a.k_ss,
+                    kvalid, hh);
+  load_row_frags<D>(vf, static_cast<const __bf16 *>(a.v) + kvo + b * a.v_sb + g * a.v_sh + (int64_t)krow * a.v_ss,
+                    kvalid, hh);
+
+  const int64_t qbytes = a.q_ss * 2, dbytes = a.do_ss * 2;
+  uint32_t qvoff[Lds<D>::KIB_PER_TILE / NW], dvoff[Lds<D>::KIB_PER_TILE / NW];
+  tile_load_offsets<D>(qvoff, qbytes, wave, lane);
+  tile_load_offsets<D>(dvoff, dbytes, wave, lane);
+  const uint32_t q_extent = (uint32_t)((L - 1) * qbytes + 2 * D);
+  const uint32_t d_extent = (uint32_t)((L - 1) * dbytes + 2 * D);
+  // a tile's statistics: thread i < 64 loads delta of row q0 + i, thread
+  // 64 + i its lse2, into a register; it is stored to LDS once the tile's
+  // loads have landed (the rows of a tile are only 4-byte aligned in HBM)
+  float st_val = 0.0f;
+  auto issue = [&](int rx, int hx, int qt, int stg) {
+    const int hq = g * a.G + hx;
+    const char *qb = static_cast<const char *>(a.q) +
+                     2 * ((a.ring_rank < 0 ? rx * a.q_rank : 0) + b * a.q_sb + hq * a.q_sh);
+    const char *db = static_cast<const char *>(a.dout) +
+                     2 * ((a.ring_rank < 0 ? rx * a.do_rank : 0) + b * a.do_sb + hq * a.do_sh);
+    issue_tile_lds<D, NW>(smem + 2 * stg * TILE, qb, q_extent, qbytes, qt * BN, L, wave, lane, qvoff);
+    issue_tile_lds<D, NW>(smem + (2 * stg + 1) * TILE, db, d_extent, dbytes, qt * BN, L, wave, lane, dvoff);
+    if (tid < 2 * BN) {
+      const int rs = a.ring_rank >= 0 ? 0 : rx;
+      const int i = qt * BN + (tid & (BN - 1));
+      const int64_t srow = (((int64_t)rs * a.Hq + hq) * a.B + b) * L + i;
+      st_val = i < L ? a.stats[srow + (tid >= BN ? a.rows : 0)] : 0.0f;
+    }
+  };
+  auto wait_tiles = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  auto store_stats = [&](int stg) {
+    if (tid < 2 * BN) reinterpret_cast<float *>(smem + 4 * TILE + stg * STATS)[tid] = st_val;
+  };
+  const TileOffsets<D> off(lane);
+
+  f32x16 dK[D / 32], dV[D / 32];
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) {
+    dK[mb] = f32x16{};
+    dV[mb] = f32x16{};
+  }
+  const float sl2 = a.scale_log2;
+  bool more = true;
+
+  auto body = [&](auto stage_tag) {
+    constexpr int STG = decltype(stage_tag)::value;
+    int r_n = r, h_n = h;
+    QRange nxt = cur;
+    ++nxt.qt;
+    normalise(r_n, h_n, nxt);
+    const bool has_next = r_n <= r_last;
+    if (has_next) issue(r_n, h_n, nxt.qt, STG ^ 1);
+
+    const char *const sQ = smem + 2 * STG * TILE;
+    const char *const sD = sQ + TILE;
+    const float *const sst = reinterpret_cast<const float *>(smem + 4 * TILE + STG * STATS);
+    const int q0 = cur.qt * BN;
+    const int qlast = min(q0 + BN, L) - 1;
+    const int qpos_min = share_pos(r, q0, c, cp);
+    const int qpos_max = share_pos(r, qlast, c, cp);
+    const bool full = __builtin_amdgcn_readfirstlane(
+        (q0 + BN <= L) & (k0 + BK <= L) & (!causal | (qpos_min >= kpos_max)) & (!packed | (qpos_max < kend_min)));
+
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      // S = Q K^T and dP = dO V^T for 32 queries x the wave's 32 keys
+      f32x16 S = f32x16{}, P = f32x16{};
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(sQ + off.row[ks] + blk * 32 * Lds<D>::ROW);
+        const bf16x8 da = *reinterpret_cast<const bf16x8 *>(sD + off.row[ks] + blk * 32 * Lds<D>::ROW);
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], S, 0, 0, 0);
+        P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ks], P, 0, 0, 0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      // this lane's queries: 32 blk + 16 (r / 8) + 8 hh + r % 8
+      const float4 *d4 = reinterpret_cast<const float4 *>(sst + 32 * blk + 8 * hh);
+      const float4 *l4 = reinterpret_cast<const float4 *>(sst + 64 + 32 * blk + 8 * hh);
+      const float4 dl[4] = {d4[0], d4[1], d4[4], d4[5]};
+      const float4 ll[4] = {l4[0], l4[1], l4[4], l4[5]};
+      if (!full) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int ql = q0 + 32 * blk + 16 * (rr / 8) + 8 * hh + (rr % 8);
+          const int qp = share_pos(r, ql, c, cp);
+          const bool vis = (ql < L) & kvalid & (!causal | (my_kpos <= qp)) & (!packed | (qp < my_kend));
+          S[rr] = vis ? S[rr] : -INFINITY;
+        }
+      }
+      bf16x8 pf[2], dsf[2];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const float4 dq4 = dl[rr / 4], lq4 = ll[rr / 4];
+        const float dlt = (rr % 4 == 0) ? dq4.x : (rr % 4 == 1) ? dq4.y : (rr % 4 == 2) ? dq4.z : dq4.w;
+        const float ls = (rr % 4 == 0) ? lq4.x : (rr % 4 == 1) ? lq4.y : (rr % 4 == 2) ? lq4.z : lq4.w;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[rr], sl2, -ls));
+        pf[rr / 8][rr % 8] = (__bf16)p;
+        dsf[rr / 8][rr % 8] = (__bf16)(p * (P[rr] - dlt));
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over this block's two 16-query slabs
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          dV[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(sD, off, mb, 2 * blk + s), pf[s], dV[mb], 0, 0, 0);
+          dK[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(sQ, off, mb, 2 * blk + s), dsf[s], dK[mb], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+    }
+    wait_tiles();
+    if (has_next) store_stats(STG ^ 1);
+    __syncthreads();
+    r = r_n;
+    h = h_n;
+    cur = nxt;
+    more = has_next;
+  };
+
+  issue(r, h, cur.qt, 0);
+  wait_tiles();
+  store_stats(0);
+  __syncthreads();
+  while (more) {
+    body(StageTag<0>{});
+    if (!more) break;
+    body(StageTag<1>{});
+  }
+
+  if (!kvalid) return;
+  float *dkp = a.dk + kvo + b * a.k_sb + g * a.k_sh + (int64_t)krow * a.k_ss;
+  float *dvp = a.dv + kvo + b * a.v_sb + g * a.v_sh + (int64_t)krow * a.v_ss;
+  const float scale = a.scale;
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      float4 *pk = reinterpret_cast<float4 *>(dkp + 32 * mb + 8 * r4 + 4 * hh);
+      float4 *pv = reinterpret_cast<float4 *>(dvp + 32 * mb + 8 * r4 + 4 * hh);
+      float4 vk = *pk, vv = *pv;
+      vk.x += dK[mb][4 * r4 + 0] * scale;
+      vk.y += dK[mb][4 * r4 + 1] * scale;
+      vk.z += dK[mb][4 * r4 + 2] * scale;
+      vk.w += dK[mb][4 * r4 + 3] * scale;
+      vv.x += dV[mb][4 * r4 + 0];
+      vv.y += dV[mb][4 * r4 + 1];
+      vv.z += dV[mb][4 * r4 + 2];
+      vv.w += dV[mb][4 * r4 + 3];
+      *pk = vk;
+      *pv = vv;
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_d(BwdArgs a, hipStream_t stream) {
+  // dQ pass
+  a.n_tiles = (a.L + BM - 1) / BM;
+  const int64_t groups = (int64_t)a.n_ranks * a.n_tiles * a.B * a.Hkv;
+  a.xcd_remap = groups % 8 == 0;
+  const int64_t q_blocks = groups * a.G;
+  if (q_blocks > 0) {
+    if (a.dq_acc)
+      hipLaunchKernelGGL((dq_bf16_kernel<D, true>), dim3((uint32_t)q_blocks), dim3(64 * NW), 0, stream, a);
+    else
+      hipLaunchKernelGGL((dq_bf16_kernel<D, false>), dim3((uint32_t)q_blocks), dim3(64 * NW), 0, stream, a);
+  }
+  // dK/dV pass
+  a.n_tiles = (a.L + BK - 1) / BK;
+  a.xcd_remap = 0;
+  const int n_slots = a.ring_rank >= 0 ? a.t_hi - a.t_lo : a.cp;
+  const int64_t k_blocks = (int64_t)a.n_tiles * n_slots * a.B * a.Hkv;
+  if (k_blocks > 0)
+    hipLaunchKernelGGL((dkdv_bf16_kernel<D>), dim3((uint32_t)k_blocks), dim3(64 * NW), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_bf16(const BwdArgs &a, int head_dim, hipStream_t stream) {
+  return head_dim == 128 ? launch_d<128>(a, stream) : launch_d<64>(a, stream);
+}
+
+}  // namespace usp

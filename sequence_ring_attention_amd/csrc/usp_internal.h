@@ -79,4 +79,52 @@ struct AttnArgs {
 hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t stream);
 hipError_t launch_attn_fp32(const AttnArgs &a, int head_dim, hipStream_t stream);
 
+// -------------------------------------------------------------- backward --
+
+struct BwdArgs {
+  const void *q;
+  const void *k;
+  const void *v;
+  const void *dout;   // dO, dtype, O's strides
+  const float *stats; // [delta (rows) | lse * log2(e) (rows)]
+  int64_t rows;       // statistics rows: n_ranks * Hq * B * L
+  void *dq;           // dtype with Q's strides, or fp32 (Hq,B,L,D) when dq_acc
+  float *dk;          // fp32, K's strides
+  float *dv;          // fp32, V's strides
+  int32_t B, Hq, Hkv, G;
+  int32_t L, c, cp, causal;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t do_sb, do_ss, do_sh;
+  int64_t kv_blk;
+  int64_t q_rank, do_rank;
+  float scale;
+  float scale_log2;
+  const int32_t *cu;
+  int32_t nseq;
+  int32_t ring_rank;  // >= 0, or -1 for every rank (full walk only)
+  int32_t t_lo, t_hi; // ring steps; the dK/dV pass covers the blocks they reach
+  int32_t dq_acc;     // 1: add into the fp32 dq accumulator (one step)
+  int32_t n_ranks;
+  int32_t n_tiles;    // set by the launchers
+  int32_t xcd_remap;  // set by the launchers
+};
+
+struct PrepArgs {
+  const void *o;
+  const void *dout;
+  const float *lse;
+  float *stats;
+  int64_t rows;  // n_ranks * Hq * B * L
+  int32_t B, Hq, L;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t do_sb, do_ss, do_sh;
+  int64_t o_rank, do_rank;
+};
+
+hipError_t launch_bwd_prep(const PrepArgs &p, int head_dim, bool bf16, hipStream_t stream);
+hipError_t launch_attn_bwd_bf16(const BwdArgs &a, int head_dim, hipStream_t stream);
+hipError_t launch_attn_bwd_fp32(const BwdArgs &a, int head_dim, hipStream_t stream);
+
 }  // namespace usp

@@ -110,3 +110,28 @@ def sample_rows(L, c, n_random, seed, extra=()):
     base = {0, 1, c - 1, c, c + 1, L - 2, L - 1, *extra}
     base |= set(rng.choice(L, size=min(n_random, L), replace=False).tolist())
     return np.array(sorted(i for i in base if 0 <= i < L))
+
+
+# Gradient bar (the backward): normwise relative error and worst element
+# relative to the largest reference magnitude, per tensor.  bf16 -- the
+# kernels round P and dS to bf16 (relative 2^-9) before the fp32-accumulated
+# products and take delta from the bf16 O, so errors of a few 2^-9 of the
+# gradient's scale are expected; fp32 -- double internally, with lse and
+# delta passed as fp32 (relative 2^-24 of |lse| on P), a few 1e-7.
+GTOL = {"bf16": (1e-2, 5e-2), "fp32": (1e-5, 1e-4)}
+
+
+def check_grad(g_gpu, g_ref, dtype, what=""):
+    g = np.asarray(g_gpu, dtype=np.float64)
+    r = np.asarray(g_ref, dtype=np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite gradient"
+    nrm_tol, max_tol = GTOL[dtype]
+    scale = float(np.abs(r).max()) if r.size else 0.0
+    if scale == 0.0:
+        assert np.all(g == 0), f"{what}: expected zeros"
+        return dict(norm=0.0, max=0.0)
+    d = g - r
+    stats = dict(norm=float(np.linalg.norm(d) / np.linalg.norm(r)), max=float(np.abs(d).max() / scale))
+    assert stats["norm"] <= nrm_tol and stats["max"] <= max_tol, f"{what}: {stats}"
+    return stats

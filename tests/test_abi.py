@@ -27,7 +27,7 @@ def declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 8, names
+    assert len(names) == 11, names
     lib = B.lib()
     for name in names:
         assert hasattr(lib, name), name
@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = B.lib()
-    assert lib.usp_abi_version() == 1
+    assert lib.usp_abi_version() == 2
     assert lib.usp_status_string(0) == b"USP_OK"
     assert lib.usp_status_string(2) == b"USP_ERR_UNSUPPORTED"
     assert lib.usp_status_string(99) == b"USP_ERR_UNKNOWN"
@@ -146,3 +146,59 @@ def test_binding_refuses_host_tensors():
     out = torch.zeros(1, 16, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         B.usp_zigzag_extract(x, out, 4, 1, 0, 0)
+
+
+FAKE4, FAKE5, FAKE6, FAKE7 = 0x40000, 0x50000, 0x60000, 0x70000
+
+
+def _bwd(d, r=0, **kw):
+    a = dict(q=FAKE, k=FAKE2, v=FAKE3, o=FAKE4, do=FAKE5, lse=FAKE6, dq=FAKE7, dk=0x80000, dv=0x90000,
+             stats=0xA0000)
+    a.update(kw)
+    return B.lib().usp_attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                a["stats"], ctypes.byref(d), r, None)
+
+
+def _step_bwd(d, r=0, t=0, **kw):
+    a = dict(q=FAKE, k=FAKE2, v=FAKE3, do=FAKE5, stats=0xA0000, dq=FAKE7, dk=0x80000, dv=0x90000)
+    a.update(kw)
+    return B.lib().usp_ring_attn_step_bwd(a["q"], a["k"], a["v"], a["do"], a["stats"], a["dq"], a["dk"], a["dv"],
+                                          ctypes.byref(d), r, t, None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(seq_len=250), 1), (dict(head_dim=96), 2), (dict(softmax_scale=-1.0), 1), (dict(cp=0), 1),
+    (dict(cu_seqlens=FAKE, num_seqs=2, causal=0), 2), (dict(o=B.UspStrides(64 * 4 * 128, 4 * 128 + 4, 128)), 1),
+])
+def test_backward_descriptor_rejects(kw, status):
+    d = _desc(**kw)
+    assert _bwd(d) == status
+    assert _step_bwd(d) == status
+    assert B.lib().usp_attn_bwd_prep(FAKE4, FAKE5, FAKE6, 0xA0000, ctypes.byref(d), 0, None) == status
+
+
+@no_gpu
+def test_backward_pointer_rank_and_step_checks():
+    d = _desc()
+    assert _bwd(d, dq=None) == 1 and _bwd(d, dk=0x80004) == 1 and _bwd(d, lse=None) == 1
+    assert _bwd(d, dq=FAKE) == 1            # dq aliases q
+    assert _bwd(d, dk=FAKE2) == 1           # dk aliases k
+    assert _bwd(d, dv=0x80000) == 1         # dv aliases dk
+    assert _bwd(d, do=FAKE4) == 1           # d_o aliases o
+    assert _bwd(d, r=4) == 1 and _bwd(d, r=-2) == 1
+    assert _step_bwd(d, r=-1) == 1 and _step_bwd(d, t=4) == 1 and _step_bwd(d, t=-1) == 1
+    assert _step_bwd(d, stats=None) == 1 and _step_bwd(d, do=FAKE5 + 8) == 1
+    lib = B.lib()
+    assert lib.usp_attn_bwd_prep(FAKE4, FAKE4, FAKE6, 0xA0000, ctypes.byref(d), 0, None) == 1
+    assert lib.usp_attn_bwd_prep(FAKE4, FAKE5, None, 0xA0000, ctypes.byref(d), 0, None) == 1
+    assert lib.usp_attn_bwd_prep(FAKE4, FAKE5, FAKE6, 0xA0000, None, 0, None) == 1
+    big = _desc(batch=1 << 14, seq_len=1 << 16, num_q_heads=1 << 10, num_kv_heads=1 << 10)
+    assert _bwd(big) in (1, 2)              # too many statistics rows / indices
+
+
+@no_gpu
+def test_backward_valid_arguments_reach_the_runtime():
+    d = _desc()
+    assert _bwd(d) == 3 and _step_bwd(d) == 3
+    assert B.lib().usp_attn_bwd_prep(FAKE4, FAKE5, FAKE6, 0xA0000, ctypes.byref(d), 0, None) == 3
