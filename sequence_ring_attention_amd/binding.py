@@ -153,8 +153,9 @@ def _check_attn(k_all, v_all, lse, desc, n_ranks):
     if k_all.shape[0] != desc.cp or v_all.shape[0] != desc.cp:
         raise ValueError("k_all / v_all need a leading dim of cp blocks")
     L = desc.seq_len // desc.cp
-    if lse.dtype != torch.float32 or lse.numel() != n_ranks * desc.num_q_heads * desc.batch * L:
-        raise ValueError("lse must be fp32 with (ranks, Hq, B, 2c) elements")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or \
+            lse.numel() != n_ranks * desc.num_q_heads * desc.batch * L:
+        raise ValueError("lse must be contiguous fp32 with (ranks, Hq, B, 2c) elements")
 
 
 def usp_ring_attn_step_fwd(q, k_all, v_all, o_step, lse_step, desc, ring_rank, step, stream=None):
@@ -199,9 +200,14 @@ def _check_stats(stats, desc, n_ranks):
         raise ValueError("stats must be contiguous fp32 with 2 * (ranks, Hq, B, 2c) elements")
 
 
+def _same_layout(a, b):
+    """Same shape and the same element strides on every dim that has more than one index."""
+    return a.shape == b.shape and all(n == 1 or sa == sb for n, sa, sb in zip(a.shape, a.stride(), b.stride()))
+
+
 def _check_dkv(k_all, v_all, dk_all, dv_all):
     for g, x in ((dk_all, k_all), (dv_all, v_all)):
-        if g.dtype != torch.float32 or g.shape != x.shape or g.stride() != x.stride():
+        if g.dtype != torch.float32 or not _same_layout(g, x):
             raise ValueError("dk_all / dv_all must be fp32 with the shape and element strides of k_all / v_all")
 
 
@@ -209,8 +215,8 @@ def usp_attn_bwd_prep(o, d_o, lse, stats, desc, ring_rank, stream=None):
     """stats = [rowsum(dO * O) | lse * log2(e)] per query row (layout in include/usp.h)."""
     _dev(o, d_o, lse, stats)
     n = desc.cp if ring_rank < 0 else 1
-    if lse.dtype != torch.float32 or lse.numel() != _stats_rows(desc, n):
-        raise ValueError("lse must be fp32 with (ranks, Hq, B, 2c) elements")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != _stats_rows(desc, n):
+        raise ValueError("lse must be contiguous fp32 with (ranks, Hq, B, 2c) elements")
     _check_stats(stats, desc, n)
     check(lib().usp_attn_bwd_prep(o.data_ptr(), d_o.data_ptr(), lse.data_ptr(), stats.data_ptr(),
                                   ctypes.byref(desc), ring_rank, _stream(stream)))
@@ -241,9 +247,9 @@ def usp_attn_bwd(q, k_all, v_all, o, d_o, lse, dq, dk_all, dv_all, stats, desc, 
     _check_attn(k_all, v_all, lse, desc, n)
     _check_stats(stats, desc, n)
     _check_dkv(k_all, v_all, dk_all, dv_all)
-    if dq.dtype != q.dtype or dq.shape != q.shape or dq.stride() != q.stride():
+    if dq.dtype != q.dtype or not _same_layout(dq, q):
         raise ValueError("dq must have q's dtype, shape and strides")
-    if d_o.shape != o.shape or d_o.stride() != o.stride() or d_o.dtype != o.dtype:
+    if d_o.dtype != o.dtype or not _same_layout(d_o, o):
         raise ValueError("d_o must have o's dtype, shape and strides")
     check(lib().usp_attn_bwd(q.data_ptr(), k_all.data_ptr(), v_all.data_ptr(), o.data_ptr(), d_o.data_ptr(),
                              lse.data_ptr(), dq.data_ptr(), dk_all.data_ptr(), dv_all.data_ptr(),

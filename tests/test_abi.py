@@ -202,3 +202,14 @@ def test_backward_valid_arguments_reach_the_runtime():
     d = _desc()
     assert _bwd(d) == 3 and _step_bwd(d) == 3
     assert B.lib().usp_attn_bwd_prep(FAKE4, FAKE5, FAKE6, 0xA0000, ctypes.byref(d), 0, None) == 3
+
+
+def test_binding_refuses_strided_lse():
+    """lse is read and written as a dense (ranks, Hq, B, 2c) array: a strided
+    view must be refused before the call."""
+    d = _desc()
+    lse = torch.zeros(1, 64, 4).permute(2, 0, 1)          # (Hq, B, 2c) elements, wrong memory order
+    kv = torch.zeros(4, 1)
+    B._check_attn(kv, kv, lse.contiguous(), d, 1)
+    with pytest.raises(ValueError):
+        B._check_attn(kv, kv, lse, d, 1)

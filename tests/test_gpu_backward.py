@@ -52,7 +52,7 @@ def _prepare(name):
     sh = [shares(x.to(dev), cp) for x in (q, k, v, do, o_t)]            # (cp, B, L, H, D)
     if layout == "hbsd":
         sh = [t.permute(0, 3, 1, 2, 4).contiguous() for t in sh]
-    lse_sh = torch.from_numpy(np.stack([lse[:, :, p] for p in pos])).float().to(dev)   # (cp, H, B, L)
+    lse_sh = torch.from_numpy(np.stack([lse[:, :, p] for p in pos])).float().contiguous().to(dev)  # (cp, H, B, L)
     cu_t = None if cu is None else torch.tensor(cu, dtype=torch.int32, device=dev)
     return dict(Bn=Bn, S=S, H=H, Hkv=Hkv, D=D, cp=cp, causal=causal, cu=cu, cu_t=cu_t, dt=dt, layout=layout,
                 qs=sh[0], ks=sh[1], vs=sh[2], dos=sh[3], os=sh[4], lse=lse_sh, lse64=lse, delta=delta, pos=pos,
@@ -96,7 +96,8 @@ def test_backward_stats(name):
         exact = terms.sum(-1)
         assert np.all(np.abs(st[0] - exact) <= 1e-6 * np.abs(terms).sum(-1) + 1e-30), name
         lse2 = f64(P["lse"][r]) * np.log2(np.e)
-        assert np.all(np.abs(st[1] - lse2) <= 4 * np.spacing(np.abs(lse2).astype(np.float32))), name
+        bad = np.abs(st[1] - lse2) > 4 * np.spacing(np.abs(lse2).astype(np.float32))
+        assert not bad.any(), (name, int(bad.sum()))
 
 
 @pytest.mark.parametrize("name", sorted(BWD_CASES))
@@ -114,10 +115,12 @@ def test_backward_walk_per_rank_and_all_ranks(name):
         torch.cuda.synchronize()
         assert ok_q() and ok_kv()
         dq_ref, dk_ref, dv_ref = P["refs"][r]
-        check_grad(_bshd(P, dq), dq_ref, dt, f"{name} r{r} dq")
+        worst = [check_grad(_bshd(P, dq), dq_ref, dt, f"{name} r{r} dq")]
         for j in range(cp):
-            check_grad(_bshd(P, dk[j]), dk_ref[j], dt, f"{name} r{r} dk[{j}]")
-            check_grad(_bshd(P, dv[j]), dv_ref[j], dt, f"{name} r{r} dv[{j}]")
+            worst.append(check_grad(_bshd(P, dk[j]), dk_ref[j], dt, f"{name} r{r} dk[{j}]"))
+            worst.append(check_grad(_bshd(P, dv[j]), dv_ref[j], dt, f"{name} r{r} dv[{j}]"))
+        say("bwd walk", name, "rank", r, "worst norm %.2e max %.2e" % (max(w["norm"] for w in worst),
+                                                                      max(w["max"] for w in worst)))
     say("bwd walk all ranks", name)
     dq, ok_q = guarded(tuple(P["qs"].shape), P["qs"].dtype, dev)
     dk, dv, ok_kv = _grads_like(P)
