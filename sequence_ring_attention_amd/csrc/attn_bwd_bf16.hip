@@ -195,17 +195,17 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
   while (cur.kt >= cur.ke && ++t < a.t_hi) cur = step_range(t);
 
   const int64_t kbytes = a.k_ss * 2, vbytes = a.v_ss * 2;
-  uint32_t kvoff[Lds<D>::KIB_PER_TILE / NW], vvoff[Lds<D>::KIB_PER_TILE / NW];
-  tile_load_offsets<D>(kvoff, kbytes, wave, lane);
-  tile_load_offsets<D>(vvoff, vbytes, wave, lane);
   const char *const kbase = static_cast<const char *>(a.k) + 2 * (b * a.k_sb + kvh * a.k_sh);
   const char *const vbase = static_cast<const char *>(a.v) + 2 * (b * a.v_sb + kvh * a.v_sh);
   const uint32_t k_extent = (uint32_t)((L - 1) * kbytes + 2 * D);
   const uint32_t v_extent = (uint32_t)((L - 1) * vbytes + 2 * D);
   auto issue_tile = [&](int j, int k0, int stg) {
     char *const st = smem + stg * Lds<D>::STAGE;
-    issue_tile_lds<D, NW>(st, kbase + 2 * j * a.kv_blk, k_extent, kbytes, k0, L, wave, lane, kvoff);
-    issue_tile_lds<D, NW>(st + Lds<D>::TILE, vbase + 2 * j * a.kv_blk, v_extent, vbytes, k0, L, wave, lane, vvoff);
+    uint32_t voff[Lds<D>::KIB_PER_TILE / NW];  // recomputed per tile: a few VALU ops, registers are short
+    tile_load_offsets<D>(voff, kbytes, wave, lane);
+    issue_tile_lds<D, NW>(st, kbase + 2 * j * a.kv_blk, k_extent, kbytes, k0, L, wave, lane, voff);
+    tile_load_offsets<D>(voff, vbytes, wave, lane);
+    issue_tile_lds<D, NW>(st + Lds<D>::TILE, vbase + 2 * j * a.kv_blk, v_extent, vbytes, k0, L, wave, lane, voff);
   };
   auto wait_tiles = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
   const TileOffsets<D> off(lane);
@@ -236,8 +236,18 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
     const int kpos_max = share_pos(j, klast, c, cp);
     const bool full = __builtin_amdgcn_readfirstlane(
         (k0 + BN <= L) & (!causal | (kpos_max <= qpos_min)) & (!packed | (kpos_min >= sst_max)));
+    // positions grow with the local index, so the keys of block j this lane's
+    // query sees are one local range; as offsets from the lane's first key
+    // row in the tile, [vlo, vhi)
+    int vlo = 0, vhi = BN;
+    if (!full) {
+      const int hi = qvalid ? min(causal ? count_le(j, my_qpos, c, cp) : L, L) : 0;
+      const int lo = packed ? count_le(j, my_sst - 1, c, cp) : 0;
+      vlo = lo - k0 - 8 * hh;
+      vhi = hi - k0 - 8 * hh;
+    }
 
-    // S^T = K Q^T and dP^T = V dO^T, two 32-key blocks each
+    // S^T = K Q^T and dP^T = V dO^T for both 32-key halves
     f32x16 S0 = f32x16{}, S1 = f32x16{}, P0 = f32x16{}, P1 = f32x16{};
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -252,20 +262,14 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
       P1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, dof[ks], P1, 0, 0, 0);
     }
     __builtin_amdgcn_s_setprio(0);
-
     if (!full) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kl = 16 * (r / 8) + 8 * hh + (r % 8);
-        const int kk0 = k0 + kl, kk1 = k0 + 32 + kl;
-        const int p0 = share_pos(j, kk0, c, cp), p1 = share_pos(j, kk1, c, cp);
-        const bool v0 = (kk0 < L) & (!causal | (p0 <= my_qpos)) & (!packed | (p0 >= my_sst));
-        const bool v1 = (kk1 < L) & (!causal | (p1 <= my_qpos)) & (!packed | (p1 >= my_sst));
-        S0[r] = v0 ? S0[r] : -INFINITY;
-        S1[r] = v1 ? S1[r] : -INFINITY;
+        const int kc = 16 * (r / 8) + (r % 8);
+        S0[r] = (kc >= vlo) & (kc < vhi) ? S0[r] : -INFINITY;
+        S1[r] = (kc + 32 >= vlo) & (kc + 32 < vhi) ? S1[r] : -INFINITY;
       }
     }
-
     // dS^T = P^T (dP^T - delta), rounded to bf16 as the N operand
     bf16x8 dsf[4];
 #pragma unroll
@@ -275,14 +279,13 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
       dsf[r / 8][r % 8] = (__bf16)(p0 * (P0[r] - delta));
       dsf[2 + r / 8][r % 8] = (__bf16)(p1 * (P1[r] - delta));
     }
-
-    // dQ^T += K^T dS^T, 16 keys per MFMA; K^T read transposed
+    // dQ^T += K^T dS^T, 16 keys per product; K^T read transposed
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) dQ[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(sK, off, mb, p),
-                                                                                 dsf[p], dQ[mb], 0, 0, 0);
+      for (int p = 0; p < 4; ++p)
+        dQ[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(sK, off, mb, p), dsf[p], dQ[mb], 0, 0, 0);
     }
     __builtin_amdgcn_s_setprio(0);
     wait_tiles();
@@ -345,7 +348,7 @@ struct QRange {
 };
 
 template <int D>
-__global__ __launch_bounds__(64 * NW, 1) void dkdv_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * NW, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdArgs a) {
   constexpr int TILE = Lds<D>::TILE;
   // stage s: Q tile at 2 s TILE, dO tile at (2 s + 1) TILE; stats of stage s
   // at 4 TILE + s STATS
@@ -476,6 +479,15 @@ __global__ __launch_bounds__(64 * NW, 1) void dkdv_bf16_kernel(BwdArgs a) {
     const int qpos_max = share_pos(r, qlast, c, cp);
     const bool full = __builtin_amdgcn_readfirstlane(
         (q0 + BN <= L) & (k0 + BK <= L) & (!causal | (qpos_min >= kpos_max)) & (!packed | (qpos_max < kend_min)));
+    // the queries of rank r that see this lane's key are one local range; as
+    // offsets from the lane's first query row in the tile, [vlo, vhi)
+    int vlo = 0, vhi = BN;
+    if (!full) {
+      const int lo = causal ? count_le(r, my_kpos - 1, c, cp) : 0;
+      const int hi = kvalid ? (packed ? count_le(r, my_kend - 1, c, cp) : L) : 0;
+      vlo = lo - q0 - 8 * hh;
+      vhi = hi - q0 - 8 * hh;
+    }
 
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -498,10 +510,8 @@ __global__ __launch_bounds__(64 * NW, 1) void dkdv_bf16_kernel(BwdArgs a) {
       if (!full) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-          const int ql = q0 + 32 * blk + 16 * (rr / 8) + 8 * hh + (rr % 8);
-          const int qp = share_pos(r, ql, c, cp);
-          const bool vis = (ql < L) & kvalid & (!causal | (my_kpos <= qp)) & (!packed | (qp < my_kend));
-          S[rr] = vis ? S[rr] : -INFINITY;
+          const int qc = 32 * blk + 16 * (rr / 8) + (rr % 8);
+          S[rr] = (qc >= vlo) & (qc < vhi) ? S[rr] : -INFINITY;
         }
       }
       bf16x8 pf[2], dsf[2];
@@ -519,9 +529,9 @@ __global__ __launch_bounds__(64 * NW, 1) void dkdv_bf16_kernel(BwdArgs a) {
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          dV[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(sD, off, mb, 2 * blk + s), pf[s], dV[mb], 0, 0, 0);
-          dK[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(sQ, off, mb, 2 * blk + s), dsf[s], dK[mb], 0, 0, 0);
+        for (int sl = 0; sl < 2; ++sl) {
+          dV[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(sD, off, mb, 2 * blk + sl), pf[sl], dV[mb], 0, 0, 0);
+          dK[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(sQ, off, mb, 2 * blk + sl), dsf[sl], dK[mb], 0, 0, 0);
         }
       }
       __builtin_amdgcn_s_setprio(0);
