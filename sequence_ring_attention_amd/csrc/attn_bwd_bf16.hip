@@ -12,7 +12,7 @@
 // tiles above the diagonal are never visited and only tiles that straddle it
 // evaluate the elementwise mask.
 //
-// Two passes, each the single owner of what it writes (no atomics, results
+// Three passes, each the single owner of what it writes (no atomics, results
 // independent of scheduling):
 //   * dQ pass -- a workgroup of 4 wavefronts owns 128 query rows of one
 //     (rank, query head, batch), walks the steps' 64-key tiles like the
@@ -22,14 +22,18 @@
 //     wave's Q and dO rows in registers; dQ^T += K^T dS^T reads K transposed
 //     from the same row-major LDS tile (ds_read_b64_tr_b16) and takes dS^T
 //     straight from the registers.
-//   * dK/dV pass -- a workgroup of 4 wavefronts owns 128 keys of one (KV
-//     block, KV head, batch); each wavefront holds its 32 keys' K and V rows
-//     in registers and keeps dK^T and dV^T there.  For every rank that
-//     reaches the block and every query head reading the KV head, the visible
-//     64-row query tiles of Q and dO stream through LDS (double buffered,
-//     buffer loads straight to LDS, the forward's swizzle) with the tile's
-//     delta and lse2.  S = Q K^T and dP = dO V^T take Q and dO rows as the M
-//     operand; dV^T += dO^T P and dK^T += Q^T dS read dO and Q transposed.
+//   * dV pass and dK pass -- a workgroup of 4 wavefronts owns 128 keys of
+//     one (KV block, KV head, batch); each wavefront holds its 32 keys' K
+//     (and, for dK, V) rows in registers and keeps one accumulator, dV^T or
+//     dK^T.  For every rank that reaches the block and every query head
+//     reading the KV head, the visible 64-row query tiles of Q and dO stream
+//     through LDS (double buffered, buffer loads straight to LDS, the
+//     forward's swizzle) with the tile's delta and lse2.  S = Q K^T and
+//     dP = dO V^T take Q and dO rows as the M operand; dV^T += dO^T P and
+//     dK^T += Q^T dS read dO and Q transposed.  One pass holding both
+//     accumulators needs about 480 registers per lane, one wavefront per
+//     SIMD; split, each pass fits two, and the pair runs faster although S
+//     is computed twice.
 // The scale is applied once, to the final dQ and dK.
 #include "attn_tiles.h"
 #include "usp_internal.h"
@@ -347,8 +351,11 @@ struct QRange {
   int qt, qe;
 };
 
-template <int D>
-__global__ __launch_bounds__(64 * NW, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdArgs a) {
+// DV: the dV pass (S, then dV^T += dO^T P); otherwise the dK pass (S and dP,
+// then dK^T += Q^T dS).  Each keeps one accumulator set, which leaves room
+// for two workgroups per CU.
+template <int D, bool DV>
+__global__ __launch_bounds__(64 * NW, 2) void dkdv_bf16_kernel(BwdArgs a) {
   constexpr int TILE = Lds<D>::TILE;
   // stage s: Q tile at 2 s TILE, dO tile at (2 s + 1) TILE; stats of stage s
   // at 4 TILE + s STATS
@@ -414,12 +421,13 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 2 : 1) void dkdv_bf16_kernel(Bwd
   normalise(r, h, cur);
   if (r > r_last) return;  // no query sees these keys: nothing to add (uniform)
 
-  bf16x8 kf[D / 16], vf[D / 16];
+  bf16x8 kf[D / 16], vf[DV ? 1 : D / 16];
   const int64_t kvo = j * a.kv_blk;
   load_row_frags<D>(kf, static_cast<const __bf16 *>(a.k) + kvo + b * a.k_sb + g * a.k_sh + (int64_t)krow * a.k_ss,
                     kvalid, hh);
-  load_row_frags<D>(vf, static_cast<const __bf16 *>(a.v) + kvo + b * a.v_sb + g * a.v_sh + (int64_t)krow * a.v_ss,
-                    kvalid, hh);
+  if (!DV)
+    load_row_frags<D>(vf, static_cast<const __bf16 *>(a.v) + kvo + b * a.v_sb + g * a.v_sh + (int64_t)krow * a.v_ss,
+                      kvalid, hh);
 
   const int64_t qbytes = a.q_ss * 2, dbytes = a.do_ss * 2;
   uint32_t qvoff[Lds<D>::KIB_PER_TILE / NW], dvoff[Lds<D>::KIB_PER_TILE / NW];
@@ -452,12 +460,9 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 2 : 1) void dkdv_bf16_kernel(Bwd
   };
   const TileOffsets<D> off(lane);
 
-  f32x16 dK[D / 32], dV[D / 32];
+  f32x16 acc[D / 32];  // dV^T or dK^T
 #pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb) {
-    dK[mb] = f32x16{};
-    dV[mb] = f32x16{};
-  }
+  for (int mb = 0; mb < D / 32; ++mb) acc[mb] = f32x16{};
   const float sl2 = a.scale_log2;
   bool more = true;
 
@@ -491,22 +496,30 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 2 : 1) void dkdv_bf16_kernel(Bwd
 
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      // S = Q K^T and dP = dO V^T for 32 queries x the wave's 32 keys
+      // S = Q K^T (and dP = dO V^T) for 32 queries x the wave's 32 keys
       f32x16 S = f32x16{}, P = f32x16{};
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(sQ + off.row[ks] + blk * 32 * Lds<D>::ROW);
-        const bf16x8 da = *reinterpret_cast<const bf16x8 *>(sD + off.row[ks] + blk * 32 * Lds<D>::ROW);
         S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], S, 0, 0, 0);
-        P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ks], P, 0, 0, 0);
+        if (!DV) {
+          const bf16x8 da = *reinterpret_cast<const bf16x8 *>(sD + off.row[ks] + blk * 32 * Lds<D>::ROW);
+          P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ks], P, 0, 0, 0);
+        }
       }
       __builtin_amdgcn_s_setprio(0);
       // this lane's queries: 32 blk + 16 (r / 8) + 8 hh + r % 8
       const float4 *d4 = reinterpret_cast<const float4 *>(sst + 32 * blk + 8 * hh);
       const float4 *l4 = reinterpret_cast<const float4 *>(sst + 64 + 32 * blk + 8 * hh);
-      const float4 dl[4] = {d4[0], d4[1], d4[4], d4[5]};
       const float4 ll[4] = {l4[0], l4[1], l4[4], l4[5]};
+      float4 dl[4];
+      if (!DV) {
+        dl[0] = d4[0];
+        dl[1] = d4[1];
+        dl[2] = d4[4];
+        dl[3] = d4[5];
+      }
       if (!full) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
@@ -514,25 +527,29 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 2 : 1) void dkdv_bf16_kernel(Bwd
           S[rr] = (qc >= vlo) & (qc < vhi) ? S[rr] : -INFINITY;
         }
       }
-      bf16x8 pf[2], dsf[2];
+      bf16x8 nf[2];  // P (dV pass) or dS (dK pass), bf16, as the N operand
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        const float4 dq4 = dl[rr / 4], lq4 = ll[rr / 4];
-        const float dlt = (rr % 4 == 0) ? dq4.x : (rr % 4 == 1) ? dq4.y : (rr % 4 == 2) ? dq4.z : dq4.w;
+        const float4 lq4 = ll[rr / 4];
         const float ls = (rr % 4 == 0) ? lq4.x : (rr % 4 == 1) ? lq4.y : (rr % 4 == 2) ? lq4.z : lq4.w;
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[rr], sl2, -ls));
-        pf[rr / 8][rr % 8] = (__bf16)p;
-        dsf[rr / 8][rr % 8] = (__bf16)(p * (P[rr] - dlt));
+        if (DV) {
+          nf[rr / 8][rr % 8] = (__bf16)p;
+        } else {
+          const float4 dq4 = dl[rr / 4];
+          const float dlt = (rr % 4 == 0) ? dq4.x : (rr % 4 == 1) ? dq4.y : (rr % 4 == 2) ? dq4.z : dq4.w;
+          nf[rr / 8][rr % 8] = (__bf16)(p * (P[rr] - dlt));
+        }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS over this block's two 16-query slabs
+      // dV^T += dO^T P or dK^T += Q^T dS over this block's two 16-query slabs
+      const char *const sT = DV ? sD : sQ;
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) {
 #pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
-          dV[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(sD, off, mb, 2 * blk + sl), pf[sl], dV[mb], 0, 0, 0);
-          dK[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(sQ, off, mb, 2 * blk + sl), dsf[sl], dK[mb], 0, 0, 0);
-        }
+        for (int sl = 0; sl < 2; ++sl)
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(sT, off, mb, 2 * blk + sl), nf[sl], acc[mb],
+                                                            0, 0, 0);
       }
       __builtin_amdgcn_s_setprio(0);
     }
@@ -556,26 +573,20 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 2 : 1) void dkdv_bf16_kernel(Bwd
   }
 
   if (!kvalid) return;
-  float *dkp = a.dk + kvo + b * a.k_sb + g * a.k_sh + (int64_t)krow * a.k_ss;
-  float *dvp = a.dv + kvo + b * a.v_sb + g * a.v_sh + (int64_t)krow * a.v_ss;
-  const float scale = a.scale;
+  float *dst = DV ? a.dv + kvo + b * a.v_sb + g * a.v_sh + (int64_t)krow * a.v_ss
+                  : a.dk + kvo + b * a.k_sb + g * a.k_sh + (int64_t)krow * a.k_ss;
+  const float mul = DV ? 1.0f : a.scale;
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      float4 *pk = reinterpret_cast<float4 *>(dkp + 32 * mb + 8 * r4 + 4 * hh);
-      float4 *pv = reinterpret_cast<float4 *>(dvp + 32 * mb + 8 * r4 + 4 * hh);
-      float4 vk = *pk, vv = *pv;
-      vk.x += dK[mb][4 * r4 + 0] * scale;
-      vk.y += dK[mb][4 * r4 + 1] * scale;
-      vk.z += dK[mb][4 * r4 + 2] * scale;
-      vk.w += dK[mb][4 * r4 + 3] * scale;
-      vv.x += dV[mb][4 * r4 + 0];
-      vv.y += dV[mb][4 * r4 + 1];
-      vv.z += dV[mb][4 * r4 + 2];
-      vv.w += dV[mb][4 * r4 + 3];
-      *pk = vk;
-      *pv = vv;
+      float4 *pd = reinterpret_cast<float4 *>(dst + 32 * mb + 8 * r4 + 4 * hh);
+      float4 val = *pd;
+      val.x += acc[mb][4 * r4 + 0] * mul;
+      val.y += acc[mb][4 * r4 + 1] * mul;
+      val.z += acc[mb][4 * r4 + 2] * mul;
+      val.w += acc[mb][4 * r4 + 3] * mul;
+      *pd = val;
     }
   }
 }
@@ -598,8 +609,10 @@ hipError_t launch_d(BwdArgs a, hipStream_t stream) {
   a.xcd_remap = 0;
   const int n_slots = a.ring_rank >= 0 ? a.t_hi - a.t_lo : a.cp;
   const int64_t k_blocks = (int64_t)a.n_tiles * n_slots * a.B * a.Hkv;
-  if (k_blocks > 0)
-    hipLaunchKernelGGL((dkdv_bf16_kernel<D>), dim3((uint32_t)k_blocks), dim3(64 * NW), 0, stream, a);
+  if (k_blocks > 0) {
+    hipLaunchKernelGGL((dkdv_bf16_kernel<D, true>), dim3((uint32_t)k_blocks), dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((dkdv_bf16_kernel<D, false>), dim3((uint32_t)k_blocks), dim3(64 * NW), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
