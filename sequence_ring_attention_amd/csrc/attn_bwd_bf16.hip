@@ -45,7 +45,8 @@ using namespace tiles;
 
 constexpr int NW = 4;          // wavefronts per workgroup
 constexpr int BM = 32 * NW;    // query rows per dQ workgroup
-constexpr int BK = 32 * NW;    // keys per dK/dV workgroup
+constexpr int KW = 8;          // wavefronts per dK/dV workgroup (32 keys each)
+constexpr int NS = 4;          // dK/dV pipeline stages (query tiles in flight + 1)
 constexpr int STATS = 512;     // bytes of one tile's delta[64] and lse2[64]
 
 __device__ inline int mod_cp(int x, int cp) {
@@ -108,13 +109,14 @@ __device__ inline bf16x8 read_tr(const char *tile, const TileOffsets<D> &o, int 
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Per-lane byte offsets of the direct tile loads (see issue_tile_lds).
-template <int D>
+// Per-lane byte offsets of the direct tile loads of a W-wavefront workgroup
+// (see issue_tile_lds).
+template <int D, int W>
 __device__ inline void tile_load_offsets(uint32_t *voff, int64_t rowbytes, int wave, int lane) {
   constexpr int CH = Lds<D>::CH;
 #pragma unroll
-  for (int i = 0; i < Lds<D>::KIB_PER_TILE / NW; ++i) {
-    const int row = (wave + NW * i) * Lds<D>::KEYS_PER_KIB + lane / CH;
+  for (int i = 0; i < Lds<D>::KIB_PER_TILE / W; ++i) {
+    const int row = (wave + W * i) * Lds<D>::KEYS_PER_KIB + lane / CH;
     voff[i] = (uint32_t)(row * rowbytes + swz<D>(row, lane % CH) * 16);
   }
 }
@@ -206,9 +208,9 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
   auto issue_tile = [&](int j, int k0, int stg) {
     char *const st = smem + stg * Lds<D>::STAGE;
     uint32_t voff[Lds<D>::KIB_PER_TILE / NW];  // recomputed per tile: a few VALU ops, registers are short
-    tile_load_offsets<D>(voff, kbytes, wave, lane);
+    tile_load_offsets<D, NW>(voff, kbytes, wave, lane);
     issue_tile_lds<D, NW>(st, kbase + 2 * j * a.kv_blk, k_extent, kbytes, k0, L, wave, lane, voff);
-    tile_load_offsets<D>(voff, vbytes, wave, lane);
+    tile_load_offsets<D, NW>(voff, vbytes, wave, lane);
     issue_tile_lds<D, NW>(st + Lds<D>::TILE, vbase + 2 * j * a.kv_blk, v_extent, vbytes, k0, L, wave, lane, voff);
   };
   auto wait_tiles = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
@@ -353,13 +355,24 @@ struct QRange {
 
 // DV: the dV pass (S, then dV^T += dO^T P); otherwise the dK pass (S and dP,
 // then dK^T += Q^T dS).  Each keeps one accumulator set, which leaves room
-// for two workgroups per CU.
-template <int D, bool DV>
-__global__ __launch_bounds__(64 * NW, 2) void dkdv_bf16_kernel(BwdArgs a) {
+// for two wavefronts per SIMD.
+//
+// Query tiles stream through an NS-stage ring in LDS, issued NS - 1 tiles
+// ahead: a Q and a dO tile (direct buffer loads, the forward's swizzle) and
+// the tile's delta and lse2 (dword direct loads by wavefronts 0 and 1).  Each
+// wavefront waits with a count of its own loads still allowed in flight, and
+// one barrier per tile both publishes the tile and frees the stage read in
+// the previous tile for the next issue.
+template <int D, bool DV, int KW>
+__global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
+  constexpr int BK = 32 * KW;  // keys per workgroup
   constexpr int TILE = Lds<D>::TILE;
-  // stage s: Q tile at 2 s TILE, dO tile at (2 s + 1) TILE; stats of stage s
-  // at 4 TILE + s STATS
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE + 2 * STATS];
+  constexpr int STAGE = 2 * TILE;                        // Q tile, then dO tile
+  constexpr int NBLK = Lds<D>::KIB_PER_TILE / KW;        // direct loads per wavefront per tile
+  constexpr int OPS = 2 * NBLK;                          // vector memory ops per wavefront per tile
+  // NS stages, then NS statistics slots (delta[64], lse2[64]), then slack
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE + NS * STATS + 1024];
+  char *const sstats = smem + NS * STAGE;
 
   // work item: key tiles in order of local index (the first chunk of a
   // share holds the earliest positions, which the most queries see)
@@ -406,20 +419,28 @@ __global__ __launch_bounds__(64 * NW, 2) void dkdv_bf16_kernel(BwdArgs a) {
     }
     return x;
   };
-  // iteration state: rank r, query head offset h in the group, tile range
-  int r = r_first, h = 0;
-  QRange cur = q_range(r);
-  auto normalise = [&](int &rx, int &hx, QRange &x) {
-    while (x.qt >= x.qe && rx <= r_last) {
-      if (++hx == a.G) {
-        hx = 0;
-        if (++rx > r_last) break;
+  // tile iterator: rank r, query head offset h in the group, tile range;
+  // exhausted when r > r_last
+  struct It {
+    int r, h;
+    QRange x;
+  };
+  auto normalise = [&](It &it) {
+    while (it.x.qt >= it.x.qe && it.r <= r_last) {
+      if (++it.h == a.G) {
+        it.h = 0;
+        if (++it.r > r_last) break;
       }
-      x = q_range(rx);
+      it.x = q_range(it.r);
     }
   };
-  normalise(r, h, cur);
-  if (r > r_last) return;  // no query sees these keys: nothing to add (uniform)
+  auto advance = [&](It &it) {
+    ++it.x.qt;
+    normalise(it);
+  };
+  It cur{r_first, 0, q_range(r_first)};
+  normalise(cur);
+  if (cur.r > r_last) return;  // no query sees these keys: nothing to add (uniform)
 
   bf16x8 kf[D / 16], vf[DV ? 1 : D / 16];
   const int64_t kvo = j * a.kv_blk;
@@ -430,55 +451,81 @@ __global__ __launch_bounds__(64 * NW, 2) void dkdv_bf16_kernel(BwdArgs a) {
                       kvalid, hh);
 
   const int64_t qbytes = a.q_ss * 2, dbytes = a.do_ss * 2;
-  uint32_t qvoff[Lds<D>::KIB_PER_TILE / NW], dvoff[Lds<D>::KIB_PER_TILE / NW];
-  tile_load_offsets<D>(qvoff, qbytes, wave, lane);
-  tile_load_offsets<D>(dvoff, dbytes, wave, lane);
+  uint32_t qvoff[NBLK], dvoff[NBLK];
+  tile_load_offsets<D, KW>(qvoff, qbytes, wave, lane);
+  tile_load_offsets<D, KW>(dvoff, dbytes, wave, lane);
   const uint32_t q_extent = (uint32_t)((L - 1) * qbytes + 2 * D);
   const uint32_t d_extent = (uint32_t)((L - 1) * dbytes + 2 * D);
-  // a tile's statistics: thread i < 64 loads delta of row q0 + i, thread
-  // 64 + i its lse2, into a register; it is stored to LDS once the tile's
-  // loads have landed (the rows of a tile are only 4-byte aligned in HBM)
-  float st_val = 0.0f;
-  auto issue = [&](int rx, int hx, int qt, int stg) {
-    const int hq = g * a.G + hx;
+  // delta and lse2 as two bounded arrays: a read past a tile's last row
+  // returns a neighbour's statistics or 0, both harmless on masked rows
+  const __amdgpu_buffer_rsrc_t delta_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.stats), 0, (uint32_t)(a.rows * 4), RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t lse2_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(a.stats + a.rows), 0, (uint32_t)(a.rows * 4), RSRC_WORD3);
+  auto issue = [&](const It &it, int stg) {
+    const int hq = g * a.G + it.h;
     const char *qb = static_cast<const char *>(a.q) +
-                     2 * ((a.ring_rank < 0 ? rx * a.q_rank : 0) + b * a.q_sb + hq * a.q_sh);
+                     2 * ((a.ring_rank < 0 ? it.r * a.q_rank : 0) + b * a.q_sb + hq * a.q_sh);
     const char *db = static_cast<const char *>(a.dout) +
-                     2 * ((a.ring_rank < 0 ? rx * a.do_rank : 0) + b * a.do_sb + hq * a.do_sh);
-    issue_tile_lds<D, NW>(smem + 2 * stg * TILE, qb, q_extent, qbytes, qt * BN, L, wave, lane, qvoff);
-    issue_tile_lds<D, NW>(smem + (2 * stg + 1) * TILE, db, d_extent, dbytes, qt * BN, L, wave, lane, dvoff);
-    if (tid < 2 * BN) {
-      const int rs = a.ring_rank >= 0 ? 0 : rx;
-      const int i = qt * BN + (tid & (BN - 1));
-      const int64_t srow = (((int64_t)rs * a.Hq + hq) * a.B + b) * L + i;
-      st_val = i < L ? a.stats[srow + (tid >= BN ? a.rows : 0)] : 0.0f;
+                     2 * ((a.ring_rank < 0 ? it.r * a.do_rank : 0) + b * a.do_sb + hq * a.do_sh);
+    char *const st = smem + stg * STAGE;
+    issue_tile_lds<D, KW>(st, qb, q_extent, qbytes, it.x.qt * BN, L, wave, lane, qvoff);
+    issue_tile_lds<D, KW>(st + TILE, db, d_extent, dbytes, it.x.qt * BN, L, wave, lane, dvoff);
+    if (wave < 2) {
+      const int rs = a.ring_rank >= 0 ? 0 : it.r;
+      const int64_t srow = (((int64_t)rs * a.Hq + hq) * a.B + b) * L + it.x.qt * BN;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wave == 0 ? delta_rsrc : lse2_rsrc,
+                                               (lds_void *)(sstats + stg * STATS + wave * (STATS / 2)), 4,
+                                               (uint32_t)((srow + lane) * 4), 0, 0, 0);
     }
   };
-  auto wait_tiles = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
-  auto store_stats = [&](int stg) {
-    if (tid < 2 * BN) reinterpret_cast<float *>(smem + 4 * TILE + stg * STATS)[tid] = st_val;
+  // wait until the tile `after` tiles before the newest one has landed
+  auto wait_tile = [&](int after) {
+    if (wave < 2) {
+      if (after >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (OPS + 1)) : "memory");
+      else if (after == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(OPS + 1) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      if (after >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * OPS) : "memory");
+      else if (after == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(OPS) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
   };
+  static_assert(NS == 4, "wait_tile covers up to two younger tiles in flight");
   const TileOffsets<D> off(lane);
 
   f32x16 acc[D / 32];  // dV^T or dK^T
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) acc[mb] = f32x16{};
   const float sl2 = a.scale_log2;
-  bool more = true;
+
+  // prologue: the first NS - 1 tiles
+  It ld = cur;
+  int pending = 0;  // tiles issued and not yet computed (uniform)
+#pragma unroll
+  for (int k = 0; k < NS - 1; ++k) {
+    if (ld.r <= r_last) {
+      issue(ld, k);
+      ++pending;
+      advance(ld);
+    }
+  }
 
   auto body = [&](auto stage_tag) {
     constexpr int STG = decltype(stage_tag)::value;
-    int r_n = r, h_n = h;
-    QRange nxt = cur;
-    ++nxt.qt;
-    normalise(r_n, h_n, nxt);
-    const bool has_next = r_n <= r_last;
-    if (has_next) issue(r_n, h_n, nxt.qt, STG ^ 1);
+    wait_tile(pending - 1);
+    __syncthreads();  // tile ready for every wavefront; the previous stage is free
+    if (ld.r <= r_last) {
+      issue(ld, (STG + NS - 1) % NS);
+      ++pending;
+      advance(ld);
+    }
 
-    const char *const sQ = smem + 2 * STG * TILE;
+    const char *const sQ = smem + STG * STAGE;
     const char *const sD = sQ + TILE;
-    const float *const sst = reinterpret_cast<const float *>(smem + 4 * TILE + STG * STATS);
-    const int q0 = cur.qt * BN;
+    const float *const sst = reinterpret_cast<const float *>(sstats + STG * STATS);
+    const int r = cur.r;
+    const int q0 = cur.x.qt * BN;
     const int qlast = min(q0 + BN, L) - 1;
     const int qpos_min = share_pos(r, q0, c, cp);
     const int qpos_max = share_pos(r, qlast, c, cp);
@@ -494,82 +541,106 @@ __global__ __launch_bounds__(64 * NW, 2) void dkdv_bf16_kernel(BwdArgs a) {
       vhi = hi - q0 - 8 * hh;
     }
 
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      // S = Q K^T (and dP = dO V^T) for 32 queries x the wave's 32 keys
-      f32x16 S = f32x16{}, P = f32x16{};
+    if (DV) {
+      // S = Q K^T for the tile's two 32-query blocks as two interleaved
+      // accumulator chains, then P and dV^T += dO^T P
+      f32x16 S2[2] = {f32x16{}, f32x16{}};
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(sQ + off.row[ks] + blk * 32 * Lds<D>::ROW);
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], S, 0, 0, 0);
-        if (!DV) {
-          const bf16x8 da = *reinterpret_cast<const bf16x8 *>(sD + off.row[ks] + blk * 32 * Lds<D>::ROW);
-          P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ks], P, 0, 0, 0);
-        }
+        const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(sQ + off.row[ks]);
+        const bf16x8 qb = *reinterpret_cast<const bf16x8 *>(sQ + off.row[ks] + 32 * Lds<D>::ROW);
+        S2[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], S2[0], 0, 0, 0);
+        S2[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb, kf[ks], S2[1], 0, 0, 0);
       }
       __builtin_amdgcn_s_setprio(0);
-      // this lane's queries: 32 blk + 16 (r / 8) + 8 hh + r % 8
-      const float4 *d4 = reinterpret_cast<const float4 *>(sst + 32 * blk + 8 * hh);
-      const float4 *l4 = reinterpret_cast<const float4 *>(sst + 64 + 32 * blk + 8 * hh);
-      const float4 ll[4] = {l4[0], l4[1], l4[4], l4[5]};
-      float4 dl[4];
-      if (!DV) {
-        dl[0] = d4[0];
-        dl[1] = d4[1];
-        dl[2] = d4[4];
-        dl[3] = d4[5];
-      }
-      if (!full) {
+      bf16x8 pf[4];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        // this lane's queries: 32 blk + 16 (r / 8) + 8 hh + r % 8
+        const float4 *l4 = reinterpret_cast<const float4 *>(sst + 64 + 32 * blk + 8 * hh);
+        const float4 ll[4] = {l4[0], l4[1], l4[4], l4[5]};
+        if (!full) {
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int qc = 32 * blk + 16 * (rr / 8) + (rr % 8);
+            S2[blk][rr] = (qc >= vlo) & (qc < vhi) ? S2[blk][rr] : -INFINITY;
+          }
+        }
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-          const int qc = 32 * blk + 16 * (rr / 8) + (rr % 8);
-          S[rr] = (qc >= vlo) & (qc < vhi) ? S[rr] : -INFINITY;
+          const float4 lq4 = ll[rr / 4];
+          const float ls = (rr % 4 == 0) ? lq4.x : (rr % 4 == 1) ? lq4.y : (rr % 4 == 2) ? lq4.z : lq4.w;
+          pf[2 * blk + rr / 8][rr % 8] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(S2[blk][rr], sl2, -ls));
         }
       }
-      bf16x8 nf[2];  // P (dV pass) or dS (dK pass), bf16, as the N operand
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const float4 lq4 = ll[rr / 4];
-        const float ls = (rr % 4 == 0) ? lq4.x : (rr % 4 == 1) ? lq4.y : (rr % 4 == 2) ? lq4.z : lq4.w;
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[rr], sl2, -ls));
-        if (DV) {
-          nf[rr / 8][rr % 8] = (__bf16)p;
-        } else {
-          const float4 dq4 = dl[rr / 4];
-          const float dlt = (rr % 4 == 0) ? dq4.x : (rr % 4 == 1) ? dq4.y : (rr % 4 == 2) ? dq4.z : dq4.w;
-          nf[rr / 8][rr % 8] = (__bf16)(p * (P[rr] - dlt));
-        }
-      }
-      // dV^T += dO^T P or dK^T += Q^T dS over this block's two 16-query slabs
-      const char *const sT = DV ? sD : sQ;
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) {
 #pragma unroll
-        for (int sl = 0; sl < 2; ++sl)
-          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(sT, off, mb, 2 * blk + sl), nf[sl], acc[mb],
-                                                            0, 0, 0);
+        for (int sl = 0; sl < 4; ++sl)
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(sD, off, mb, sl), pf[sl], acc[mb], 0, 0, 0);
       }
       __builtin_amdgcn_s_setprio(0);
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        // S = Q K^T and dP = dO V^T for 32 queries x the wave's 32 keys
+        f32x16 S = f32x16{}, P = f32x16{};
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(sQ + off.row[ks] + blk * 32 * Lds<D>::ROW);
+          const bf16x8 da = *reinterpret_cast<const bf16x8 *>(sD + off.row[ks] + blk * 32 * Lds<D>::ROW);
+          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], S, 0, 0, 0);
+          P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ks], P, 0, 0, 0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+        const float4 *d4 = reinterpret_cast<const float4 *>(sst + 32 * blk + 8 * hh);
+        const float4 *l4 = reinterpret_cast<const float4 *>(sst + 64 + 32 * blk + 8 * hh);
+        const float4 dl[4] = {d4[0], d4[1], d4[4], d4[5]};
+        const float4 ll[4] = {l4[0], l4[1], l4[4], l4[5]};
+        if (!full) {
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int qc = 32 * blk + 16 * (rr / 8) + (rr % 8);
+            S[rr] = (qc >= vlo) & (qc < vhi) ? S[rr] : -INFINITY;
+          }
+        }
+        bf16x8 dsf[2];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const float4 dq4 = dl[rr / 4], lq4 = ll[rr / 4];
+          const float dlt = (rr % 4 == 0) ? dq4.x : (rr % 4 == 1) ? dq4.y : (rr % 4 == 2) ? dq4.z : dq4.w;
+          const float ls = (rr % 4 == 0) ? lq4.x : (rr % 4 == 1) ? lq4.y : (rr % 4 == 2) ? lq4.z : lq4.w;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[rr], sl2, -ls));
+          dsf[rr / 8][rr % 8] = (__bf16)(p * (P[rr] - dlt));
+        }
+        // dK^T += Q^T dS over this block's two 16-query slabs
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb) {
+#pragma unroll
+          for (int sl = 0; sl < 2; ++sl)
+            acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(sQ, off, mb, 2 * blk + sl), dsf[sl], acc[mb],
+                                                              0, 0, 0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+      }
     }
-    wait_tiles();
-    if (has_next) store_stats(STG ^ 1);
-    __syncthreads();
-    r = r_n;
-    h = h_n;
-    cur = nxt;
-    more = has_next;
+    --pending;
+    advance(cur);
   };
 
-  issue(r, h, cur.qt, 0);
-  wait_tiles();
-  store_stats(0);
-  __syncthreads();
-  while (more) {
+  while (true) {
     body(StageTag<0>{});
-    if (!more) break;
+    if (pending == 0) break;
     body(StageTag<1>{});
+    if (pending == 0) break;
+    body(StageTag<2>{});
+    if (pending == 0) break;
+    body(StageTag<3>{});
+    if (pending == 0) break;
   }
 
   if (!kvalid) return;
@@ -604,14 +675,14 @@ hipError_t launch_d(BwdArgs a, hipStream_t stream) {
     else
       hipLaunchKernelGGL((dq_bf16_kernel<D, false>), dim3((uint32_t)q_blocks), dim3(64 * NW), 0, stream, a);
   }
-  // dK/dV pass
-  a.n_tiles = (a.L + BK - 1) / BK;
+  // dV and dK passes
+  a.n_tiles = (a.L + 32 * KW - 1) / (32 * KW);
   a.xcd_remap = 0;
   const int n_slots = a.ring_rank >= 0 ? a.t_hi - a.t_lo : a.cp;
   const int64_t k_blocks = (int64_t)a.n_tiles * n_slots * a.B * a.Hkv;
   if (k_blocks > 0) {
-    hipLaunchKernelGGL((dkdv_bf16_kernel<D, true>), dim3((uint32_t)k_blocks), dim3(64 * NW), 0, stream, a);
-    hipLaunchKernelGGL((dkdv_bf16_kernel<D, false>), dim3((uint32_t)k_blocks), dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((dkdv_bf16_kernel<D, true, KW>), dim3((uint32_t)k_blocks), dim3(64 * KW), 0, stream, a);
+    hipLaunchKernelGGL((dkdv_bf16_kernel<D, false, KW>), dim3((uint32_t)k_blocks), dim3(64 * KW), 0, stream, a);
   }
   return hipGetLastError();
 }
