@@ -40,10 +40,13 @@
 //     are XOR-swizzled by the row index, chosen so that the K operand reads
 //     (16 rows, one chunk) and the transposed V reads (4 rows, two chunks)
 //     hit distinct banks;
-//   * the running max is only moved (and O rescaled) when a tile's max
-//     exceeds it by more than 2^8: below that the probabilities are computed
-//     against the stale max, which changes nothing but the reference point of
-//     the final division (o = O / l and lse = m + log l stay exact).
+//   * the running max is a reference point, not the exact max: a tile's
+//     probabilities are computed against it as long as they stay in range
+//     (every lane's sum of its 32 below 2^64), so the tile max is only taken
+//     on the first tiles of a row or when that check fails, and the reference
+//     then moves (and O is rescaled) only if the tile max exceeds it by more
+//     than 2^8.  This changes nothing but the reference point of the final
+//     division (o = O / l and lse = m + log l stay exact).
 //
 // Grid order: heaviest query tiles first (the last rows of a share see the
 // most keys), and the Hq / Hkv query heads that read one KV head run back to
@@ -65,7 +68,11 @@ constexpr float TAU = 8.0f;  // log2 headroom before the running max must move
 template <int D, bool PARTIAL, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int BM = 32 * NW;
-  __shared__ __attribute__((aligned(1024))) char smem[Lds<D>::BYTES];
+  // one array per stage: reads of one stage and the direct loads filling the
+  // other are then provably disjoint, and the compiler does not make the
+  // reads wait for those loads
+  __shared__ __attribute__((aligned(1024))) char smem0[Lds<D>::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem1[Lds<D>::STAGE];
 
   // ---------------------------------------------------------- work item --
   const int bid = blockIdx.x;
@@ -160,7 +167,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
   const uint32_t k_extent = (uint32_t)((L - 1) * kbytes + 2 * D);
   const uint32_t v_extent = (uint32_t)((L - 1) * vbytes + 2 * D);
   auto issue_tile = [&](int j, int k0, int stg) {
-    char *const st = smem + stg * Lds<D>::STAGE;
+    char *const st = stg == 0 ? smem0 : smem1;
     issue_tile_lds<D, NW>(st, kbase + 2 * j * a.kv_blk, k_extent, kbytes, k0, L, wave, lane, kvoff);
     issue_tile_lds<D, NW>(st + Lds<D>::TILE, vbase + 2 * j * a.kv_blk, v_extent, vbytes, k0, L, wave, lane, vvoff);
   };
@@ -209,7 +216,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
     advance(t_nxt, nxt);
     if (t_nxt < a.t_hi) issue_tile(nxt.j, nxt.kt * BN, STG ^ 1);
 
-    const char *const sK = smem + STG * Lds<D>::STAGE;
+    const char *const sK = STG == 0 ? smem0 : smem1;
     const char *const sV = sK + Lds<D>::TILE;
     const int j = cur.j;
     const int k0 = cur.kt * BN;
@@ -230,6 +237,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
       S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], S0, 0, 0, 0);
       S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[ks], S1, 0, 0, 0);
     }
+    // keep LDS reads of K several products ahead: half of them up front, then
+    // two products per two reads, then the rest of the products
+    __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
     __builtin_amdgcn_s_setprio(0);
 
     if (!full) {  // diagonal, sample-boundary or ragged tile: elementwise mask
@@ -245,34 +261,53 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
       }
     }
 
-    // online softmax (base 2, scale folded in), running max moved lazily
-    float mx = S0[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S0[r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S1[r]);
-    mx = partner_max(mx) * sl2;
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + TAU) != 0) {  // some row's max moved: rescale (wave-uniform)
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) O[mb] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = m_run == -INFINITY ? 0.0f : m_run;
-    float ps0 = 0.0f, ps1 = 0.0f;
+    // online softmax (base 2, scale folded in) against the running reference
+    // m_run.  The tile's row max is only taken when some row has no reference
+    // yet or when a probability left the safe range (a lane's sum of 32 is
+    // not below 2^64, which also catches inf); otherwise the probabilities of
+    // the stale reference are used as they are, which changes nothing but
+    // the reference point of the final division.  When the max is taken, the
+    // reference only moves if the tile max exceeds it by more than 2^TAU.
     bf16x8 pf[4];
+    float ps;
+    auto probs = [&](float m_use) {
+      // the row sum takes the unrounded probabilities: lse is exact to fp32
+      // rounding, while O's weights are their bf16 roundings
+      float ps0 = 0.0f, ps1 = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[r], sl2, -m_use));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[r], sl2, -m_use));
-      ps0 += p0;
-      ps1 += p1;
-      pf[r / 8][r % 8] = (__bf16)p0;
-      pf[2 + r / 8][r % 8] = (__bf16)p1;
+      for (int r = 0; r < 16; ++r) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[r], sl2, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[r], sl2, -m_use));
+        ps0 += p0;
+        ps1 += p1;
+        pf[r / 8][r % 8] = (__bf16)p0;
+        pf[2 + r / 8][r % 8] = (__bf16)p1;
+      }
+      ps = ps0 + ps1;
+    };
+    bool need_max = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
+    if (!need_max) {
+      probs(m_run);
+      need_max = __builtin_amdgcn_ballot_w64(!(ps < 0x1p64f)) != 0;
     }
-    l_run += ps0 + ps1;
+    if (need_max) {  // wave-uniform
+      float mx = S0[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S0[r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S1[r]);
+      mx = partner_max(mx) * sl2;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + TAU) != 0) {  // some row's reference moves: rescale
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb) O[mb] *= alpha;
+        m_run = m_new;
+      }
+      probs(m_run == -INFINITY ? 0.0f : m_run);
+    }
+    l_run += ps;
 
     // O^T += V^T P^T, 16 keys per MFMA; V^T read transposed from row-major V
     __builtin_amdgcn_s_setprio(1);

@@ -125,7 +125,10 @@ __device__ inline void tile_load_offsets(uint32_t *voff, int64_t rowbytes, int w
 
 template <int D, bool ACC>
 __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[Lds<D>::BYTES];
+  // one array per stage, as in the forward: reads of one stage are then
+  // provably disjoint from the direct loads filling the other
+  __shared__ __attribute__((aligned(1024))) char smem0[Lds<D>::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem1[Lds<D>::STAGE];
 
   // work item: as the forward (heaviest query tiles first, the query heads
   // of one KV head back to back on one XCD)
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
   const uint32_t k_extent = (uint32_t)((L - 1) * kbytes + 2 * D);
   const uint32_t v_extent = (uint32_t)((L - 1) * vbytes + 2 * D);
   auto issue_tile = [&](int j, int k0, int stg) {
-    char *const st = smem + stg * Lds<D>::STAGE;
+    char *const st = stg == 0 ? smem0 : smem1;
     uint32_t voff[Lds<D>::KIB_PER_TILE / NW];  // recomputed per tile: a few VALU ops, registers are short
     tile_load_offsets<D, NW>(voff, kbytes, wave, lane);
     issue_tile_lds<D, NW>(st, kbase + 2 * j * a.kv_blk, k_extent, kbytes, k0, L, wave, lane, voff);
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
     advance(t_nxt, nxt);
     if (t_nxt < a.t_hi) issue_tile(nxt.j, nxt.kt * BN, STG ^ 1);
 
-    const char *const sK = smem + STG * Lds<D>::STAGE;
+    const char *const sK = STG == 0 ? smem0 : smem1;
     const char *const sV = sK + Lds<D>::TILE;
     const int j = cur.j;
     const int k0 = cur.kt * BN;
@@ -370,9 +373,15 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
   constexpr int STAGE = 2 * TILE;                        // Q tile, then dO tile
   constexpr int NBLK = Lds<D>::KIB_PER_TILE / KW;        // direct loads per wavefront per tile
   constexpr int OPS = 2 * NBLK;                          // vector memory ops per wavefront per tile
-  // NS stages, then NS statistics slots (delta[64], lse2[64]), then slack
-  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE + NS * STATS + 1024];
-  char *const sstats = smem + NS * STAGE;
+  // one array per stage (tiles, then the tile's delta[64] and lse2[64]):
+  // the reads of one stage are then provably disjoint from the direct loads
+  // filling the others, and the compiler does not make them wait for those
+  __shared__ __attribute__((aligned(1024))) char ring0[STAGE + STATS];
+  __shared__ __attribute__((aligned(1024))) char ring1[STAGE + STATS];
+  __shared__ __attribute__((aligned(1024))) char ring2[STAGE + STATS];
+  __shared__ __attribute__((aligned(1024))) char ring3[STAGE + STATS];
+  // every stage index below is a compile-time constant after unrolling
+  auto stage_base = [&](int stg) -> char * { return stg == 0 ? ring0 : stg == 1 ? ring1 : stg == 2 ? ring2 : ring3; };
 
   // work item: key tiles in order of local index (the first chunk of a
   // share holds the earliest positions, which the most queries see)
@@ -391,7 +400,7 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
   const bool causal = a.causal != 0, packed = a.cu != nullptr;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hh = lane >> 5;
   const int k0 = kt * BK;
   const int krow = k0 + 32 * wave + n;
@@ -468,14 +477,14 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
                      2 * ((a.ring_rank < 0 ? it.r * a.q_rank : 0) + b * a.q_sb + hq * a.q_sh);
     const char *db = static_cast<const char *>(a.dout) +
                      2 * ((a.ring_rank < 0 ? it.r * a.do_rank : 0) + b * a.do_sb + hq * a.do_sh);
-    char *const st = smem + stg * STAGE;
+    char *const st = stage_base(stg);
     issue_tile_lds<D, KW>(st, qb, q_extent, qbytes, it.x.qt * BN, L, wave, lane, qvoff);
     issue_tile_lds<D, KW>(st + TILE, db, d_extent, dbytes, it.x.qt * BN, L, wave, lane, dvoff);
     if (wave < 2) {
       const int rs = a.ring_rank >= 0 ? 0 : it.r;
       const int64_t srow = (((int64_t)rs * a.Hq + hq) * a.B + b) * L + it.x.qt * BN;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wave == 0 ? delta_rsrc : lse2_rsrc,
-                                               (lds_void *)(sstats + stg * STATS + wave * (STATS / 2)), 4,
+                                               (lds_void *)(st + STAGE + wave * (STATS / 2)), 4,
                                                (uint32_t)((srow + lane) * 4), 0, 0, 0);
     }
   };
@@ -514,16 +523,20 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
   auto body = [&](auto stage_tag) {
     constexpr int STG = decltype(stage_tag)::value;
     wait_tile(pending - 1);
-    __syncthreads();  // tile ready for every wavefront; the previous stage is free
+    // tile ready for every wavefront; the previous stage is free.  All LDS
+    // writes here are direct loads each wavefront has just waited for, so a
+    // plain barrier suffices: a workgroup fence would also drain the loads
+    // still in flight for the next stages
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (ld.r <= r_last) {
       issue(ld, (STG + NS - 1) % NS);
       ++pending;
       advance(ld);
     }
 
-    const char *const sQ = smem + STG * STAGE;
+    const char *const sQ = stage_base(STG);
     const char *const sD = sQ + TILE;
-    const float *const sst = reinterpret_cast<const float *>(sstats + STG * STATS);
+    const float *const sst = reinterpret_cast<const float *>(sQ + STAGE);
     const int r = cur.r;
     const int q0 = cur.x.qt * BN;
     const int qlast = min(q0 + BN, L) - 1;
