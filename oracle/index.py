@@ -41,6 +41,27 @@ def zigzag_share_positions(S, rd, ring_rank):
     return zigzag_local_positions(S, rd, 1, ring_rank, 0)
 
 
+def zigzag_per_sample_positions(cu_seqlens, rd, ring_rank):
+    """Positions held by ring rank r when Algorithm 2's split is applied to
+    every packed sample on its own ([USP review] section 三, Algorithm 2, with
+    the packing of [ByteScale notes]): sample n, whose length must divide by
+    2*rd, is cut into 2*rd chunks and the rank takes chunks r and 2*rd-1-r;
+    the share is these pieces in sample order.  With one sample this is
+    :func:`zigzag_share_positions`."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    parts = []
+    for n in range(len(cu) - 1):
+        chunks = _chunk(np.arange(cu[n], cu[n + 1], dtype=np.int64), 2 * rd)
+        parts += [chunks[ring_rank], chunks[2 * rd - ring_rank - 1]]
+    return np.concatenate(parts)
+
+
+def zigzag_per_sample_local_positions(cu_seqlens, rd, ud, ring_rank, ulysses_rank):
+    """Per-sample zigzag share of ring rank r, then Algorithm 2's Ulysses
+    split: the u-th of ud equal parts."""
+    return _chunk(zigzag_per_sample_positions(cu_seqlens, rd, ring_rank), ud)[ulysses_rank]
+
+
 def zigzag_extract(x, rd, ud, ring_rank, ulysses_rank):
     """Local shard of (B, S, H, D) array ``x`` for rank (r, u): (B, 2c/ud, H, D)."""
     pos = zigzag_local_positions(x.shape[1], rd, ud, ring_rank, ulysses_rank)

@@ -49,11 +49,14 @@ def ring_attention_rank(q_local, q_pos, k_blocks, v_blocks, k_pos_blocks, ring_r
     return (o, lse, partials) if return_partials else (o, lse)
 
 
-def usp_attention(Q, K, V, rd, ud, scale, causal=True, cu_seqlens=None):
+def usp_attention(Q, K, V, rd, ud, scale, causal=True, cu_seqlens=None, per_sample=False):
     """Algorithm 1 with Algorithm 2's split, on all rd*ud virtual ranks.
 
     Q: (B, S, H, D); K, V: (B, S, Hkv, D) in global token order.  Returns
-    o: (B, S, H, D) in global order and lse: (H, B, S).
+    o: (B, S, H, D) in global order and lse: (H, B, S).  ``per_sample``
+    applies the split to every packed sample of ``cu_seqlens`` on its own
+    (:func:`index.zigzag_per_sample_positions`) instead of to the whole
+    packed stream.
     """
     B, S, H, D = Q.shape
     Hkv = K.shape[2]
@@ -61,8 +64,15 @@ def usp_attention(Q, K, V, rd, ud, scale, causal=True, cu_seqlens=None):
         raise ValueError("head counts must divide by the Ulysses degree")
 
     # Algorithm 2: every rank's local tokens.
+    if per_sample:
+        if cu_seqlens is None:
+            raise ValueError("the per-sample split needs cu_seqlens")
+        local = lambda r, u: ix.zigzag_per_sample_local_positions(cu_seqlens, rd, ud, r, u)
+    else:
+        local = lambda r, u: ix.zigzag_local_positions(S, rd, ud, r, u)
+
     def shards(X):
-        return [[ix.zigzag_extract(X, rd, ud, r, u) for u in range(ud)] for r in range(rd)]
+        return [[X[:, local(r, u)].copy() for u in range(ud)] for r in range(rd)]
     Qs, Ks, Vs = shards(Q), shards(K), shards(V)
 
     # Algorithm 1 steps 1-3: AllToAll4D over each Ulysses group (fixed r).
@@ -72,8 +82,7 @@ def usp_attention(Q, K, V, rd, ud, scale, causal=True, cu_seqlens=None):
     Qh, Kh, Vh = a2a(Qs), a2a(Ks), a2a(Vs)
 
     # Positions after the gather: peer shards concatenated in Ulysses order.
-    share_pos = [np.concatenate([ix.zigzag_local_positions(S, rd, ud, r, u) for u in range(ud)])
-                 for r in range(rd)]
+    share_pos = [np.concatenate([local(r, u) for u in range(ud)]) for r in range(rd)]
 
     # Algorithm 1 step 4: the ring, per (r, u).
     Oh = [[None] * ud for _ in range(rd)]
@@ -91,7 +100,7 @@ def usp_attention(Q, K, V, rd, ud, scale, causal=True, cu_seqlens=None):
     O = np.zeros((B, S, H, D))
     for r in range(rd):
         for u in range(ud):
-            O[:, ix.zigzag_local_positions(S, rd, ud, r, u)] = ix.ulysses_inv(Oh[r], u)
+            O[:, local(r, u)] = ix.ulysses_inv(Oh[r], u)
     return O, lse
 
 
