@@ -42,7 +42,10 @@
 extern "C" {
 #endif
 
-#define USP_ABI_VERSION 2
+#define USP_ABI_VERSION 3
+
+/* Most packed samples one call takes (their boundaries travel by value). */
+#define USP_MAX_SEQS 256
 
 typedef enum {
   USP_OK = 0,
@@ -86,11 +89,18 @@ typedef struct {
   int64_t q_rank_stride;  /* usp_attn_fwd with ring_rank = -1: elements from
                              rank r's query share to rank r + 1's               */
   int64_t o_rank_stride;  /* same, for the output O                            */
-  const int32_t *cu_seqlens; /* device; num_seqs + 1 increasing global
-                             boundaries from 0 to S of packed samples (a key is
-                             visible only inside its query's sample; needs
-                             causal = 1).  NULL = one sequence.                 */
-  int32_t num_seqs;
+  const int32_t *cu_seqlens; /* HOST memory, read during the call only:
+                             num_seqs + 1 strictly increasing global boundaries
+                             from 0 to S of packed samples (a key is visible
+                             only inside its query's sample; needs causal = 1).
+                             NULL = one sequence.                               */
+  int32_t num_seqs;       /* 1 .. USP_MAX_SEQS when cu_seqlens is set           */
+  int32_t zigzag_per_sample; /* 0: the shares are Algorithm 2's split of the
+                             whole packed stream.  1: of every sample on its own
+                             (see usp_zigzag_extract_varlen): ring rank r holds
+                             chunks r and 2 cp - 1 - r of each sample, in sample
+                             order.  Needs cu_seqlens, every sample length a
+                             multiple of 2 cp.                                  */
 } usp_attn_desc;
 
 /*
@@ -117,6 +127,27 @@ usp_status usp_zigzag_extract(const void *x, void *out, usp_dtype dtype, int64_t
                               int64_t seq_len, int64_t heads, int64_t head_dim, int32_t rd,
                               int32_t ud, int32_t ring_rank, int32_t ulysses_rank,
                               int32_t inverse, void *stream);
+
+/*
+ * Per-sample zigzag split of packed samples -- [USP review] section 三,
+ * Algorithm 2 applied to every sample on its own: sample n (boundaries
+ * cu_seqlens[n] .. cu_seqlens[n + 1], length a multiple of 2 rd) is cut into
+ * 2 rd chunks, ring rank r takes chunks r and 2 rd - 1 - r of every sample in
+ * sample order (a share of S / rd tokens), and Ulysses rank u the u-th of ud
+ * equal parts of that share.  Every rank then carries the same causal work
+ * ([CP vs Ulysses] Figure 2's pairing, sample by sample).  With one sample it
+ * equals usp_zigzag_extract.
+ *
+ * Shapes, modes and errors as usp_zigzag_extract, plus: cu_seqlens is HOST
+ * memory read during the call (num_seqs + 1 boundaries from 0 to seq_len,
+ * strictly increasing, 1 <= num_seqs <= USP_MAX_SEQS, every length a
+ * multiple of 2 rd), else USP_ERR_INVALID_ARG.
+ */
+usp_status usp_zigzag_extract_varlen(const void *x, void *out, usp_dtype dtype, int64_t batch,
+                                     int64_t seq_len, int64_t heads, int64_t head_dim,
+                                     int32_t rd, int32_t ud, int32_t ring_rank,
+                                     int32_t ulysses_rank, int32_t inverse,
+                                     const int32_t *cu_seqlens, int32_t num_seqs, void *stream);
 
 /*
  * Ulysses AllToAll4D as a single-GPU permutation -- [USP review] section 三:
@@ -160,6 +191,10 @@ usp_status usp_ulysses_a2a_layout(const void *in, void *out, usp_dtype dtype, in
 usp_status usp_ring_attn_step_fwd(const void *q, const void *k_all, const void *v_all,
                                   float *o_step, float *lse_step, const usp_attn_desc *desc,
                                   int32_t ring_rank, int32_t step, void *stream);
+/* (Descriptor errors of every attention entry point also cover cu_seqlens:
+ * USP_ERR_INVALID_ARG unless it holds num_seqs + 1 strictly increasing
+ * boundaries from 0 to seq_len with 1 <= num_seqs <= USP_MAX_SEQS, and, with
+ * zigzag_per_sample, every length a multiple of 2 cp.) */
 
 /*
  * LSE merge, in place on the accumulator -- [CP vs Ulysses], concepts

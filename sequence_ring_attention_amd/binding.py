@@ -9,6 +9,7 @@ is not built the first call raises ``RuntimeError``: there is no fallback.
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -17,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libusp.so")
 USP_OK, USP_ERR_INVALID_ARG, USP_ERR_UNSUPPORTED, USP_ERR_HIP = 0, 1, 2, 3
 USP_DTYPE_BF16, USP_DTYPE_FP32 = 0, 1
 
-EXPORTED = ["usp_zigzag_extract", "usp_ulysses_a2a_layout", "usp_ring_attn_step_fwd",
+EXPORTED = ["usp_zigzag_extract", "usp_zigzag_extract_varlen", "usp_ulysses_a2a_layout", "usp_ring_attn_step_fwd",
             "usp_lse_merge", "usp_attn_fwd", "usp_attn_bwd_prep", "usp_ring_attn_step_bwd", "usp_attn_bwd",
             "usp_status_string", "usp_last_error_detail", "usp_abi_version"]
 
@@ -43,7 +44,7 @@ class UspAttnDesc(ctypes.Structure):
                 ("q", UspStrides), ("k", UspStrides), ("v", UspStrides), ("o", UspStrides),
                 ("kv_block_stride", ctypes.c_int64), ("q_rank_stride", ctypes.c_int64),
                 ("o_rank_stride", ctypes.c_int64), ("cu_seqlens", ctypes.c_void_p),
-                ("num_seqs", ctypes.c_int32)]
+                ("num_seqs", ctypes.c_int32), ("zigzag_per_sample", ctypes.c_int32)]
 
 
 _lib = None
@@ -58,6 +59,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, i64, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int
         L.usp_zigzag_extract.argtypes = [vp, vp, st, i64, i64, i64, i64, i32, i32, i32, i32, i32, vp]
+        L.usp_zigzag_extract_varlen.argtypes = [vp, vp, st, i64, i64, i64, i64, i32, i32, i32, i32, i32, vp, i32,
+                                                vp]
         L.usp_ulysses_a2a_layout.argtypes = [vp, vp, st, i64, i64, i64, i64, i32, i32, i32, vp]
         L.usp_ring_attn_step_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, i32, vp]
         L.usp_lse_merge.argtypes = [vp, vp, vp, vp, i64, i64, vp]
@@ -66,7 +69,7 @@ def lib():
         L.usp_ring_attn_step_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc),
                                              i32, i32, vp]
         L.usp_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, vp]
-        for f in ("usp_zigzag_extract", "usp_ulysses_a2a_layout", "usp_ring_attn_step_fwd",
+        for f in ("usp_zigzag_extract", "usp_zigzag_extract_varlen", "usp_ulysses_a2a_layout", "usp_ring_attn_step_fwd",
                   "usp_lse_merge", "usp_attn_fwd", "usp_attn_bwd_prep", "usp_ring_attn_step_bwd",
                   "usp_attn_bwd"):
             getattr(L, f).restype = st
@@ -125,6 +128,31 @@ def usp_zigzag_extract(x, out, rd, ud, ring_rank, ulysses_rank, inverse=False, s
         raise ValueError(f"shard buffer must hold {shard_elems} elements")
     check(lib().usp_zigzag_extract(x.data_ptr(), out.data_ptr(), _dtype(x), B, S, H, D, rd, ud,
                                    ring_rank, ulysses_rank, int(inverse), _stream(stream)))
+    return out
+
+
+def host_cu_seqlens(cu_seqlens):
+    """Packed-sample boundaries as a contiguous host int32 array (the C calls
+    read them from host memory; a GPU tensor is copied back first)."""
+    if isinstance(cu_seqlens, torch.Tensor):
+        cu_seqlens = cu_seqlens.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(cu_seqlens), dtype=np.int32)
+
+
+def usp_zigzag_extract_varlen(x, out, rd, ud, ring_rank, ulysses_rank, cu_seqlens, inverse=False, stream=None):
+    """Per-sample zigzag: as usp_zigzag_extract, with Algorithm 2's split
+    applied to every packed sample (lengths multiples of 2*rd)."""
+    _dev(x, out)
+    _contig(x, out)
+    B, S, H, D = (out if inverse else x).shape
+    groups = rd * ud if ring_rank < 0 else (ud if ulysses_rank < 0 else 1)
+    shard_elems = groups * B * (S // (rd * ud)) * H * D
+    if (x if inverse else out).numel() != shard_elems:
+        raise ValueError(f"shard buffer must hold {shard_elems} elements")
+    cu = host_cu_seqlens(cu_seqlens)
+    check(lib().usp_zigzag_extract_varlen(x.data_ptr(), out.data_ptr(), _dtype(x), B, S, H, D, rd, ud,
+                                          ring_rank, ulysses_rank, int(inverse), cu.ctypes.data, cu.size - 1,
+                                          _stream(stream)))
     return out
 
 
@@ -258,13 +286,15 @@ def usp_attn_bwd(q, k_all, v_all, o, d_o, lse, dq, dk_all, dv_all, stats, desc, 
 
 
 def attn_desc(seq_len, cp, q, k_all, v_all, o=None, layout="bshd", causal=True, softmax_scale=None,
-              cu_seqlens=None, all_ranks=False):
+              cu_seqlens=None, all_ranks=False, zigzag_per_sample=False):
     """Build a ``UspAttnDesc`` from tensors.
 
     ``layout`` names the order of the last four dims of every tensor: "bshd"
     (sequence-major, [batch, seq, head, dim]) or "hbsd" (head-major, after the
     Ulysses layout).  ``k_all``/``v_all`` have a leading cp (block) dim; with
-    ``all_ranks`` so do ``q`` and ``o``.
+    ``all_ranks`` so do ``q`` and ``o``.  ``cu_seqlens``: packed-sample
+    boundaries (any int sequence; kept as a host array on the descriptor);
+    ``zigzag_per_sample``: the shares are the per-sample zigzag split.
     """
     pos = {"bshd": (0, 1, 2), "hbsd": (1, 2, 0)}[layout]
 
@@ -295,6 +325,8 @@ def attn_desc(seq_len, cp, q, k_all, v_all, o=None, layout="bshd", causal=True, 
         d.o_rank_stride = o.stride(0) if all_ranks else 0
     d.q_rank_stride = q.stride(0) if all_ranks else 0
     if cu_seqlens is not None:
-        d.cu_seqlens = cu_seqlens.data_ptr()
-        d.num_seqs = cu_seqlens.numel() - 1
+        d._cu_host = host_cu_seqlens(cu_seqlens)   # the descriptor points into this array
+        d.cu_seqlens = d._cu_host.ctypes.data
+        d.num_seqs = d._cu_host.size - 1
+    d.zigzag_per_sample = int(zigzag_per_sample)
     return d

@@ -57,6 +57,32 @@ void plan_pieces(usp::CopyPlan &p) {
 
 constexpr int64_t kMaxIndex = (int64_t)1 << 31;
 
+// Packed-sample boundaries from host memory into the kernels' by-value copy.
+// `split` > 0: the per-sample zigzag over `split` ring ranks, which needs
+// every length to divide by 2 split.
+usp_status read_samples(const int32_t *cu, int32_t nseq, int64_t seq_len, int32_t split, usp::Samples &out,
+                        const char *who) {
+  out = usp::Samples{};
+  if (!cu) {
+    if (split > 0) return fail(USP_ERR_INVALID_ARG, "%s: the per-sample split needs cu_seqlens", who);
+    return USP_OK;
+  }
+  if (nseq < 1 || nseq > USP_MAX_SEQS)
+    return fail(USP_ERR_INVALID_ARG, "%s: num_seqs %d outside 1..%d", who, (int)nseq, (int)USP_MAX_SEQS);
+  if (cu[0] != 0 || (int64_t)cu[nseq] != seq_len)
+    return fail(USP_ERR_INVALID_ARG, "%s: cu_seqlens must run from 0 to seq_len", who);
+  for (int32_t n = 0; n < nseq; ++n) {
+    if (cu[n + 1] <= cu[n]) return fail(USP_ERR_INVALID_ARG, "%s: cu_seqlens must increase strictly", who);
+    if (split > 0 && (cu[n + 1] - cu[n]) % (2 * split) != 0)
+      return fail(USP_ERR_INVALID_ARG, "%s: sample %d of length %d does not divide into 2*%d chunks", who, (int)n,
+                  (int)(cu[n + 1] - cu[n]), (int)split);
+  }
+  out.nseq = nseq;
+  out.per_sample = split > 0;
+  for (int32_t n = 0; n <= nseq; ++n) out.cu[n] = cu[n];
+  return USP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -117,6 +143,47 @@ usp_status usp_zigzag_extract(const void *x, void *out, usp_dtype dtype, int64_t
   p.p[7] = ulysses_rank;
   plan_pieces(p);
   return hip_result(usp::launch_copy(p, static_cast<hipStream_t>(stream)), "zigzag_extract launch");
+}
+
+usp_status usp_zigzag_extract_varlen(const void *x, void *out, usp_dtype dtype, int64_t batch,
+                                     int64_t seq_len, int64_t heads, int64_t head_dim,
+                                     int32_t rd, int32_t ud, int32_t ring_rank,
+                                     int32_t ulysses_rank, int32_t inverse,
+                                     const int32_t *cu_seqlens, int32_t num_seqs, void *stream) {
+  const char *who = "zigzag_extract_varlen";
+  if (!x || !out) return fail(USP_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (!aligned16(x) || !aligned16(out)) return fail(USP_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", who);
+  if (x == out) return fail(USP_ERR_INVALID_ARG, "%s: x and out must differ", who);
+  if (!dtype_ok(dtype)) return fail(USP_ERR_INVALID_ARG, "%s: unknown dtype %d", who, (int)dtype);
+  if (batch < 1 || seq_len < 1 || heads < 1 || head_dim < 1 || rd < 1 || ud < 1)
+    return fail(USP_ERR_INVALID_ARG, "%s: sizes and degrees must be >= 1", who);
+  if (inverse != 0 && inverse != 1) return fail(USP_ERR_INVALID_ARG, "%s: inverse must be 0 or 1", who);
+  if (seq_len % (2 * (int64_t)rd * ud) != 0)
+    return fail(USP_ERR_INVALID_ARG, "%s: seq_len %lld not divisible by 2*rd*ud", who, (long long)seq_len);
+  if (ring_rank < -1 || ring_rank >= rd || ulysses_rank < -1 || ulysses_rank >= ud)
+    return fail(USP_ERR_INVALID_ARG, "%s: rank out of range", who);
+  if (ring_rank == -1 && ulysses_rank != -1)
+    return fail(USP_ERR_INVALID_ARG, "%s: ring_rank = -1 needs ulysses_rank = -1", who);
+  const int64_t row_bytes = heads * head_dim * elem_bytes(dtype);
+  if (row_bytes % 16 != 0)
+    return fail(USP_ERR_UNSUPPORTED, "%s: heads*head_dim*element size must be a multiple of 16 bytes", who);
+  if (batch * seq_len >= kMaxIndex) return fail(USP_ERR_UNSUPPORTED, "%s: too many rows", who);
+  if (!cu_seqlens) return fail(USP_ERR_INVALID_ARG, "%s: null cu_seqlens", who);
+  usp::ZigzagVarlenArgs a{};
+  usp_status s = read_samples(cu_seqlens, num_seqs, seq_len, rd, a.sm, who);
+  if (s != USP_OK) return s;
+  a.src = static_cast<const char *>(x);
+  a.dst = static_cast<char *>(out);
+  a.row_bytes = row_bytes;
+  a.B = (int32_t)batch;
+  a.S = (int32_t)seq_len;
+  a.rd = rd;
+  a.ud = ud;
+  a.T = (int32_t)(seq_len / ((int64_t)rd * ud));
+  a.ring_rank = ring_rank;
+  a.ulysses_rank = ulysses_rank;
+  a.inverse = inverse;
+  return hip_result(usp::launch_zigzag_varlen(a, static_cast<hipStream_t>(stream)), "zigzag_extract_varlen launch");
 }
 
 usp_status usp_ulysses_a2a_layout(const void *in, void *out, usp_dtype dtype, int64_t batch,
@@ -207,7 +274,8 @@ usp_status attn_prepare(const void *q, const void *k, const void *v, const void 
     return fail(USP_ERR_UNSUPPORTED, "%s: head_dim %lld (supported: 64, 128)", who, (long long)d->head_dim);
   if (d->cu_seqlens && !d->causal)
     return fail(USP_ERR_UNSUPPORTED, "%s: packed samples (cu_seqlens) need causal = 1", who);
-  if (d->cu_seqlens && d->num_seqs < 1) return fail(USP_ERR_INVALID_ARG, "%s: num_seqs must be >= 1", who);
+  if (d->zigzag_per_sample != 0 && d->zigzag_per_sample != 1)
+    return fail(USP_ERR_INVALID_ARG, "%s: zigzag_per_sample must be 0 or 1", who);
   if (ring_rank < (all_ranks_ok ? -1 : 0) || ring_rank >= d->cp)
     return fail(USP_ERR_INVALID_ARG, "%s: ring_rank %d out of range", who, (int)ring_rank);
   const int64_t L = d->seq_len / d->cp;
@@ -244,14 +312,12 @@ usp_status attn_prepare(const void *q, const void *k, const void *v, const void 
   a.o_rank = d->o_rank_stride;
   a.scale = d->softmax_scale;
   a.scale_log2 = (float)((double)d->softmax_scale * 1.4426950408889634074);
-  a.cu = d->cu_seqlens;
-  a.nseq = d->num_seqs;
   a.ring_rank = ring_rank;
   a.n_ranks = ring_rank < 0 ? d->cp : 1;
   a.n_qtiles = (int32_t)((L + 127) / 128);
   const int64_t groups = (int64_t)a.n_ranks * a.n_qtiles * a.B * a.Hkv;
   a.xcd_remap = groups % 8 == 0;
-  return USP_OK;
+  return read_samples(d->cu_seqlens, d->num_seqs, d->seq_len, d->zigzag_per_sample ? d->cp : 0, a.sm, who);
 }
 
 usp_status attn_launch(const usp::AttnArgs &a, const usp_attn_desc *d, void *stream, const char *who) {
@@ -309,8 +375,7 @@ usp_status bwd_prepare(const void *q, const void *k, const void *v, const void *
   b.do_rank = a.o_rank;
   b.scale = a.scale;
   b.scale_log2 = a.scale_log2;
-  b.cu = a.cu;
-  b.nseq = a.nseq;
+  b.sm = a.sm;
   b.ring_rank = ring_rank;
   b.n_ranks = a.n_ranks;
   return USP_OK;

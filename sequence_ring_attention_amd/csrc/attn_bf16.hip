@@ -98,8 +98,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
     lt = a.n_qtiles - 1 - order / a.cp;
   }
   const int hq = kvh * a.G + g;
-  const int c = a.c, cp = a.cp, L = a.L;
-  const bool causal = a.causal != 0, packed = a.cu != nullptr;
+  const int cp = a.cp, L = a.L;
+  const ShareMap sm(a.c, a.cp, a.L, a.sm);
+  const bool causal = a.causal != 0, packed = sm.packed();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -108,14 +109,14 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
   const int qrow = q0 + wave * 32 + n;
   const bool qvalid = qrow < L;
   const int qlast = min(q0 + BM, L) - 1;
-  const int qpos_min = share_pos(rank, q0, c, cp);
-  const int qpos_max = share_pos(rank, qlast, c, cp);
-  const int my_qpos = qvalid ? share_pos(rank, qrow, c, cp) : -1;
+  const int qpos_min = sm.pos(rank, q0);
+  const int qpos_max = sm.pos(rank, qlast);
+  const int my_qpos = qvalid ? sm.pos(rank, qrow) : -1;
   int sst_min = 0, sst_max = 0, my_sst = 0;
-  if (a.cu) {
-    sst_min = seg_start(a.cu, a.nseq, qpos_min);
-    sst_max = seg_start(a.cu, a.nseq, qpos_max);
-    my_sst = qvalid ? seg_start(a.cu, a.nseq, my_qpos) : 0x7fffffff;
+  if (packed) {
+    sst_min = sm.seg_start(qpos_min);
+    sst_max = sm.seg_start(qpos_max);
+    my_sst = qvalid ? sm.seg_start(my_qpos) : 0x7fffffff;
   }
 
   // ------------------------------------------------------- Q fragments --
@@ -135,8 +136,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
     StepRange r;
     r.j = (rank - t) % cp;
     if (r.j < 0) r.j += cp;
-    const int hi = a.causal ? count_le(r.j, qpos_max, c, cp) : L;
-    const int lo = a.cu ? count_le(r.j, sst_min - 1, c, cp) : 0;
+    const int hi = a.causal ? sm.count_le(r.j, qpos_max) : L;
+    const int lo = packed ? sm.count_le(r.j, sst_min - 1) : 0;
     if (hi <= lo) {
       r.kt = r.ke = 0;
     } else {
@@ -222,8 +223,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
     const int k0 = cur.kt * BN;
     // tile class: every (query, key) pair of the workgroup visible?
     const int klast = min(k0 + BN, L) - 1;
-    const int kpos_min = share_pos(j, k0, c, cp);
-    const int kpos_max = share_pos(j, klast, c, cp);
+    const int kpos_min = sm.pos(j, k0);
+    const int kpos_max = sm.pos(j, klast);
     const bool full = __builtin_amdgcn_readfirstlane(
         (k0 + BN <= L) & (!causal | (kpos_max <= qpos_min)) & (!packed | (kpos_min >= sst_max)));
 
@@ -249,15 +250,17 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
     __builtin_amdgcn_s_setprio(0);
 
     if (!full) {  // diagonal, sample-boundary or ragged tile: elementwise mask
+      // positions grow with the local row, so the keys of block j this lane's
+      // query sees are one local range; as offsets from the lane's first key
+      // row in the tile, [vlo, vhi)
+      const int hi = qvalid ? (causal ? sm.count_le(j, my_qpos) : L) : 0;
+      const int lo = packed ? sm.count_le(j, my_sst - 1) : 0;
+      const int vlo = lo - k0 - 8 * hh, vhi = hi - k0 - 8 * hh;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kl = 16 * (r / 8) + 8 * hh + (r % 8);
-        const int kk0 = k0 + kl, kk1 = k0 + 32 + kl;
-        const int p0 = share_pos(j, kk0, c, cp), p1 = share_pos(j, kk1, c, cp);
-        const bool v0 = (kk0 < L) & (!causal | (p0 <= my_qpos)) & (!packed | (p0 >= my_sst));
-        const bool v1 = (kk1 < L) & (!causal | (p1 <= my_qpos)) & (!packed | (p1 >= my_sst));
-        S0[r] = v0 ? S0[r] : -INFINITY;
-        S1[r] = v1 ? S1[r] : -INFINITY;
+        const int kc = 16 * (r / 8) + (r % 8);
+        S0[r] = ((kc >= vlo) & (kc < vhi)) ? S0[r] : -INFINITY;
+        S1[r] = ((kc + 32 >= vlo) & (kc + 32 < vhi)) ? S1[r] : -INFINITY;
       }
     }
 

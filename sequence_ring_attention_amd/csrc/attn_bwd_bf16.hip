@@ -54,16 +54,6 @@ __device__ inline int mod_cp(int x, int cp) {
   return x < 0 ? x + cp : x;
 }
 
-// Index n of the packed sample holding `pos`: cu[n] <= pos < cu[n + 1].
-__device__ inline int seg_index(const int32_t *cu, int nseq, int pos) {
-  int lo = 0, hi = nseq;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (cu[mid] <= pos) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
 // Rows of a bf16 matrix as the N operand of v_mfma_f32_32x32x16_bf16: lane
 // (n, hh) holds row n, dims 16 ks + 8 hh .. + 7.
 template <int D>
@@ -155,8 +145,9 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
     lt = a.n_tiles - 1 - order / a.cp;
   }
   const int hq = kvh * a.G + g;
-  const int c = a.c, cp = a.cp, L = a.L;
-  const bool causal = a.causal != 0, packed = a.cu != nullptr;
+  const int cp = a.cp, L = a.L;
+  const ShareMap sm(a.c, a.cp, a.L, a.sm);
+  const bool causal = a.causal != 0, packed = sm.packed();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -165,14 +156,14 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
   const int qrow = q0 + wave * 32 + n;
   const bool qvalid = qrow < L;
   const int qlast = min(q0 + BM, L) - 1;
-  const int qpos_min = share_pos(rank, q0, c, cp);
-  const int qpos_max = share_pos(rank, qlast, c, cp);
-  const int my_qpos = qvalid ? share_pos(rank, qrow, c, cp) : -1;
+  const int qpos_min = sm.pos(rank, q0);
+  const int qpos_max = sm.pos(rank, qlast);
+  const int my_qpos = qvalid ? sm.pos(rank, qrow) : -1;
   int sst_min = 0, sst_max = 0, my_sst = 0;
   if (packed) {
-    sst_min = a.cu[seg_index(a.cu, a.nseq, qpos_min)];
-    sst_max = a.cu[seg_index(a.cu, a.nseq, qpos_max)];
-    my_sst = qvalid ? a.cu[seg_index(a.cu, a.nseq, my_qpos)] : 0x7fffffff;
+    sst_min = sm.seg_start(qpos_min);
+    sst_max = sm.seg_start(qpos_max);
+    my_sst = qvalid ? sm.seg_start(my_qpos) : 0x7fffffff;
   }
   const int rs = a.ring_rank >= 0 ? 0 : rank;
   const int64_t srow = (((int64_t)rs * a.Hq + hq) * a.B + b) * L + qrow;
@@ -189,8 +180,8 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
   auto step_range = [&](int t) {
     StepRange r;
     r.j = mod_cp(rank - t, cp);
-    const int hi = causal ? count_le(r.j, qpos_max, c, cp) : L;
-    const int lo = packed ? count_le(r.j, sst_min - 1, c, cp) : 0;
+    const int hi = causal ? sm.count_le(r.j, qpos_max) : L;
+    const int lo = packed ? sm.count_le(r.j, sst_min - 1) : 0;
     if (hi <= lo) {
       r.kt = r.ke = 0;
     } else {
@@ -241,8 +232,8 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
     const int j = cur.j;
     const int k0 = cur.kt * BN;
     const int klast = min(k0 + BN, L) - 1;
-    const int kpos_min = share_pos(j, k0, c, cp);
-    const int kpos_max = share_pos(j, klast, c, cp);
+    const int kpos_min = sm.pos(j, k0);
+    const int kpos_max = sm.pos(j, klast);
     const bool full = __builtin_amdgcn_readfirstlane(
         (k0 + BN <= L) & (!causal | (kpos_max <= qpos_min)) & (!packed | (kpos_min >= sst_max)));
     // positions grow with the local index, so the keys of block j this lane's
@@ -250,8 +241,8 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
     // row in the tile, [vlo, vhi)
     int vlo = 0, vhi = BN;
     if (!full) {
-      const int hi = qvalid ? min(causal ? count_le(j, my_qpos, c, cp) : L, L) : 0;
-      const int lo = packed ? count_le(j, my_sst - 1, c, cp) : 0;
+      const int hi = qvalid ? min(causal ? sm.count_le(j, my_qpos) : L, L) : 0;
+      const int lo = packed ? sm.count_le(j, my_sst - 1) : 0;
       vlo = lo - k0 - 8 * hh;
       vhi = hi - k0 - 8 * hh;
     }
@@ -275,8 +266,8 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kc = 16 * (r / 8) + (r % 8);
-        S0[r] = (kc >= vlo) & (kc < vhi) ? S0[r] : -INFINITY;
-        S1[r] = (kc + 32 >= vlo) & (kc + 32 < vhi) ? S1[r] : -INFINITY;
+        S0[r] = ((kc >= vlo) & (kc < vhi)) ? S0[r] : -INFINITY;
+        S1[r] = ((kc + 32 >= vlo) & (kc + 32 < vhi)) ? S1[r] : -INFINITY;
       }
     }
     // dS^T = P^T (dP^T - delta), rounded to bf16 as the N operand
@@ -396,8 +387,9 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
   const int j = a.ring_rank >= 0 ? mod_cp(a.ring_rank - (a.t_lo + slot), a.cp) : slot;
   const int r_first = a.ring_rank >= 0 ? a.ring_rank : 0;
   const int r_last = a.ring_rank >= 0 ? a.ring_rank : a.cp - 1;
-  const int c = a.c, cp = a.cp, L = a.L;
-  const bool causal = a.causal != 0, packed = a.cu != nullptr;
+  const int L = a.L;
+  const ShareMap sm(a.c, a.cp, a.L, a.sm);
+  const bool causal = a.causal != 0, packed = sm.packed();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -406,20 +398,20 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
   const int krow = k0 + 32 * wave + n;
   const bool kvalid = krow < L;
   const int klast = min(k0 + BK, L) - 1;
-  const int kpos_min = share_pos(j, k0, c, cp);
-  const int kpos_max = share_pos(j, klast, c, cp);
-  const int my_kpos = kvalid ? share_pos(j, krow, c, cp) : 0x7fffffff;
+  const int kpos_min = sm.pos(j, k0);
+  const int kpos_max = sm.pos(j, klast);
+  const int my_kpos = kvalid ? sm.pos(j, krow) : 0x7fffffff;
   int kend_min = 0x7fffffff, kend_max = 0x7fffffff, my_kend = 0x7fffffff;
   if (packed) {
-    kend_min = a.cu[seg_index(a.cu, a.nseq, kpos_min) + 1];
-    kend_max = a.cu[seg_index(a.cu, a.nseq, kpos_max) + 1];
-    my_kend = kvalid ? a.cu[seg_index(a.cu, a.nseq, my_kpos) + 1] : 0;
+    kend_min = sm.seg_end(kpos_min);
+    kend_max = sm.seg_end(kpos_max);
+    my_kend = kvalid ? sm.seg_end(my_kpos) : 0;
   }
 
   auto q_range = [&](int r) {
     QRange x;
-    const int lo = causal ? count_le(r, kpos_min - 1, c, cp) : 0;
-    const int hi = packed ? count_le(r, kend_max - 1, c, cp) : L;
+    const int lo = causal ? sm.count_le(r, kpos_min - 1) : 0;
+    const int hi = packed ? sm.count_le(r, kend_max - 1) : L;
     if (hi <= lo) {
       x.qt = x.qe = 0;
     } else {
@@ -540,16 +532,16 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
     const int r = cur.r;
     const int q0 = cur.x.qt * BN;
     const int qlast = min(q0 + BN, L) - 1;
-    const int qpos_min = share_pos(r, q0, c, cp);
-    const int qpos_max = share_pos(r, qlast, c, cp);
+    const int qpos_min = sm.pos(r, q0);
+    const int qpos_max = sm.pos(r, qlast);
     const bool full = __builtin_amdgcn_readfirstlane(
         (q0 + BN <= L) & (k0 + BK <= L) & (!causal | (qpos_min >= kpos_max)) & (!packed | (qpos_max < kend_min)));
     // the queries of rank r that see this lane's key are one local range; as
     // offsets from the lane's first query row in the tile, [vlo, vhi)
     int vlo = 0, vhi = BN;
     if (!full) {
-      const int lo = causal ? count_le(r, my_kpos - 1, c, cp) : 0;
-      const int hi = kvalid ? (packed ? count_le(r, my_kend - 1, c, cp) : L) : 0;
+      const int lo = causal ? sm.count_le(r, my_kpos - 1) : 0;
+      const int hi = kvalid ? (packed ? sm.count_le(r, my_kend - 1) : L) : 0;
       vlo = lo - q0 - 8 * hh;
       vhi = hi - q0 - 8 * hh;
     }
@@ -577,7 +569,7 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) {
             const int qc = 32 * blk + 16 * (rr / 8) + (rr % 8);
-            S2[blk][rr] = (qc >= vlo) & (qc < vhi) ? S2[blk][rr] : -INFINITY;
+            S2[blk][rr] = ((qc >= vlo) & (qc < vhi)) ? S2[blk][rr] : -INFINITY;
           }
         }
 #pragma unroll
@@ -617,7 +609,7 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) {
             const int qc = 32 * blk + 16 * (rr / 8) + (rr % 8);
-            S[rr] = (qc >= vlo) & (qc < vhi) ? S[rr] : -INFINITY;
+            S[rr] = ((qc >= vlo) & (qc < vhi)) ? S[rr] : -INFINITY;
           }
         }
         bf16x8 dsf[2];

@@ -23,20 +23,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr double kLog2e = 1.4426950408889634074;
 
-__device__ inline int share_pos(int rank, int i, int c, int cp) {
-  return i < c ? rank * c + i : (2 * cp - 1 - rank) * c + (i - c);
-}
-
-// Index n of the packed sample holding `pos`: cu[n] <= pos < cu[n + 1].
-__device__ inline int seg_index(const int32_t *cu, int nseq, int pos) {
-  int lo = 0, hi = nseq;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (cu[mid] <= pos) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
 __device__ inline double wave_sum(double x) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
@@ -64,8 +50,9 @@ __global__ __launch_bounds__(kThreads) void dq_fp32_kernel(BwdArgs a) {
   const int rank = a.ring_rank >= 0 ? a.ring_rank : (int)(rest / a.Hq);
   const int rs = a.ring_rank >= 0 ? 0 : rank;
   const int kvh = hq / a.G;
-  const int qpos = share_pos(rank, qrow, a.c, a.cp);
-  const int sst = a.cu ? a.cu[seg_index(a.cu, a.nseq, qpos)] : 0;
+  const ShareMap sm(a.c, a.cp, a.L, a.sm);
+  const int qpos = sm.pos(rank, qrow);
+  const int sst = sm.packed() ? sm.seg_start(qpos) : 0;
   const int64_t srow = (((int64_t)rs * a.Hq + hq) * a.B + b) * a.L + qrow;
   const double delta = (double)a.stats[srow];
   const double lse2 = (double)a.stats[a.rows + srow];
@@ -87,9 +74,9 @@ __global__ __launch_bounds__(kThreads) void dq_fp32_kernel(BwdArgs a) {
     const float *kb = static_cast<const float *>(a.k) + j * a.kv_blk + b * a.k_sb + kvh * a.k_sh;
     const float *vb = static_cast<const float *>(a.v) + j * a.kv_blk + b * a.v_sb + kvh * a.v_sh;
     for (int kk = 0; kk < a.L; ++kk) {
-      const int kpos = share_pos(j, kk, a.c, a.cp);
+      const int kpos = sm.pos(j, kk);
       if (a.causal && kpos > qpos) continue;
-      if (a.cu && kpos < sst) continue;
+      if (kpos < sst) continue;  // another packed sample (sst = 0 for one sequence)
       double s = 0.0, g = 0.0;
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
@@ -135,8 +122,9 @@ __global__ __launch_bounds__(kThreads) void dkdv_fp32_kernel(BwdArgs a) {
   const int j = a.ring_rank >= 0 ? mod_cp(a.ring_rank - (a.t_lo + slot), a.cp) : slot;
   const int r_first = a.ring_rank >= 0 ? a.ring_rank : 0;
   const int r_last = a.ring_rank >= 0 ? a.ring_rank : a.cp - 1;
-  const int kpos = share_pos(j, krow, a.c, a.cp);
-  const int kend = a.cu ? a.cu[seg_index(a.cu, a.nseq, kpos) + 1] : 0x7fffffff;
+  const ShareMap sm(a.c, a.cp, a.L, a.sm);
+  const int kpos = sm.pos(j, krow);
+  const int kend = sm.packed() ? sm.seg_end(kpos) : 0x7fffffff;
 
   const int64_t kvo = j * a.kv_blk;
   const float *kp = static_cast<const float *>(a.k) + kvo + b * a.k_sb + (int64_t)krow * a.k_ss + g * a.k_sh;
@@ -159,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void dkdv_fp32_kernel(BwdArgs a) {
                         b * a.do_sb + hq * a.do_sh;
       const int64_t srow0 = (((int64_t)rs * a.Hq + hq) * a.B + b) * a.L;
       for (int i = 0; i < a.L; ++i) {
-        const int qpos = share_pos(r, i, a.c, a.cp);
+        const int qpos = sm.pos(r, i);
         if (a.causal && qpos < kpos) continue;
         if (qpos >= kend) continue;  // another packed sample
         double s = 0.0, gd = 0.0;

@@ -5,7 +5,8 @@
 // in double: a product of two floats is exact in double, so the only
 // rounding that reaches the fp32 outputs is the final one.
 //
-// Semantics as the bf16 kernel: ring rank r at step t reads KV block
+// Semantics as the bf16 kernel (positions from the share map of either
+// split): ring rank r at step t reads KV block
 // (r - t) mod cp ("Context Parallel 与 Ulysses", concepts section and
 // Figure 1); a key is visible iff its global position is <= the query's
 // (causal) and, for packed samples, inside the query's sample.  The fold over
@@ -16,19 +17,6 @@ namespace usp {
 namespace {
 
 constexpr int kThreads = 256;
-
-__device__ inline int share_pos(int rank, int i, int c, int cp) {
-  return i < c ? rank * c + i : (2 * cp - 1 - rank) * c + (i - c);
-}
-
-__device__ inline int seg_start(const int32_t *cu, int nseq, int pos) {
-  int lo = 0, hi = nseq;  // cu[lo] <= pos < cu[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (cu[mid] <= pos) lo = mid; else hi = mid;
-  }
-  return cu[lo];
-}
 
 __device__ inline double wave_sum(double x) {
 #pragma unroll
@@ -51,8 +39,9 @@ __global__ __launch_bounds__(kThreads) void attn_fp32_kernel(AttnArgs a) {
   const int hq = (int)(rest % a.Hq);
   const int rank = a.ring_rank >= 0 ? a.ring_rank : (int)(rest / a.Hq);
   const int kvh = hq / a.G;
-  const int qpos = share_pos(rank, qrow, a.c, a.cp);
-  const int sst = a.cu ? seg_start(a.cu, a.nseq, qpos) : 0;
+  const ShareMap sm(a.c, a.cp, a.L, a.sm);
+  const int qpos = sm.pos(rank, qrow);
+  const int sst = sm.packed() ? sm.seg_start(qpos) : 0;
 
   const float *qp = static_cast<const float *>(a.q) + (a.ring_rank < 0 ? rank * a.q_rank : 0) +
                     b * a.q_sb + (int64_t)qrow * a.q_ss + hq * a.q_sh;
@@ -70,9 +59,9 @@ __global__ __launch_bounds__(kThreads) void attn_fp32_kernel(AttnArgs a) {
     const float *kb = static_cast<const float *>(a.k) + j * a.kv_blk + b * a.k_sb + kvh * a.k_sh;
     const float *vb = static_cast<const float *>(a.v) + j * a.kv_blk + b * a.v_sb + kvh * a.v_sh;
     for (int kk = 0; kk < a.L; ++kk) {
-      const int kpos = share_pos(j, kk, a.c, a.cp);
+      const int kpos = sm.pos(j, kk);
       if (a.causal && kpos > qpos) continue;
-      if (a.cu && kpos < sst) continue;
+      if (kpos < sst) continue;  // another packed sample (sst = 0 for one sequence)
       double part = 0.0;
 #pragma unroll
       for (int e = 0; e < PER; ++e) part += qv[e] * (double)kb[(int64_t)kk * a.k_ss + lane + 64 * e];

@@ -1,12 +1,7 @@
 // Device helpers shared by the bf16 attention kernels (forward and
-// backward): 64-row bf16 tiles staged global -> LDS with direct buffer loads,
-// the XOR swizzle of their 16-byte chunks, zigzag share positions and packed
-// sample boundaries.
-//
-// Positions: ring rank r's share holds zigzag chunks r and 2 cp - 1 - r of
-// the sequence cut into 2 cp chunks of c tokens ([USP review] section 三,
-// Algorithm 2), so local index i sits at global position r c + i (i < c) or
-// (2 cp - 1 - r) c + i - c (i >= c); positions increase with i.
+// backward): 64-row bf16 tiles staged global -> LDS with direct buffer loads
+// and the XOR swizzle of their 16-byte chunks.  Positions of share rows come
+// from positions.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -70,29 +65,6 @@ __device__ inline float partner_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-
-// Global position of local index i of ring rank `rank`'s share.
-__device__ inline int share_pos(int rank, int i, int c, int cp) {
-  return i < c ? rank * c + i : (2 * cp - 1 - rank) * c + (i - c);
-}
-
-// Number of local indices of block j whose position is <= p (positions of a
-// share increase with the local index, so this is a prefix length).
-__device__ inline int count_le(int j, int p, int c, int cp) {
-  const int a = min(max(p - j * c + 1, 0), c);
-  const int b = min(max(p - (2 * cp - 1 - j) * c + 1, 0), c);
-  return a + b;
-}
-
-__device__ inline int seg_start(const int32_t *cu, int nseq, int pos) {
-  int lo = 0, hi = nseq;  // cu[lo] <= pos < cu[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (cu[mid] <= pos) lo = mid; else hi = mid;
-  }
-  return cu[lo];
-}
-
 
 // Issue one 64-key tile of a KV block (K or V) into an LDS tile with buffer
 // loads straight to LDS.  Wave w fills KiB blocks w, w + 4, ...; lane l of a

@@ -139,7 +139,49 @@ __global__ __launch_bounds__(kThreads) void copy_rows_kernel(CopyPlan P) {
   }
 }
 
+// Per-sample zigzag extract ([USP review] section 三, Algorithm 2 applied to
+// every packed sample): row t of the shard of (ring rank r, Ulysses rank u)
+// is row u T + t of rank r's share, whose global position the share map
+// gives.  One thread per 16-byte vector; the shard buffer is rank-major
+// (ranks in use, Ulysses ranks in use, B, T, row).
+__global__ __launch_bounds__(kThreads) void zigzag_varlen_kernel(ZigzagVarlenArgs a) {
+  const int64_t vecs = a.row_bytes / 16;
+  const int n_u = a.ulysses_rank >= 0 ? 1 : a.ud;
+  const int n_r = a.ring_rank >= 0 ? 1 : a.rd;
+  const int64_t total = (int64_t)n_r * n_u * a.B * a.T * vecs;
+  const ShareMap sm(0, a.rd, a.S / a.rd, a.sm);
+  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * kThreads) {
+    const int64_t vec = idx % vecs;
+    const int64_t srow = idx / vecs;  // row of the shard buffer
+    int64_t rest = srow;
+    const int t = (int)(rest % a.T);
+    rest /= a.T;
+    const int b = (int)(rest % a.B);
+    rest /= a.B;
+    const int ui = (int)(rest % n_u);
+    const int ri = (int)(rest / n_u);
+    const int r = a.ring_rank >= 0 ? a.ring_rank : ri;
+    const int u = a.ulysses_rank >= 0 ? a.ulysses_rank : ui;
+    const int64_t grow = (int64_t)b * a.S + sm.pos(r, u * a.T + t);  // row of (B, S, H, D)
+    const int64_t from = (a.inverse ? srow : grow) * a.row_bytes + vec * 16;
+    const int64_t to = (a.inverse ? grow : srow) * a.row_bytes + vec * 16;
+    __builtin_nontemporal_store(__builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.src + from)),
+                                reinterpret_cast<u32x4 *>(a.dst + to));
+  }
+}
+
 }  // namespace
+
+hipError_t launch_zigzag_varlen(const ZigzagVarlenArgs &a, hipStream_t stream) {
+  const int64_t n_u = a.ulysses_rank >= 0 ? 1 : a.ud, n_r = a.ring_rank >= 0 ? 1 : a.rd;
+  const int64_t total = n_r * n_u * a.B * a.T * (a.row_bytes / 16);
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = (total + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(zigzag_varlen_kernel, dim3((uint32_t)(blocks < 8192 ? blocks : 8192)), dim3(kThreads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_copy(const CopyPlan &plan, hipStream_t stream) {
   const uint64_t total = (uint64_t)plan.n_items * plan.pieces_per_item;

@@ -1,0 +1,74 @@
+// Global positions of the rows of a ring rank's share, for both splits of
+// the sequence into shares ([USP review] section 三, Algorithm 2):
+//   * whole stream: the sequence is cut into 2 cp chunks of c tokens and
+//     rank r holds chunks r and 2 cp - 1 - r, so local row i sits at
+//     r c + i (i < c) or (2 cp - 1 - r) c + i - c;
+//   * per sample: every packed sample n (boundaries cu[n], cu[n + 1], length
+//     a multiple of 2 cp) is cut into 2 cp chunks of m_n tokens and rank r
+//     holds chunks r and 2 cp - 1 - r of every sample, in sample order; the
+//     rows of sample n start at local row cu[n] / cp.
+// Positions increase with the local row in both, which is what lets the
+// kernels bound tiles by their first and last rows and turn "position <= p"
+// into a prefix length (count_le).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace usp {
+
+constexpr int kMaxSeqs = 256;
+
+// Packed samples and the split, passed by value with the kernel arguments.
+struct Samples {
+  int32_t nseq;        // 0: one sequence, no sample mask
+  int32_t per_sample;  // 1: per-sample split (needs nseq >= 1)
+  int32_t cu[kMaxSeqs + 1];
+};
+
+struct ShareMap {
+  int c, cp, L;
+  const Samples *sm;  // points into the kernel arguments
+
+  __device__ ShareMap(int c_, int cp_, int L_, const Samples &s) : c(c_), cp(cp_), L(L_), sm(&s) {}
+
+  __device__ bool packed() const { return sm->nseq > 0; }
+
+  // Sample n holding global position p: cu[n] <= p < cu[n + 1].
+  __device__ int sample_of(int p) const {
+    int lo = 0, hi = sm->nseq;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (sm->cu[mid] <= p) lo = mid; else hi = mid;
+    }
+    return lo;
+  }
+
+  // Global position of local row i of `rank`'s share.
+  __device__ int pos(int rank, int i) const {
+    if (!sm->per_sample) return i < c ? rank * c + i : (2 * cp - 1 - rank) * c + (i - c);
+    const int n = sample_of(i * cp);  // the sample's rows start at local row cu[n] / cp
+    const int b = sm->cu[n], m = (sm->cu[n + 1] - b) / (2 * cp), o = i - b / cp;
+    return b + (o < m ? rank * m + o : (2 * cp - 1 - rank) * m + (o - m));
+  }
+
+  // Number of local rows of `rank`'s share at positions <= p (a prefix).
+  __device__ int count_le(int rank, int p) const {
+    if (!sm->per_sample) {
+      const int a = min(max(p - rank * c + 1, 0), c);
+      const int b = min(max(p - (2 * cp - 1 - rank) * c + 1, 0), c);
+      return a + b;
+    }
+    if (p < 0) return 0;
+    if (p >= cp * L) return L;
+    const int n = sample_of(p);
+    const int b = sm->cu[n], m = (sm->cu[n + 1] - b) / (2 * cp), q = p - b;
+    return b / cp + min(max(q - rank * m + 1, 0), m) + min(max(q - (2 * cp - 1 - rank) * m + 1, 0), m);
+  }
+
+  // First position of the sample holding p, and the first position after it.
+  __device__ int seg_start(int p) const { return sm->cu[sample_of(p)]; }
+  __device__ int seg_end(int p) const { return sm->cu[sample_of(p) + 1]; }
+};
+
+}  // namespace usp

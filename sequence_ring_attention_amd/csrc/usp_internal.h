@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "positions.h"
+
 namespace usp {
 
 // ---------------------------------------------------------------- copies --
@@ -39,6 +41,20 @@ struct CopyPlan {
 
 hipError_t launch_copy(const CopyPlan &plan, hipStream_t stream);
 
+// Per-sample zigzag extract (or its inverse): a row gather whose source row
+// comes from the share map of Samples.
+struct ZigzagVarlenArgs {
+  const char *src;
+  char *dst;
+  int64_t row_bytes;  // H * D * element size (a multiple of 16)
+  int32_t B, S, rd, ud, T;  // T = S / (rd ud) rows per shard
+  int32_t ring_rank, ulysses_rank;  // fixed ranks, or -1 for all
+  int32_t inverse;
+  Samples sm;
+};
+
+hipError_t launch_zigzag_varlen(const ZigzagVarlenArgs &a, hipStream_t stream);
+
 // ----------------------------------------------------------------- merge --
 
 hipError_t launch_lse_merge(float *o_acc, float *lse_acc, const float *o_step,
@@ -66,14 +82,13 @@ struct AttnArgs {
   int64_t q_rank, o_rank;
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
-  const int32_t *cu; // packed-sample boundaries or null
-  int32_t nseq;
   int32_t ring_rank; // >= 0, or -1 for every rank
   int32_t t_lo, t_hi; // ring steps to walk
   int32_t partial;    // 1: write fp32 partial (o_step, lse_step)
   int32_t n_qtiles;   // query tiles per share
   int32_t n_ranks;    // ranks in this launch (1 or cp)
   int32_t xcd_remap;  // 1: group blocks sharing a KV head on one XCD
+  Samples sm;         // packed samples and the split of the shares
 };
 
 hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t stream);
@@ -101,14 +116,13 @@ struct BwdArgs {
   int64_t q_rank, do_rank;
   float scale;
   float scale_log2;
-  const int32_t *cu;
-  int32_t nseq;
   int32_t ring_rank;  // >= 0, or -1 for every rank (full walk only)
   int32_t t_lo, t_hi; // ring steps; the dK/dV pass covers the blocks they reach
   int32_t dq_acc;     // 1: add into the fp32 dq accumulator (one step)
   int32_t n_ranks;
   int32_t n_tiles;    // set by the launchers
   int32_t xcd_remap;  // set by the launchers
+  Samples sm;         // packed samples and the split of the shares
 };
 
 struct PrepArgs {

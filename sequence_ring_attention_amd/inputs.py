@@ -9,7 +9,8 @@ Recipe: for workload k (1-based), Q, K and V are drawn with
 for i = 1, 2, 3, then cast to bfloat16 (round to nearest even) unless the
 workload is float32.  Packed-sample lengths for the variable-length workload
 are log-uniform in [512, 16384] drawn with ``numpy.random.default_rng(5004)``
-until the running sum reaches S; the last sample is cut to fit.
+until the running sum reaches S; the last sample is cut to fit.  For the
+per-sample split every length is rounded down to a multiple of 2 cp first.
 
 The shapes follow the pages' Llama-style long-context workloads (32 query
 heads, 8 KV heads for GQA, head dim 128); no dataset is involved.
@@ -82,16 +83,22 @@ def workload_qkv(w):
     return qkv(w.B, w.S, w.H, w.Hkv, w.D, w.dtype, 1000 * w.index)
 
 
-def packed_cu_seqlens(S, seed=5004, lo=512, hi=16384):
+def packed_cu_seqlens(S, seed=5004, lo=512, hi=16384, multiple=1):
     """Boundaries (int32, n+1 entries from 0 to S) of samples with lengths
-    log-uniform in [lo, hi], drawn until they cover S; the last is cut."""
+    log-uniform in [lo, hi], drawn until they cover S; the last is cut.
+    ``multiple``: every length is rounded down to a multiple of it (at least
+    one multiple), as a split of each sample into equal chunks needs; S must
+    divide by it.  multiple = 1 draws exactly the unrounded lengths."""
+    if S % multiple:
+        raise ValueError("S must divide by multiple")
     rng = np.random.default_rng(seed)
     bounds = [0]
     while bounds[-1] < S:
         n = int(round(math.exp(rng.uniform(math.log(lo), math.log(hi)))))
+        n = max(multiple, n - n % multiple)
         bounds.append(min(S, bounds[-1] + n))
     return np.asarray(bounds, dtype=np.int32)
 
 
-def workload_cu_seqlens(w):
-    return packed_cu_seqlens(w.S, seed=1000 * w.index + 4) if w.packed else None
+def workload_cu_seqlens(w, multiple=1):
+    return packed_cu_seqlens(w.S, seed=1000 * w.index + 4, multiple=multiple) if w.packed else None

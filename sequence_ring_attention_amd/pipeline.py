@@ -23,8 +23,11 @@ from . import binding as B
 
 
 class OneGpuShare:
-    def __init__(self, Q, K, V, rd, ud, ring_rank, ulysses_rank, causal=True, cu_seqlens=None):
-        """Q (B, S, H, D), K/V (B, S, Hkv, D): global tensors on the GPU."""
+    def __init__(self, Q, K, V, rd, ud, ring_rank, ulysses_rank, causal=True, cu_seqlens=None, per_sample=False):
+        """Q (B, S, H, D), K/V (B, S, Hkv, D): global tensors on the GPU.
+        ``cu_seqlens``: packed-sample boundaries; ``per_sample``: the shares
+        are the per-sample zigzag split (Algorithm 2 on every sample) instead
+        of the split of the whole packed stream."""
         self.Q, self.K, self.V = Q, K, V
         self.rd, self.ud, self.r, self.u = rd, ud, ring_rank, ulysses_rank
         Bn, S, H, D = Q.shape
@@ -33,7 +36,10 @@ class OneGpuShare:
             raise ValueError("grid does not divide the problem")
         self.Bn, self.S, self.H, self.Hkv, self.D = Bn, S, H, Hkv, D
         self.T, self.L = S // (rd * ud), S // rd
-        self.causal, self.cu = causal, cu_seqlens
+        self.causal, self.per_sample = causal, per_sample
+        self.cu = None if cu_seqlens is None else B.host_cu_seqlens(cu_seqlens)
+        if per_sample and self.cu is None:
+            raise ValueError("the per-sample split needs cu_seqlens")
         dev, dt = Q.device, Q.dtype
         T, L = self.T, self.L
         e = lambda *s: torch.empty(*s, dtype=dt, device=dev)
@@ -53,14 +59,21 @@ class OneGpuShare:
     def desc(self, u):
         if u not in self._descs:
             self._descs[u] = B.attn_desc(self.S, self.rd, self.qh[u], self.kh[u], self.vh[u], o=self.oh[u],
-                                         layout="hbsd", causal=self.causal, cu_seqlens=self.cu)
+                                         layout="hbsd", causal=self.causal, cu_seqlens=self.cu,
+                                         zigzag_per_sample=self.per_sample)
         return self._descs[u]
 
     # ------------------------------------------------------------ pieces --
+    def _extract(self, X, out, r, u):
+        if self.per_sample:
+            B.usp_zigzag_extract_varlen(X, out, self.rd, self.ud, r, u, self.cu)
+        else:
+            B.usp_zigzag_extract(X, out, self.rd, self.ud, r, u)
+
     def _kv_blocks(self, r, u, scratch_k, scratch_v):
         """Ring rank r's K/V head block u, head-major, into the ring slots."""
-        B.usp_zigzag_extract(self.K, scratch_k, self.rd, self.ud, r, -1)
-        B.usp_zigzag_extract(self.V, scratch_v, self.rd, self.ud, r, -1)
+        self._extract(self.K, scratch_k, r, -1)
+        self._extract(self.V, scratch_v, r, -1)
         B.usp_ulysses_a2a_layout(scratch_k, self.kh[u, r], self.ud, u)
         B.usp_ulysses_a2a_layout(scratch_v, self.vh[u, r], self.ud, u)
 
@@ -76,9 +89,9 @@ class OneGpuShare:
         for u in range(self.ud):
             for r in range(self.rd):
                 self._kv_blocks(r, u, sk, sv)
-        B.usp_zigzag_extract(self.Q, self.qz, self.rd, self.ud, self.r, -1)
-        B.usp_zigzag_extract(self.K, self.kz, self.rd, self.ud, self.r, -1)
-        B.usp_zigzag_extract(self.V, self.vz, self.rd, self.ud, self.r, -1)
+        self._extract(self.Q, self.qz, self.r, -1)
+        self._extract(self.K, self.kz, self.r, -1)
+        self._extract(self.V, self.vz, self.r, -1)
         for u in range(self.ud):
             if u != self.u:
                 B.usp_ulysses_a2a_layout(self.qz, self.qh[u], self.ud, u)
@@ -92,9 +105,9 @@ class OneGpuShare:
         r, u, rd, ud = self.r, self.u, self.rd, self.ud
         mark = (lambda i: marks[i].record()) if marks is not None else (lambda i: None)
         mark(0)
-        B.usp_zigzag_extract(self.Q, self.qz[u], rd, ud, r, u)
-        B.usp_zigzag_extract(self.K, self.kz[u], rd, ud, r, u)
-        B.usp_zigzag_extract(self.V, self.vz[u], rd, ud, r, u)
+        self._extract(self.Q, self.qz[u], r, u)
+        self._extract(self.K, self.kz[u], r, u)
+        self._extract(self.V, self.vz[u], r, u)
         mark(1)
         B.usp_ulysses_a2a_layout(self.qz, self.qh[u], ud, u)
         B.usp_ulysses_a2a_layout(self.kz, self.kh[u, r], ud, u)

@@ -27,7 +27,7 @@ def declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     lib = B.lib()
     for name in names:
         assert hasattr(lib, name), name
@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = B.lib()
-    assert lib.usp_abi_version() == 2
+    assert lib.usp_abi_version() == 3
     assert lib.usp_status_string(0) == b"USP_OK"
     assert lib.usp_status_string(2) == b"USP_ERR_UNSUPPORTED"
     assert lib.usp_status_string(99) == b"USP_ERR_UNKNOWN"
@@ -213,3 +213,50 @@ def test_binding_refuses_strided_lse():
     B._check_attn(kv, kv, lse.contiguous(), d, 1)
     with pytest.raises(ValueError):
         B._check_attn(kv, kv, lse, d, 1)
+
+
+def _host_cu(vals):
+    import numpy as np
+    return np.ascontiguousarray(np.asarray(vals, dtype=np.int32))
+
+
+@no_gpu
+@pytest.mark.parametrize("cu,per_sample,status", [
+    ([0, 100, 256], 0, 3),          # valid: reaches the launch (no GPU here)
+    ([1, 100, 256], 0, 1),          # does not start at 0
+    ([0, 100, 200], 0, 1),          # does not end at seq_len
+    ([0, 100, 100, 256], 0, 1),     # not strictly increasing
+    ([0, 96, 256], 1, 3),           # per-sample, lengths multiples of 2*cp = 8
+    ([0, 100, 256], 1, 1),          # per-sample, 100 does not divide into 8 chunks
+])
+def test_attention_host_cu_seqlens_checks(cu, per_sample, status):
+    arr = _host_cu(cu)
+    d = _desc(cu_seqlens=arr.ctypes.data, num_seqs=arr.size - 1, zigzag_per_sample=per_sample)
+    assert B.lib().usp_attn_fwd(FAKE, FAKE2, FAKE3, FAKE, FAKE2, ctypes.byref(d), 0, None) == status
+
+
+@no_gpu
+def test_attention_per_sample_needs_cu_and_sample_count_limit():
+    lib = B.lib()
+    d = _desc(zigzag_per_sample=1)
+    assert lib.usp_attn_fwd(FAKE, FAKE2, FAKE3, FAKE, FAKE2, ctypes.byref(d), 0, None) == 1
+    d = _desc(zigzag_per_sample=2)
+    assert lib.usp_attn_fwd(FAKE, FAKE2, FAKE3, FAKE, FAKE2, ctypes.byref(d), 0, None) == 1
+    many = _host_cu(list(range(0, 257)) + [256])   # 257 samples
+    d = _desc(cu_seqlens=many.ctypes.data, num_seqs=257)
+    assert lib.usp_attn_fwd(FAKE, FAKE2, FAKE3, FAKE, FAKE2, ctypes.byref(d), 0, None) == 1
+
+
+@no_gpu
+@pytest.mark.parametrize("cu,kw,status", [
+    ([0, 32, 64], {}, 3), ([0, 36, 64], {}, 1), ([0, 32, 60], {}, 1), (None, {}, 1),
+    ([0, 32, 64], dict(u=2), 1), ([0, 32, 64], dict(r=-1, u=0), 1), ([0, 32, 64], dict(S=60), 1),
+])
+def test_zigzag_varlen_rejects(cu, kw, status):
+    a = dict(x=FAKE, out=FAKE2, dtype=0, B=1, S=64, H=2, D=64, rd=4, ud=2, r=0, u=0, inv=0)
+    a.update(kw)
+    arr = None if cu is None else _host_cu(cu)
+    ptr = None if arr is None else arr.ctypes.data
+    n = 0 if arr is None else arr.size - 1
+    assert B.lib().usp_zigzag_extract_varlen(a["x"], a["out"], a["dtype"], a["B"], a["S"], a["H"], a["D"], a["rd"],
+                                             a["ud"], a["r"], a["u"], a["inv"], ptr, n, None) == status
