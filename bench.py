@@ -42,6 +42,7 @@ def parse():
     p.add_argument("--ulysses-rank", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads' timings")
+    p.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     p.add_argument("--cpu-rows", type=int, default=384, help="query rows of the oracle sample")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB (for scaling HBM byte counters)")
@@ -207,6 +208,7 @@ def extra_workloads():
         ms = _time(lambda: B.usp_attn_fwd(qr, ks, vs, o, lse, d, r))
         entry[f"rank{r}"] = {"TFLOP": fl / 1e12, "ms": ms, "TFLOP/s": fl / (ms * 1e-3) / 1e12}
     res[w.name] = entry
+    res[w.name + "_split_balance"] = split_balance(w, q, k, v, zig_shares)
     return res
 
 
@@ -243,6 +245,80 @@ def cpu_baseline(w, r, u, n_rows):
                       f"{w.S} keys, fp64 numpy, {dt:.2f} s, {flops / 1e9:.1f} GFLOP causal-effective",
             "seconds": dt, "host_cpu_count": os.cpu_count(),
             "affinity_cores": len(os.sched_getaffinity(0))}
+
+
+def split_balance(w, q, k, v, zig_shares):
+    """The packed workload's samples with lengths rounded down to multiples
+    of 2 cp, walked by every rank under both splits of the shares: Algorithm
+    2 on the whole packed stream, and on every sample (usp_zigzag_extract_varlen).
+    A real ring waits for its slowest rank each step, so the figure of merit
+    is the slowest rank's walk against the mean."""
+    import numpy as np
+    import torch
+    from sequence_ring_attention_amd import binding as B
+    from sequence_ring_attention_amd import inputs
+    dev = q.device
+    cu = inputs.workload_cu_seqlens(w, multiple=2 * w.rd)
+    c = w.chunk
+    m = np.diff(cu).astype(np.int64) // (2 * w.rd)
+    per_sample_pairs = int(((2 * w.rd - 1) * m * m + m * (m + 1)).sum())   # the same on every rank
+    out = {"num_samples": len(cu) - 1, "lengths_multiple_of": 2 * w.rd}
+    for split in ("stream", "per_sample"):
+        if split == "stream":
+            qs, ks, vs = zig_shares(q, w.rd), zig_shares(k, w.rd), zig_shares(v, w.rd)
+        else:
+            def varlen_shares(x):
+                o = torch.empty((w.rd, 1, x.shape[0], x.shape[1] // w.rd) + tuple(x.shape[2:]), dtype=x.dtype,
+                                device=dev)
+                B.usp_zigzag_extract_varlen(x, o, w.rd, 1, -1, -1, cu)
+                return o[:, 0]
+            qs, ks, vs = varlen_shares(q), varlen_shares(k), varlen_shares(v)
+        ranks = []
+        for r in range(w.rd):
+            if split == "stream":
+                pos = np.concatenate([np.arange(r * c, (r + 1) * c),
+                                      np.arange((2 * w.rd - 1 - r) * c, (2 * w.rd - r) * c)])
+                pairs = packed_pairs(cu, pos)
+            else:
+                pairs = per_sample_pairs
+            fl = 4.0 * w.D * w.H * w.B * pairs
+            qr = qs[r].contiguous()
+            o = torch.empty_like(qr)
+            lse = torch.empty(w.H, w.B, w.share, dtype=torch.float32, device=dev)
+            d = B.attn_desc(w.S, w.rd, qr, ks, vs, o=o, cu_seqlens=cu, zigzag_per_sample=split == "per_sample")
+            ms = _time(lambda: B.usp_attn_fwd(qr, ks, vs, o, lse, d, r))
+            ranks.append({"TFLOP": fl / 1e12, "ms": ms, "TFLOP/s": fl / (ms * 1e-3) / 1e12})
+        times = [x["ms"] for x in ranks]
+        out[split] = {"ranks": ranks, "slowest_ms": max(times), "mean_ms": sum(times) / len(times),
+                      "slowest_over_mean": max(times) / (sum(times) / len(times))}
+    out["slowest_rank_speedup"] = out["stream"]["slowest_ms"] / out["per_sample"]["slowest_ms"]
+    return out
+
+
+def backward_walk(share, fwd_flops, reps=5):
+    """The ring backward of the same share (usp_attn_bwd: per-row statistics,
+    dQ pass, dK/dV pass) after its forward, with a seeded upstream gradient.
+    Algorithmic work: five products of the forward's shape (S, dP, dV, dK,
+    dQ), 2.5 times the forward's flops; the two passes execute seven."""
+    import torch
+    from sequence_ring_attention_amd import binding as B
+    from sequence_ring_attention_amd import inputs
+    u = share.u
+    q, k, v, o, lse = share.qh[u], share.kh[u], share.vh[u], share.oh[u], share.lse[u]
+    d_o = inputs.randn(tuple(o.shape), 99, "bf16").to(o.device)
+    dq = torch.empty_like(q)
+    dk = torch.zeros(k.shape, dtype=torch.float32, device=k.device)
+    dv = torch.zeros(v.shape, dtype=torch.float32, device=v.device)
+    stats = torch.empty(2 * lse.numel(), dtype=torch.float32, device=q.device)
+    desc = share.desc(u)
+    prep_ms = _time(lambda: B.usp_attn_bwd_prep(o, d_o, lse, stats, desc, share.r), reps)
+    bwd_ms = _time(lambda: B.usp_attn_bwd(q, k, v, o, d_o, lse, dq, dk, dv, stats, desc, share.r), reps)
+    flops = 2.5 * fwd_flops
+    prep_bytes = 2 * o.numel() * o.element_size() + 3 * lse.numel() * 4
+    return {"entry": "usp_attn_bwd", "ms": bwd_ms, "TFLOP/s": flops / (bwd_ms * 1e-3) / 1e12,
+            "frac_mfma": flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "work_per_launch_tflop": flops / 1e12, "executed_products": 7, "algorithmic_products": 5,
+            "prep": {"ms": prep_ms, "bytes": prep_bytes, "GB/s": prep_bytes / (prep_ms * 1e-3) / 1e9}}
 
 
 def main():
@@ -344,6 +420,9 @@ def main():
         },
         "wall_s_timed": wall,
     }
+    if not args.no_backward:
+        print("[bench] backward of the same share", file=sys.stderr, flush=True)
+        result["backward"] = backward_walk(share, flops)
     if not args.no_extra:
         print("[bench] other workloads", file=sys.stderr, flush=True)
         del share, Q, K, V

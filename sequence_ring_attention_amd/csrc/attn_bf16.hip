@@ -65,7 +65,9 @@ using namespace tiles;
 
 constexpr float TAU = 8.0f;  // log2 headroom before the running max must move
 
-template <int D, bool PARTIAL, int NW>
+// PS: built for the per-sample split (the other build serves the split of the
+// whole stream and holds no per-sample state)
+template <int D, bool PARTIAL, int NW, bool PS>
 __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int BM = 32 * NW;
   // one array per stage: reads of one stage and the direct loads filling the
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
   }
   const int hq = kvh * a.G + g;
   const int cp = a.cp, L = a.L;
-  const ShareMap sm(a.c, a.cp, a.L, a.sm);
+  const ShareMap sm(a.c, a.cp, a.L, a.sm, PS);
   const bool causal = a.causal != 0, packed = sm.packed();
 
   const int tid = threadIdx.x;
@@ -144,6 +146,13 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
       r.kt = lo / BN;
       r.ke = (hi + BN - 1) / BN;
     }
+    // a key row i of block j is at or before position p iff i < count_le(j, p),
+    // so "every key <= the first query" and "every key in the last query's
+    // sample" are bounds on the tile's rows
+    r.fhi = a.causal ? sm.count_le(r.j, qpos_min) : L;
+    r.flo = packed ? sm.count_le(r.j, sst_max - 1) : 0;
+    r.lhi = qvalid ? (causal ? sm.count_le(r.j, my_qpos) : L) : 0;
+    r.llo = packed ? sm.count_le(r.j, my_sst - 1) : 0;
     return r;
   };
   int t = a.t_lo;
@@ -219,14 +228,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
 
     const char *const sK = STG == 0 ? smem0 : smem1;
     const char *const sV = sK + Lds<D>::TILE;
-    const int j = cur.j;
     const int k0 = cur.kt * BN;
     // tile class: every (query, key) pair of the workgroup visible?
-    const int klast = min(k0 + BN, L) - 1;
-    const int kpos_min = sm.pos(j, k0);
-    const int kpos_max = sm.pos(j, klast);
-    const bool full = __builtin_amdgcn_readfirstlane(
-        (k0 + BN <= L) & (!causal | (kpos_max <= qpos_min)) & (!packed | (kpos_min >= sst_max)));
+    const bool full = __builtin_amdgcn_readfirstlane((k0 >= cur.flo) & (k0 + BN <= cur.fhi));
 
     // S^T = K Q^T for two 32-key blocks
     f32x16 S0 = f32x16{}, S1 = f32x16{};
@@ -253,9 +257,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
       // positions grow with the local row, so the keys of block j this lane's
       // query sees are one local range; as offsets from the lane's first key
       // row in the tile, [vlo, vhi)
-      const int hi = qvalid ? (causal ? sm.count_le(j, my_qpos) : L) : 0;
-      const int lo = packed ? sm.count_le(j, my_sst - 1) : 0;
-      const int vlo = lo - k0 - 8 * hh, vhi = hi - k0 - 8 * hh;
+      const int vlo = cur.llo - k0 - 8 * hh, vhi = cur.lhi - k0 - 8 * hh;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kc = 16 * (r / 8) + (r % 8);
@@ -387,6 +389,14 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
 
 }  // namespace
 
+template <int D, int NW, bool PS>
+void launch_one(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t stream) {
+  if (a.partial)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, true, NW, PS>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<D, false, NW, PS>), grid, block, 0, stream, a);
+}
+
 template <int NW>
 hipError_t launch_nw(AttnArgs a, int head_dim, hipStream_t stream) {
   constexpr int BM = 32 * NW;
@@ -396,17 +406,11 @@ hipError_t launch_nw(AttnArgs a, int head_dim, hipStream_t stream) {
   const int64_t blocks = groups * a.G;
   if (blocks == 0) return hipSuccess;
   const dim3 grid((uint32_t)blocks), block(64 * NW);
-  if (head_dim == 128) {
-    if (a.partial)
-      hipLaunchKernelGGL((attn_bf16_kernel<128, true, NW>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((attn_bf16_kernel<128, false, NW>), grid, block, 0, stream, a);
-  } else {
-    if (a.partial)
-      hipLaunchKernelGGL((attn_bf16_kernel<64, true, NW>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((attn_bf16_kernel<64, false, NW>), grid, block, 0, stream, a);
-  }
+  const bool ps = a.sm.per_sample != 0;
+  if (head_dim == 128)
+    ps ? launch_one<128, NW, true>(a, grid, block, stream) : launch_one<128, NW, false>(a, grid, block, stream);
+  else
+    ps ? launch_one<64, NW, true>(a, grid, block, stream) : launch_one<64, NW, false>(a, grid, block, stream);
   return hipGetLastError();
 }
 

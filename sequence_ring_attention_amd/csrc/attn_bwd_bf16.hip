@@ -113,7 +113,9 @@ __device__ inline void tile_load_offsets(uint32_t *voff, int64_t rowbytes, int w
 
 // ================================================================ dQ pass ==
 
-template <int D, bool ACC>
+// PS: built for the per-sample split (the other build serves the split of the
+// whole stream and holds no per-sample state)
+template <int D, bool ACC, bool PS>
 __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
   // one array per stage, as in the forward: reads of one stage are then
   // provably disjoint from the direct loads filling the other
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
   }
   const int hq = kvh * a.G + g;
   const int cp = a.cp, L = a.L;
-  const ShareMap sm(a.c, a.cp, a.L, a.sm);
+  const ShareMap sm(a.c, a.cp, a.L, a.sm, PS);
   const bool causal = a.causal != 0, packed = sm.packed();
 
   const int tid = threadIdx.x;
@@ -159,11 +161,12 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
   const int qpos_min = sm.pos(rank, q0);
   const int qpos_max = sm.pos(rank, qlast);
   const int my_qpos = qvalid ? sm.pos(rank, qrow) : -1;
-  int sst_min = 0, sst_max = 0, my_sst = 0;
+  int sst_min = 0, sst_max = 0, my_sst = 0, my_send = 0;
   if (packed) {
     sst_min = sm.seg_start(qpos_min);
     sst_max = sm.seg_start(qpos_max);
     my_sst = qvalid ? sm.seg_start(my_qpos) : 0x7fffffff;
+    if (PS) my_send = qvalid ? sm.seg_end(my_qpos) : 0x7fffffff;
   }
   const int rs = a.ring_rank >= 0 ? 0 : rank;
   const int64_t srow = (((int64_t)rs * a.Hq + hq) * a.B + b) * L + qrow;
@@ -188,6 +191,9 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
       r.kt = lo / BN;
       r.ke = (hi + BN - 1) / BN;
     }
+    // key row i of block j is at or before position p iff i < count_le(j, p)
+    r.fhi = causal ? sm.count_le(r.j, qpos_min) : L;
+    r.flo = packed ? sm.count_le(r.j, sst_max - 1) : 0;
     return r;
   };
   int t = a.t_lo;
@@ -229,20 +235,15 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
 
     const char *const sK = STG == 0 ? smem0 : smem1;
     const char *const sV = sK + Lds<D>::TILE;
-    const int j = cur.j;
     const int k0 = cur.kt * BN;
-    const int klast = min(k0 + BN, L) - 1;
-    const int kpos_min = sm.pos(j, k0);
-    const int kpos_max = sm.pos(j, klast);
-    const bool full = __builtin_amdgcn_readfirstlane(
-        (k0 + BN <= L) & (!causal | (kpos_max <= qpos_min)) & (!packed | (kpos_min >= sst_max)));
+    const bool full = __builtin_amdgcn_readfirstlane((k0 >= cur.flo) & (k0 + BN <= cur.fhi));
     // positions grow with the local index, so the keys of block j this lane's
     // query sees are one local range; as offsets from the lane's first key
     // row in the tile, [vlo, vhi)
     int vlo = 0, vhi = BN;
     if (!full) {
-      const int hi = qvalid ? min(causal ? sm.count_le(j, my_qpos) : L, L) : 0;
-      const int lo = packed ? sm.count_le(j, my_sst - 1) : 0;
+      const int hi = qvalid ? (causal ? sm.count_le_in(cur.j, my_qpos, my_sst, my_send) : L) : 0;
+      const int lo = packed ? sm.count_le_in(cur.j, my_sst - 1, my_sst, my_send) : 0;
       vlo = lo - k0 - 8 * hh;
       vhi = hi - k0 - 8 * hh;
     }
@@ -343,8 +344,12 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
 // Query tiles (64 rows) of rank r's share that can see a key tile whose
 // positions span [kpos_min, kpos_max]: causal -- queries at or after
 // kpos_min; packed -- queries before the end of kpos_max's sample.
+// Query tiles [qt, qe) of one rank that see some key of the tile, and the
+// tiles whose every query sees every key (first row >= flo, one past the last
+// row <= fhi).
 struct QRange {
   int qt, qe;
+  int flo, fhi;
 };
 
 // DV: the dV pass (S, then dV^T += dO^T P); otherwise the dK pass (S and dP,
@@ -356,8 +361,8 @@ struct QRange {
 // the tile's delta and lse2 (dword direct loads by wavefronts 0 and 1).  Each
 // wavefront waits with a count of its own loads still allowed in flight, and
 // one barrier per tile both publishes the tile and frees the stage read in
-// the previous tile for the next issue.
-template <int D, bool DV, int KW>
+// the previous tile for the next issue.  PS as in the dQ pass.
+template <int D, bool DV, int KW, bool PS>
 __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
   constexpr int BK = 32 * KW;  // keys per workgroup
   constexpr int TILE = Lds<D>::TILE;
@@ -388,7 +393,7 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
   const int r_first = a.ring_rank >= 0 ? a.ring_rank : 0;
   const int r_last = a.ring_rank >= 0 ? a.ring_rank : a.cp - 1;
   const int L = a.L;
-  const ShareMap sm(a.c, a.cp, a.L, a.sm);
+  const ShareMap sm(a.c, a.cp, a.L, a.sm, PS);
   const bool causal = a.causal != 0, packed = sm.packed();
 
   const int tid = threadIdx.x;
@@ -418,6 +423,9 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
       x.qt = lo / BN;
       x.qe = (hi + BN - 1) / BN;
     }
+    // query row i of rank r is at or before position p iff i < count_le(r, p)
+    x.flo = causal ? sm.count_le(r, kpos_max - 1) : 0;
+    x.fhi = packed ? sm.count_le(r, kend_min - 1) : L;
     return x;
   };
   // tile iterator: rank r, query head offset h in the group, tile range;
@@ -441,6 +449,8 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
   };
   It cur{r_first, 0, q_range(r_first)};
   normalise(cur);
+  // this lane's key's visible query rows of rank lane_r, [lane_lo, lane_hi)
+  int lane_r = -1, lane_lo = 0, lane_hi = 0;
   if (cur.r > r_last) return;  // no query sees these keys: nothing to add (uniform)
 
   bf16x8 kf[D / 16], vf[DV ? 1 : D / 16];
@@ -531,19 +541,19 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
     const float *const sst = reinterpret_cast<const float *>(sQ + STAGE);
     const int r = cur.r;
     const int q0 = cur.x.qt * BN;
-    const int qlast = min(q0 + BN, L) - 1;
-    const int qpos_min = sm.pos(r, q0);
-    const int qpos_max = sm.pos(r, qlast);
-    const bool full = __builtin_amdgcn_readfirstlane(
-        (q0 + BN <= L) & (k0 + BK <= L) & (!causal | (qpos_min >= kpos_max)) & (!packed | (qpos_max < kend_min)));
+    const bool full =
+        __builtin_amdgcn_readfirstlane((k0 + BK <= L) & (q0 >= cur.x.flo) & (q0 + BN <= cur.x.fhi));
     // the queries of rank r that see this lane's key are one local range; as
     // offsets from the lane's first query row in the tile, [vlo, vhi)
     int vlo = 0, vhi = BN;
     if (!full) {
-      const int lo = causal ? sm.count_le(r, my_kpos - 1) : 0;
-      const int hi = kvalid ? (packed ? sm.count_le(r, my_kend - 1) : L) : 0;
-      vlo = lo - q0 - 8 * hh;
-      vhi = hi - q0 - 8 * hh;
+      if (r != lane_r) {  // uniform: the range moves with the rank only
+        lane_r = r;
+        lane_lo = causal ? sm.count_le(r, my_kpos - 1) : 0;
+        lane_hi = kvalid ? (packed ? sm.count_le(r, my_kend - 1) : L) : 0;
+      }
+      vlo = lane_lo - q0 - 8 * hh;
+      vhi = lane_hi - q0 - 8 * hh;
     }
 
     if (DV) {
@@ -675,10 +685,18 @@ hipError_t launch_d(BwdArgs a, hipStream_t stream) {
   a.xcd_remap = groups % 8 == 0;
   const int64_t q_blocks = groups * a.G;
   if (q_blocks > 0) {
-    if (a.dq_acc)
-      hipLaunchKernelGGL((dq_bf16_kernel<D, true>), dim3((uint32_t)q_blocks), dim3(64 * NW), 0, stream, a);
-    else
-      hipLaunchKernelGGL((dq_bf16_kernel<D, false>), dim3((uint32_t)q_blocks), dim3(64 * NW), 0, stream, a);
+    const dim3 grid((uint32_t)q_blocks), block(64 * NW);
+    if (a.sm.per_sample) {
+      if (a.dq_acc)
+        hipLaunchKernelGGL((dq_bf16_kernel<D, true, true>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((dq_bf16_kernel<D, false, true>), grid, block, 0, stream, a);
+    } else {
+      if (a.dq_acc)
+        hipLaunchKernelGGL((dq_bf16_kernel<D, true, false>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((dq_bf16_kernel<D, false, false>), grid, block, 0, stream, a);
+    }
   }
   // dV and dK passes
   a.n_tiles = (a.L + 32 * KW - 1) / (32 * KW);
@@ -686,8 +704,14 @@ hipError_t launch_d(BwdArgs a, hipStream_t stream) {
   const int n_slots = a.ring_rank >= 0 ? a.t_hi - a.t_lo : a.cp;
   const int64_t k_blocks = (int64_t)a.n_tiles * n_slots * a.B * a.Hkv;
   if (k_blocks > 0) {
-    hipLaunchKernelGGL((dkdv_bf16_kernel<D, true, KW>), dim3((uint32_t)k_blocks), dim3(64 * KW), 0, stream, a);
-    hipLaunchKernelGGL((dkdv_bf16_kernel<D, false, KW>), dim3((uint32_t)k_blocks), dim3(64 * KW), 0, stream, a);
+    const dim3 grid((uint32_t)k_blocks), block(64 * KW);
+    if (a.sm.per_sample) {
+      hipLaunchKernelGGL((dkdv_bf16_kernel<D, true, KW, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((dkdv_bf16_kernel<D, false, KW, true>), grid, block, 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((dkdv_bf16_kernel<D, true, KW, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((dkdv_bf16_kernel<D, false, KW, false>), grid, block, 0, stream, a);
+    }
   }
   return hipGetLastError();
 }

@@ -96,8 +96,14 @@ __device__ inline void issue_tile_lds(char *tile, const char *blk, uint32_t exte
 }
 
 // The key range of block j one query tile can see, in 64-key tiles.
+// One ring step of a tile walk: block j, its tiles [kt, ke) that hold some
+// visible pair, the tiles with every pair visible (first row >= flo and one
+// past the last row <= fhi), and the lane's own visible rows [llo, lhi).  All
+// are local rows of the walked share, found once per step.
 struct StepRange {
   int j, kt, ke;
+  int flo, fhi;
+  int llo, lhi;
 };
 
 }  // namespace tiles

@@ -29,8 +29,12 @@ struct Samples {
 struct ShareMap {
   int c, cp, L;
   const Samples *sm;  // points into the kernel arguments
+  bool ps;            // per-sample split
 
-  __device__ ShareMap(int c_, int cp_, int L_, const Samples &s) : c(c_), cp(cp_), L(L_), sm(&s) {}
+  // A kernel built for the whole-stream split only passes per_sample_ok =
+  // false, which removes the per-sample branches at compile time.
+  __device__ ShareMap(int c_, int cp_, int L_, const Samples &s, bool per_sample_ok = true)
+      : c(c_), cp(cp_), L(L_), sm(&s), ps(per_sample_ok && s.per_sample) {}
 
   __device__ bool packed() const { return sm->nseq > 0; }
 
@@ -46,7 +50,7 @@ struct ShareMap {
 
   // Global position of local row i of `rank`'s share.
   __device__ int pos(int rank, int i) const {
-    if (!sm->per_sample) return i < c ? rank * c + i : (2 * cp - 1 - rank) * c + (i - c);
+    if (!ps) return i < c ? rank * c + i : (2 * cp - 1 - rank) * c + (i - c);
     const int n = sample_of(i * cp);  // the sample's rows start at local row cu[n] / cp
     const int b = sm->cu[n], m = (sm->cu[n + 1] - b) / (2 * cp), o = i - b / cp;
     return b + (o < m ? rank * m + o : (2 * cp - 1 - rank) * m + (o - m));
@@ -54,7 +58,7 @@ struct ShareMap {
 
   // Number of local rows of `rank`'s share at positions <= p (a prefix).
   __device__ int count_le(int rank, int p) const {
-    if (!sm->per_sample) {
+    if (!ps) {
       const int a = min(max(p - rank * c + 1, 0), c);
       const int b = min(max(p - (2 * cp - 1 - rank) * c + 1, 0), c);
       return a + b;
@@ -64,6 +68,15 @@ struct ShareMap {
     const int n = sample_of(p);
     const int b = sm->cu[n], m = (sm->cu[n + 1] - b) / (2 * cp), q = p - b;
     return b / cp + min(max(q - rank * m + 1, 0), m) + min(max(q - (2 * cp - 1 - rank) * m + 1, 0), m);
+  }
+
+  // count_le(rank, p) for s0 - 1 <= p < s1, where [s0, s1) is a sample: the
+  // per-sample split then needs no search (the samples before it put s0 / cp
+  // rows in every share).
+  __device__ int count_le_in(int rank, int p, int s0, int s1) const {
+    if (!ps) return count_le(rank, p);
+    const int m = (s1 - s0) / (2 * cp), q = p - s0;
+    return s0 / cp + min(max(q - rank * m + 1, 0), m) + min(max(q - (2 * cp - 1 - rank) * m + 1, 0), m);
   }
 
   // First position of the sample holding p, and the first position after it.
