@@ -63,7 +63,7 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}))
 
 
-WALK_SOURCES = ("attn_bf16.hip", "attn_tiles.h")
+WALK_SOURCES = ("attn_bf16.hip", "attn_tiles.h", "positions.h")
 
 
 def kernel_source_hash():
