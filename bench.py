@@ -124,6 +124,93 @@ def _time(fn, reps=5):
     return sorted(out)[len(out) // 2]
 
 
+_FLUSH = []
+
+
+def _time_flushed(fn, nbytes, reps=20):
+    """HIP-event times of fn() with a 1 GiB buffer written before every
+    repetition, so the 256 MB last-level cache holds none of fn's data:
+    median, min and max ms, and the median rate for `nbytes` moved."""
+    import torch
+    if not _FLUSH:
+        _FLUSH.append(torch.empty(2**30, dtype=torch.uint8, device="cuda:0"))
+    flush = _FLUSH[0]
+    fn()
+    times = []
+    for _ in range(reps):
+        flush.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    times.sort()
+    ms = times[len(times) // 2]
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"bytes": nbytes, "ms": ms, "ms_min": times[0], "ms_max": times[-1], "GB/s": gbs,
+            "frac_hbm": gbs / PEAK_HBM_GBS, "reps": reps}
+
+
+def copy_launches(share, w):
+    """Each copy entry point and the merge as one launch at the bench
+    workload's sizes, timed with the last-level cache flushed: the zigzag
+    extract of the whole Q for every (ring, Ulysses) rank and its inverse,
+    one rank's extract, the Ulysses layout of the ring group's Q shards for
+    both Ulysses ranks and its inverse, and the LSE merge of one step's
+    partials of the share."""
+    import torch
+    from sequence_ring_attention_amd import binding as B
+    Q, rd, ud = share.Q, w.rd, w.ud
+    e = Q.element_size()
+    res = {}
+    allz = torch.empty((rd * ud,) + tuple(share.qz.shape[1:]), dtype=Q.dtype, device=Q.device)
+    res["zigzag_extract_all_ranks_q"] = _time_flushed(lambda: B.usp_zigzag_extract(Q, allz, rd, ud, -1, -1),
+                                                      2 * Q.numel() * e)
+    back = torch.empty_like(Q)
+    res["zigzag_extract_inverse_all_ranks_q"] = _time_flushed(
+        lambda: B.usp_zigzag_extract(allz, back, rd, ud, -1, -1, inverse=True), 2 * Q.numel() * e)
+    del allz, back
+    one = torch.empty_like(share.qz[0])
+    res["zigzag_extract_one_rank_q"] = _time_flushed(lambda: B.usp_zigzag_extract(Q, one, rd, ud, 0, 0),
+                                                     2 * one.numel() * e)
+    del one
+    res["ulysses_layout_fwd_all_q"] = _time_flushed(lambda: B.usp_ulysses_a2a_layout(share.qz, share.qh, ud, -1),
+                                                    2 * share.qz.numel() * e)
+    outs = torch.empty((ud,) + tuple(share.out.shape), dtype=Q.dtype, device=Q.device)
+    res["ulysses_layout_inv_all_o"] = _time_flushed(
+        lambda: B.usp_ulysses_a2a_layout(share.oh, outs, ud, -1, inverse=True), 2 * share.oh.numel() * e)
+    del outs
+    hb, L = w.H // ud, w.S // rd
+    rows = hb * w.B * L
+    acc = torch.zeros(hb, w.B, L, w.D, dtype=torch.float32, device=Q.device)
+    lacc = torch.zeros(hb, w.B, L, dtype=torch.float32, device=Q.device)
+    ost, lst = torch.zeros_like(acc), torch.zeros_like(lacc)
+    res["lse_merge_step"] = _time_flushed(lambda: B.usp_lse_merge(acc, lacc, ost, lst),
+                                          3 * rows * w.D * 4 + 3 * rows * 4)
+    return res
+
+
+def other_share_walk(Q, K, V, w, r, u, flops, steps=5):
+    """The walk of another ring rank's share of the same grid (every share
+    holds the same causal work under the zigzag split)."""
+    import torch
+    from sequence_ring_attention_amd.pipeline import OneGpuShare
+    sh = OneGpuShare(Q, K, V, w.rd, w.ud, r, u)
+    sh.prepare_peers()
+    sh.step()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    marks = [[ev() for _ in range(5)] for _ in range(steps)]
+    for s in range(steps):
+        sh.step(marks[s])
+    torch.cuda.synchronize()
+    walk = sorted(marks[s][2].elapsed_time(marks[s][3]) for s in range(steps))
+    ms = walk[len(walk) // 2]
+    return {"share": {"ring_rank": r, "ulysses_rank": u}, "walk_ms": ms, "walk_ms_min": walk[0],
+            "walk_ms_max": walk[-1], "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+            "frac_mfma": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def packed_pairs(cu, pos):
     """Visible (query, key) pairs of queries at `pos` under the causal
     same-sample mask: a query at p sees p - start(sample of p) + 1 keys."""
@@ -166,6 +253,10 @@ def extra_workloads():
     qs, ks, vs = zig_shares(q, w.rd), zig_shares(k, w.rd), zig_shares(v, w.rd)
     fl_rank = 4.0 * w.D * w.H * w.B * 2 * w.rd * w.chunk * w.chunk
     entry = {"TFLOP_per_rank": fl_rank / 1e12}
+    qz = torch.empty((w.rd, 1) + tuple(qs.shape[1:]), dtype=q.dtype, device=dev)
+    entry["zigzag_extract_all_ranks_q"] = _time_flushed(lambda: B.usp_zigzag_extract(q, qz, w.rd, 1, -1, -1),
+                                                        2 * q.numel() * q.element_size())
+    del qz
     for r in (0, w.rd - 1):
         qr = qs[r].contiguous()
         o = torch.empty_like(qr)
@@ -420,9 +511,18 @@ def main():
         },
         "wall_s_timed": wall,
     }
+    walks = sorted(marks[s][2].elapsed_time(marks[s][3]) for s in range(args.steps))
+    result["kernels"]["ring_walk_attention"].update(
+        {"ms_median": walks[len(walks) // 2], "ms_min": walks[0], "ms_max": walks[-1]})
     if not args.no_backward:
         print("[bench] backward of the same share", file=sys.stderr, flush=True)
         result["backward"] = backward_walk(share, flops)
+    if not args.no_extra:
+        print("[bench] copy launches, cache flushed", file=sys.stderr, flush=True)
+        result["copy_launches"] = copy_launches(share, w)
+        r2 = w.rd - 1 if r != w.rd - 1 else 0
+        print(f"[bench] walk of share ({r2}, {u})", file=sys.stderr, flush=True)
+        result["other_share"] = other_share_walk(Q, K, V, w, r2, u, flops)
     if not args.no_extra:
         print("[bench] other workloads", file=sys.stderr, flush=True)
         del share, Q, K, V

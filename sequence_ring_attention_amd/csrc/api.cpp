@@ -53,6 +53,10 @@ void plan_pieces(usp::CopyPlan &p) {
   p.pieces_per_item = (uint32_t)((p.rows_per_item + rows - 1) / rows);
   p.row_vecs = (uint32_t)(p.row_bytes / 16);
   p.row_vecs_shift = log2_exact(p.row_vecs);
+  if (p.src_row_bytes == 0) {  // rows of equal size on both sides
+    p.src_row_bytes = p.row_bytes;
+    p.grp_shift = 31;
+  }
 }
 
 constexpr int64_t kMaxIndex = (int64_t)1 << 31;
@@ -222,6 +226,16 @@ usp_status usp_ulysses_a2a_layout(const void *in, void *out, usp_dtype dtype, in
   p.n_items = (uint32_t)(G * hb * batch * N);
   p.rows_per_item = (uint32_t)Ls;
   p.row_bytes = (uint64_t)row_bytes;
+  const uint32_t head_shift = log2_exact((uint64_t)row_bytes / 16);
+  if (inverse && head_shift < 31) {
+    // output-major inverse: a row is one token's hb heads (contiguous in the
+    // output), gathered from the hb head planes
+    p.kind = usp::kUlyssesInvRows;
+    p.n_items = (uint32_t)(G * batch * N);
+    p.row_bytes = (uint64_t)(hb * row_bytes);
+    p.src_row_bytes = (uint64_t)row_bytes;
+    p.grp_shift = head_shift;
+  }
   p.p[0] = batch;
   p.p[1] = seq_len;
   p.p[2] = heads;

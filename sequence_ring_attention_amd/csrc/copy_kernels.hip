@@ -13,7 +13,11 @@
 // Ulysses (same section, the AllToAll4D box (bs, L/N, hc, hd) ->
 // (hc/N, bs, L, hd)): for fixed (head h', batch b, source peer u') the
 // Ls = L/N rows of D elements are strided by hc*D on the sequence-major side
-// and contiguous on the head-major side.
+// and contiguous on the head-major side.  The forward copies such head rows
+// (strided reads, contiguous writes).  The inverse writes whole output runs
+// instead: for fixed (token, source peer u') the hc/N heads are contiguous in
+// the output, so a row is that run, gathered from hc/N head-major planes;
+// writes then stream and only reads gather, as in the forward.
 #include "usp_internal.h"
 
 namespace usp {
@@ -27,12 +31,14 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 struct RowMap {
   int64_t src_base, src_stride, dst_base, dst_stride;  // in rows
   int64_t split, src_jump, dst_jump;                   // rows t >= split add the jumps
+  int64_t src_grp;                                     // source rows between the pieces of a gathered row
 };
 
 __device__ inline RowMap decode(const CopyPlan &P, uint32_t item) {
   RowMap m;
   m.split = INT64_MAX;
   m.src_jump = m.dst_jump = 0;
+  m.src_grp = 0;
   if (P.kind == kZigzagFwd || P.kind == kZigzagInv) {
     const int64_t B = P.p[0], S = P.p[1], c = P.p[2], rd = P.p[3], ud = P.p[4], T = P.p[5];
     const int64_t r_fix = P.p[6], u_fix = P.p[7];
@@ -79,6 +85,22 @@ __device__ inline RowMap decode(const CopyPlan &P, uint32_t item) {
     m.dst_stride = 1;
     m.src_base = ((up * bs + b) * Ls) * hc + u * hb + hp;
     m.src_stride = hc;
+  } else if (P.kind == kUlyssesInvRows) {
+    // item (g, b, u'); row t = token t of output shard g, its heads
+    // [u' hb, (u' + 1) hb) from head planes h' of peer u' (src_grp apart)
+    const int64_t bs = P.p[0], L = P.p[1], N = P.p[3], hb = P.p[4], Ls = P.p[5];
+    const int64_t u_fix = P.p[6];
+    int64_t rest = item;
+    const int64_t up = rest % N;
+    rest /= N;
+    const int64_t b = rest % bs;
+    const int64_t g = rest / bs;
+    const int64_t u = u_fix < 0 ? g : u_fix;
+    m.src_base = (up * hb * bs + b) * L + u * Ls;
+    m.src_stride = 1;
+    m.src_grp = bs * L;
+    m.dst_base = (g * bs + b) * Ls * N + up;
+    m.dst_stride = N;
   } else {  // kUlyssesInv
     const int64_t bs = P.p[0], L = P.p[1], hc = P.p[2], N = P.p[3], hb = P.p[4], Ls = P.p[5];
     const int64_t u_fix = P.p[6];
@@ -124,10 +146,13 @@ __global__ __launch_bounds__(kThreads) void copy_rows_kernel(CopyPlan P) {
           }
           const int64_t t = (int64_t)row0 + row;
           const bool second = t >= m.split;
-          const int64_t srow = m.src_base + t * m.src_stride + (second ? m.src_jump : 0);
+          // piece of a gathered row (0 unless grp_shift < 31) and its vector
+          const uint32_t grp = P.grp_shift < 31 ? col >> P.grp_shift : 0;
+          const uint32_t gcol = col - (grp << (P.grp_shift & 31));
+          const int64_t srow = m.src_base + t * m.src_stride + grp * m.src_grp + (second ? m.src_jump : 0);
           const int64_t drow = m.dst_base + t * m.dst_stride + (second ? m.dst_jump : 0);
           buf[k] = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4 *>(P.src + srow * (int64_t)P.row_bytes) + col);
+              reinterpret_cast<const u32x4 *>(P.src + srow * (int64_t)P.src_row_bytes) + gcol);
           doff[k] = drow * (int64_t)P.row_bytes + (int64_t)col * 16;
         }
       }

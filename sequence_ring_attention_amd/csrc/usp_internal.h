@@ -21,6 +21,7 @@ enum CopyKind : int32_t {
   kZigzagInv = 1,  // shards -> global
   kUlyssesFwd = 2, // (N, bs, L/N, hc, hd) -> (G, hc/N, bs, L, hd)
   kUlyssesInv = 3, // (N, hc/N, bs, L, hd) -> (G, bs, L/N, hc, hd)
+  kUlyssesInvRows = 4, // the same, a row being one token's hc/N heads of the output
 };
 
 struct CopyPlan {
@@ -33,7 +34,9 @@ struct CopyPlan {
   uint32_t row_vecs_shift;  // log2(row_vecs) when a power of two, else 31
   uint32_t rows_per_piece;  // rows a workgroup copies per piece
   uint32_t pieces_per_item;
-  uint64_t row_bytes;
+  uint64_t row_bytes;      // destination row
+  uint64_t src_row_bytes;  // source row (row_bytes, or one head's hd elements for kUlyssesInvRows)
+  uint32_t grp_shift;      // log2(16-byte vectors per source row) when a row gathers several, else 31
   // zigzag: B, S (rows), chunk c, rd, ud, shard rows T, fixed ranks (or -1)
   // ulysses: bs, L, hc, N, hb = hc/N, Ls = L/N, fixed rank (or -1)
   int64_t p[10];
