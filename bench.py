@@ -266,19 +266,18 @@ def extra_workloads():
         entry[f"rank{r}_walk_ms"] = ms
         entry[f"rank{r}_TFLOP/s"] = fl_rank / (ms * 1e-3) / 1e12
     qr = qs[0].contiguous()
-    acc = torch.empty(w.H, w.B, w.share, w.D, dtype=torch.float32, device=dev)
-    lacc = torch.empty(w.H, w.B, w.share, dtype=torch.float32, device=dev)
+    acc = torch.zeros(w.H, w.B, w.share, w.D, dtype=torch.float32, device=dev)
+    lacc = torch.zeros(w.H, w.B, w.share, dtype=torch.float32, device=dev)
     ost, lst = torch.empty_like(acc), torch.empty_like(lacc)
     d = B.attn_desc(w.S, w.rd, qr, ks, vs)
     step_ms = [_time(lambda t=t: B.usp_ring_attn_step_fwd(qr, ks, vs, ost, lst, d, 0, t)) for t in range(w.rd)]
-    merge_ms = _time(lambda: B.usp_lse_merge(acc, lacc, ost, lst))
     rows = w.H * w.B * w.share
-    merge_bytes = 3 * rows * w.D * 4 + 3 * rows * 4
+    merge = _time_flushed(lambda: B.usp_lse_merge(acc, lacc, ost, lst), 3 * rows * w.D * 4 + 3 * rows * 4)
     entry["rank0_step_ms"] = step_ms
     entry["rank0_step_TFLOP/s"] = [fl_rank / w.rd / (m * 1e-3) / 1e12 for m in step_ms]
-    entry["merge_ms"] = merge_ms
-    entry["merge_GB/s"] = merge_bytes / (merge_ms * 1e-3) / 1e9
-    entry["merge_frac_hbm"] = entry["merge_GB/s"] / PEAK_HBM_GBS
+    entry["merge_ms"] = merge["ms"]
+    entry["merge_GB/s"] = merge["GB/s"]
+    entry["merge_frac_hbm"] = merge["frac_hbm"]
     res[w.name] = entry
 
     # packed variable-length 32K, cp = 4: each rank

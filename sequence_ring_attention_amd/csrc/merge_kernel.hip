@@ -15,6 +15,89 @@ namespace usp {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kUnroll = 8;  // vector loads per lane in flight (64-row path)
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ inline float4 as_float4(f32x4 v) { return make_float4(v.x, v.y, v.z, v.w); }
+__device__ inline f32x4 as_f32x4(float4 v) { return f32x4{v.x, v.y, v.z, v.w}; }
+
+// The weights of the two partials and the merged lse of one row.
+__device__ inline void merge_weights(double l1, double l2, double &a1, double &a2, double &lse) {
+  const bool e1 = l1 == -INFINITY, e2 = l2 == -INFINITY;
+  if (e1 && e2) {
+    a1 = 0.0;
+    a2 = 0.0;
+    lse = -INFINITY;
+  } else if (e2) {
+    a1 = 1.0;
+    a2 = 0.0;
+    lse = l1;
+  } else if (e1) {
+    a1 = 0.0;
+    a2 = 1.0;
+    lse = l2;
+  } else {
+    const double M = l1 > l2 ? l1 : l2;
+    const double w = exp((l1 > l2 ? l2 : l1) - M);  // in (0, 1]
+    lse = M + log1p(w);
+    const double big = 1.0 / (1.0 + w), small = w / (1.0 + w);
+    a1 = l1 > l2 ? big : small;
+    a2 = l1 > l2 ? small : big;
+  }
+}
+
+__device__ inline float4 blend(double a1, float4 x, double a2, float4 y) {
+  float4 r;
+  r.x = (float)(a1 * (double)x.x + a2 * (double)y.x);
+  r.y = (float)(a1 * (double)x.y + a2 * (double)y.y);
+  r.z = (float)(a1 * (double)x.z + a2 * (double)y.z);
+  r.w = (float)(a1 * (double)x.w + a2 * (double)y.w);
+  return r;
+}
+
+// Rows of 2^d4_shift float4 (at most 64): a wavefront takes 64 rows, each
+// lane computing the weights of one of them, then streams the rows' vectors
+// (64 consecutive per load, kUnroll loads in flight) and takes each vector's
+// row weights from the lane that computed them.  Each row's lse is read and
+// written by its own lane only.
+__global__ __launch_bounds__(kThreads) void lse_merge_rows64_kernel(float *o_acc, float *lse_acc,
+                                                                    const float *o_step, const float *lse_step,
+                                                                    int64_t rows, int32_t d4_shift) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
+  const int d4 = 1 << d4_shift;
+  for (int64_t row0 = wave * 64; row0 < rows; row0 += nwaves * 64) {
+    const int64_t my_row = row0 + lane;
+    const bool live = my_row < rows;
+    double a1 = 0.0, a2 = 0.0, lse = -INFINITY;
+    merge_weights(live ? (double)lse_acc[my_row] : -INFINITY, live ? (double)lse_step[my_row] : -INFINITY, a1,
+                  a2, lse);
+    float4 *acc = reinterpret_cast<float4 *>(o_acc) + row0 * d4;
+    const float4 *stp = reinterpret_cast<const float4 *>(o_step) + row0 * d4;
+    const int64_t nvec = (rows - row0 < 64 ? rows - row0 : 64) * d4;  // vectors of the rows in range
+    for (int it0 = 0; it0 < d4; it0 += kUnroll) {
+      float4 x[kUnroll], y[kUnroll];
+#pragma unroll
+      for (int k = 0; k < kUnroll; ++k) {
+        const int v = (it0 + k) * 64 + lane;
+        if (it0 + k < d4 && v < nvec) {
+          x[k] = as_float4(__builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(acc + v)));
+          y[k] = as_float4(__builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(stp + v)));
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kUnroll; ++k) {
+        const int v = (it0 + k) * 64 + lane;
+        const int src = v >> d4_shift;  // the vector's row within the 64
+        const double b1 = __shfl(a1, src), b2 = __shfl(a2, src);
+        if (it0 + k < d4 && v < nvec)
+          __builtin_nontemporal_store(as_f32x4(blend(b1, x[k], b2, y[k])), reinterpret_cast<f32x4 *>(acc + v));
+      }
+    }
+    if (live) lse_acc[my_row] = (float)lse;
+  }
+}
 
 __global__ __launch_bounds__(kThreads) void lse_merge_kernel(float *o_acc, float *lse_acc,
                                                              const float *o_step,
@@ -35,40 +118,12 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(float *o_acc, float
       l1 = (double)lse_acc[row];
       l2 = (double)lse_step[row];
     }
-    const bool e1 = l1 == -INFINITY, e2 = l2 == -INFINITY;
     double a1, a2, lse;
-    if (e1 && e2) {
-      a1 = 0.0;
-      a2 = 0.0;
-      lse = -INFINITY;
-    } else if (e2) {
-      a1 = 1.0;
-      a2 = 0.0;
-      lse = l1;
-    } else if (e1) {
-      a1 = 0.0;
-      a2 = 1.0;
-      lse = l2;
-    } else {
-      const double M = l1 > l2 ? l1 : l2;
-      const double w = exp((l1 > l2 ? l2 : l1) - M);  // in (0, 1]
-      lse = M + log1p(w);
-      const double big = 1.0 / (1.0 + w), small = w / (1.0 + w);
-      a1 = l1 > l2 ? big : small;
-      a2 = l1 > l2 ? small : big;
-    }
+    merge_weights(l1, l2, a1, a2, lse);
     if (live) {
       float4 *acc = reinterpret_cast<float4 *>(o_acc + row * (int64_t)d4 * 4);
       const float4 *stp = reinterpret_cast<const float4 *>(o_step + row * (int64_t)d4 * 4);
-      for (int col = col0; col < d4; col += lanes_per_row) {
-        const float4 x = acc[col], y = stp[col];
-        float4 r;
-        r.x = (float)(a1 * (double)x.x + a2 * (double)y.x);
-        r.y = (float)(a1 * (double)x.y + a2 * (double)y.y);
-        r.z = (float)(a1 * (double)x.z + a2 * (double)y.z);
-        r.w = (float)(a1 * (double)x.w + a2 * (double)y.w);
-        acc[col] = r;
-      }
+      for (int col = col0; col < d4; col += lanes_per_row) acc[col] = blend(a1, acc[col], a2, stp[col]);
     }
     // every lane of this row read lse_acc[row] above (same wavefront, program order)
     if (live && col0 == 0) lse_acc[row] = (float)lse;
@@ -82,6 +137,15 @@ hipError_t launch_lse_merge(float *o_acc, float *lse_acc, const float *o_step,
                             hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   const int32_t d4 = (int32_t)(head_dim / 4);
+  if (d4 <= 64 && (d4 & (d4 - 1)) == 0) {
+    int32_t shift = 0;
+    while ((1 << shift) < d4) ++shift;
+    int64_t blocks = (rows + 4 * 64 - 1) / (4 * 64);  // 4 waves per block, 64 rows each
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(lse_merge_rows64_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, o_acc, lse_acc,
+                       o_step, lse_step, rows, shift);
+    return hipGetLastError();
+  }
   int32_t rows_per_wave = 1, lanes_per_row = 64;
   if (d4 <= 64 && 64 % d4 == 0) {
     rows_per_wave = 64 / d4;
