@@ -228,11 +228,11 @@ usp_status usp_ulysses_a2a_layout(const void *in, void *out, usp_dtype dtype, in
   p.row_bytes = (uint64_t)row_bytes;
   const uint32_t head_shift = log2_exact((uint64_t)row_bytes / 16);
   if (inverse && head_shift < 31) {
-    // output-major inverse: a row is one token's hb heads (contiguous in the
-    // output), gathered from the hb head planes
+    // output-major inverse: a row is one token's heads (contiguous in the
+    // output), gathered from the head planes
     p.kind = usp::kUlyssesInvRows;
-    p.n_items = (uint32_t)(G * batch * N);
-    p.row_bytes = (uint64_t)(hb * row_bytes);
+    p.n_items = (uint32_t)(G * batch);
+    p.row_bytes = (uint64_t)(heads * row_bytes);
     p.src_row_bytes = (uint64_t)row_bytes;
     p.grp_shift = head_shift;
   }

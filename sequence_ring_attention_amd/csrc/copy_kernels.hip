@@ -14,10 +14,11 @@
 // (hc/N, bs, L, hd)): for fixed (head h', batch b, source peer u') the
 // Ls = L/N rows of D elements are strided by hc*D on the sequence-major side
 // and contiguous on the head-major side.  The forward copies such head rows
-// (strided reads, contiguous writes).  The inverse writes whole output runs
-// instead: for fixed (token, source peer u') the hc/N heads are contiguous in
-// the output, so a row is that run, gathered from hc/N head-major planes;
-// writes then stream and only reads gather, as in the forward.
+// (strided reads, contiguous writes).  The inverse writes whole output rows
+// instead: a token's hc heads are contiguous in the output, and head
+// u' hc/N + h' is plane u' hc/N + h' of the head-major input, so a row is
+// gathered from the hc planes; writes then stream and only reads gather, as
+// in the forward.
 #include "usp_internal.h"
 
 namespace usp {
@@ -86,21 +87,17 @@ __device__ inline RowMap decode(const CopyPlan &P, uint32_t item) {
     m.src_base = ((up * bs + b) * Ls) * hc + u * hb + hp;
     m.src_stride = hc;
   } else if (P.kind == kUlyssesInvRows) {
-    // item (g, b, u'); row t = token t of output shard g, its heads
-    // [u' hb, (u' + 1) hb) from head planes h' of peer u' (src_grp apart)
-    const int64_t bs = P.p[0], L = P.p[1], N = P.p[3], hb = P.p[4], Ls = P.p[5];
+    // item (g, b); row t = token t of output shard g, all hc heads, head hh
+    // from plane hh = u' hb + h' of the head-major input (src_grp apart)
+    const int64_t bs = P.p[0], L = P.p[1], Ls = P.p[5];
     const int64_t u_fix = P.p[6];
-    int64_t rest = item;
-    const int64_t up = rest % N;
-    rest /= N;
-    const int64_t b = rest % bs;
-    const int64_t g = rest / bs;
+    const int64_t b = item % bs, g = item / bs;
     const int64_t u = u_fix < 0 ? g : u_fix;
-    m.src_base = (up * hb * bs + b) * L + u * Ls;
+    m.src_base = b * L + u * Ls;
     m.src_stride = 1;
     m.src_grp = bs * L;
-    m.dst_base = (g * bs + b) * Ls * N + up;
-    m.dst_stride = N;
+    m.dst_base = (g * bs + b) * Ls;
+    m.dst_stride = 1;
   } else {  // kUlyssesInv
     const int64_t bs = P.p[0], L = P.p[1], hc = P.p[2], N = P.p[3], hb = P.p[4], Ls = P.p[5];
     const int64_t u_fix = P.p[6];

@@ -21,7 +21,7 @@ enum CopyKind : int32_t {
   kZigzagInv = 1,  // shards -> global
   kUlyssesFwd = 2, // (N, bs, L/N, hc, hd) -> (G, hc/N, bs, L, hd)
   kUlyssesInv = 3, // (N, hc/N, bs, L, hd) -> (G, bs, L/N, hc, hd)
-  kUlyssesInvRows = 4, // the same, a row being one token's hc/N heads of the output
+  kUlyssesInvRows = 4, // the same, a row being one token's hc heads of the output
 };
 
 struct CopyPlan {
