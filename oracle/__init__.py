@@ -24,6 +24,11 @@ Sources (cited by title and section in every function):
 * [ByteScale notes] the Notion notes on ByteScale (sequence packing).
 * [YunChang] the YunChang (long-context-attention) README translation, for the
   user-facing layout [batch, seq_len, num_heads, head_dim].
+* [UPipe page] "Untied Ulysses：基于分头切分的高效上下文并行方案" -- the
+  ai-stack.site summary of UPipe.  Its section 2 (核心方法与创新) names
+  headwise chunking: attention heads pushed through in fine-grained chunks so
+  that the attention's intermediate tensors exist for one chunk at a time.
+  The rest of the page is commentary; only that idea is used.
 
 Modules:
 
@@ -32,7 +37,8 @@ Modules:
 * ``merge``     -- the LSE merge rule of [CP vs Ulysses].
 * ``index``     -- zigzag split, Ulysses layout, ring schedule, tile classes,
   causal load accounting.
-* ``usp``       -- Algorithms 1 and 2 composed over a virtual (ud x rd) grid.
+* ``usp``       -- Algorithms 1 and 2 composed over a virtual (ud x rd) grid,
+  also with the head blocks pushed through in chunks ([UPipe page]).
 * ``comm``      -- the per-GPU communication-volume formulas (design input only).
 * ``backward``  -- gradients of the attention (dQ, dK, dV): of the whole
   sequence, of one ring step given the forward's lse, and of one ring rank.

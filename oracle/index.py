@@ -130,6 +130,46 @@ def ulysses_inv(head_shards, ulysses_rank):
     return np.ascontiguousarray(np.concatenate(parts, axis=2))
 
 
+def ulysses_fwd_heads(shards, ulysses_rank, h0, nh):
+    """Head chunk [h0, h0 + nh) of Ulysses rank u's head block after the
+    forward all-to-all ([UPipe page] section 2, headwise chunking: the
+    all-to-all moves one chunk of every head block at a time).
+
+    ``shards``: the N sequence shards of the group, each (bs, L/N, hc, hd).
+    Element [i, b, u' L/N + t, :] of the result is element
+    [b, t, u hc/N + h0 + i, :] of shard u'.  Result: (nh, bs, L, hd).
+    """
+    N = len(shards)
+    bs, ls, hc, hd = shards[0].shape
+    hb = hc // N
+    if hc % N or h0 < 0 or nh < 1 or h0 + nh > hb:
+        raise ValueError("head chunk outside the head block")
+    out = np.empty((nh, bs, N * ls, hd), dtype=shards[0].dtype)
+    for up, sh in enumerate(shards):
+        for i in range(nh):
+            out[i, :, up * ls:(up + 1) * ls, :] = sh[:, :, ulysses_rank * hb + h0 + i, :]
+    return out
+
+
+def ulysses_inv_heads(head_chunks, ulysses_rank, h0, hc, out):
+    """Inverse all-to-all of one head chunk for Ulysses rank u, into ``out``
+    ((bs, L/N, hc, hd), rank u's output shard): peer u' computed heads
+    u' hc/N + h0 .. + nh of the whole gathered sequence, and rank u takes its
+    sequence slice u of them.  Heads outside the chunk are left as they are.
+
+    ``head_chunks``: the N peers' chunk outputs, each (nh, bs, L, hd).
+    """
+    N = len(head_chunks)
+    nh, bs, L, hd = head_chunks[0].shape
+    hb, ls = hc // N, L // N
+    if hc % N or L % N or h0 < 0 or h0 + nh > hb:
+        raise ValueError("head chunk outside the head block")
+    for up, hcnk in enumerate(head_chunks):
+        for i in range(nh):
+            out[:, :, up * hb + h0 + i, :] = hcnk[i, :, ulysses_rank * ls:(ulysses_rank + 1) * ls, :]
+    return out
+
+
 # --------------------------------------------------------------------------
 # Ring schedule ([CP vs Ulysses] concepts section and Figure 1)
 # --------------------------------------------------------------------------

@@ -104,6 +104,70 @@ def usp_attention(Q, K, V, rd, ud, scale, causal=True, cu_seqlens=None, per_samp
     return O, lse
 
 
+def kv_head_chunk(h0, nh, G):
+    """KV heads serving query heads [h0, h0 + nh) of a head block: query head h
+    reads KV head h // G, so the chunk's KV heads are [h0 / G, (h0 + nh) / G)."""
+    return h0 // G, nh // G
+
+
+def usp_attention_head_chunks(Q, K, V, rd, ud, scale, head_chunk, causal=True, cu_seqlens=None,
+                              per_sample=False):
+    """Algorithm 1 with each Ulysses head block pushed through the forward
+    all-to-all, the ring and the inverse all-to-all ``head_chunk`` query heads
+    at a time ([UPipe page] section 2, headwise chunking).
+
+    For chunk [h0, h0 + nh) of every head block the all-to-all moves those
+    query heads and their KV heads (:func:`kv_head_chunk`), the ring runs on
+    them alone, and the inverse all-to-all puts their outputs back; only one
+    chunk's head-major tensors exist at a time.  nh must divide the block's
+    hc / ud query heads and be a multiple of the GQA group G.  Same
+    arguments and results as :func:`usp_attention`.
+    """
+    B, S, H, D = Q.shape
+    Hkv = K.shape[2]
+    if H % ud or Hkv % ud or H % Hkv:
+        raise ValueError("head counts must divide by the Ulysses degree")
+    hb, G, nh = H // ud, H // Hkv, head_chunk
+    if nh < 1 or hb % nh or nh % G:
+        raise ValueError("the chunk must divide the head block and hold whole GQA groups")
+    if per_sample:
+        if cu_seqlens is None:
+            raise ValueError("the per-sample split needs cu_seqlens")
+        local = lambda r, u: ix.zigzag_per_sample_local_positions(cu_seqlens, rd, ud, r, u)
+    else:
+        local = lambda r, u: ix.zigzag_local_positions(S, rd, ud, r, u)
+    Qs = [[Q[:, local(r, u)].copy() for u in range(ud)] for r in range(rd)]
+    Ks = [[K[:, local(r, u)].copy() for u in range(ud)] for r in range(rd)]
+    Vs = [[V[:, local(r, u)].copy() for u in range(ud)] for r in range(rd)]
+    share_pos = [np.concatenate([local(r, u) for u in range(ud)]) for r in range(rd)]
+    out = [[np.zeros((B, S // (rd * ud), H, D)) for u in range(ud)] for r in range(rd)]
+    lse = np.full((H, B, S), -np.inf)
+    for h0 in range(0, hb, nh):
+        k0, nk = kv_head_chunk(h0, nh, G)
+        # forward all-to-all of the chunk, over each Ulysses group
+        Qh = [[ulysses_to_seq_major(ix.ulysses_fwd_heads(Qs[r], u, h0, nh)) for u in range(ud)] for r in range(rd)]
+        Kh = [[ulysses_to_seq_major(ix.ulysses_fwd_heads(Ks[r], u, k0, nk)) for u in range(ud)] for r in range(rd)]
+        Vh = [[ulysses_to_seq_major(ix.ulysses_fwd_heads(Vs[r], u, k0, nk)) for u in range(ud)] for r in range(rd)]
+        # the ring on the chunk's heads
+        Oh = [[None] * ud for _ in range(rd)]
+        for r in range(rd):
+            for u in range(ud):
+                o_ru, lse_ru = ring_attention_rank(
+                    Qh[r][u], share_pos[r], [Kh[j][u] for j in range(rd)], [Vh[j][u] for j in range(rd)],
+                    share_pos, r, scale, causal, cu_seqlens)
+                Oh[r][u] = np.ascontiguousarray(np.transpose(o_ru, (2, 0, 1, 3)))
+                lse[u * hb + h0:u * hb + h0 + nh][:, :, share_pos[r]] = lse_ru
+        # inverse all-to-all of the chunk's outputs
+        for r in range(rd):
+            for u in range(ud):
+                ix.ulysses_inv_heads(Oh[r], u, h0, H, out[r][u])
+    O = np.zeros((B, S, H, D))
+    for r in range(rd):
+        for u in range(ud):
+            O[:, local(r, u)] = out[r][u]
+    return O, lse
+
+
 def ulysses_to_seq_major(x):
     """(hc/N, bs, L, hd) -> (bs, L, hc/N, hd): a view change for the attention
     routine, which takes the [batch, seq, head, dim] layout."""
