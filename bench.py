@@ -211,6 +211,35 @@ def other_share_walk(Q, K, V, w, r, u, flops, steps=5):
             "frac_mfma": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
+def head_chunk_steps(Q, K, V, w, r, u, flops, whole_ms, whole_bytes, chunks=(8, 4, 2), steps=5):
+    """The share stepped with its head block pushed through in chunks
+    (headwise chunking): step time and the head-major bytes one chunk's
+    attention works on, beside the whole block's."""
+    import torch
+    from sequence_ring_attention_amd.pipeline import OneGpuShare
+    res = {"whole_block": {"heads": w.H // w.ud, "ms": whole_ms, "TFLOP/s": flops / (whole_ms * 1e-3) / 1e12,
+                           "head_major_bytes": whole_bytes}}
+    for nh in chunks:
+        sh = OneGpuShare(Q, K, V, w.rd, w.ud, r, u, head_chunk=nh)
+        sh.prepare_peers()
+        sh.step()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            sh.step()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        res[f"chunks_of_{nh}"] = {"heads": nh, "ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+                                  "head_major_bytes": sh.head_major_bytes(),
+                                  "head_major_fraction": sh.head_major_bytes() / whole_bytes,
+                                  "step_time_ratio": ms / whole_ms}
+        del sh
+        torch.cuda.empty_cache()
+    return res
+
+
 def packed_pairs(cu, pos):
     """Visible (query, key) pairs of queries at `pos` under the causal
     same-sample mask: a query at p sees p - start(sample of p) + 1 keys."""
@@ -522,6 +551,8 @@ def main():
         r2 = w.rd - 1 if r != w.rd - 1 else 0
         print(f"[bench] walk of share ({r2}, {u})", file=sys.stderr, flush=True)
         result["other_share"] = other_share_walk(Q, K, V, w, r2, u, flops)
+        print("[bench] head chunks", file=sys.stderr, flush=True)
+        result["head_chunks"] = head_chunk_steps(Q, K, V, w, r, u, flops, ms_step, share.head_major_bytes())
     if not args.no_extra:
         print("[bench] other workloads", file=sys.stderr, flush=True)
         del share, Q, K, V

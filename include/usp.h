@@ -14,6 +14,9 @@
  *   [YunChang]      the YunChang README translation: the user-facing layout
  *                   [batch, seq_len, num_heads, head_dim] and the attention
  *                   call's options (dropout, window, softcap, ALiBi ...).
+ *   [UPipe page]    "Untied Ulysses：基于分头切分的高效上下文并行方案"
+ *                   (ai-stack.site summary of UPipe), section 2: headwise
+ *                   chunking of the Ulysses head blocks.
  *
  * Conventions shared by every entry point:
  *   - Every buffer is device memory owned by the caller.  The library
@@ -42,7 +45,7 @@
 extern "C" {
 #endif
 
-#define USP_ABI_VERSION 3
+#define USP_ABI_VERSION 4
 
 /* Most packed samples one call takes (their boundaries travel by value). */
 #define USP_MAX_SEQS 256
@@ -170,6 +173,28 @@ usp_status usp_ulysses_a2a_layout(const void *in, void *out, usp_dtype dtype, in
                                   int64_t seq_len, int64_t heads, int64_t head_dim,
                                   int32_t ulysses_degree, int32_t ulysses_rank, int32_t inverse,
                                   void *stream);
+
+/*
+ * The Ulysses layout of one chunk of heads -- headwise chunking ([UPipe
+ * page] "Untied Ulysses", section 2): the all-to-all moves heads
+ * [head_offset, head_offset + num_heads) of every head block at a time, so
+ * that the attention's head-major tensors exist for one chunk only.  With
+ * head_offset = 0 and num_heads = hc/N it is usp_ulysses_a2a_layout.
+ *
+ * Forward: in = (N, bs, L/N, hc, hd); out = (num_heads, bs, L, hd) for rank
+ *   u, or (N, num_heads, bs, L, hd) for -1:
+ *     Y_u[i, b, u' (L/N) + t, :] = X_u'[b, t, u (hc/N) + head_offset + i, :].
+ * Inverse: in = the N peers' chunk outputs (N, num_heads, bs, L, hd); out =
+ *   rank u's (bs, L/N, hc, hd), or (N, bs, L/N, hc, hd) for -1.  Only heads
+ *   u' (hc/N) + head_offset + i of the output are written; the rest of out
+ *   is left as it is.
+ * Errors: as usp_ulysses_a2a_layout, plus USP_ERR_INVALID_ARG unless
+ *   0 <= head_offset and 1 <= num_heads and head_offset + num_heads <= hc/N.
+ */
+usp_status usp_ulysses_a2a_layout_heads(const void *in, void *out, usp_dtype dtype, int64_t batch,
+                                        int64_t seq_len, int64_t heads, int64_t head_dim,
+                                        int32_t ulysses_degree, int32_t ulysses_rank, int64_t head_offset,
+                                        int64_t num_heads, int32_t inverse, void *stream);
 
 /*
  * One ring step -- [CP vs Ulysses], concepts section and Figure 1: at step t

@@ -106,8 +106,10 @@ def usp_attention(Q, K, V, rd, ud, scale, causal=True, cu_seqlens=None, per_samp
 
 def kv_head_chunk(h0, nh, G):
     """KV heads serving query heads [h0, h0 + nh) of a head block: query head h
-    reads KV head h // G, so the chunk's KV heads are [h0 / G, (h0 + nh) / G)."""
-    return h0 // G, nh // G
+    reads KV head h // G, so a chunk of whole GQA groups has KV heads
+    [h0 / G, (h0 + nh) / G), and a chunk inside one group (nh dividing G)
+    has that group's single KV head."""
+    return h0 // G, max(nh // G, 1)
 
 
 def usp_attention_head_chunks(Q, K, V, rd, ud, scale, head_chunk, causal=True, cu_seqlens=None,
@@ -120,16 +122,16 @@ def usp_attention_head_chunks(Q, K, V, rd, ud, scale, head_chunk, causal=True, c
     query heads and their KV heads (:func:`kv_head_chunk`), the ring runs on
     them alone, and the inverse all-to-all puts their outputs back; only one
     chunk's head-major tensors exist at a time.  nh must divide the block's
-    hc / ud query heads and be a multiple of the GQA group G.  Same
-    arguments and results as :func:`usp_attention`.
+    hc / ud query heads and be a multiple or a divisor of the GQA group G.
+    Same arguments and results as :func:`usp_attention`.
     """
     B, S, H, D = Q.shape
     Hkv = K.shape[2]
     if H % ud or Hkv % ud or H % Hkv:
         raise ValueError("head counts must divide by the Ulysses degree")
     hb, G, nh = H // ud, H // Hkv, head_chunk
-    if nh < 1 or hb % nh or nh % G:
-        raise ValueError("the chunk must divide the head block and hold whole GQA groups")
+    if nh < 1 or hb % nh or (nh % G and G % nh):
+        raise ValueError("the chunk must divide the head block and hold whole GQA groups or lie in one")
     if per_sample:
         if cu_seqlens is None:
             raise ValueError("the per-sample split needs cu_seqlens")

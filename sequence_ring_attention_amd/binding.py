@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libusp.so")
 USP_OK, USP_ERR_INVALID_ARG, USP_ERR_UNSUPPORTED, USP_ERR_HIP = 0, 1, 2, 3
 USP_DTYPE_BF16, USP_DTYPE_FP32 = 0, 1
 
-EXPORTED = ["usp_zigzag_extract", "usp_zigzag_extract_varlen", "usp_ulysses_a2a_layout", "usp_ring_attn_step_fwd",
+EXPORTED = ["usp_zigzag_extract", "usp_zigzag_extract_varlen", "usp_ulysses_a2a_layout",
+            "usp_ulysses_a2a_layout_heads", "usp_ring_attn_step_fwd",
             "usp_lse_merge", "usp_attn_fwd", "usp_attn_bwd_prep", "usp_ring_attn_step_bwd", "usp_attn_bwd",
             "usp_status_string", "usp_last_error_detail", "usp_abi_version"]
 
@@ -62,6 +63,7 @@ def lib():
         L.usp_zigzag_extract_varlen.argtypes = [vp, vp, st, i64, i64, i64, i64, i32, i32, i32, i32, i32, vp, i32,
                                                 vp]
         L.usp_ulysses_a2a_layout.argtypes = [vp, vp, st, i64, i64, i64, i64, i32, i32, i32, vp]
+        L.usp_ulysses_a2a_layout_heads.argtypes = [vp, vp, st, i64, i64, i64, i64, i32, i32, i64, i64, i32, vp]
         L.usp_ring_attn_step_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, i32, vp]
         L.usp_lse_merge.argtypes = [vp, vp, vp, vp, i64, i64, vp]
         L.usp_attn_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, vp]
@@ -69,7 +71,8 @@ def lib():
         L.usp_ring_attn_step_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc),
                                              i32, i32, vp]
         L.usp_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, vp]
-        for f in ("usp_zigzag_extract", "usp_zigzag_extract_varlen", "usp_ulysses_a2a_layout", "usp_ring_attn_step_fwd",
+        for f in ("usp_zigzag_extract", "usp_zigzag_extract_varlen", "usp_ulysses_a2a_layout",
+                  "usp_ulysses_a2a_layout_heads", "usp_ring_attn_step_fwd",
                   "usp_lse_merge", "usp_attn_fwd", "usp_attn_bwd_prep", "usp_ring_attn_step_bwd",
                   "usp_attn_bwd"):
             getattr(L, f).restype = st
@@ -174,6 +177,32 @@ def usp_ulysses_a2a_layout(inp, out, degree, rank, inverse=False, stream=None):
         raise ValueError("out has the wrong number of elements")
     check(lib().usp_ulysses_a2a_layout(inp.data_ptr(), out.data_ptr(), _dtype(inp), bs, L, hc, hd,
                                        degree, rank, int(inverse), _stream(stream)))
+    return out
+
+
+def usp_ulysses_a2a_layout_heads(inp, out, degree, rank, head_offset, num_heads, inverse=False, stream=None):
+    """Heads [head_offset, head_offset + num_heads) of every head block.
+    Forward: inp (N, bs, L/N, hc, hd) -> out (num_heads, bs, L, hd) [rank u]
+    or (N, ...) [rank -1].  Inverse: inp (N, num_heads, bs, L, hd) -> the
+    chunk's heads of out (bs, L/N, hc, hd) [or (N, ...)], hc read from out."""
+    _dev(inp, out)
+    _contig(inp, out)
+    if not inverse:
+        N, bs, ls, hc, hd = inp.shape
+        L = ls * N
+        want = (degree if rank < 0 else 1) * num_heads * bs * L * hd
+    else:
+        N, nh, bs, L, hd = inp.shape
+        hc = out.shape[-2]
+        if nh != num_heads:
+            raise ValueError("inp must hold num_heads heads per peer")
+        want = (degree if rank < 0 else 1) * bs * (L // degree) * hc * hd
+    if N != degree:
+        raise ValueError("leading dimension of inp must equal the Ulysses degree")
+    if out.numel() != want:
+        raise ValueError("out has the wrong number of elements")
+    check(lib().usp_ulysses_a2a_layout_heads(inp.data_ptr(), out.data_ptr(), _dtype(inp), bs, L, hc, hd, degree,
+                                             rank, head_offset, num_heads, int(inverse), _stream(stream)))
     return out
 
 

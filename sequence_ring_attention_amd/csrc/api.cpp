@@ -57,6 +57,7 @@ void plan_pieces(usp::CopyPlan &p) {
     p.src_row_bytes = p.row_bytes;
     p.grp_shift = 31;
   }
+  if (p.dst_unit_bytes == 0) p.dst_unit_bytes = p.row_bytes;
 }
 
 constexpr int64_t kMaxIndex = (int64_t)1 << 31;
@@ -190,49 +191,59 @@ usp_status usp_zigzag_extract_varlen(const void *x, void *out, usp_dtype dtype, 
   return hip_result(usp::launch_zigzag_varlen(a, static_cast<hipStream_t>(stream)), "zigzag_extract_varlen launch");
 }
 
-usp_status usp_ulysses_a2a_layout(const void *in, void *out, usp_dtype dtype, int64_t batch,
-                                  int64_t seq_len, int64_t heads, int64_t head_dim,
-                                  int32_t ulysses_degree, int32_t ulysses_rank, int32_t inverse,
-                                  void *stream) {
-  if (!in || !out) return fail(USP_ERR_INVALID_ARG, "ulysses_a2a_layout: null pointer");
+namespace {
+
+// The Ulysses layout of heads [h0, h0 + nh) of every head block (the whole
+// block when h0 = 0, nh = heads / degree).
+usp_status ulysses_layout(const char *who, const void *in, void *out, usp_dtype dtype, int64_t batch,
+                          int64_t seq_len, int64_t heads, int64_t head_dim, int32_t ulysses_degree,
+                          int32_t ulysses_rank, int64_t h0, int64_t nh, int32_t inverse, void *stream) {
+  if (!in || !out) return fail(USP_ERR_INVALID_ARG, "%s: null pointer", who);
   if (!aligned16(in) || !aligned16(out))
-    return fail(USP_ERR_INVALID_ARG, "ulysses_a2a_layout: pointers must be 16-byte aligned");
-  if (in == out) return fail(USP_ERR_INVALID_ARG, "ulysses_a2a_layout: in and out must differ");
-  if (!dtype_ok(dtype)) return fail(USP_ERR_INVALID_ARG, "ulysses_a2a_layout: unknown dtype %d", (int)dtype);
+    return fail(USP_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", who);
+  if (in == out) return fail(USP_ERR_INVALID_ARG, "%s: in and out must differ", who);
+  if (!dtype_ok(dtype)) return fail(USP_ERR_INVALID_ARG, "%s: unknown dtype %d", who, (int)dtype);
   if (batch < 1 || seq_len < 1 || heads < 1 || head_dim < 1 || ulysses_degree < 1)
-    return fail(USP_ERR_INVALID_ARG, "ulysses_a2a_layout: sizes and degree must be >= 1");
-  if (inverse != 0 && inverse != 1) return fail(USP_ERR_INVALID_ARG, "ulysses_a2a_layout: inverse must be 0 or 1");
+    return fail(USP_ERR_INVALID_ARG, "%s: sizes and degree must be >= 1", who);
+  if (inverse != 0 && inverse != 1) return fail(USP_ERR_INVALID_ARG, "%s: inverse must be 0 or 1", who);
   const int64_t N = ulysses_degree;
   if (heads % N != 0)
-    return fail(USP_ERR_INVALID_ARG, "ulysses_a2a_layout: heads %lld not divisible by degree %lld",
-                (long long)heads, (long long)N);
+    return fail(USP_ERR_INVALID_ARG, "%s: heads %lld not divisible by degree %lld", who, (long long)heads,
+                (long long)N);
   if (seq_len % N != 0)
-    return fail(USP_ERR_INVALID_ARG, "ulysses_a2a_layout: seq_len %lld not divisible by degree %lld",
-                (long long)seq_len, (long long)N);
+    return fail(USP_ERR_INVALID_ARG, "%s: seq_len %lld not divisible by degree %lld", who, (long long)seq_len,
+                (long long)N);
   if (ulysses_rank < -1 || ulysses_rank >= ulysses_degree)
-    return fail(USP_ERR_INVALID_ARG, "ulysses_a2a_layout: rank out of range");
+    return fail(USP_ERR_INVALID_ARG, "%s: rank out of range", who);
+  const int64_t hb = heads / N, Ls = seq_len / N;
+  if (h0 < 0 || nh < 1 || h0 + nh > hb)
+    return fail(USP_ERR_INVALID_ARG, "%s: head range [%lld, %lld) outside the head block of %lld", who,
+                (long long)h0, (long long)(h0 + nh), (long long)hb);
   const int64_t row_bytes = head_dim * elem_bytes(dtype);
   if (row_bytes % 16 != 0)
-    return fail(USP_ERR_UNSUPPORTED, "ulysses_a2a_layout: head_dim*element size must be a multiple of 16 bytes");
-  if (N * batch * seq_len * heads >= kMaxIndex)
-    return fail(USP_ERR_UNSUPPORTED, "ulysses_a2a_layout: too many rows");
+    return fail(USP_ERR_UNSUPPORTED, "%s: head_dim*element size must be a multiple of 16 bytes", who);
+  if (N * batch * seq_len * heads >= kMaxIndex) return fail(USP_ERR_UNSUPPORTED, "%s: too many rows", who);
 
   const int64_t G = ulysses_rank < 0 ? N : 1;
-  const int64_t hb = heads / N, Ls = seq_len / N;
   usp::CopyPlan p{};
   p.src = static_cast<const char *>(in);
   p.dst = static_cast<char *>(out);
   p.kind = inverse ? usp::kUlyssesInv : usp::kUlyssesFwd;
-  p.n_items = (uint32_t)(G * hb * batch * N);
+  p.n_items = (uint32_t)(G * nh * batch * N);
   p.rows_per_item = (uint32_t)Ls;
   p.row_bytes = (uint64_t)row_bytes;
+  int64_t peers_per_item = 1;
   const uint32_t head_shift = log2_exact((uint64_t)row_bytes / 16);
   if (inverse && head_shift < 31) {
-    // output-major inverse: a row is one token's heads (contiguous in the
-    // output), gathered from the head planes
+    // output-major inverse: a row is one token's heads of the chunk (all of
+    // its heads when the chunk is the whole block), contiguous in the
+    // output and gathered from the head planes
+    const bool whole = nh == hb;
+    peers_per_item = whole ? 1 : N;
     p.kind = usp::kUlyssesInvRows;
-    p.n_items = (uint32_t)(G * batch);
-    p.row_bytes = (uint64_t)(heads * row_bytes);
+    p.n_items = (uint32_t)(G * batch * peers_per_item);
+    p.row_bytes = (uint64_t)((whole ? heads : nh) * row_bytes);
+    p.dst_unit_bytes = (uint64_t)row_bytes;
     p.src_row_bytes = (uint64_t)row_bytes;
     p.grp_shift = head_shift;
   }
@@ -243,8 +254,30 @@ usp_status usp_ulysses_a2a_layout(const void *in, void *out, usp_dtype dtype, in
   p.p[4] = hb;
   p.p[5] = Ls;
   p.p[6] = ulysses_rank;
+  p.p[7] = h0;
+  p.p[8] = nh;
+  p.p[9] = peers_per_item;
   plan_pieces(p);
-  return hip_result(usp::launch_copy(p, static_cast<hipStream_t>(stream)), "ulysses_a2a_layout launch");
+  return hip_result(usp::launch_copy(p, static_cast<hipStream_t>(stream)), "ulysses layout launch");
+}
+
+}  // namespace
+
+usp_status usp_ulysses_a2a_layout(const void *in, void *out, usp_dtype dtype, int64_t batch,
+                                  int64_t seq_len, int64_t heads, int64_t head_dim,
+                                  int32_t ulysses_degree, int32_t ulysses_rank, int32_t inverse,
+                                  void *stream) {
+  const int64_t hb = ulysses_degree >= 1 && heads >= 1 ? heads / ulysses_degree : 1;
+  return ulysses_layout("ulysses_a2a_layout", in, out, dtype, batch, seq_len, heads, head_dim, ulysses_degree,
+                        ulysses_rank, 0, hb < 1 ? 1 : hb, inverse, stream);
+}
+
+usp_status usp_ulysses_a2a_layout_heads(const void *in, void *out, usp_dtype dtype, int64_t batch,
+                                        int64_t seq_len, int64_t heads, int64_t head_dim,
+                                        int32_t ulysses_degree, int32_t ulysses_rank, int64_t head_offset,
+                                        int64_t num_heads, int32_t inverse, void *stream) {
+  return ulysses_layout("ulysses_a2a_layout_heads", in, out, dtype, batch, seq_len, heads, head_dim, ulysses_degree,
+                        ulysses_rank, head_offset, num_heads, inverse, stream);
 }
 
 usp_status usp_lse_merge(float *o_acc, float *lse_acc, const float *o_step, const float *lse_step,

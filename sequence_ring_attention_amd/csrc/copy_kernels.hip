@@ -73,45 +73,51 @@ __device__ inline RowMap decode(const CopyPlan &P, uint32_t item) {
     m.split = split;
   } else if (P.kind == kUlyssesFwd) {
     const int64_t bs = P.p[0], L = P.p[1], hc = P.p[2], N = P.p[3], hb = P.p[4], Ls = P.p[5];
-    const int64_t u_fix = P.p[6];
+    const int64_t u_fix = P.p[6], h0 = P.p[7], nh = P.p[8];
     int64_t rest = item;
     const int64_t up = rest % N;
     rest /= N;
     const int64_t b = rest % bs;
     rest /= bs;
-    const int64_t hp = rest % hb;
-    const int64_t g = rest / hb;
+    const int64_t hp = rest % nh;
+    const int64_t g = rest / nh;
     const int64_t u = u_fix < 0 ? g : u_fix;
-    m.dst_base = ((g * hb + hp) * bs + b) * L + up * Ls;
+    m.dst_base = ((g * nh + hp) * bs + b) * L + up * Ls;
     m.dst_stride = 1;
-    m.src_base = ((up * bs + b) * Ls) * hc + u * hb + hp;
+    m.src_base = ((up * bs + b) * Ls) * hc + u * hb + h0 + hp;
     m.src_stride = hc;
   } else if (P.kind == kUlyssesInvRows) {
-    // item (g, b); row t = token t of output shard g, all hc heads, head hh
-    // from plane hh = u' hb + h' of the head-major input (src_grp apart)
-    const int64_t bs = P.p[0], L = P.p[1], Ls = P.p[5];
-    const int64_t u_fix = P.p[6];
-    const int64_t b = item % bs, g = item / bs;
+    // item (g, b, peer group); row t = token t of output shard g: heads
+    // u' hb + h0 .. + nh of one peer u' (np = N), or all hc heads when the
+    // chunk is the whole block (np = 1, u' = 0: head hh is plane hh); head i
+    // of the row comes from input plane u' nh + i (src_grp rows apart), and
+    // destination offsets count head rows
+    const int64_t bs = P.p[0], L = P.p[1], hc = P.p[2], hb = P.p[4], Ls = P.p[5];
+    const int64_t u_fix = P.p[6], h0 = P.p[7], nh = P.p[8], np = P.p[9];
+    int64_t rest = item;
+    const int64_t up = rest % np;
+    rest /= np;
+    const int64_t b = rest % bs, g = rest / bs;
     const int64_t u = u_fix < 0 ? g : u_fix;
-    m.src_base = b * L + u * Ls;
+    m.src_base = (up * nh * bs + b) * L + u * Ls;
     m.src_stride = 1;
     m.src_grp = bs * L;
-    m.dst_base = (g * bs + b) * Ls;
-    m.dst_stride = 1;
-  } else {  // kUlyssesInv
+    m.dst_base = (g * bs + b) * Ls * hc + up * hb + h0;
+    m.dst_stride = hc;
+  } else {  // kUlyssesInv: one head row per row
     const int64_t bs = P.p[0], L = P.p[1], hc = P.p[2], N = P.p[3], hb = P.p[4], Ls = P.p[5];
-    const int64_t u_fix = P.p[6];
+    const int64_t u_fix = P.p[6], h0 = P.p[7], nh = P.p[8];
     int64_t rest = item;
-    const int64_t hp = rest % hb;
-    rest /= hb;
+    const int64_t hp = rest % nh;
+    rest /= nh;
     const int64_t up = rest % N;
     rest /= N;
     const int64_t b = rest % bs;
     const int64_t g = rest / bs;
     const int64_t u = u_fix < 0 ? g : u_fix;
-    m.src_base = ((up * hb + hp) * bs + b) * L + u * Ls;
+    m.src_base = ((up * nh + hp) * bs + b) * L + u * Ls;
     m.src_stride = 1;
-    m.dst_base = ((g * bs + b) * Ls) * hc + up * hb + hp;
+    m.dst_base = ((g * bs + b) * Ls) * hc + up * hb + h0 + hp;
     m.dst_stride = hc;
   }
   return m;
@@ -150,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void copy_rows_kernel(CopyPlan P) {
           const int64_t drow = m.dst_base + t * m.dst_stride + (second ? m.dst_jump : 0);
           buf[k] = __builtin_nontemporal_load(
               reinterpret_cast<const u32x4 *>(P.src + srow * (int64_t)P.src_row_bytes) + gcol);
-          doff[k] = drow * (int64_t)P.row_bytes + (int64_t)col * 16;
+          doff[k] = drow * (int64_t)P.dst_unit_bytes + (int64_t)col * 16;
         }
       }
 #pragma unroll

@@ -19,9 +19,10 @@ namespace usp {
 enum CopyKind : int32_t {
   kZigzagFwd = 0,  // global (B,S,H,D) -> shards
   kZigzagInv = 1,  // shards -> global
-  kUlyssesFwd = 2, // (N, bs, L/N, hc, hd) -> (G, hc/N, bs, L, hd)
-  kUlyssesInv = 3, // (N, hc/N, bs, L, hd) -> (G, bs, L/N, hc, hd)
-  kUlyssesInvRows = 4, // the same, a row being one token's hc heads of the output
+  // Ulysses kinds move heads [h0, h0 + nh) of every head block (all hc/N by default)
+  kUlyssesFwd = 2, // (N, bs, L/N, hc, hd) -> (G, nh, bs, L, hd)
+  kUlyssesInv = 3, // (N, nh, bs, L, hd) -> (G, bs, L/N, hc, hd), the chunk's heads
+  kUlyssesInvRows = 4, // the same, a row being one token's heads of the chunk in the output
 };
 
 struct CopyPlan {
@@ -35,10 +36,12 @@ struct CopyPlan {
   uint32_t rows_per_piece;  // rows a workgroup copies per piece
   uint32_t pieces_per_item;
   uint64_t row_bytes;      // destination row
+  uint64_t dst_unit_bytes; // unit of destination row offsets (row_bytes, or one head's hd elements)
   uint64_t src_row_bytes;  // source row (row_bytes, or one head's hd elements for kUlyssesInvRows)
   uint32_t grp_shift;      // log2(16-byte vectors per source row) when a row gathers several, else 31
   // zigzag: B, S (rows), chunk c, rd, ud, shard rows T, fixed ranks (or -1)
-  // ulysses: bs, L, hc, N, hb = hc/N, Ls = L/N, fixed rank (or -1)
+  // ulysses: bs, L, hc, N, hb = hc/N, Ls = L/N, fixed rank (or -1), h0, nh,
+  //          peers per item (kUlyssesInvRows)
   int64_t p[10];
 };
 

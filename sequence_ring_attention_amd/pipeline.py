@@ -15,6 +15,10 @@ Ulysses ranks' shards and outputs (all-to-all) and the other ring ranks' KV
 blocks (ring P2P).  Here they are produced once by ``prepare_peers`` with
 the same kernels, outside ``step``; ``step`` is exactly the per-GPU work.
 
+With ``head_chunk`` (headwise chunking, [UPipe page] section 2) steps 2-4
+run once per chunk of ``head_chunk`` query heads of the head block (and
+their KV heads): the head-major tensors then hold one chunk at a time.
+
 This module only allocates buffers and sequences C-ABI calls.
 """
 import torch
@@ -23,11 +27,14 @@ from . import binding as B
 
 
 class OneGpuShare:
-    def __init__(self, Q, K, V, rd, ud, ring_rank, ulysses_rank, causal=True, cu_seqlens=None, per_sample=False):
+    def __init__(self, Q, K, V, rd, ud, ring_rank, ulysses_rank, causal=True, cu_seqlens=None, per_sample=False,
+                 head_chunk=None):
         """Q (B, S, H, D), K/V (B, S, Hkv, D): global tensors on the GPU.
         ``cu_seqlens``: packed-sample boundaries; ``per_sample``: the shares
         are the per-sample zigzag split (Algorithm 2 on every sample) instead
-        of the split of the whole packed stream."""
+        of the split of the whole packed stream.  ``head_chunk``: query heads
+        per chunk (dividing H / ud, a multiple or a divisor of H / Hkv), or
+        None for the whole head block at once."""
         self.Q, self.K, self.V = Q, K, V
         self.rd, self.ud, self.r, self.u = rd, ud, ring_rank, ulysses_rank
         Bn, S, H, D = Q.shape
@@ -37,6 +44,13 @@ class OneGpuShare:
         self.Bn, self.S, self.H, self.Hkv, self.D = Bn, S, H, Hkv, D
         self.T, self.L = S // (rd * ud), S // rd
         self.causal, self.per_sample = causal, per_sample
+        hb, G = H // ud, H // Hkv
+        if head_chunk is not None and head_chunk != hb:
+            if head_chunk < 1 or hb % head_chunk or (head_chunk % G and G % head_chunk):
+                raise ValueError("head_chunk must divide H / ud and hold whole GQA groups or lie in one")
+            self.chunk = int(head_chunk)
+        else:
+            self.chunk = None
         self.cu = None if cu_seqlens is None else B.host_cu_seqlens(cu_seqlens)
         if per_sample and self.cu is None:
             raise ValueError("the per-sample split needs cu_seqlens")
@@ -45,14 +59,19 @@ class OneGpuShare:
         e = lambda *s: torch.empty(*s, dtype=dt, device=dev)
         # group shards of ring group r (slot u is ours, the others are the peers')
         self.qz, self.kz, self.vz = e(ud, Bn, T, H, D), e(ud, Bn, T, Hkv, D), e(ud, Bn, T, Hkv, D)
-        # head-major Q of every Ulysses rank in the group, and the ring's KV
-        # blocks (block j = ring rank j's share) for every head block
-        self.qh = e(ud, H // ud, Bn, L, D)
+        # the ring's KV blocks (block j = ring rank j's share) for every head block
         self.kh = e(ud, rd, Hkv // ud, Bn, L, D)
         self.vh = e(ud, rd, Hkv // ud, Bn, L, D)
-        # outputs of every Ulysses rank of the group, and lse
-        self.oh = e(ud, H // ud, Bn, L, D)
-        self.lse = torch.empty(ud, H // ud, Bn, L, dtype=torch.float32, device=dev)
+        if self.chunk is None:
+            # head-major Q and outputs of every Ulysses rank in the group
+            self.qh = e(ud, hb, Bn, L, D)
+            self.oh = e(ud, hb, Bn, L, D)
+        else:
+            # one chunk of query heads, head-major (reused by every chunk), and
+            # the group's outputs chunk by chunk: [c, u'] = rank u''s heads of chunk c
+            self.qc = e(self.chunk, Bn, L, D)
+            self.ohc = e(hb // self.chunk, ud, self.chunk, Bn, L, D)
+        self.lse = torch.empty(ud, hb, Bn, L, dtype=torch.float32, device=dev)
         self.out = e(Bn, T, H, D)     # this GPU's output shard after the inverse layout
         self._descs = {}
 
@@ -80,6 +99,32 @@ class OneGpuShare:
     def _walk(self, u):
         B.usp_attn_fwd(self.qh[u], self.kh[u], self.vh[u], self.oh[u], self.lse[u], self.desc(u), self.r)
 
+    # ------------------------------------------------------ head chunks --
+    def _chunk_heads(self, c):
+        """Query heads [h0, h0 + nh) and KV heads [k0, k0 + nk) of chunk c
+        (query head h reads KV head h // G; a chunk inside one GQA group
+        has that group's KV head)."""
+        nh, G = self.chunk, self.H // self.Hkv
+        return c * nh, nh, c * nh // G, max(nh // G, 1)
+
+    def _chunk_desc(self):
+        if "chunk" not in self._descs:
+            _, _, k0, nk = self._chunk_heads(0)
+            self._descs["chunk"] = B.attn_desc(self.S, self.rd, self.qc, self.kh[0][:, k0:k0 + nk],
+                                               self.vh[0][:, k0:k0 + nk], o=self.ohc[0, 0], layout="hbsd",
+                                               causal=self.causal, cu_seqlens=self.cu,
+                                               zigzag_per_sample=self.per_sample)
+        return self._descs["chunk"]
+
+    def _walk_chunk(self, u, c):
+        """Ulysses rank u's walk over chunk c's heads, its query heads in qc."""
+        h0, nh, k0, nk = self._chunk_heads(c)
+        B.usp_attn_fwd(self.qc, self.kh[u][:, k0:k0 + nk], self.vh[u][:, k0:k0 + nk], self.ohc[c, u],
+                       self.lse[u, h0:h0 + nh], self._chunk_desc(), self.r)
+
+    def _chunks(self):
+        return range(self.H // self.ud // self.chunk)
+
     def prepare_peers(self):
         """Everything the peers would send: other ring ranks' KV blocks (all
         head blocks), the group's other shards, and the other Ulysses ranks'
@@ -93,15 +138,24 @@ class OneGpuShare:
         self._extract(self.K, self.kz, self.r, -1)
         self._extract(self.V, self.vz, self.r, -1)
         for u in range(self.ud):
-            if u != self.u:
+            if u == self.u:
+                continue
+            if self.chunk is None:
                 B.usp_ulysses_a2a_layout(self.qz, self.qh[u], self.ud, u)
                 self._walk(u)
+            else:
+                for c in self._chunks():
+                    h0, nh, _, _ = self._chunk_heads(c)
+                    B.usp_ulysses_a2a_layout_heads(self.qz, self.qc, self.ud, u, h0, nh)
+                    self._walk_chunk(u, c)
 
     def step(self, marks=None):
         """The per-GPU hot path: extract, layout, ring walk, inverse layout.
 
         ``marks``: optional 5 events recorded on the current stream around
-        the four phases (for per-kernel timing)."""
+        the four phases (for per-kernel timing).  With head chunks the
+        layouts and walks of the chunks interleave: marks 1 and 2 then both
+        follow the extract, and marks 3 and 4 both close the step."""
         r, u, rd, ud = self.r, self.u, self.rd, self.ud
         mark = (lambda i: marks[i].record()) if marks is not None else (lambda i: None)
         mark(0)
@@ -109,6 +163,21 @@ class OneGpuShare:
         self._extract(self.K, self.kz[u], r, u)
         self._extract(self.V, self.vz[u], r, u)
         mark(1)
+        if self.chunk is not None:
+            mark(2)
+            k_done = -1
+            for c in self._chunks():
+                h0, nh, k0, nk = self._chunk_heads(c)
+                B.usp_ulysses_a2a_layout_heads(self.qz, self.qc, ud, u, h0, nh)
+                if k0 != k_done:  # chunks inside one GQA group share its KV head
+                    B.usp_ulysses_a2a_layout_heads(self.kz, self.kh[u, r, k0:k0 + nk], ud, u, k0, nk)
+                    B.usp_ulysses_a2a_layout_heads(self.vz, self.vh[u, r, k0:k0 + nk], ud, u, k0, nk)
+                    k_done = k0
+                self._walk_chunk(u, c)
+                B.usp_ulysses_a2a_layout_heads(self.ohc[c], self.out, ud, u, h0, nh, inverse=True)
+            mark(3)
+            mark(4)
+            return self.out
         B.usp_ulysses_a2a_layout(self.qz, self.qh[u], ud, u)
         B.usp_ulysses_a2a_layout(self.kz, self.kh[u, r], ud, u)
         B.usp_ulysses_a2a_layout(self.vz, self.vh[u, r], ud, u)
@@ -120,6 +189,17 @@ class OneGpuShare:
         return self.out
 
     # ------------------------------------------------------- accounting --
+    def head_major_bytes(self):
+        """Bytes of the head-major tensors one chunk's attention works on
+        (its query heads, one ring block of their KV heads, its outputs):
+        what headwise chunking bounds."""
+        e = self.Q.element_size()
+        if self.chunk is None:
+            nh, nk = self.H // self.ud, self.Hkv // self.ud
+        else:
+            _, nh, _, nk = self._chunk_heads(0)
+        return (2 * nh + 2 * nk) * self.Bn * self.L * self.D * e
+
     def copy_bytes(self):
         """Bytes each copy phase of one step reads plus writes (every element
         once): zigzag extract of Q, K, V; forward layout of Q, K, V; inverse

@@ -27,7 +27,7 @@ def declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     lib = B.lib()
     for name in names:
         assert hasattr(lib, name), name
@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = B.lib()
-    assert lib.usp_abi_version() == 3
+    assert lib.usp_abi_version() == 4
     assert lib.usp_status_string(0) == b"USP_OK"
     assert lib.usp_status_string(2) == b"USP_ERR_UNSUPPORTED"
     assert lib.usp_status_string(99) == b"USP_ERR_UNKNOWN"
@@ -79,6 +79,24 @@ def _uly(**kw):
 ])
 def test_ulysses_rejects(kw, status):
     assert _uly(**kw) == status
+
+
+def _uly_heads(**kw):
+    a = dict(i=FAKE, o=FAKE2, dtype=0, B=1, L=64, H=8, D=64, N=2, u=0, h0=0, nh=2, inv=0)
+    a.update(kw)
+    return B.lib().usp_ulysses_a2a_layout_heads(a["i"], a["o"], a["dtype"], a["B"], a["L"], a["H"], a["D"],
+                                                a["N"], a["u"], a["h0"], a["nh"], a["inv"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(h0=-1), 1), (dict(nh=0), 1), (dict(h0=3, nh=2), 1), (dict(nh=5), 1), (dict(h0=4, nh=1), 1),
+    (dict(i=None), 1), (dict(o=FAKE), 1), (dict(H=7), 1), (dict(L=63), 1), (dict(u=2), 1), (dict(D=4), 2),
+    (dict(inv=2), 1), (dict(inv=1, h0=2, nh=3), 1),
+])
+def test_ulysses_heads_rejects(kw, status):
+    assert _uly_heads(**kw) == status
+    assert b"ulysses_a2a_layout_heads" in B.lib().usp_last_error_detail()
 
 
 @no_gpu

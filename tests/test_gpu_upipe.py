@@ -1,0 +1,131 @@
+"""GPU parity of headwise chunking ([UPipe page] section 2): the Ulysses
+layout of a head range (bit-exact against the oracle, in every mode, and
+leaving the heads outside the chunk untouched), and the one-GPU share run
+chunk by chunk: bitwise equal to the unchunked share (the heads are
+independent and every kernel computes a head the same way), and within the
+bf16 bars of the oracle's chunked USP."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import index as ix
+from oracle import usp as ou
+from sequence_ring_attention_amd import binding as B
+from sequence_ring_attention_amd import inputs
+from sequence_ring_attention_amd.pipeline import OneGpuShare
+from tests.gpu_common import bits, check_close, device, f64, guarded, say
+
+pytestmark = pytest.mark.gpu
+
+LAYOUT_CASES = [  # B, Ls, hc, hd, dtype, N
+    (1, 96, 8, 128, "bf16", 2),
+    (2, 40, 12, 64, "bf16", 3),
+    (1, 64, 8, 64, "fp32", 4),
+    (1, 32, 4, 24, "bf16", 2),    # 48-byte head rows: the head-row inverse
+    (2, 17, 6, 128, "fp32", 1),
+]
+
+
+@pytest.mark.parametrize("case", LAYOUT_CASES)
+def test_layout_heads_bitexact(case):
+    Bn, Ls, hc, hd, dt, N = case
+    dev = device()
+    hb, L = hc // N, Ls * N
+    tdt = torch.float32 if dt == "fp32" else torch.bfloat16
+    x = inputs.randn((N, Bn, Ls, hc, hd), 61, dt)
+    xd = x.to(dev)
+    xs = [bits(x[i]) for i in range(N)]
+    for h0, nh in sorted({(0, hb), (0, 1), (hb - 1, 1), (hb // 2, hb - hb // 2), (1, max(1, hb - 2))}):
+        if h0 + nh > hb or nh < 1:
+            continue
+        ref = np.stack([ix.ulysses_fwd_heads(xs, u, h0, nh) for u in range(N)])     # (N, nh, B, L, hd)
+        say("layout heads fwd", case, h0, nh)
+        out, ok = guarded((N, nh, Bn, L, hd), tdt, dev)
+        B.usp_ulysses_a2a_layout_heads(xd, out, N, -1, h0, nh)
+        torch.cuda.synchronize()
+        assert ok() and np.array_equal(bits(out), ref)
+        for u in range(N):
+            one, ok = guarded((nh, Bn, L, hd), tdt, dev)
+            B.usp_ulysses_a2a_layout_heads(xd, one, N, u, h0, nh)
+            torch.cuda.synchronize()
+            assert ok() and np.array_equal(bits(one), ref[u])
+        # inverse of the chunk into a prefilled output: the chunk's heads
+        # come back, every other head keeps its old bits
+        hin = inputs.randn((N, nh, Bn, L, hd), 62, dt)
+        hs = [bits(hin[i]) for i in range(N)]
+        base = inputs.randn((N, Bn, Ls, hc, hd), 63, dt)
+        exp = bits(base).copy()
+        for u in range(N):
+            ix.ulysses_inv_heads(hs, u, h0, hc, exp[u])
+        say("layout heads inv", case, h0, nh)
+        back, ok = guarded((N, Bn, Ls, hc, hd), tdt, dev)
+        back.copy_(base.to(dev))
+        B.usp_ulysses_a2a_layout_heads(hin.to(dev), back, N, -1, h0, nh, inverse=True)
+        torch.cuda.synchronize()
+        assert ok() and np.array_equal(bits(back), exp)
+        for u in range(N):
+            one, ok = guarded((Bn, Ls, hc, hd), tdt, dev)
+            one.copy_(base[u].to(dev))
+            B.usp_ulysses_a2a_layout_heads(hin.to(dev), one, N, u, h0, nh, inverse=True)
+            torch.cuda.synchronize()
+            assert ok() and np.array_equal(bits(one), exp[u])
+
+
+SHARE_CASES = {  # B, S, H, Hkv, D, rd, ud, chunk, cu, per_sample
+    "gqa_chunk2": (1, 2048, 8, 4, 128, 2, 2, 2, None, False),
+    "gqa_chunk4_of8_rd4": (1, 4096, 16, 4, 128, 4, 2, 4, None, False),
+    "gqa_chunk2_inside_a_group_of4": (1, 2048, 16, 4, 128, 2, 2, 2, None, False),
+    "mha_d64_chunk1_b2": (2, 1024, 4, 4, 64, 2, 2, 1, None, False),
+    "packed_per_sample_chunk2": (1, 2048, 8, 4, 128, 2, 2, 2, [0, 400, 416, 1680, 2048], True),
+}
+
+
+def _run_share(q, k, v, rd, ud, r, u, chunk, cu, ps):
+    share = OneGpuShare(q, k, v, rd, ud, r, u, cu_seqlens=cu, per_sample=ps, head_chunk=chunk)
+    share.prepare_peers()
+    out = share.step().clone()
+    torch.cuda.synchronize()
+    return out, share.lse[u].clone()
+
+
+@pytest.mark.parametrize("name", sorted(SHARE_CASES))
+def test_chunked_share_equals_unchunked_and_oracle(name):
+    Bn, S, H, Hkv, D, rd, ud, nh, cu, ps = SHARE_CASES[name]
+    dev = device()
+    q, k, v = inputs.qkv(Bn, S, H, Hkv, D, "bf16", 880 + sorted(SHARE_CASES).index(name))
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o_ref, lse_ref = ou.usp_attention_head_chunks(f64(q), f64(k), f64(v), rd, ud, D ** -0.5, nh, True, cu, ps)
+    T, hb = S // (rd * ud), H // ud
+    for r, u in [(0, 0), (rd - 1, ud - 1)]:
+        say("share", name, r, u, "whole head block")
+        o_full, l_full = _run_share(qd, kd, vd, rd, ud, r, u, None, cu, ps)
+        say("share", name, r, u, "chunks of", nh)
+        o_ch, l_ch = _run_share(qd, kd, vd, rd, ud, r, u, nh, cu, ps)
+        assert torch.equal(o_ch, o_full) and torch.equal(l_ch, l_full)
+        pos = (ix.zigzag_per_sample_local_positions(cu, rd, ud, r, u) if ps
+               else ix.zigzag_local_positions(S, rd, ud, r, u))
+        check_close(f64(o_ch), f64(l_ch[:, :, u * T:(u + 1) * T]), o_ref[:, pos],
+                    lse_ref[u * hb:(u + 1) * hb][:, :, pos], "bf16", f"{name} ({r},{u})", out_bf16=True)
+
+
+def test_chunked_share_rejects_bad_chunks():
+    dev = device()
+    q, k, v = inputs.qkv(1, 256, 24, 4, 64, "bf16", 890)
+    for bad in (5, 4, 0):          # does not divide 12; neither whole GQA groups of 6 nor inside one; empty
+        with pytest.raises(ValueError):
+            OneGpuShare(q.to(dev), k.to(dev), v.to(dev), 2, 2, 0, 0, head_chunk=bad)
+
+
+def test_usp_hybrid_s128k_share_in_head_chunks_is_bitwise_the_same():
+    """The benchmark's share, its 16-head block pushed through in 8 chunks of
+    2 query heads, each inside one GQA group of 4 (one eighth of the
+    head-major query and output tensors at a time)."""
+    w = inputs.WORKLOADS["usp_hybrid_s128k_ud2_rd4"]
+    dev = device()
+    q, k, v = (t.to(dev) for t in inputs.workload_qkv(w))
+    say(w.name, "share (0,0) whole head block")
+    o_full, l_full = _run_share(q, k, v, w.rd, w.ud, 0, 0, None, None, False)
+    say(w.name, "share (0,0) chunks of 2 heads")
+    o_ch, l_ch = _run_share(q, k, v, w.rd, w.ud, 0, 0, 2, None, False)
+    assert torch.isfinite(o_ch).all()
+    assert torch.equal(o_ch, o_full) and torch.equal(l_ch, l_full)

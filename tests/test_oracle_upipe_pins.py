@@ -7,8 +7,10 @@ u1  the forward layout of a head chunk is that chunk of the full layout
 u2  the inverse of every chunk, over all chunks, is the full inverse, and
     forward then inverse restores the chunk's heads;
 u3  the chunked USP equals the unchunked USP and the one-shot definition, for
-    MHA, GQA, packed samples (both splits) and non-causal attention;
-u4  chunks that split a head block unevenly or split a GQA group are refused;
+    MHA, GQA (chunks of whole groups and chunks inside a group), packed
+    samples (both splits) and non-causal attention;
+u4  chunks that split a head block unevenly, or that neither hold whole GQA
+    groups nor lie inside one, are refused;
 u5  planted mistakes (a KV chunk that never advances; a head offset that
     forgets the Ulysses rank) fail u3.
 """
@@ -60,6 +62,8 @@ def test_u2_inverse_chunks_make_the_full_inverse_and_undo_the_forward(N, hc, nh)
 CASES = {  # B, S, H, Hkv, D, rd, ud, chunk, causal, cu, per_sample
     "mha_chunk1": (1, 64, 4, 4, 8, 2, 2, 1, True, None, False),
     "gqa_chunk2": (1, 96, 8, 4, 8, 3, 2, 2, True, None, False),
+    "gqa_chunk2_inside_a_group_of4": (1, 64, 8, 2, 8, 2, 2, 2, True, None, False),
+    "gqa_chunk1_of_group2": (1, 64, 8, 4, 8, 2, 2, 1, True, None, False),
     "gqa_b2_chunk2_of4": (2, 64, 8, 2, 8, 2, 1, 4, True, None, False),
     "packed_stream": (1, 128, 8, 4, 8, 2, 2, 2, True, [0, 24, 40, 96, 128], False),
     "packed_per_sample": (1, 128, 8, 4, 8, 2, 2, 2, True, [0, 32, 40, 96, 128], True),
@@ -90,8 +94,9 @@ def test_u4_rejects_uneven_chunks_and_split_groups():
     Q, K, V = qkv(1, 32, 8, 4, 8)
     with pytest.raises(ValueError):
         ou.usp_attention_head_chunks(Q, K, V, 2, 2, 0.3, 3)      # 3 does not divide the block of 4
+    Q, K, V = qkv(1, 32, 24, 4, 8)
     with pytest.raises(ValueError):
-        ou.usp_attention_head_chunks(Q, K, V, 2, 2, 0.3, 1)      # splits a GQA group of 2
+        ou.usp_attention_head_chunks(Q, K, V, 2, 2, 0.3, 4)      # 4 heads: neither whole groups of 6 nor in one
     with pytest.raises(ValueError):
         ix.ulysses_fwd_heads(shards(2, 1, 2, 8, 4), 0, 3, 2)     # runs past the head block
 
