@@ -111,6 +111,23 @@ __device__ inline void tile_load_offsets(uint32_t *voff, int64_t rowbytes, int w
   }
 }
 
+// Schedule of a product over D whose M operand rows come from LDS (two
+// reads per pair of products): half the reads first, then two reads per
+// two products.  The operands are read into registers ahead of the products
+// in the source as well; without both, the compiler issues each read right
+// before the product that consumes it and waits for it there.
+template <int D>
+__device__ inline void schedule_row_products() {
+  __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
+}
+
+
 // ================================================================ dQ pass ==
 
 // PS: built for the per-sample split (the other build serves the split of the
@@ -561,13 +578,18 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
       // accumulator chains, then P and dV^T += dO^T P
       f32x16 S2[2] = {f32x16{}, f32x16{}};
       __builtin_amdgcn_s_setprio(1);
+      bf16x8 qa[D / 16], qb[D / 16];
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(sQ + off.row[ks]);
-        const bf16x8 qb = *reinterpret_cast<const bf16x8 *>(sQ + off.row[ks] + 32 * Lds<D>::ROW);
-        S2[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], S2[0], 0, 0, 0);
-        S2[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb, kf[ks], S2[1], 0, 0, 0);
+        qa[ks] = *reinterpret_cast<const bf16x8 *>(sQ + off.row[ks]);
+        qb[ks] = *reinterpret_cast<const bf16x8 *>(sQ + off.row[ks] + 32 * Lds<D>::ROW);
       }
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        S2[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], S2[0], 0, 0, 0);
+        S2[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[ks], kf[ks], S2[1], 0, 0, 0);
+      }
+      schedule_row_products<D>();
       __builtin_amdgcn_s_setprio(0);
       bf16x8 pf[4];
 #pragma unroll
@@ -590,11 +612,19 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
         }
       }
       __builtin_amdgcn_s_setprio(1);
+      // operands of the next accumulator are read while this one's products run
+      bf16x8 vt[2][4];
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) vt[0][sl] = read_tr<D>(sD, off, 0, sl);
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) {
+        if (mb + 1 < D / 32) {
+#pragma unroll
+          for (int sl = 0; sl < 4; ++sl) vt[(mb + 1) & 1][sl] = read_tr<D>(sD, off, mb + 1, sl);
+        }
 #pragma unroll
         for (int sl = 0; sl < 4; ++sl)
-          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(sD, off, mb, sl), pf[sl], acc[mb], 0, 0, 0);
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[mb & 1][sl], pf[sl], acc[mb], 0, 0, 0);
       }
       __builtin_amdgcn_s_setprio(0);
     } else {
@@ -603,13 +633,18 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
         // S = Q K^T and dP = dO V^T for 32 queries x the wave's 32 keys
         f32x16 S = f32x16{}, P = f32x16{};
         __builtin_amdgcn_s_setprio(1);
+        bf16x8 qa[D / 16], da[D / 16];
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-          const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(sQ + off.row[ks] + blk * 32 * Lds<D>::ROW);
-          const bf16x8 da = *reinterpret_cast<const bf16x8 *>(sD + off.row[ks] + blk * 32 * Lds<D>::ROW);
-          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], S, 0, 0, 0);
-          P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ks], P, 0, 0, 0);
+          qa[ks] = *reinterpret_cast<const bf16x8 *>(sQ + off.row[ks] + blk * 32 * Lds<D>::ROW);
+          da[ks] = *reinterpret_cast<const bf16x8 *>(sD + off.row[ks] + blk * 32 * Lds<D>::ROW);
         }
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], S, 0, 0, 0);
+          P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ks], vf[ks], P, 0, 0, 0);
+        }
+        schedule_row_products<D>();
         __builtin_amdgcn_s_setprio(0);
         const float4 *d4 = reinterpret_cast<const float4 *>(sst + 32 * blk + 8 * hh);
         const float4 *l4 = reinterpret_cast<const float4 *>(sst + 64 + 32 * blk + 8 * hh);
@@ -633,12 +668,18 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
         }
         // dK^T += Q^T dS over this block's two 16-query slabs
         __builtin_amdgcn_s_setprio(1);
+        bf16x8 qt[2][2];
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) qt[0][sl] = read_tr<D>(sQ, off, 0, 2 * blk + sl);
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb) {
+          if (mb + 1 < D / 32) {
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl) qt[(mb + 1) & 1][sl] = read_tr<D>(sQ, off, mb + 1, 2 * blk + sl);
+          }
 #pragma unroll
           for (int sl = 0; sl < 2; ++sl)
-            acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(sQ, off, mb, 2 * blk + sl), dsf[sl], acc[mb],
-                                                              0, 0, 0);
+            acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[mb & 1][sl], dsf[sl], acc[mb], 0, 0, 0);
         }
         __builtin_amdgcn_s_setprio(0);
       }
