@@ -111,20 +111,19 @@ __device__ inline void tile_load_offsets(uint32_t *voff, int64_t rowbytes, int w
   }
 }
 
-// Schedule of a product over D whose M operand rows come from LDS (two
-// reads per pair of products): half the reads first, then two reads per
-// two products.  The operands are read into registers ahead of the products
-// in the source as well; without both, the compiler issues each read right
-// before the product that consumes it and waits for it there.
-template <int D>
-__device__ inline void schedule_row_products() {
-  __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
+// Schedule of N products that each take one operand row from LDS: AHEAD
+// reads first, then two reads per two products.  Without it the compiler
+// issues each read right before the product that consumes it and waits for
+// it there; the operands are read ahead in the source as well.
+template <int N, int AHEAD>
+__device__ inline void schedule_products() {
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
+  for (int i = 0; i < (N - AHEAD) / 2; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
 }
 
 
@@ -265,37 +264,49 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
       vhi = hi - k0 - 8 * hh;
     }
 
-    // S^T = K Q^T and dP^T = V dO^T for both 32-key halves
-    f32x16 S0 = f32x16{}, S1 = f32x16{}, P0 = f32x16{}, P1 = f32x16{};
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(sK + off.row[ks]);
-      const bf16x8 kb = *reinterpret_cast<const bf16x8 *>(sK + off.row[ks] + 32 * Lds<D>::ROW);
-      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], S0, 0, 0, 0);
-      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[ks], S1, 0, 0, 0);
-      const bf16x8 va = *reinterpret_cast<const bf16x8 *>(sV + off.row[ks]);
-      const bf16x8 vb = *reinterpret_cast<const bf16x8 *>(sV + off.row[ks] + 32 * Lds<D>::ROW);
-      P0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dof[ks], P0, 0, 0, 0);
-      P1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, dof[ks], P1, 0, 0, 0);
-    }
-    __builtin_amdgcn_s_setprio(0);
-    if (!full) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kc = 16 * (r / 8) + (r % 8);
-        S0[r] = ((kc >= vlo) & (kc < vhi)) ? S0[r] : -INFINITY;
-        S1[r] = ((kc + 32 >= vlo) & (kc + 32 < vhi)) ? S1[r] : -INFINITY;
-      }
-    }
-    // dS^T = P^T (dP^T - delta), rounded to bf16 as the N operand
+    // per 32-key half: S^T = K Q^T and dP^T = V dO^T, then that half's
+    // dS^T = P^T (dP^T - delta), rounded to bf16 as the N operand of the dQ
+    // product.  One half's accumulators at a time leave the registers to
+    // read a half's K and V rows ahead of its products.
     bf16x8 dsf[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[r], sl2, -lse2));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[r], sl2, -lse2));
-      dsf[r / 8][r % 8] = (__bf16)(p0 * (P0[r] - delta));
-      dsf[2 + r / 8][r % 8] = (__bf16)(p1 * (P1[r] - delta));
+    for (int half = 0; half < 2; ++half) {
+      f32x16 S = f32x16{}, P = f32x16{};
+      // K and V rows of two k-steps in registers; the next two are read while
+      // this pair's four products run
+      bf16x8 kr[2][2], vr[2][2];
+      auto read_pair = [&](int slot, int ks0) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          kr[slot][j] = *reinterpret_cast<const bf16x8 *>(sK + off.row[ks0 + j] + half * 32 * Lds<D>::ROW);
+          vr[slot][j] = *reinterpret_cast<const bf16x8 *>(sV + off.row[ks0 + j] + half * 32 * Lds<D>::ROW);
+        }
+      };
+      __builtin_amdgcn_s_setprio(1);
+      read_pair(0, 0);
+#pragma unroll
+      for (int g = 0; g < D / 32; ++g) {
+        if (g + 1 < D / 32) read_pair((g + 1) & 1, 2 * (g + 1));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[g & 1][j], qf[2 * g + j], S, 0, 0, 0);
+          P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[g & 1][j], dof[2 * g + j], P, 0, 0, 0);
+        }
+      }
+      schedule_products<D / 8, 4>();
+      __builtin_amdgcn_s_setprio(0);
+      if (!full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kc = 32 * half + 16 * (r / 8) + (r % 8);
+          S[r] = ((kc >= vlo) & (kc < vhi)) ? S[r] : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], sl2, -lse2));
+        dsf[2 * half + r / 8][r % 8] = (__bf16)(p * (P[r] - delta));
+      }
     }
     // dQ^T += K^T dS^T, 16 keys per product; K^T read transposed
     __builtin_amdgcn_s_setprio(1);
@@ -589,7 +600,7 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
         S2[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], S2[0], 0, 0, 0);
         S2[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[ks], kf[ks], S2[1], 0, 0, 0);
       }
-      schedule_row_products<D>();
+      schedule_products<D / 8, D / 16>();
       __builtin_amdgcn_s_setprio(0);
       bf16x8 pf[4];
 #pragma unroll
@@ -644,7 +655,7 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
           S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], S, 0, 0, 0);
           P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ks], vf[ks], P, 0, 0, 0);
         }
-        schedule_row_products<D>();
+        schedule_products<D / 8, D / 16>();
         __builtin_amdgcn_s_setprio(0);
         const float4 *d4 = reinterpret_cast<const float4 *>(sst + 32 * blk + 8 * hh);
         const float4 *l4 = reinterpret_cast<const float4 *>(sst + 64 + 32 * blk + 8 * hh);
