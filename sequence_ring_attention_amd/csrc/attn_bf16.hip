@@ -316,18 +316,27 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
 
     // O^T += V^T P^T, 16 keys per MFMA; V^T read transposed from row-major V
     __builtin_amdgcn_s_setprio(1);
+    // the next accumulator's V operands are read while this one's products run
+    auto read_v = [&](int mb, int p) {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4 *)(const_cast<char *>(sV) + voff[mb][0] + p * 16 * Lds<D>::ROW));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4 *)(const_cast<char *>(sV) + voff[mb][1] + p * 16 * Lds<D>::ROW));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 vt[2][4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) vt[0][p] = read_v(0, p);
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
+      if (mb + 1 < D / 32) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4 *)(const_cast<char *>(sV) + voff[mb][0] + p * 16 * Lds<D>::ROW));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4 *)(const_cast<char *>(sV) + voff[mb][1] + p * 16 * Lds<D>::ROW));
-        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[p], O[mb], 0, 0, 0);
+        for (int p = 0; p < 4; ++p) vt[(mb + 1) & 1][p] = read_v(mb + 1, p);
       }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[mb & 1][p], pf[p], O[mb], 0, 0, 0);
     }
+    schedule_tr_products<4 * (D / 32), 4>();
     __builtin_amdgcn_s_setprio(0);
     wait_tiles();
     __syncthreads();

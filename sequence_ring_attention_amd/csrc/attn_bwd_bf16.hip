@@ -637,6 +637,7 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
         for (int sl = 0; sl < 4; ++sl)
           acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[mb & 1][sl], pf[sl], acc[mb], 0, 0, 0);
       }
+      schedule_tr_products<4 * (D / 32), 4>();
       __builtin_amdgcn_s_setprio(0);
     } else {
 #pragma unroll
@@ -692,6 +693,7 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
           for (int sl = 0; sl < 2; ++sl)
             acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[mb & 1][sl], dsf[sl], acc[mb], 0, 0, 0);
         }
+        schedule_tr_products<2 * (D / 32), 4>();
         __builtin_amdgcn_s_setprio(0);
       }
     }

@@ -96,6 +96,21 @@ __device__ inline void issue_tile_lds(char *tile, const char *blk, uint32_t exte
 }
 
 // The key range of block j one query tile can see, in 64-key tiles.
+// Schedule of N products whose M operand is read transposed from LDS (two
+// reads per product): the reads of AHEAD products first, then two reads per
+// product, so reads run that many products ahead of their use.  Without it
+// the compiler reads each operand right before its product and waits there.
+template <int N, int AHEAD>
+__device__ inline void schedule_tr_products() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
 // One ring step of a tile walk: block j, its tiles [kt, ke) that hold some
 // visible pair, the tiles with every pair visible (first row >= flo and one
 // past the last row <= fhi), and the lane's own visible rows [llo, lhi).  All
