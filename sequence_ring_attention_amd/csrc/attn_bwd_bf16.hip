@@ -46,7 +46,7 @@ using namespace tiles;
 constexpr int NW = 4;          // wavefronts per workgroup
 constexpr int BM = 32 * NW;    // query rows per dQ workgroup
 constexpr int KW = 8;          // wavefronts per dK/dV workgroup (32 keys each)
-constexpr int NS = 4;          // dK/dV pipeline stages (query tiles in flight + 1): 2 or 4
+constexpr int NS = 3;          // dK/dV pipeline stages (query tiles in flight + 1): 2, 3 or 4
 constexpr int STATS = 512;     // bytes of one tile's delta[64] and lse2[64]
 
 __device__ inline int mod_cp(int x, int cp) {
@@ -392,7 +392,7 @@ struct QRange {
 // the previous tile for the next issue.  PS as in the dQ pass.
 template <int D, bool DV, int KW, int NS, bool PS>
 __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
-  static_assert(NS == 2 || NS == 4, "two or four pipeline stages");
+  static_assert(NS >= 2 && NS <= 4, "two to four pipeline stages");
   constexpr int BK = 32 * KW;  // keys per workgroup
   constexpr int TILE = Lds<D>::TILE;
   constexpr int STAGE = 2 * TILE;                        // Q tile, then dO tile
@@ -401,11 +401,11 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
   // one array per stage (tiles, then the tile's delta[64] and lse2[64]):
   // the reads of one stage are then provably disjoint from the direct loads
   // filling the others, and the compiler does not make them wait for those
-  constexpr int XS = NS == 4 ? STAGE + STATS : 16;  // stages 2 and 3 exist with four stages only
+  constexpr int X2 = NS >= 3 ? STAGE + STATS : 16, X3 = NS == 4 ? STAGE + STATS : 16;  // stages in use
   __shared__ __attribute__((aligned(1024))) char ring0[STAGE + STATS];
   __shared__ __attribute__((aligned(1024))) char ring1[STAGE + STATS];
-  __shared__ __attribute__((aligned(1024))) char ring2[XS];
-  __shared__ __attribute__((aligned(1024))) char ring3[XS];
+  __shared__ __attribute__((aligned(1024))) char ring2[X2];
+  __shared__ __attribute__((aligned(1024))) char ring3[X3];
   // every stage index below is a compile-time constant after unrolling
   auto stage_base = [&](int stg) -> char * { return stg == 0 ? ring0 : stg == 1 ? ring1 : stg == 2 ? ring2 : ring3; };
 
@@ -708,9 +708,11 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
     if (pending == 0) break;
     body(StageTag<1>{});
     if (pending == 0) break;
-    if constexpr (NS == 4) {
+    if constexpr (NS >= 3) {
       body(StageTag<2>{});
       if (pending == 0) break;
+    }
+    if constexpr (NS == 4) {
       body(StageTag<3>{});
       if (pending == 0) break;
     }
