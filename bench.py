@@ -369,9 +369,10 @@ def cpu_baseline(w, r, u, n_rows):
 def split_balance(w, q, k, v, zig_shares):
     """The packed workload's samples with lengths rounded down to multiples
     of 2 cp, walked by every rank under both splits of the shares: Algorithm
-    2 on the whole packed stream, and on every sample (usp_zigzag_extract_varlen).
-    A real ring waits for its slowest rank each step, so the figure of merit
-    is the slowest rank's walk against the mean."""
+    2 on the whole packed stream, and on every sample (usp_zigzag_extract_varlen);
+    each rank's forward walk and its backward.  A real ring waits for its
+    slowest rank each step, so the figure of merit is the slowest rank's time
+    against the mean."""
     import numpy as np
     import torch
     from sequence_ring_attention_amd import binding as B
@@ -406,11 +407,22 @@ def split_balance(w, q, k, v, zig_shares):
             lse = torch.empty(w.H, w.B, w.share, dtype=torch.float32, device=dev)
             d = B.attn_desc(w.S, w.rd, qr, ks, vs, o=o, cu_seqlens=cu, zigzag_per_sample=split == "per_sample")
             ms = _time(lambda: B.usp_attn_fwd(qr, ks, vs, o, lse, d, r))
-            ranks.append({"TFLOP": fl / 1e12, "ms": ms, "TFLOP/s": fl / (ms * 1e-3) / 1e12})
+            # the rank's backward from this forward (2.5 times its work: S, dP, dV, dK, dQ)
+            d_o = inputs.randn(tuple(qr.shape), 99, "bf16").to(dev)
+            dq = torch.empty_like(qr)
+            dk = torch.zeros(ks.shape, dtype=torch.float32, device=dev)
+            dv = torch.zeros(vs.shape, dtype=torch.float32, device=dev)
+            stats = torch.empty(2 * lse.numel(), dtype=torch.float32, device=dev)
+            bms = _time(lambda: B.usp_attn_bwd(qr, ks, vs, o, d_o, lse, dq, dk, dv, stats, d, r))
+            ranks.append({"TFLOP": fl / 1e12, "ms": ms, "TFLOP/s": fl / (ms * 1e-3) / 1e12,
+                          "bwd_ms": bms, "bwd_TFLOP/s": 2.5 * fl / (bms * 1e-3) / 1e12})
         times = [x["ms"] for x in ranks]
+        btimes = [x["bwd_ms"] for x in ranks]
         out[split] = {"ranks": ranks, "slowest_ms": max(times), "mean_ms": sum(times) / len(times),
-                      "slowest_over_mean": max(times) / (sum(times) / len(times))}
+                      "slowest_over_mean": max(times) / (sum(times) / len(times)),
+                      "bwd_slowest_ms": max(btimes), "bwd_slowest_over_mean": max(btimes) / (sum(btimes) / len(btimes))}
     out["slowest_rank_speedup"] = out["stream"]["slowest_ms"] / out["per_sample"]["slowest_ms"]
+    out["bwd_slowest_rank_speedup"] = out["stream"]["bwd_slowest_ms"] / out["per_sample"]["bwd_slowest_ms"]
     return out
 
 

@@ -71,17 +71,24 @@ def test_layout_heads_bitexact(case):
             assert ok() and np.array_equal(bits(one), exp[u])
 
 
-SHARE_CASES = {  # B, S, H, Hkv, D, rd, ud, chunk, cu, per_sample
+SHARE_CASES = {  # B, S, H, Hkv, D, rd, ud, chunk, cu, per_sample[, dtype, causal]
     "gqa_chunk2": (1, 2048, 8, 4, 128, 2, 2, 2, None, False),
     "gqa_chunk4_of8_rd4": (1, 4096, 16, 4, 128, 4, 2, 4, None, False),
     "gqa_chunk2_inside_a_group_of4": (1, 2048, 16, 4, 128, 2, 2, 2, None, False),
     "mha_d64_chunk1_b2": (2, 1024, 4, 4, 64, 2, 2, 1, None, False),
     "packed_per_sample_chunk2": (1, 2048, 8, 4, 128, 2, 2, 2, [0, 400, 416, 1680, 2048], True),
+    "fp32_gqa_chunk1_d64": (1, 256, 8, 4, 64, 2, 2, 1, None, False, "fp32", True),
+    "noncausal_chunk2": (1, 1024, 8, 2, 128, 2, 2, 2, None, False, "bf16", False),
 }
 
 
-def _run_share(q, k, v, rd, ud, r, u, chunk, cu, ps):
-    share = OneGpuShare(q, k, v, rd, ud, r, u, cu_seqlens=cu, per_sample=ps, head_chunk=chunk)
+def _case(name):
+    c = SHARE_CASES[name]
+    return c + ("bf16", True) if len(c) == 10 else c
+
+
+def _run_share(q, k, v, rd, ud, r, u, chunk, cu, ps, causal=True):
+    share = OneGpuShare(q, k, v, rd, ud, r, u, causal=causal, cu_seqlens=cu, per_sample=ps, head_chunk=chunk)
     share.prepare_peers()
     out = share.step().clone()
     torch.cuda.synchronize()
@@ -90,22 +97,22 @@ def _run_share(q, k, v, rd, ud, r, u, chunk, cu, ps):
 
 @pytest.mark.parametrize("name", sorted(SHARE_CASES))
 def test_chunked_share_equals_unchunked_and_oracle(name):
-    Bn, S, H, Hkv, D, rd, ud, nh, cu, ps = SHARE_CASES[name]
+    Bn, S, H, Hkv, D, rd, ud, nh, cu, ps, dt, causal = _case(name)
     dev = device()
-    q, k, v = inputs.qkv(Bn, S, H, Hkv, D, "bf16", 880 + sorted(SHARE_CASES).index(name))
+    q, k, v = inputs.qkv(Bn, S, H, Hkv, D, dt, 880 + sorted(SHARE_CASES).index(name))
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    o_ref, lse_ref = ou.usp_attention_head_chunks(f64(q), f64(k), f64(v), rd, ud, D ** -0.5, nh, True, cu, ps)
+    o_ref, lse_ref = ou.usp_attention_head_chunks(f64(q), f64(k), f64(v), rd, ud, D ** -0.5, nh, causal, cu, ps)
     T, hb = S // (rd * ud), H // ud
     for r, u in [(0, 0), (rd - 1, ud - 1)]:
         say("share", name, r, u, "whole head block")
-        o_full, l_full = _run_share(qd, kd, vd, rd, ud, r, u, None, cu, ps)
+        o_full, l_full = _run_share(qd, kd, vd, rd, ud, r, u, None, cu, ps, causal)
         say("share", name, r, u, "chunks of", nh)
-        o_ch, l_ch = _run_share(qd, kd, vd, rd, ud, r, u, nh, cu, ps)
+        o_ch, l_ch = _run_share(qd, kd, vd, rd, ud, r, u, nh, cu, ps, causal)
         assert torch.equal(o_ch, o_full) and torch.equal(l_ch, l_full)
         pos = (ix.zigzag_per_sample_local_positions(cu, rd, ud, r, u) if ps
                else ix.zigzag_local_positions(S, rd, ud, r, u))
         check_close(f64(o_ch), f64(l_ch[:, :, u * T:(u + 1) * T]), o_ref[:, pos],
-                    lse_ref[u * hb:(u + 1) * hb][:, :, pos], "bf16", f"{name} ({r},{u})", out_bf16=True)
+                    lse_ref[u * hb:(u + 1) * hb][:, :, pos], dt, f"{name} ({r},{u})", out_bf16=dt == "bf16")
 
 
 def test_chunked_share_rejects_bad_chunks():
