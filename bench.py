@@ -156,9 +156,10 @@ def copy_launches(share, w):
     """Each copy entry point and the merge as one launch at the bench
     workload's sizes, timed with the last-level cache flushed: the zigzag
     extract of the whole Q for every (ring, Ulysses) rank and its inverse,
-    one rank's extract, the Ulysses layout of the ring group's Q shards for
-    both Ulysses ranks and its inverse, and the LSE merge of one step's
-    partials of the share."""
+    one rank's extract, the step's batched extract and layout of the share's
+    Q, K and V, the Ulysses layout of the ring group's Q shards for both
+    Ulysses ranks and its inverse, and the LSE merge of one step's partials
+    of the share."""
     import torch
     from sequence_ring_attention_amd import binding as B
     Q, rd, ud = share.Q, w.rd, w.ud
@@ -175,6 +176,16 @@ def copy_launches(share, w):
     res["zigzag_extract_one_rank_q"] = _time_flushed(lambda: B.usp_zigzag_extract(Q, one, rd, ud, 0, 0),
                                                      2 * one.numel() * e)
     del one
+    # the step's two batched launches: Q, K and V of the share together
+    r, u = share.r, share.u
+    qkv_out = (share.qz[u], share.kz[u], share.vz[u])
+    res["zigzag_extract_one_rank_qkv"] = _time_flushed(
+        lambda: B.usp_zigzag_extract_n((Q, share.K, share.V), qkv_out, rd, ud, r, u),
+        2 * sum(t.numel() for t in qkv_out) * e)
+    qkv_hm = (share.qh[u], share.kh[u, r], share.vh[u, r])
+    res["ulysses_layout_fwd_one_rank_qkv"] = _time_flushed(
+        lambda: B.usp_ulysses_a2a_layout_n((share.qz, share.kz, share.vz), qkv_hm, ud, u),
+        2 * sum(t.numel() for t in qkv_hm) * e)
     res["ulysses_layout_fwd_all_q"] = _time_flushed(lambda: B.usp_ulysses_a2a_layout(share.qz, share.qh, ud, -1),
                                                     2 * share.qz.numel() * e)
     outs = torch.empty((ud,) + tuple(share.out.shape), dtype=Q.dtype, device=Q.device)

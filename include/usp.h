@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define USP_ABI_VERSION 4
+#define USP_ABI_VERSION 5
 
 /* Most packed samples one call takes (their boundaries travel by value). */
 #define USP_MAX_SEQS 256
@@ -131,6 +131,25 @@ usp_status usp_zigzag_extract(const void *x, void *out, usp_dtype dtype, int64_t
                               int32_t ud, int32_t ring_rank, int32_t ulysses_rank,
                               int32_t inverse, void *stream);
 
+/* Most tensors one batched copy call (the _n entry points) moves. */
+#define USP_MAX_COPY_BATCH 4
+
+/*
+ * Zigzag split of several tensors in one launch -- the same Algorithm 2 map
+ * as usp_zigzag_extract, applied to n tensors (Q, K and V of one step) that
+ * share dtype, B, S, D and the ranks but may differ in head count: tensor i
+ * is x[i] -> out[i] with heads[i] heads, exactly as usp_zigzag_extract would
+ * copy it.  x, out and heads are host arrays of n entries, read during the
+ * call; the caller owns every buffer.
+ * Errors: as usp_zigzag_extract for every tensor, plus USP_ERR_INVALID_ARG
+ *   for n outside [1, USP_MAX_COPY_BATCH], a null array, or an output whose
+ *   byte extent overlaps any input's or another output's.
+ */
+usp_status usp_zigzag_extract_n(int32_t n, const void *const *x, void *const *out, const int64_t *heads,
+                                usp_dtype dtype, int64_t batch, int64_t seq_len, int64_t head_dim,
+                                int32_t rd, int32_t ud, int32_t ring_rank, int32_t ulysses_rank,
+                                int32_t inverse, void *stream);
+
 /*
  * Per-sample zigzag split of packed samples -- [USP review] section 三,
  * Algorithm 2 applied to every sample on its own: sample n (boundaries
@@ -173,6 +192,23 @@ usp_status usp_ulysses_a2a_layout(const void *in, void *out, usp_dtype dtype, in
                                   int64_t seq_len, int64_t heads, int64_t head_dim,
                                   int32_t ulysses_degree, int32_t ulysses_rank, int32_t inverse,
                                   void *stream);
+
+/*
+ * The Ulysses layout of several tensors in one launch -- the same
+ * AllToAll4D permutation as usp_ulysses_a2a_layout ([USP review] section
+ * 三), applied to n tensors (Q, K and V) that share dtype, bs, L, hd, the
+ * degree, the rank and the direction but may differ in head count: tensor i
+ * is in[i] -> out[i] with heads[i] heads (hc), exactly as
+ * usp_ulysses_a2a_layout would copy it.  in, out and heads are host arrays
+ * of n entries, read during the call.
+ * Errors: as usp_ulysses_a2a_layout for every tensor, plus
+ *   USP_ERR_INVALID_ARG for n outside [1, USP_MAX_COPY_BATCH], a null array,
+ *   or an output whose byte extent overlaps any input's or another output's.
+ */
+usp_status usp_ulysses_a2a_layout_n(int32_t n, const void *const *in, void *const *out, const int64_t *heads,
+                                    usp_dtype dtype, int64_t batch, int64_t seq_len, int64_t head_dim,
+                                    int32_t ulysses_degree, int32_t ulysses_rank, int32_t inverse,
+                                    void *stream);
 
 /*
  * The Ulysses layout of one chunk of heads -- headwise chunking ([UPipe

@@ -18,8 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libusp.so")
 USP_OK, USP_ERR_INVALID_ARG, USP_ERR_UNSUPPORTED, USP_ERR_HIP = 0, 1, 2, 3
 USP_DTYPE_BF16, USP_DTYPE_FP32 = 0, 1
 
-EXPORTED = ["usp_zigzag_extract", "usp_zigzag_extract_varlen", "usp_ulysses_a2a_layout",
-            "usp_ulysses_a2a_layout_heads", "usp_ring_attn_step_fwd",
+EXPORTED = ["usp_zigzag_extract", "usp_zigzag_extract_n", "usp_zigzag_extract_varlen", "usp_ulysses_a2a_layout",
+            "usp_ulysses_a2a_layout_n", "usp_ulysses_a2a_layout_heads", "usp_ring_attn_step_fwd",
             "usp_lse_merge", "usp_attn_fwd", "usp_attn_bwd_prep", "usp_ring_attn_step_bwd", "usp_attn_bwd",
             "usp_status_string", "usp_last_error_detail", "usp_abi_version"]
 
@@ -64,6 +64,8 @@ def lib():
                                                 vp]
         L.usp_ulysses_a2a_layout.argtypes = [vp, vp, st, i64, i64, i64, i64, i32, i32, i32, vp]
         L.usp_ulysses_a2a_layout_heads.argtypes = [vp, vp, st, i64, i64, i64, i64, i32, i32, i64, i64, i32, vp]
+        L.usp_zigzag_extract_n.argtypes = [i32, vp, vp, vp, st, i64, i64, i64, i32, i32, i32, i32, i32, vp]
+        L.usp_ulysses_a2a_layout_n.argtypes = [i32, vp, vp, vp, st, i64, i64, i64, i32, i32, i32, vp]
         L.usp_ring_attn_step_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, i32, vp]
         L.usp_lse_merge.argtypes = [vp, vp, vp, vp, i64, i64, vp]
         L.usp_attn_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, vp]
@@ -71,7 +73,8 @@ def lib():
         L.usp_ring_attn_step_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc),
                                              i32, i32, vp]
         L.usp_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, vp]
-        for f in ("usp_zigzag_extract", "usp_zigzag_extract_varlen", "usp_ulysses_a2a_layout",
+        for f in ("usp_zigzag_extract", "usp_zigzag_extract_n", "usp_zigzag_extract_varlen", "usp_ulysses_a2a_layout",
+                  "usp_ulysses_a2a_layout_n",
                   "usp_ulysses_a2a_layout_heads", "usp_ring_attn_step_fwd",
                   "usp_lse_merge", "usp_attn_fwd", "usp_attn_bwd_prep", "usp_ring_attn_step_bwd",
                   "usp_attn_bwd"):
@@ -134,6 +137,38 @@ def usp_zigzag_extract(x, out, rd, ud, ring_rank, ulysses_rank, inverse=False, s
     return out
 
 
+def _ptr_arrays(srcs, dsts, heads):
+    n = len(srcs)
+    if n != len(dsts) or n != len(heads):
+        raise ValueError("one output and one head count per input")
+    return (n, (ctypes.c_void_p * n)(*[t.data_ptr() for t in srcs]),
+            (ctypes.c_void_p * n)(*[t.data_ptr() for t in dsts]), (ctypes.c_int64 * n)(*heads))
+
+
+def usp_zigzag_extract_n(xs, outs, rd, ud, ring_rank, ulysses_rank, inverse=False, stream=None):
+    """usp_zigzag_extract of several tensors (same dtype, B, S, D; own head
+    counts) in one launch."""
+    xs, outs = list(xs), list(outs)
+    _dev(*xs, *outs)
+    _contig(*xs, *outs)
+    heads = []
+    for x, out in zip(xs, outs):
+        if x.dtype != xs[0].dtype:
+            raise ValueError("all tensors must share the dtype")
+        B, S, H, D = (out if inverse else x).shape
+        if (B, S, D) != tuple((outs[0] if inverse else xs[0]).shape[i] for i in (0, 1, 3)):
+            raise ValueError("all tensors must share B, S and D")
+        groups = rd * ud if ring_rank < 0 else (ud if ulysses_rank < 0 else 1)
+        if (x if inverse else out).numel() != groups * B * (S // (rd * ud)) * H * D:
+            raise ValueError("a shard buffer has the wrong number of elements")
+        heads.append(H)
+    B, S, _, D = (outs[0] if inverse else xs[0]).shape
+    n, src, dst, hs = _ptr_arrays(xs, outs, heads)
+    check(lib().usp_zigzag_extract_n(n, src, dst, hs, _dtype(xs[0]), B, S, D, rd, ud, ring_rank, ulysses_rank,
+                                     int(inverse), _stream(stream)))
+    return outs
+
+
 def host_cu_seqlens(cu_seqlens):
     """Packed-sample boundaries as a contiguous host int32 array (the C calls
     read them from host memory; a GPU tensor is copied back first)."""
@@ -178,6 +213,37 @@ def usp_ulysses_a2a_layout(inp, out, degree, rank, inverse=False, stream=None):
     check(lib().usp_ulysses_a2a_layout(inp.data_ptr(), out.data_ptr(), _dtype(inp), bs, L, hc, hd,
                                        degree, rank, int(inverse), _stream(stream)))
     return out
+
+
+def usp_ulysses_a2a_layout_n(inps, outs, degree, rank, inverse=False, stream=None):
+    """usp_ulysses_a2a_layout of several tensors (same dtype, bs, L, hd; own
+    head counts) in one launch; shapes per tensor as usp_ulysses_a2a_layout."""
+    inps, outs = list(inps), list(outs)
+    _dev(*inps, *outs)
+    _contig(*inps, *outs)
+    heads, dims = [], None
+    for inp, out in zip(inps, outs):
+        if inp.dtype != inps[0].dtype:
+            raise ValueError("all tensors must share the dtype")
+        if not inverse:
+            N, bs, ls, hc, hd = inp.shape
+            L = ls * N
+        else:
+            N, hb, bs, L, hd = inp.shape
+            hc = hb * N
+        if N != degree:
+            raise ValueError("leading dimension of every input must equal the Ulysses degree")
+        if dims is not None and (bs, L, hd) != dims:
+            raise ValueError("all tensors must share bs, L and hd")
+        dims = (bs, L, hd)
+        if out.numel() != (degree if rank < 0 else 1) * bs * L * (hc // degree) * hd:
+            raise ValueError("an output has the wrong number of elements")
+        heads.append(hc)
+    bs, L, hd = dims
+    n, src, dst, hs = _ptr_arrays(inps, outs, heads)
+    check(lib().usp_ulysses_a2a_layout_n(n, src, dst, hs, _dtype(inps[0]), bs, L, hd, degree, rank, int(inverse),
+                                         _stream(stream)))
+    return outs
 
 
 def usp_ulysses_a2a_layout_heads(inp, out, degree, rank, head_offset, num_heads, inverse=False, stream=None):

@@ -61,6 +61,7 @@ void plan_pieces(usp::CopyPlan &p) {
 }
 
 constexpr int64_t kMaxIndex = (int64_t)1 << 31;
+static_assert(usp::kMaxCopyBatch == USP_MAX_COPY_BATCH, "batched copy limit");
 
 // Packed-sample boundaries from host memory into the kernels' by-value copy.
 // `split` > 0: the per-sample zigzag over `split` ring ranks, which needs
@@ -106,31 +107,35 @@ const char *usp_last_error_detail(void) { return g_detail; }
 
 int32_t usp_abi_version(void) { return USP_ABI_VERSION; }
 
-usp_status usp_zigzag_extract(const void *x, void *out, usp_dtype dtype, int64_t batch,
-                              int64_t seq_len, int64_t heads, int64_t head_dim, int32_t rd,
-                              int32_t ud, int32_t ring_rank, int32_t ulysses_rank,
-                              int32_t inverse, void *stream) {
-  if (!x || !out) return fail(USP_ERR_INVALID_ARG, "zigzag_extract: null pointer");
+namespace {
+
+// Validate one zigzag extract and fill its copy plan; `in_bytes` and
+// `out_bytes` are the byte extents the copy reads and writes.
+usp_status zigzag_plan(const char *who, const void *x, void *out, usp_dtype dtype, int64_t batch, int64_t seq_len,
+                       int64_t heads, int64_t head_dim, int32_t rd, int32_t ud, int32_t ring_rank,
+                       int32_t ulysses_rank, int32_t inverse, usp::CopyPlan &p, int64_t &in_bytes,
+                       int64_t &out_bytes) {
+  if (!x || !out) return fail(USP_ERR_INVALID_ARG, "%s: null pointer", who);
   if (!aligned16(x) || !aligned16(out))
-    return fail(USP_ERR_INVALID_ARG, "zigzag_extract: pointers must be 16-byte aligned");
-  if (x == out) return fail(USP_ERR_INVALID_ARG, "zigzag_extract: x and out must differ");
-  if (!dtype_ok(dtype)) return fail(USP_ERR_INVALID_ARG, "zigzag_extract: unknown dtype %d", (int)dtype);
+    return fail(USP_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", who);
+  if (x == out) return fail(USP_ERR_INVALID_ARG, "%s: x and out must differ", who);
+  if (!dtype_ok(dtype)) return fail(USP_ERR_INVALID_ARG, "%s: unknown dtype %d", who, (int)dtype);
   if (batch < 1 || seq_len < 1 || heads < 1 || head_dim < 1 || rd < 1 || ud < 1)
-    return fail(USP_ERR_INVALID_ARG, "zigzag_extract: sizes and degrees must be >= 1");
-  if (inverse != 0 && inverse != 1) return fail(USP_ERR_INVALID_ARG, "zigzag_extract: inverse must be 0 or 1");
+    return fail(USP_ERR_INVALID_ARG, "%s: sizes and degrees must be >= 1", who);
+  if (inverse != 0 && inverse != 1) return fail(USP_ERR_INVALID_ARG, "%s: inverse must be 0 or 1", who);
   if (seq_len % (2 * (int64_t)rd * ud) != 0)
-    return fail(USP_ERR_INVALID_ARG, "zigzag_extract: seq_len %lld not divisible by 2*rd*ud = %lld",
+    return fail(USP_ERR_INVALID_ARG, "%s: seq_len %lld not divisible by 2*rd*ud = %lld", who,
                 (long long)seq_len, (long long)(2 * (int64_t)rd * ud));
   if (ring_rank < -1 || ring_rank >= rd || ulysses_rank < -1 || ulysses_rank >= ud)
-    return fail(USP_ERR_INVALID_ARG, "zigzag_extract: rank out of range");
+    return fail(USP_ERR_INVALID_ARG, "%s: rank out of range", who);
   if (ring_rank == -1 && ulysses_rank != -1)
-    return fail(USP_ERR_INVALID_ARG, "zigzag_extract: ring_rank = -1 needs ulysses_rank = -1");
+    return fail(USP_ERR_INVALID_ARG, "%s: ring_rank = -1 needs ulysses_rank = -1", who);
   const int64_t row_bytes = heads * head_dim * elem_bytes(dtype);
   if (row_bytes % 16 != 0)
-    return fail(USP_ERR_UNSUPPORTED, "zigzag_extract: heads*head_dim*element size must be a multiple of 16 bytes");
-  if (batch * seq_len >= kMaxIndex) return fail(USP_ERR_UNSUPPORTED, "zigzag_extract: too many rows");
+    return fail(USP_ERR_UNSUPPORTED, "%s: heads*head_dim*element size must be a multiple of 16 bytes", who);
+  if (batch * seq_len >= kMaxIndex) return fail(USP_ERR_UNSUPPORTED, "%s: too many rows", who);
 
-  usp::CopyPlan p{};
+  p = usp::CopyPlan{};
   p.src = static_cast<const char *>(x);
   p.dst = static_cast<char *>(out);
   p.kind = inverse ? usp::kZigzagInv : usp::kZigzagFwd;
@@ -147,7 +152,61 @@ usp_status usp_zigzag_extract(const void *x, void *out, usp_dtype dtype, int64_t
   p.p[6] = ring_rank;
   p.p[7] = ulysses_rank;
   plan_pieces(p);
+  const int64_t global = batch * seq_len * row_bytes, shards = (int64_t)p.n_items * p.rows_per_item * row_bytes;
+  in_bytes = inverse ? shards : global;
+  out_bytes = inverse ? global : shards;
+  return USP_OK;
+}
+
+bool overlap(const void *a, int64_t na, const void *b, int64_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+// A batch of n copies must not write where any of them reads or another writes.
+usp_status batch_disjoint(const char *who, int32_t n, const usp::CopyPlan *p, const int64_t *in_bytes,
+                          const int64_t *out_bytes) {
+  for (int32_t i = 0; i < n; ++i)
+    for (int32_t j = 0; j < n; ++j) {
+      if (overlap(p[i].dst, out_bytes[i], p[j].src, in_bytes[j]))
+        return fail(USP_ERR_INVALID_ARG, "%s: output %d overlaps input %d", who, (int)i, (int)j);
+      if (i != j && overlap(p[i].dst, out_bytes[i], p[j].dst, out_bytes[j]))
+        return fail(USP_ERR_INVALID_ARG, "%s: outputs %d and %d overlap", who, (int)i, (int)j);
+    }
+  return USP_OK;
+}
+
+}  // namespace
+
+usp_status usp_zigzag_extract(const void *x, void *out, usp_dtype dtype, int64_t batch,
+                              int64_t seq_len, int64_t heads, int64_t head_dim, int32_t rd,
+                              int32_t ud, int32_t ring_rank, int32_t ulysses_rank,
+                              int32_t inverse, void *stream) {
+  usp::CopyPlan p;
+  int64_t nin, nout;
+  const usp_status st = zigzag_plan("zigzag_extract", x, out, dtype, batch, seq_len, heads, head_dim, rd, ud,
+                                    ring_rank, ulysses_rank, inverse, p, nin, nout);
+  if (st != USP_OK) return st;
   return hip_result(usp::launch_copy(p, static_cast<hipStream_t>(stream)), "zigzag_extract launch");
+}
+
+usp_status usp_zigzag_extract_n(int32_t n, const void *const *x, void *const *out, const int64_t *heads,
+                                usp_dtype dtype, int64_t batch, int64_t seq_len, int64_t head_dim, int32_t rd,
+                                int32_t ud, int32_t ring_rank, int32_t ulysses_rank, int32_t inverse,
+                                void *stream) {
+  if (n < 1 || n > usp::kMaxCopyBatch)
+    return fail(USP_ERR_INVALID_ARG, "zigzag_extract_n: n = %d outside [1, %d]", (int)n, usp::kMaxCopyBatch);
+  if (!x || !out || !heads) return fail(USP_ERR_INVALID_ARG, "zigzag_extract_n: null array");
+  usp::CopyPlan p[usp::kMaxCopyBatch];
+  int64_t nin[usp::kMaxCopyBatch], nout[usp::kMaxCopyBatch];
+  for (int32_t i = 0; i < n; ++i) {
+    const usp_status st = zigzag_plan("zigzag_extract_n", x[i], out[i], dtype, batch, seq_len, heads[i], head_dim,
+                                      rd, ud, ring_rank, ulysses_rank, inverse, p[i], nin[i], nout[i]);
+    if (st != USP_OK) return st;
+  }
+  const usp_status st = batch_disjoint("zigzag_extract_n", n, p, nin, nout);
+  if (st != USP_OK) return st;
+  return hip_result(usp::launch_copy_n(p, n, static_cast<hipStream_t>(stream)), "zigzag_extract_n launch");
 }
 
 usp_status usp_zigzag_extract_varlen(const void *x, void *out, usp_dtype dtype, int64_t batch,
@@ -195,9 +254,10 @@ namespace {
 
 // The Ulysses layout of heads [h0, h0 + nh) of every head block (the whole
 // block when h0 = 0, nh = heads / degree).
-usp_status ulysses_layout(const char *who, const void *in, void *out, usp_dtype dtype, int64_t batch,
-                          int64_t seq_len, int64_t heads, int64_t head_dim, int32_t ulysses_degree,
-                          int32_t ulysses_rank, int64_t h0, int64_t nh, int32_t inverse, void *stream) {
+usp_status ulysses_plan(const char *who, const void *in, void *out, usp_dtype dtype, int64_t batch,
+                        int64_t seq_len, int64_t heads, int64_t head_dim, int32_t ulysses_degree,
+                        int32_t ulysses_rank, int64_t h0, int64_t nh, int32_t inverse, usp::CopyPlan &p,
+                        int64_t &in_bytes, int64_t &out_bytes) {
   if (!in || !out) return fail(USP_ERR_INVALID_ARG, "%s: null pointer", who);
   if (!aligned16(in) || !aligned16(out))
     return fail(USP_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", who);
@@ -225,7 +285,7 @@ usp_status ulysses_layout(const char *who, const void *in, void *out, usp_dtype 
   if (N * batch * seq_len * heads >= kMaxIndex) return fail(USP_ERR_UNSUPPORTED, "%s: too many rows", who);
 
   const int64_t G = ulysses_rank < 0 ? N : 1;
-  usp::CopyPlan p{};
+  p = usp::CopyPlan{};
   p.src = static_cast<const char *>(in);
   p.dst = static_cast<char *>(out);
   p.kind = inverse ? usp::kUlyssesInv : usp::kUlyssesFwd;
@@ -258,6 +318,24 @@ usp_status ulysses_layout(const char *who, const void *in, void *out, usp_dtype 
   p.p[8] = nh;
   p.p[9] = peers_per_item;
   plan_pieces(p);
+  // extents: one rank's sequence-major shard holds every head, its
+  // head-major tensor the chunk's; N of them are read, G written
+  const int64_t eb = elem_bytes(dtype);
+  const int64_t shard = batch * Ls * heads * head_dim * eb;
+  const int64_t planes = nh * batch * seq_len * head_dim * eb;
+  in_bytes = N * (inverse ? planes : shard);
+  out_bytes = G * (inverse ? shard : planes);
+  return USP_OK;
+}
+
+usp_status ulysses_layout(const char *who, const void *in, void *out, usp_dtype dtype, int64_t batch,
+                          int64_t seq_len, int64_t heads, int64_t head_dim, int32_t ulysses_degree,
+                          int32_t ulysses_rank, int64_t h0, int64_t nh, int32_t inverse, void *stream) {
+  usp::CopyPlan p;
+  int64_t nin, nout;
+  const usp_status st = ulysses_plan(who, in, out, dtype, batch, seq_len, heads, head_dim, ulysses_degree,
+                                     ulysses_rank, h0, nh, inverse, p, nin, nout);
+  if (st != USP_OK) return st;
   return hip_result(usp::launch_copy(p, static_cast<hipStream_t>(stream)), "ulysses layout launch");
 }
 
@@ -270,6 +348,26 @@ usp_status usp_ulysses_a2a_layout(const void *in, void *out, usp_dtype dtype, in
   const int64_t hb = ulysses_degree >= 1 && heads >= 1 ? heads / ulysses_degree : 1;
   return ulysses_layout("ulysses_a2a_layout", in, out, dtype, batch, seq_len, heads, head_dim, ulysses_degree,
                         ulysses_rank, 0, hb < 1 ? 1 : hb, inverse, stream);
+}
+
+usp_status usp_ulysses_a2a_layout_n(int32_t n, const void *const *in, void *const *out, const int64_t *heads,
+                                    usp_dtype dtype, int64_t batch, int64_t seq_len, int64_t head_dim,
+                                    int32_t ulysses_degree, int32_t ulysses_rank, int32_t inverse, void *stream) {
+  if (n < 1 || n > usp::kMaxCopyBatch)
+    return fail(USP_ERR_INVALID_ARG, "ulysses_a2a_layout_n: n = %d outside [1, %d]", (int)n, usp::kMaxCopyBatch);
+  if (!in || !out || !heads) return fail(USP_ERR_INVALID_ARG, "ulysses_a2a_layout_n: null array");
+  usp::CopyPlan p[usp::kMaxCopyBatch];
+  int64_t nin[usp::kMaxCopyBatch], nout[usp::kMaxCopyBatch];
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t hb = ulysses_degree >= 1 && heads[i] >= 1 ? heads[i] / ulysses_degree : 1;
+    const usp_status st = ulysses_plan("ulysses_a2a_layout_n", in[i], out[i], dtype, batch, seq_len, heads[i],
+                                       head_dim, ulysses_degree, ulysses_rank, 0, hb < 1 ? 1 : hb, inverse, p[i],
+                                       nin[i], nout[i]);
+    if (st != USP_OK) return st;
+  }
+  const usp_status st = batch_disjoint("ulysses_a2a_layout_n", n, p, nin, nout);
+  if (st != USP_OK) return st;
+  return hip_result(usp::launch_copy_n(p, n, static_cast<hipStream_t>(stream)), "ulysses_a2a_layout_n launch");
 }
 
 usp_status usp_ulysses_a2a_layout_heads(const void *in, void *out, usp_dtype dtype, int64_t batch,

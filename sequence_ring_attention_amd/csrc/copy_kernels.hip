@@ -123,47 +123,62 @@ __device__ inline RowMap decode(const CopyPlan &P, uint32_t item) {
   return m;
 }
 
-__global__ __launch_bounds__(kThreads) void copy_rows_kernel(CopyPlan P) {
-  const uint32_t total = P.n_items * P.pieces_per_item;
-  for (uint32_t piece = blockIdx.x; piece < total; piece += gridDim.x) {
-    const uint32_t item = piece / P.pieces_per_item;
-    const uint32_t row0 = (piece - item * P.pieces_per_item) * P.rows_per_piece;
-    const uint32_t nrows = min(P.rows_per_piece, P.rows_per_item - row0);
-    const RowMap m = decode(P, item);
-    const uint32_t nvec = nrows * P.row_vecs;
-    for (uint32_t v0 = threadIdx.x; v0 < nvec; v0 += kThreads * kUnroll) {
-      u32x4 buf[kUnroll];
-      int64_t doff[kUnroll];
+// One piece (a run of rows of one item) of plan P, by the whole workgroup.
+__device__ inline void copy_piece(const CopyPlan &P, uint32_t piece) {
+  const uint32_t item = piece / P.pieces_per_item;
+  const uint32_t row0 = (piece - item * P.pieces_per_item) * P.rows_per_piece;
+  const uint32_t nrows = min(P.rows_per_piece, P.rows_per_item - row0);
+  const RowMap m = decode(P, item);
+  const uint32_t nvec = nrows * P.row_vecs;
+  for (uint32_t v0 = threadIdx.x; v0 < nvec; v0 += kThreads * kUnroll) {
+    u32x4 buf[kUnroll];
+    int64_t doff[kUnroll];
 #pragma unroll
-      for (int k = 0; k < kUnroll; ++k) {
-        const uint32_t idx = v0 + k * kThreads;
-        doff[k] = -1;
-        if (idx < nvec) {
-          uint32_t row, col;
-          if (P.row_vecs_shift < 31) {
-            row = idx >> P.row_vecs_shift;
-            col = idx & (P.row_vecs - 1);
-          } else {
-            row = idx / P.row_vecs;
-            col = idx - row * P.row_vecs;
-          }
-          const int64_t t = (int64_t)row0 + row;
-          const bool second = t >= m.split;
-          // piece of a gathered row (0 unless grp_shift < 31) and its vector
-          const uint32_t grp = P.grp_shift < 31 ? col >> P.grp_shift : 0;
-          const uint32_t gcol = col - (grp << (P.grp_shift & 31));
-          const int64_t srow = m.src_base + t * m.src_stride + grp * m.src_grp + (second ? m.src_jump : 0);
-          const int64_t drow = m.dst_base + t * m.dst_stride + (second ? m.dst_jump : 0);
-          buf[k] = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4 *>(P.src + srow * (int64_t)P.src_row_bytes) + gcol);
-          doff[k] = drow * (int64_t)P.dst_unit_bytes + (int64_t)col * 16;
+    for (int k = 0; k < kUnroll; ++k) {
+      const uint32_t idx = v0 + k * kThreads;
+      doff[k] = -1;
+      if (idx < nvec) {
+        uint32_t row, col;
+        if (P.row_vecs_shift < 31) {
+          row = idx >> P.row_vecs_shift;
+          col = idx & (P.row_vecs - 1);
+        } else {
+          row = idx / P.row_vecs;
+          col = idx - row * P.row_vecs;
         }
-      }
-#pragma unroll
-      for (int k = 0; k < kUnroll; ++k) {
-        if (doff[k] >= 0) __builtin_nontemporal_store(buf[k], reinterpret_cast<u32x4 *>(P.dst + doff[k]));
+        const int64_t t = (int64_t)row0 + row;
+        const bool second = t >= m.split;
+        // piece of a gathered row (0 unless grp_shift < 31) and its vector
+        const uint32_t grp = P.grp_shift < 31 ? col >> P.grp_shift : 0;
+        const uint32_t gcol = col - (grp << (P.grp_shift & 31));
+        const int64_t srow = m.src_base + t * m.src_stride + grp * m.src_grp + (second ? m.src_jump : 0);
+        const int64_t drow = m.dst_base + t * m.dst_stride + (second ? m.dst_jump : 0);
+        buf[k] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(P.src + srow * (int64_t)P.src_row_bytes) + gcol);
+        doff[k] = drow * (int64_t)P.dst_unit_bytes + (int64_t)col * 16;
       }
     }
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      if (doff[k] >= 0) __builtin_nontemporal_store(buf[k], reinterpret_cast<u32x4 *>(P.dst + doff[k]));
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void copy_rows_kernel(CopyPlan P) {
+  const uint32_t total = P.n_items * P.pieces_per_item;
+  for (uint32_t piece = blockIdx.x; piece < total; piece += gridDim.x) copy_piece(P, piece);
+}
+
+// Several plans in one launch: the pieces of plan i are global pieces
+// [first[i], first[i + 1]), dealt to the workgroups like those of one plan.
+__global__ __launch_bounds__(kThreads) void copy_rows_n_kernel(CopyBatch C) {
+  const uint32_t total = C.first[C.n];
+  for (uint32_t piece = blockIdx.x; piece < total; piece += gridDim.x) {
+    int i = 0;
+#pragma unroll
+    for (int k = 1; k < kMaxCopyBatch; ++k) i += (k < C.n) & (piece >= C.first[k]);
+    copy_piece(C.plan[i], piece - C.first[i]);
   }
 }
 
@@ -208,6 +223,21 @@ hipError_t launch_zigzag_varlen(const ZigzagVarlenArgs &a, hipStream_t stream) {
   const int64_t blocks = (total + kThreads - 1) / kThreads;
   hipLaunchKernelGGL(zigzag_varlen_kernel, dim3((uint32_t)(blocks < 8192 ? blocks : 8192)), dim3(kThreads), 0,
                      stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_n(const CopyPlan *plans, int n, hipStream_t stream) {
+  CopyBatch C{};
+  C.n = n;
+  C.first[0] = 0;
+  for (int i = 0; i < n; ++i) {
+    C.plan[i] = plans[i];
+    C.first[i + 1] = C.first[i] + plans[i].n_items * plans[i].pieces_per_item;
+  }
+  const uint32_t total = C.first[n];
+  if (total == 0) return hipSuccess;
+  const uint32_t grid = total < 8192 ? total : 8192;
+  hipLaunchKernelGGL(copy_rows_n_kernel, dim3(grid), dim3(kThreads), 0, stream, C);
   return hipGetLastError();
 }
 

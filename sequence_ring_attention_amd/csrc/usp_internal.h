@@ -47,6 +47,16 @@ struct CopyPlan {
 
 hipError_t launch_copy(const CopyPlan &plan, hipStream_t stream);
 
+// Up to kMaxCopyBatch plans in one launch (Q, K and V of one layout step).
+constexpr int kMaxCopyBatch = 4;
+struct CopyBatch {
+  CopyPlan plan[kMaxCopyBatch];
+  uint32_t first[kMaxCopyBatch + 1];  // first global piece of each plan; first[n] = total
+  int32_t n;
+};
+
+hipError_t launch_copy_n(const CopyPlan *plans, int n, hipStream_t stream);
+
 // Per-sample zigzag extract (or its inverse): a row gather whose source row
 // comes from the share map of Samples.
 struct ZigzagVarlenArgs {

@@ -159,9 +159,12 @@ class OneGpuShare:
         r, u, rd, ud = self.r, self.u, self.rd, self.ud
         mark = (lambda i: marks[i].record()) if marks is not None else (lambda i: None)
         mark(0)
-        self._extract(self.Q, self.qz[u], r, u)
-        self._extract(self.K, self.kz[u], r, u)
-        self._extract(self.V, self.vz[u], r, u)
+        if self.per_sample:
+            self._extract(self.Q, self.qz[u], r, u)
+            self._extract(self.K, self.kz[u], r, u)
+            self._extract(self.V, self.vz[u], r, u)
+        else:  # Q, K and V in one launch
+            B.usp_zigzag_extract_n((self.Q, self.K, self.V), (self.qz[u], self.kz[u], self.vz[u]), rd, ud, r, u)
         mark(1)
         if self.chunk is not None:
             mark(2)
@@ -178,9 +181,7 @@ class OneGpuShare:
             mark(3)
             mark(4)
             return self.out
-        B.usp_ulysses_a2a_layout(self.qz, self.qh[u], ud, u)
-        B.usp_ulysses_a2a_layout(self.kz, self.kh[u, r], ud, u)
-        B.usp_ulysses_a2a_layout(self.vz, self.vh[u, r], ud, u)
+        B.usp_ulysses_a2a_layout_n((self.qz, self.kz, self.vz), (self.qh[u], self.kh[u, r], self.vh[u, r]), ud, u)
         mark(2)
         self._walk(u)
         mark(3)

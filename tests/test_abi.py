@@ -27,7 +27,7 @@ def declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     lib = B.lib()
     for name in names:
         assert hasattr(lib, name), name
@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = B.lib()
-    assert lib.usp_abi_version() == 4
+    assert lib.usp_abi_version() == 5
     assert lib.usp_status_string(0) == b"USP_OK"
     assert lib.usp_status_string(2) == b"USP_ERR_UNSUPPORTED"
     assert lib.usp_status_string(99) == b"USP_ERR_UNKNOWN"
@@ -148,6 +148,83 @@ def test_attention_rank_and_step_ranges():
     assert walk(4) == 1 and walk(-2) == 1
     assert lib.usp_attn_fwd(FAKE, FAKE2, FAKE3, FAKE, FAKE2, None, 0, None) == 1
     assert lib.usp_attn_fwd(None, FAKE2, FAKE3, FAKE, FAKE2, ctypes.byref(d), 0, None) == 1
+
+
+def _arrays(xs, outs, heads):
+    n = len(xs)
+    return ((ctypes.c_void_p * n)(*xs), (ctypes.c_void_p * n)(*outs), (ctypes.c_int64 * n)(*heads))
+
+
+# distinct, far-apart fake buffers (1 MiB apart): extents of the small shapes below never meet
+F = [0x1000000 * (i + 1) for i in range(8)]
+
+
+def _zz_n(n=3, xs=None, outs=None, heads=None, **kw):
+    a = dict(dtype=0, B=1, S=64, D=64, rd=4, ud=1, r=0, u=0, inv=0)
+    a.update(kw)
+    xs = F[:3] if xs is None else xs
+    outs = F[3:6] if outs is None else outs
+    heads = [4, 2, 2] if heads is None else heads
+    x, o, h = _arrays(xs, outs, heads)
+    return B.lib().usp_zigzag_extract_n(n, x, o, h, a["dtype"], a["B"], a["S"], a["D"], a["rd"], a["ud"], a["r"],
+                                        a["u"], a["inv"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=0), 1), (dict(n=5, xs=F[:5], outs=[F[5], F[6], F[7], F[7] + 4096, F[7] + 8192], heads=[2] * 5), 1),
+    (dict(xs=[F[0], None, F[2]]), 1), (dict(outs=[F[3], F[4] + 8, F[5]]), 1), (dict(heads=[4, 0, 2]), 1),
+    (dict(S=60), 1), (dict(r=4), 1), (dict(inv=2), 1), (dict(heads=[4, 1, 2], D=2), 2),
+    # output 1 lies inside input 0 (the global tensor of 64 rows x 4 heads x 64 x 2 bytes)
+    (dict(outs=[F[3], F[0] + 1024, F[5]]), 1),
+    # outputs 0 and 2 share their first bytes
+    (dict(outs=[F[3], F[4], F[3] + 16]), 1),
+])
+def test_zigzag_n_rejects(kw, status):
+    assert _zz_n(**kw) == status
+    assert b"zigzag_extract_n" in B.lib().usp_last_error_detail()
+
+
+@no_gpu
+def test_zigzag_n_rejects_null_arrays():
+    x, o, h = _arrays(F[:3], F[3:6], [4, 2, 2])
+    lib = B.lib()
+    assert lib.usp_zigzag_extract_n(3, None, o, h, 0, 1, 64, 64, 4, 1, 0, 0, 0, None) == 1
+    assert lib.usp_zigzag_extract_n(3, x, o, None, 0, 1, 64, 64, 4, 1, 0, 0, 0, None) == 1
+    assert lib.usp_ulysses_a2a_layout_n(3, x, None, h, 0, 1, 64, 64, 2, 0, 0, None) == 1
+
+
+def _uly_n(n=3, ins=None, outs=None, heads=None, **kw):
+    a = dict(dtype=0, B=1, L=64, D=64, N=2, u=0, inv=0)
+    a.update(kw)
+    ins = F[:3] if ins is None else ins
+    outs = F[3:6] if outs is None else outs
+    heads = [8, 2, 2] if heads is None else heads
+    i, o, h = _arrays(ins, outs, heads)
+    return B.lib().usp_ulysses_a2a_layout_n(n, i, o, h, a["dtype"], a["B"], a["L"], a["D"], a["N"], a["u"],
+                                            a["inv"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=0), 1), (dict(n=5), 1), (dict(heads=[8, 3, 2]), 1), (dict(L=63), 1), (dict(u=2), 1),
+    (dict(D=4), 2), (dict(inv=-1), 1), (dict(ins=[F[0], F[1] + 4, F[2]]), 1),
+    (dict(outs=[F[3], F[1] + 512, F[5]]), 1), (dict(outs=[F[3], F[4], F[4] + 1024]), 1),
+])
+def test_ulysses_n_rejects(kw, status):
+    assert _uly_n(**kw) == status
+    assert b"ulysses_a2a_layout_n" in B.lib().usp_last_error_detail()
+
+
+@no_gpu
+def test_batched_copies_reach_the_runtime():
+    """Valid batches pass validation and fail only at launch without a GPU."""
+    assert _zz_n() == 3
+    assert b"launch" in B.lib().usp_last_error_detail()
+    assert _zz_n(n=1, heads=[4]) == 3
+    assert _uly_n() == 3
+    assert _uly_n(inv=1, u=-1) == 3
+    assert b"launch" in B.lib().usp_last_error_detail()
 
 
 @no_gpu

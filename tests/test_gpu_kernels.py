@@ -107,6 +107,82 @@ def test_ulysses_layout_bitexact(case):
         assert ok() and np.array_equal(bits(one), ref_inv[u])
 
 
+# ----------------------------------------------------- batched copies (n) --
+
+ZZN_CASES = [  # B, S, D, rd, ud, heads of each tensor, dtype
+    (1, 96, 64, 3, 2, (4, 2, 2), "bf16"),
+    (2, 256, 64, 4, 1, (2, 1), "fp32"),
+    (1, 1024, 128, 4, 2, (8, 2, 2, 2), "bf16"),
+    (3, 40, 8, 2, 2, (1, 3, 2), "bf16"),      # rows of 16 and 48 bytes in one launch
+]
+
+
+@pytest.mark.parametrize("case", ZZN_CASES)
+def test_zigzag_extract_n_bitexact(case):
+    """Several tensors in one launch: each equals the oracle's Algorithm 2
+    gather, in every rank mode, and the inverse restores every tensor."""
+    Bn, S, D, rd, ud, heads, dt = case
+    dev = device()
+    T = S // (rd * ud)
+    xs = [inputs.randn((Bn, S, H, D), 30 + i, dt) for i, H in enumerate(heads)]
+    xds = [x.to(dev) for x in xs]
+    refs = [ix.zigzag_extract_all(bits(x), rd, ud) for x in xs]          # (rd, ud, B, T, H, D) each
+    say("zigzag_n all", case)
+    outs = [guarded((rd, ud, Bn, T, H, D), xs[0].dtype, dev) for H in heads]
+    B.usp_zigzag_extract_n(xds, [o for o, _ in outs], rd, ud, -1, -1)
+    torch.cuda.synchronize()
+    for (o, ok), ref in zip(outs, refs):
+        assert ok() and np.array_equal(bits(o), ref)
+    for r, u in ((0, -1), (rd - 1, ud - 1)):
+        say("zigzag_n ranks", case, r, u)
+        shp = (Bn, T) if u >= 0 else (ud, Bn, T)
+        part = [guarded((*shp, H, D), xs[0].dtype, dev) for H in heads]
+        B.usp_zigzag_extract_n(xds, [o for o, _ in part], rd, ud, r, u)
+        torch.cuda.synchronize()
+        for (o, ok), ref in zip(part, refs):
+            assert ok() and np.array_equal(bits(o), ref[r, u] if u >= 0 else ref[r])
+    say("zigzag_n inverse", case)
+    backs = [guarded((Bn, S, H, D), xs[0].dtype, dev) for H in heads]
+    B.usp_zigzag_extract_n([o for o, _ in outs], [b for b, _ in backs], rd, ud, -1, -1, inverse=True)
+    torch.cuda.synchronize()
+    for (b, ok), x in zip(backs, xs):
+        assert ok() and np.array_equal(bits(b), bits(x))
+
+
+ULYN_CASES = [  # N, bs, L, heads of each tensor, hd, dtype
+    (2, 1, 64, (4, 2, 2), 64, "bf16"),
+    (4, 2, 96, (8, 4, 4), 128, "bf16"),
+    (3, 1, 30, (6, 3), 8, "fp32"),
+]
+
+
+@pytest.mark.parametrize("case", ULYN_CASES)
+def test_ulysses_layout_n_bitexact(case):
+    """Q, K and V layouts in one launch, both directions: each equals the
+    oracle's AllToAll4D permutation."""
+    N, bs, L, heads, hd, dt = case
+    dev = device()
+    xs = [inputs.randn((N, bs, L // N, hc, hd), 40 + i, dt) for i, hc in enumerate(heads)]
+    xds = [x.to(dev) for x in xs]
+    refs = [np.stack([ix.ulysses_fwd([bits(x[u]) for u in range(N)], u) for u in range(N)]) for x in xs]
+    for u in (-1, N - 1):
+        say("ulysses_n fwd", case, u)
+        outs = [guarded(((N,) if u < 0 else ()) + (hc // N, bs, L, hd), xs[0].dtype, dev) for hc in heads]
+        B.usp_ulysses_a2a_layout_n(xds, [o for o, _ in outs], N, u)
+        torch.cuda.synchronize()
+        for (o, ok), ref in zip(outs, refs):
+            assert ok() and np.array_equal(bits(o), ref if u < 0 else ref[u])
+    hm = [torch.from_numpy(ref).view(xs[0].dtype).to(dev) for ref in refs]   # (N, hc/N, bs, L, hd) each
+    for u in (-1, 0):
+        say("ulysses_n inv", case, u)
+        outs = [guarded(((N,) if u < 0 else ()) + (bs, L // N, hc, hd), xs[0].dtype, dev) for hc in heads]
+        B.usp_ulysses_a2a_layout_n(hm, [o for o, _ in outs], N, u, inverse=True)
+        torch.cuda.synchronize()
+        for (o, ok), x, ref in zip(outs, xs, refs):
+            exp = bits(x) if u < 0 else ix.ulysses_inv(list(ref), u)
+            assert ok() and np.array_equal(bits(o), exp)
+
+
 # ------------------------------------------------------------------ merge --
 
 @pytest.mark.parametrize("rows,D", [(1000, 128), (77, 64), (5, 4), (33, 96), (300, 256)])
