@@ -232,25 +232,37 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
     // tile class: every (query, key) pair of the workgroup visible?
     const bool full = __builtin_amdgcn_readfirstlane((k0 >= cur.flo) & (k0 + BN <= cur.fhi));
 
-    // S^T = K Q^T for two 32-key blocks
+    // S^T = K Q^T for two 32-key blocks.  The K rows of k-step ks + AH are
+    // read while k-step ks's two products run, and the products alternate
+    // between the two accumulators, so neither chain waits on the other.
     f32x16 S0 = f32x16{}, S1 = f32x16{};
     __builtin_amdgcn_s_setprio(1);  // keep the matrix core fed while the SIMD's other wave runs softmax
+    {
+      constexpr int NKS = D / 16, AH = 3;
+      bf16x8 kr[AH + 1][2];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(sK + koff[ks]);
-      const bf16x8 kb = *reinterpret_cast<const bf16x8 *>(sK + koff[ks] + 32 * Lds<D>::ROW);
-      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], S0, 0, 0, 0);
-      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[ks], S1, 0, 0, 0);
-    }
-    // keep LDS reads of K several products ahead: half of them up front, then
-    // two products per two reads, then the rest of the products
-    __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
+      for (int i = 0; i < AH; ++i) {
+        kr[i][0] = *reinterpret_cast<const bf16x8 *>(sK + koff[i]);
+        kr[i][1] = *reinterpret_cast<const bf16x8 *>(sK + koff[i] + 32 * Lds<D>::ROW);
+      }
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (ks + AH < NKS) {
+          kr[(ks + AH) % (AH + 1)][0] = *reinterpret_cast<const bf16x8 *>(sK + koff[ks + AH]);
+          kr[(ks + AH) % (AH + 1)][1] = *reinterpret_cast<const bf16x8 *>(sK + koff[ks + AH] + 32 * Lds<D>::ROW);
+        }
+        S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[ks % (AH + 1)][0], qf[ks], S0, 0, 0, 0);
+        S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[ks % (AH + 1)][1], qf[ks], S1, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * AH, 0);
+#pragma unroll
+      for (int i = 0; i < NKS - AH; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * AH, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
     __builtin_amdgcn_s_setprio(0);
 
     if (!full) {  // diagonal, sample-boundary or ragged tile: elementwise mask
@@ -316,7 +328,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
 
     // O^T += V^T P^T, 16 keys per MFMA; V^T read transposed from row-major V
     __builtin_amdgcn_s_setprio(1);
-    // the next accumulator's V operands are read while this one's products run
+    // one 16-key group of P at a time across all D / 32 accumulators (the
+    // chains interleave); the next group's V operands are read meanwhile
     auto read_v = [&](int mb, int p) {
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) s16x4 *)(const_cast<char *>(sV) + voff[mb][0] + p * 16 * Lds<D>::ROW));
@@ -324,19 +337,20 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
           (__attribute__((address_space(3))) s16x4 *)(const_cast<char *>(sV) + voff[mb][1] + p * 16 * Lds<D>::ROW));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    bf16x8 vt[2][4];
+    bf16x8 vt[2][D / 32];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) vt[0][p] = read_v(0, p);
+    for (int mb = 0; mb < D / 32; ++mb) vt[0][mb] = read_v(mb, 0);
 #pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) {
-      if (mb + 1 < D / 32) {
+    for (int p = 0; p < 4; ++p) {
+      if (p + 1 < 4) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) vt[(mb + 1) & 1][p] = read_v(mb + 1, p);
+        for (int mb = 0; mb < D / 32; ++mb) vt[(p + 1) & 1][mb] = read_v(mb, p + 1);
       }
 #pragma unroll
-      for (int p = 0; p < 4; ++p) O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[mb & 1][p], pf[p], O[mb], 0, 0, 0);
+      for (int mb = 0; mb < D / 32; ++mb)
+        O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[p & 1][mb], pf[p], O[mb], 0, 0, 0);
     }
-    schedule_tr_products<4 * (D / 32), 4>();
+    schedule_tr_products<4 * (D / 32), D / 32>();
     __builtin_amdgcn_s_setprio(0);
     wait_tiles();
     __syncthreads();
