@@ -342,9 +342,29 @@ def extra_workloads():
     return res
 
 
-def cpu_baseline(w, r, u, n_rows):
+def sample_rows(w, n_rows):
+    """The seeded query rows (local rows of a share) of the oracle sample."""
+    import numpy as np
+    rng = np.random.default_rng(1234)
+    return np.sort(rng.choice(w.S // w.rd, size=n_rows, replace=False))
+
+
+def gpu_sample(share, w, n_rows):
+    """The sample rows of the share's outputs after a step, on the host:
+    o (B, n, hb, D) from the head-major bf16 output and lse (hb, B, n)."""
+    import torch
+    rows = torch.from_numpy(sample_rows(w, n_rows)).to(share.oh.device)
+    u = share.u
+    o = share.oh[u].index_select(2, rows).to(torch.float64).cpu().numpy().transpose(1, 2, 0, 3)
+    lse = share.lse[u].index_select(2, rows).to(torch.float64).cpu().numpy()
+    return o, lse
+
+
+def cpu_baseline(w, r, u, n_rows, gpu=None):
     """The oracle as it stands on a bounded sample: n_rows query rows of this
-    share (all its heads) against the whole sequence, fp64 on the host."""
+    share (all its heads) against the whole sequence, fp64 on the host.  With
+    ``gpu`` (the same rows of a step's GPU output, from gpu_sample), o (bf16)
+    and lse are compared with the oracle's: max and mean abs error."""
     import numpy as np
     import torch
     from oracle import attention as oa
@@ -357,12 +377,16 @@ def cpu_baseline(w, r, u, n_rows):
     kn = k[:, :, kv_lo:kv_hi].to(torch.float64).numpy()
     vn = v[:, :, kv_lo:kv_hi].to(torch.float64).numpy()
     pos = ix.zigzag_share_positions(w.S, w.rd, r)
-    rng = np.random.default_rng(1234)
-    rows = np.sort(rng.choice(len(pos), size=n_rows, replace=False))
+    rows = sample_rows(w, n_rows)
     qp = pos[rows]
     t0 = time.perf_counter()
-    oa.masked_attention(qn[:, qp], kn, vn, w.scale, q_pos=qp)
+    o_ref, l_ref = oa.masked_attention(qn[:, qp], kn, vn, w.scale, q_pos=qp)   # (B, n, hb, D), (hb, B, n)
     dt = time.perf_counter() - t0
+    errors = None
+    if gpu is not None:
+        eo, el = np.abs(gpu[0] - o_ref), np.abs(gpu[1] - l_ref)
+        errors = {"rows": int(n_rows), "heads": hb, "o_max_abs": float(eo.max()), "o_mean_abs": float(eo.mean()),
+                  "lse_max_abs": float(el.max()), "bars": {"o_max_abs": 1e-2, "o_mean_abs": 1e-3, "lse_max_abs": 1e-3}}
     pairs = int((qp + 1).sum())                       # causal: position p sees p + 1 keys
     flops = 4.0 * w.D * hb * w.B * pairs
     try:
@@ -374,7 +398,7 @@ def cpu_baseline(w, r, u, n_rows):
             "sample": f"{n_rows} random query rows of share (r={r}, u={u}) x {hb} heads vs all "
                       f"{w.S} keys, fp64 numpy, {dt:.2f} s, {flops / 1e9:.1f} GFLOP causal-effective",
             "seconds": dt, "host_cpu_count": os.cpu_count(),
-            "affinity_cores": len(os.sched_getaffinity(0))}
+            "affinity_cores": len(os.sched_getaffinity(0)), "gpu_vs_oracle": errors}
 
 
 def split_balance(w, q, k, v, zig_shares):
@@ -435,6 +459,27 @@ def split_balance(w, q, k, v, zig_shares):
     out["slowest_rank_speedup"] = out["stream"]["slowest_ms"] / out["per_sample"]["slowest_ms"]
     out["bwd_slowest_rank_speedup"] = out["stream"]["bwd_slowest_ms"] / out["per_sample"]["bwd_slowest_ms"]
     return out
+
+
+def ring_steps(share, flops):
+    """The share's walk as cp separate ring steps (usp_ring_attn_step_fwd,
+    fp32 partials) and LSE merges, each launch timed alone: the step-wise
+    form a real ring runs while the next KV block is in flight."""
+    import torch
+    from sequence_ring_attention_amd import binding as B
+    u, r = share.u, share.r
+    q, k, v = share.qh[u], share.kh[u], share.vh[u]
+    desc = share.desc(u)
+    ost = torch.empty(tuple(q.shape), dtype=torch.float32, device=q.device)
+    lst = torch.empty(tuple(share.lse[u].shape), dtype=torch.float32, device=q.device)
+    acc, lacc = torch.zeros_like(ost), torch.full_like(lst, float("-inf"))
+    step_ms = [_time(lambda t=t: B.usp_ring_attn_step_fwd(q, k, v, ost, lst, desc, r, t)) for t in range(share.rd)]
+    rows = lst.numel()
+    merge = _time_flushed(lambda: B.usp_lse_merge(acc, lacc, ost, lst), 3 * rows * q.shape[-1] * 4 + 3 * rows * 4)
+    per_step = flops / share.rd
+    return {"step_ms": step_ms, "step_TFLOP/s": [per_step / (m * 1e-3) / 1e12 for m in step_ms],
+            "step_frac_mfma": [per_step / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS for m in step_ms],
+            "work_per_step_tflop": per_step / 1e12, "merge": merge}
 
 
 def backward_walk(share, fwd_flops, reps=5):
@@ -563,6 +608,7 @@ def main():
         },
         "wall_s_timed": wall,
     }
+    sample = None if args.no_cpu_baseline else gpu_sample(share, w, args.cpu_rows)   # outputs of the last step
     walks = sorted(marks[s][2].elapsed_time(marks[s][3]) for s in range(args.steps))
     result["kernels"]["ring_walk_attention"].update(
         {"ms_median": walks[len(walks) // 2], "ms_min": walks[0], "ms_max": walks[-1]})
@@ -570,6 +616,8 @@ def main():
         print("[bench] backward of the same share", file=sys.stderr, flush=True)
         result["backward"] = backward_walk(share, flops)
     if not args.no_extra:
+        print("[bench] ring steps one by one", file=sys.stderr, flush=True)
+        result["ring_steps"] = ring_steps(share, flops)
         print("[bench] copy launches, cache flushed", file=sys.stderr, flush=True)
         result["copy_launches"] = copy_launches(share, w)
         r2 = w.rd - 1 if r != w.rd - 1 else 0
@@ -584,7 +632,7 @@ def main():
         result["workloads"] = extra_workloads()
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, r, u, args.cpu_rows)
+        result["cpu_baseline"] = cpu_baseline(w, r, u, args.cpu_rows, sample)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
