@@ -222,16 +222,17 @@ def other_share_walk(Q, K, V, w, r, u, flops, steps=5):
             "frac_mfma": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
-def head_chunk_steps(Q, K, V, w, r, u, flops, whole_ms, whole_bytes, chunks=(8, 4, 2), steps=5):
+def head_chunk_steps(Q, K, V, w, r, u, flops, whole_ms, whole_bytes, chunks=(8, 4, 2), overlapped=(4, 2), steps=5):
     """The share stepped with its head block pushed through in chunks
-    (headwise chunking): step time and the head-major bytes one chunk's
-    attention works on, beside the whole block's."""
+    (headwise chunking): step time and the head-major bytes the chunks in
+    flight work on, beside the whole block's; chunks run one after another,
+    and for ``overlapped`` also alternating between two streams."""
     import torch
     from sequence_ring_attention_amd.pipeline import OneGpuShare
     res = {"whole_block": {"heads": w.H // w.ud, "ms": whole_ms, "TFLOP/s": flops / (whole_ms * 1e-3) / 1e12,
                            "head_major_bytes": whole_bytes}}
-    for nh in chunks:
-        sh = OneGpuShare(Q, K, V, w.rd, w.ud, r, u, head_chunk=nh)
+    for nh, ov in [(nh, False) for nh in chunks] + [(nh, True) for nh in overlapped]:
+        sh = OneGpuShare(Q, K, V, w.rd, w.ud, r, u, head_chunk=nh, overlap_chunks=ov)
         sh.prepare_peers()
         sh.step()
         torch.cuda.synchronize()
@@ -242,7 +243,7 @@ def head_chunk_steps(Q, K, V, w, r, u, flops, whole_ms, whole_bytes, chunks=(8, 
         b.record()
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / steps
-        res[f"chunks_of_{nh}"] = {"heads": nh, "ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+        res[f"chunks_of_{nh}" + ("_two_streams" if ov else "")] = {"heads": nh, "ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
                                   "head_major_bytes": sh.head_major_bytes(),
                                   "head_major_fraction": sh.head_major_bytes() / whole_bytes,
                                   "step_time_ratio": ms / whole_ms}

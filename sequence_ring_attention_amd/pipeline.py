@@ -17,7 +17,11 @@ the same kernels, outside ``step``; ``step`` is exactly the per-GPU work.
 
 With ``head_chunk`` (headwise chunking, [UPipe page] section 2) steps 2-4
 run once per chunk of ``head_chunk`` query heads of the head block (and
-their KV heads): the head-major tensors then hold one chunk at a time.
+their KV heads): the head-major tensors then hold one chunk at a time.  With
+``overlap_chunks`` as well, consecutive chunks alternate between the current
+stream and a second one (default priority), each with its own head-major
+query buffer, so one chunk's walk can fill the CUs another leaves idle: two
+chunks' query tensors are then held at once.
 
 This module only allocates buffers and sequences C-ABI calls.
 """
@@ -28,13 +32,14 @@ from . import binding as B
 
 class OneGpuShare:
     def __init__(self, Q, K, V, rd, ud, ring_rank, ulysses_rank, causal=True, cu_seqlens=None, per_sample=False,
-                 head_chunk=None):
+                 head_chunk=None, overlap_chunks=False):
         """Q (B, S, H, D), K/V (B, S, Hkv, D): global tensors on the GPU.
         ``cu_seqlens``: packed-sample boundaries; ``per_sample``: the shares
         are the per-sample zigzag split (Algorithm 2 on every sample) instead
         of the split of the whole packed stream.  ``head_chunk``: query heads
         per chunk (dividing H / ud, a multiple or a divisor of H / Hkv), or
-        None for the whole head block at once."""
+        None for the whole head block at once.  ``overlap_chunks``: run
+        consecutive chunks on two streams (needs ``head_chunk``)."""
         self.Q, self.K, self.V = Q, K, V
         self.rd, self.ud, self.r, self.u = rd, ud, ring_rank, ulysses_rank
         Bn, S, H, D = Q.shape
@@ -69,8 +74,14 @@ class OneGpuShare:
         else:
             # one chunk of query heads, head-major (reused by every chunk), and
             # the group's outputs chunk by chunk: [c, u'] = rank u''s heads of chunk c
-            self.qc = e(self.chunk, Bn, L, D)
+            # one buffer per stream in use; qc is the first
+            self.qcs = [e(self.chunk, Bn, L, D) for _ in range(2 if overlap_chunks else 1)]
+            self.qc = self.qcs[0]
             self.ohc = e(hb // self.chunk, ud, self.chunk, Bn, L, D)
+        if overlap_chunks and self.chunk is None:
+            raise ValueError("overlap_chunks needs head_chunk")
+        self.overlap = bool(overlap_chunks)
+        self._side = torch.cuda.Stream(device=dev) if self.overlap else None
         self.lse = torch.empty(ud, hb, Bn, L, dtype=torch.float32, device=dev)
         self.out = e(Bn, T, H, D)     # this GPU's output shard after the inverse layout
         self._descs = {}
@@ -116,11 +127,11 @@ class OneGpuShare:
                                                zigzag_per_sample=self.per_sample)
         return self._descs["chunk"]
 
-    def _walk_chunk(self, u, c):
+    def _walk_chunk(self, u, c, qc=None):
         """Ulysses rank u's walk over chunk c's heads, its query heads in qc."""
         h0, nh, k0, nk = self._chunk_heads(c)
-        B.usp_attn_fwd(self.qc, self.kh[u][:, k0:k0 + nk], self.vh[u][:, k0:k0 + nk], self.ohc[c, u],
-                       self.lse[u, h0:h0 + nh], self._chunk_desc(), self.r)
+        B.usp_attn_fwd(self.qc if qc is None else qc, self.kh[u][:, k0:k0 + nk], self.vh[u][:, k0:k0 + nk],
+                       self.ohc[c, u], self.lse[u, h0:h0 + nh], self._chunk_desc(), self.r)
 
     def _chunks(self):
         return range(self.H // self.ud // self.chunk)
@@ -168,16 +179,19 @@ class OneGpuShare:
         mark(1)
         if self.chunk is not None:
             mark(2)
-            k_done = -1
-            for c in self._chunks():
-                h0, nh, k0, nk = self._chunk_heads(c)
-                B.usp_ulysses_a2a_layout_heads(self.qz, self.qc, ud, u, h0, nh)
-                if k0 != k_done:  # chunks inside one GQA group share its KV head
-                    B.usp_ulysses_a2a_layout_heads(self.kz, self.kh[u, r, k0:k0 + nk], ud, u, k0, nk)
-                    B.usp_ulysses_a2a_layout_heads(self.vz, self.vh[u, r, k0:k0 + nk], ud, u, k0, nk)
-                    k_done = k0
-                self._walk_chunk(u, c)
-                B.usp_ulysses_a2a_layout_heads(self.ohc[c], self.out, ud, u, h0, nh, inverse=True)
+            if self.overlap:
+                self._chunks_overlapped(r, u, ud)
+            else:
+                k_done = -1
+                for c in self._chunks():
+                    h0, nh, k0, nk = self._chunk_heads(c)
+                    B.usp_ulysses_a2a_layout_heads(self.qz, self.qc, ud, u, h0, nh)
+                    if k0 != k_done:  # chunks inside one GQA group share its KV head
+                        B.usp_ulysses_a2a_layout_heads(self.kz, self.kh[u, r, k0:k0 + nk], ud, u, k0, nk)
+                        B.usp_ulysses_a2a_layout_heads(self.vz, self.vh[u, r, k0:k0 + nk], ud, u, k0, nk)
+                        k_done = k0
+                    self._walk_chunk(u, c)
+                    B.usp_ulysses_a2a_layout_heads(self.ohc[c], self.out, ud, u, h0, nh, inverse=True)
             mark(3)
             mark(4)
             return self.out
@@ -189,17 +203,48 @@ class OneGpuShare:
         mark(4)
         return self.out
 
+    def _chunks_overlapped(self, r, u, ud):
+        """The chunks on two streams: chunk c on stream c % 2 with query
+        buffer c % 2.  Work on one stream is ordered, so a buffer is reused
+        only after its previous chunk's walk; a GQA group's K/V layout is
+        done once, and a chunk on the other stream waits for its event.  The
+        side stream starts after the extract and the current stream waits for
+        it before the step ends."""
+        main = torch.cuda.current_stream()
+        streams = (main, self._side)
+        self._side.wait_stream(main)
+        kv_ready = {}
+        for c in self._chunks():
+            s = streams[c % 2]
+            h0, nh, k0, nk = self._chunk_heads(c)
+            with torch.cuda.stream(s):
+                qc = self.qcs[c % 2]
+                B.usp_ulysses_a2a_layout_heads(self.qz, qc, ud, u, h0, nh)
+                if k0 not in kv_ready:
+                    B.usp_ulysses_a2a_layout_heads(self.kz, self.kh[u, r, k0:k0 + nk], ud, u, k0, nk)
+                    B.usp_ulysses_a2a_layout_heads(self.vz, self.vh[u, r, k0:k0 + nk], ud, u, k0, nk)
+                    ev = torch.cuda.Event()
+                    ev.record(s)
+                    kv_ready[k0] = (ev, c % 2)
+                elif kv_ready[k0][1] != c % 2:
+                    s.wait_event(kv_ready[k0][0])
+                self._walk_chunk(u, c, qc)
+                B.usp_ulysses_a2a_layout_heads(self.ohc[c], self.out, ud, u, h0, nh, inverse=True)
+        main.wait_stream(self._side)
+
     # ------------------------------------------------------- accounting --
     def head_major_bytes(self):
         """Bytes of the head-major tensors one chunk's attention works on
         (its query heads, one ring block of their KV heads, its outputs):
-        what headwise chunking bounds."""
+        what headwise chunking bounds.  With overlapped chunks two chunks are
+        in flight, so twice that."""
         e = self.Q.element_size()
         if self.chunk is None:
             nh, nk = self.H // self.ud, self.Hkv // self.ud
         else:
             _, nh, _, nk = self._chunk_heads(0)
-        return (2 * nh + 2 * nk) * self.Bn * self.L * self.D * e
+        in_flight = 2 if self.overlap else 1
+        return in_flight * (2 * nh + 2 * nk) * self.Bn * self.L * self.D * e
 
     def copy_bytes(self):
         """Bytes each copy phase of one step reads plus writes (every element

@@ -87,8 +87,9 @@ def _case(name):
     return c + ("bf16", True) if len(c) == 10 else c
 
 
-def _run_share(q, k, v, rd, ud, r, u, chunk, cu, ps, causal=True):
-    share = OneGpuShare(q, k, v, rd, ud, r, u, causal=causal, cu_seqlens=cu, per_sample=ps, head_chunk=chunk)
+def _run_share(q, k, v, rd, ud, r, u, chunk, cu, ps, causal=True, overlap=False):
+    share = OneGpuShare(q, k, v, rd, ud, r, u, causal=causal, cu_seqlens=cu, per_sample=ps, head_chunk=chunk,
+                        overlap_chunks=overlap)
     share.prepare_peers()
     out = share.step().clone()
     torch.cuda.synchronize()
@@ -109,6 +110,9 @@ def test_chunked_share_equals_unchunked_and_oracle(name):
         say("share", name, r, u, "chunks of", nh)
         o_ch, l_ch = _run_share(qd, kd, vd, rd, ud, r, u, nh, cu, ps, causal)
         assert torch.equal(o_ch, o_full) and torch.equal(l_ch, l_full)
+        say("share", name, r, u, "chunks of", nh, "on two streams")
+        o_ov, l_ov = _run_share(qd, kd, vd, rd, ud, r, u, nh, cu, ps, causal, overlap=True)
+        assert torch.equal(o_ov, o_full) and torch.equal(l_ov, l_full)
         pos = (ix.zigzag_per_sample_local_positions(cu, rd, ud, r, u) if ps
                else ix.zigzag_local_positions(S, rd, ud, r, u))
         check_close(f64(o_ch), f64(l_ch[:, :, u * T:(u + 1) * T]), o_ref[:, pos],
@@ -121,6 +125,8 @@ def test_chunked_share_rejects_bad_chunks():
     for bad in (5, 4, 0):          # does not divide 12; neither whole GQA groups of 6 nor inside one; empty
         with pytest.raises(ValueError):
             OneGpuShare(q.to(dev), k.to(dev), v.to(dev), 2, 2, 0, 0, head_chunk=bad)
+    with pytest.raises(ValueError):   # two streams of chunks need chunks
+        OneGpuShare(q.to(dev), k.to(dev), v.to(dev), 2, 2, 0, 0, overlap_chunks=True)
 
 
 def test_usp_hybrid_s128k_share_in_head_chunks_is_bitwise_the_same():
@@ -136,3 +142,6 @@ def test_usp_hybrid_s128k_share_in_head_chunks_is_bitwise_the_same():
     o_ch, l_ch = _run_share(q, k, v, w.rd, w.ud, 0, 0, 2, None, False)
     assert torch.isfinite(o_ch).all()
     assert torch.equal(o_ch, o_full) and torch.equal(l_ch, l_full)
+    say(w.name, "share (0,0) chunks of 2 heads on two streams")
+    o_ov, l_ov = _run_share(q, k, v, w.rd, w.ud, 0, 0, 2, None, False, overlap=True)
+    assert torch.equal(o_ov, o_full) and torch.equal(l_ov, l_full)
