@@ -143,7 +143,9 @@ usp_status usp_zigzag_extract(const void *x, void *out, usp_dtype dtype, int64_t
  * call; the caller owns every buffer.
  * Errors: as usp_zigzag_extract for every tensor, plus USP_ERR_INVALID_ARG
  *   for n outside [1, USP_MAX_COPY_BATCH], a null array, or an output whose
- *   byte extent overlaps any input's or another output's.
+ *   byte extent overlaps any input's or another output's, and
+ *   USP_ERR_UNSUPPORTED when the tensors together hold 2^32 or more 64 KiB
+ *   copy pieces.
  */
 usp_status usp_zigzag_extract_n(int32_t n, const void *const *x, void *const *out, const int64_t *heads,
                                 usp_dtype dtype, int64_t batch, int64_t seq_len, int64_t head_dim,
@@ -203,7 +205,9 @@ usp_status usp_ulysses_a2a_layout(const void *in, void *out, usp_dtype dtype, in
  * of n entries, read during the call.
  * Errors: as usp_ulysses_a2a_layout for every tensor, plus
  *   USP_ERR_INVALID_ARG for n outside [1, USP_MAX_COPY_BATCH], a null array,
- *   or an output whose byte extent overlaps any input's or another output's.
+ *   or an output whose byte extent overlaps any input's or another output's,
+ *   and USP_ERR_UNSUPPORTED when the tensors together hold 2^32 or more copy
+ *   pieces.
  */
 usp_status usp_ulysses_a2a_layout_n(int32_t n, const void *const *in, void *const *out, const int64_t *heads,
                                     usp_dtype dtype, int64_t batch, int64_t seq_len, int64_t head_dim,

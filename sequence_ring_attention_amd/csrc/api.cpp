@@ -163,9 +163,13 @@ bool overlap(const void *a, int64_t na, const void *b, int64_t nb) {
   return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
 }
 
-// A batch of n copies must not write where any of them reads or another writes.
+// A batch of n copies must not write where any of them reads or another
+// writes, and its pieces are counted in 32 bits on the device.
 usp_status batch_disjoint(const char *who, int32_t n, const usp::CopyPlan *p, const int64_t *in_bytes,
                           const int64_t *out_bytes) {
+  uint64_t pieces = 0;
+  for (int32_t i = 0; i < n; ++i) pieces += (uint64_t)p[i].n_items * p[i].pieces_per_item;
+  if (pieces > 0xffffffffull) return fail(USP_ERR_UNSUPPORTED, "%s: too many pieces for one launch", who);
   for (int32_t i = 0; i < n; ++i)
     for (int32_t j = 0; j < n; ++j) {
       if (overlap(p[i].dst, out_bytes[i], p[j].src, in_bytes[j]))

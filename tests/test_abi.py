@@ -186,6 +186,16 @@ def test_zigzag_n_rejects(kw, status):
 
 
 @no_gpu
+def test_zigzag_n_rejects_more_pieces_than_one_launch_counts():
+    """Four every-rank extracts of 64 KiB rows (one row per piece), 2^31 pieces
+    each: the batch holds 2^33 pieces, beyond the device's 32-bit piece index.
+    (Validation only: the fake buffers are never touched.)"""
+    S = (1 << 31) - 32                           # below the row limit, divisible by 2 rd ud = 8
+    assert _zz_n(n=4, xs=F[:4], outs=F[4:8], heads=[256] * 4, S=S, D=128, r=-1, u=-1) == 2
+    assert b"too many pieces" in B.lib().usp_last_error_detail()
+
+
+@no_gpu
 def test_zigzag_n_rejects_null_arrays():
     x, o, h = _arrays(F[:3], F[3:6], [4, 2, 2])
     lib = B.lib()
