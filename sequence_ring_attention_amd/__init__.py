@@ -9,8 +9,14 @@ _BINDING_NAMES = {"usp_zigzag_extract", "usp_ulysses_a2a_layout", "usp_ring_attn
                   "usp_lse_merge", "usp_attn_fwd", "attn_desc", "UspError", "UspAttnDesc", "lib"}
 
 
+_API_NAMES = {"zigzag_extract", "attn", "rank_to_grid"}
+
+
 def __getattr__(name):
     if name in _BINDING_NAMES:
         from . import binding
         return getattr(binding, name)
+    if name in _API_NAMES:
+        from . import api
+        return getattr(api, name)
     raise AttributeError(name)
