@@ -514,7 +514,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share on a single MI355X; --gpus {args.gpus} is not "
-              "supported (no multi-GPU path in this build).", file=sys.stderr)
+              "supported: the library runs one GPU's share and has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
