@@ -250,8 +250,11 @@ usp_status usp_ulysses_a2a_layout_heads(const void *in, void *out, usp_dtype dty
  *   lse_step: fp32 (Hq, B, 2c), contiguous
  * Errors: USP_ERR_INVALID_ARG for a bad descriptor (see usp_attn_desc), null
  *   or misaligned pointers, ring_rank or step outside [0, cp);
- *   USP_ERR_UNSUPPORTED for head_dim other than 64/128, or cu_seqlens with
- *   causal = 0.
+ *   USP_ERR_UNSUPPORTED for head_dim other than 64/128, cu_seqlens with
+ *   causal = 0, or (bf16) a block whose 2c rows of one (batch, head) slice
+ *   span 4 GiB or more at the given row stride (the bf16 kernels address a
+ *   slice with 32-bit byte offsets; the head-major layout keeps it dense).
+ *   The backward entry points apply the same limit to Q's and dO's rows.
  */
 usp_status usp_ring_attn_step_fwd(const void *q, const void *k_all, const void *v_all,
                                   float *o_step, float *lse_step, const usp_attn_desc *desc,

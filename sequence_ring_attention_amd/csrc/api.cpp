@@ -401,6 +401,12 @@ usp_status usp_lse_merge(float *o_acc, float *lse_acc, const float *o_step, cons
 namespace {
 
 // Shared checks of the attention descriptor; fills the kernel arguments.
+// The bf16 kernels stage one (batch, head) slice of a share through a buffer
+// descriptor and 32-bit byte offsets, which must cover its L rows.
+bool rows_span_32bit(int64_t L, int64_t row_stride, int64_t e, int64_t head_dim) {
+  return (L - 1) * row_stride * e + head_dim * e <= (int64_t)0xffffffff;
+}
+
 usp_status attn_prepare(const void *q, const void *k, const void *v, const void *o, const float *lse,
                         const usp_attn_desc *d, int32_t ring_rank, bool all_ranks_ok,
                         usp::AttnArgs &a, const char *who) {
@@ -437,6 +443,11 @@ usp_status attn_prepare(const void *q, const void *k, const void *v, const void 
   for (int64_t s : strides)
     if (s < 0 || (s * e) % 16 != 0)
       return fail(USP_ERR_INVALID_ARG, "%s: strides must be >= 0 and keep 16-byte alignment", who);
+  if (d->dtype == USP_DTYPE_BF16 &&
+      (!rows_span_32bit(L, d->k.s, e, d->head_dim) || !rows_span_32bit(L, d->v.s, e, d->head_dim)))
+    return fail(USP_ERR_UNSUPPORTED, "%s: the %lld rows of a K/V block slice span 4 GiB or more at row stride "
+                "%lld (the head-major layout keeps them dense)", who, (long long)L,
+                (long long)(d->k.s > d->v.s ? d->k.s : d->v.s));
 
   a = usp::AttnArgs{};
   a.q = q;
@@ -506,6 +517,10 @@ usp_status bwd_prepare(const void *q, const void *k, const void *v, const void *
   const int64_t rows = stats_rows(d, ring_rank);
   if (rows >= kMaxStatsRows)
     return fail(USP_ERR_INVALID_ARG, "%s: %lld statistics rows (limit 2^29)", who, (long long)rows);
+  if (d->dtype == USP_DTYPE_BF16 && (!rows_span_32bit(a.L, d->q.s, 2, d->head_dim) ||
+                                     !rows_span_32bit(a.L, d->o.s, 2, d->head_dim)))
+    return fail(USP_ERR_UNSUPPORTED, "%s: the %lld rows of a Q/dO slice span 4 GiB or more (the head-major "
+                "layout keeps them dense)", who, (long long)a.L);
   b = usp::BwdArgs{};
   b.q = q;
   b.k = k;

@@ -238,6 +238,29 @@ def test_batched_copies_reach_the_runtime():
 
 
 @no_gpu
+def test_bf16_attention_rejects_rows_beyond_32_bit_offsets():
+    """A sequence-major (B, 2c, H, D) MHA share of 512K + 64 tokens with 32 heads:
+    a K/V slice spans just over 512K rows x 8 KiB = 4 GiB, beyond the bf16 kernels'
+    32-bit offsets, so the call is refused; the head-major layout (row
+    stride D) of the same share is accepted (it then fails only at launch,
+    there being no GPU).  fp32 kernels take 64-bit offsets and are not
+    limited.  Fake buffers: validation only."""
+    L, cp, H, D = (1 << 19) + 64, 4, 32, 128
+    lib = B.lib()
+    d = B.UspAttnDesc()
+    d.batch, d.seq_len, d.num_q_heads, d.num_kv_heads, d.head_dim = 1, L * cp, H, H, D
+    d.dtype, d.softmax_scale, d.causal, d.cp = 0, D ** -0.5, 1, cp
+    for st in (d.q, d.k, d.v, d.o):                      # (B, 2c, H, D)
+        st.s, st.h, st.b = H * D, D, L * H * D
+    d.kv_block_stride = L * H * D
+    assert lib.usp_attn_fwd(FAKE, FAKE2, FAKE3, 0x40000, 0x50000, ctypes.byref(d), 0, None) == 2
+    assert b"4 GiB" in lib.usp_last_error_detail()
+    for st in (d.q, d.k, d.v, d.o):                      # (H, B, 2c, D)
+        st.s, st.h, st.b = D, L * D, L * D
+    assert lib.usp_attn_fwd(FAKE, FAKE2, FAKE3, 0x40000, 0x50000, ctypes.byref(d), 0, None) == 3
+
+
+@no_gpu
 def test_valid_arguments_reach_the_runtime_and_report_hip_errors():
     """With no GPU present, a call that passes validation fails at launch with
     USP_ERR_HIP and a message, never a crash."""
@@ -269,6 +292,24 @@ def _step_bwd(d, r=0, t=0, **kw):
     a.update(kw)
     return B.lib().usp_ring_attn_step_bwd(a["q"], a["k"], a["v"], a["do"], a["stats"], a["dq"], a["dk"], a["dv"],
                                           ctypes.byref(d), r, t, None)
+
+
+@no_gpu
+def test_bf16_backward_rejects_q_rows_beyond_32_bit_offsets():
+    """K and V head-major (dense rows), Q and dO sequence-major with 32 heads
+    over just over 512K rows: the key-stationary passes' Q/dO slices span
+    4 GiB or more, so the backward is refused before launch."""
+    L, cp, H, D = (1 << 19) + 64, 4, 32, 128
+    d = B.UspAttnDesc()
+    d.batch, d.seq_len, d.num_q_heads, d.num_kv_heads, d.head_dim = 1, L * cp, H, 1, D
+    d.dtype, d.softmax_scale, d.causal, d.cp = 0, D ** -0.5, 1, cp
+    for st in (d.q, d.o):                                # (B, 2c, H, D)
+        st.s, st.h, st.b = H * D, D, L * H * D
+    for st in (d.k, d.v):                                # (Hkv, B, 2c, D)
+        st.s, st.h, st.b = D, L * D, L * D
+    d.kv_block_stride = L * D
+    assert _bwd(d) == 2
+    assert b"Q/dO" in B.lib().usp_last_error_detail()
 
 
 @no_gpu
