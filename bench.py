@@ -37,7 +37,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--ring-rank", type=int, default=0)
     p.add_argument("--ulysses-rank", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
