@@ -144,7 +144,7 @@ usp_status usp_zigzag_extract(const void *x, void *out, usp_dtype dtype, int64_t
  * Errors: as usp_zigzag_extract for every tensor, plus USP_ERR_INVALID_ARG
  *   for n outside [1, USP_MAX_COPY_BATCH], a null array, or an output whose
  *   byte extent overlaps any input's or another output's, and
- *   USP_ERR_UNSUPPORTED when the tensors together hold 2^32 or more 64 KiB
+ *   USP_ERR_UNSUPPORTED when the tensors together hold 2^32 or more 8 KiB
  *   copy pieces.
  */
 usp_status usp_zigzag_extract_n(int32_t n, const void *const *x, void *const *out, const int64_t *heads,
