@@ -302,6 +302,16 @@ usp_status ulysses_plan(const char *who, const void *in, void *out, usp_dtype dt
   p.row_bytes = (uint64_t)row_bytes;
   int64_t peers_per_item = 1;
   const uint32_t head_shift = log2_exact((uint64_t)row_bytes / 16);
+  if (!inverse && head_shift < 31) {
+    // source-major forward: a row is one token's heads of the chunk,
+    // contiguous in the source, scattered to the chunk's head planes
+    p.kind = usp::kUlyssesFwdRows;
+    p.n_items = (uint32_t)(G * batch * N);
+    p.row_bytes = (uint64_t)(nh * row_bytes);
+    p.dst_unit_bytes = (uint64_t)row_bytes;
+    p.src_row_bytes = (uint64_t)row_bytes;
+    p.grp_shift = head_shift;
+  }
   if (inverse && head_shift < 31) {
     // output-major inverse: a row is one token's heads of the chunk (all of
     // its heads when the chunk is the whole block), contiguous in the

@@ -36,6 +36,7 @@ struct RowMap {
   int64_t src_base, src_stride, dst_base, dst_stride;  // in rows
   int64_t split, src_jump, dst_jump;                   // rows t >= split add the jumps
   int64_t src_grp;                                     // source rows between the pieces of a gathered row
+  int64_t dst_grp;                                     // destination rows between the pieces of a scattered row
 };
 
 __device__ inline RowMap decode(const CopyPlan &P, uint32_t item) {
@@ -43,6 +44,7 @@ __device__ inline RowMap decode(const CopyPlan &P, uint32_t item) {
   m.split = INT64_MAX;
   m.src_jump = m.dst_jump = 0;
   m.src_grp = 0;
+  m.dst_grp = 0;
   if (P.kind == kZigzagFwd || P.kind == kZigzagInv) {
     const int64_t B = P.p[0], S = P.p[1], c = P.p[2], rd = P.p[3], ud = P.p[4], T = P.p[5];
     const int64_t r_fix = P.p[6], u_fix = P.p[7];
@@ -89,6 +91,23 @@ __device__ inline RowMap decode(const CopyPlan &P, uint32_t item) {
     m.dst_stride = 1;
     m.src_base = ((up * bs + b) * Ls) * hc + u * hb + h0 + hp;
     m.src_stride = hc;
+  } else if (P.kind == kUlyssesFwdRows) {
+    // item (g, b, peer u'); row t = token t of shard u': its heads
+    // u hb + h0 .. + nh, contiguous in the source (head rows count the
+    // offsets); head i of the row goes to output plane g nh + i (dst_grp
+    // rows apart), row b L + u' Ls + t
+    const int64_t bs = P.p[0], L = P.p[1], hc = P.p[2], N = P.p[3], hb = P.p[4], Ls = P.p[5];
+    const int64_t u_fix = P.p[6], h0 = P.p[7], nh = P.p[8];
+    int64_t rest = item;
+    const int64_t up = rest % N;
+    rest /= N;
+    const int64_t b = rest % bs, g = rest / bs;
+    const int64_t u = u_fix < 0 ? g : u_fix;
+    m.src_base = ((up * bs + b) * Ls) * hc + u * hb + h0;
+    m.src_stride = hc;
+    m.dst_base = (g * nh * bs + b) * L + up * Ls;
+    m.dst_stride = 1;
+    m.dst_grp = bs * L;
   } else if (P.kind == kUlyssesInvRows) {
     // item (g, b, peer group); row t = token t of output shard g: heads
     // u' hb + h0 .. + nh of one peer u' (np = N), or all hc heads when the
@@ -151,14 +170,18 @@ __device__ inline void copy_piece(const CopyPlan &P, uint32_t piece) {
         }
         const int64_t t = (int64_t)row0 + row;
         const bool second = t >= m.split;
-        // piece of a gathered row (0 unless grp_shift < 31) and its vector
+        // head row of a gathered or scattered row (0 unless grp_shift < 31)
+        // and the vector within it; a gathered row reads head rows from
+        // several source planes, a scattered one writes them to several
+        // destination planes
         const uint32_t grp = P.grp_shift < 31 ? col >> P.grp_shift : 0;
         const uint32_t gcol = col - (grp << (P.grp_shift & 31));
+        const bool scatter = P.kind == kUlyssesFwdRows;
         const int64_t srow = m.src_base + t * m.src_stride + grp * m.src_grp + (second ? m.src_jump : 0);
-        const int64_t drow = m.dst_base + t * m.dst_stride + (second ? m.dst_jump : 0);
+        const int64_t drow = m.dst_base + t * m.dst_stride + grp * m.dst_grp + (second ? m.dst_jump : 0);
         buf[k] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4 *>(P.src + srow * (int64_t)P.src_row_bytes) + gcol);
-        doff[k] = drow * (int64_t)P.dst_unit_bytes + (int64_t)col * 16;
+            reinterpret_cast<const u32x4 *>(P.src + srow * (int64_t)P.src_row_bytes) + (scatter ? col : gcol));
+        doff[k] = drow * (int64_t)P.dst_unit_bytes + (int64_t)(scatter ? gcol : col) * 16;
       }
     }
 #pragma unroll

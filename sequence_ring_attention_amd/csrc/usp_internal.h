@@ -23,6 +23,7 @@ enum CopyKind : int32_t {
   kUlyssesFwd = 2, // (N, bs, L/N, hc, hd) -> (G, nh, bs, L, hd)
   kUlyssesInv = 3, // (N, nh, bs, L, hd) -> (G, bs, L/N, hc, hd), the chunk's heads
   kUlyssesInvRows = 4, // the same, a row being one token's heads of the chunk in the output
+  kUlyssesFwdRows = 5, // kUlyssesFwd, a row being one token's heads of the chunk in the source
 };
 
 struct CopyPlan {
@@ -38,10 +39,11 @@ struct CopyPlan {
   uint64_t row_bytes;      // destination row
   uint64_t dst_unit_bytes; // unit of destination row offsets (row_bytes, or one head's hd elements)
   uint64_t src_row_bytes;  // source row (row_bytes, or one head's hd elements for kUlyssesInvRows)
-  uint32_t grp_shift;      // log2(16-byte vectors per source row) when a row gathers several, else 31
+  uint32_t grp_shift;      // log2(16-byte vectors per head row) when a row gathers (kUlyssesInvRows) or
+                           // scatters (kUlyssesFwdRows) head rows, else 31
   // zigzag: B, S (rows), chunk c, rd, ud, shard rows T, fixed ranks (or -1)
   // ulysses: bs, L, hc, N, hb = hc/N, Ls = L/N, fixed rank (or -1), h0, nh,
-  //          peers per item (kUlyssesInvRows)
+  //          peers per item (kUlyssesInvRows, kUlyssesFwdRows)
   int64_t p[10];
 };
 
