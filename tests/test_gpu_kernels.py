@@ -73,6 +73,7 @@ ULY_CASES = [  # N, bs, L, hc, hd, dtype
     (4, 2, 96, 8, 128, "bf16"),
     (3, 1, 30, 6, 8, "fp32"),
     (1, 2, 16, 4, 64, "bf16"),         # N = 1: plain (bs,L,hc,hd) -> (hc,bs,L,hd) transpose
+    (2, 2, 32, 4, 24, "bf16"),         # 48-byte heads (three vectors): the head-row copy kinds
 ]
 
 
@@ -153,6 +154,7 @@ ULYN_CASES = [  # N, bs, L, heads of each tensor, hd, dtype
     (2, 1, 64, (4, 2, 2), 64, "bf16"),
     (4, 2, 96, (8, 4, 4), 128, "bf16"),
     (3, 1, 30, (6, 3), 8, "fp32"),
+    (2, 1, 32, (4, 2), 24, "bf16"),    # 48-byte heads: the head-row copy kinds
 ]
 
 

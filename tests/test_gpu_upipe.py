@@ -21,7 +21,7 @@ LAYOUT_CASES = [  # B, Ls, hc, hd, dtype, N
     (1, 96, 8, 128, "bf16", 2),
     (2, 40, 12, 64, "bf16", 3),
     (1, 64, 8, 64, "fp32", 4),
-    (1, 32, 4, 24, "bf16", 2),    # 48-byte head rows: the head-row inverse
+    (1, 32, 4, 24, "bf16", 2),    # 48-byte head rows: the head-row copy kinds, forward and inverse
     (2, 17, 6, 128, "fp32", 1),
 ]
 
