@@ -52,6 +52,9 @@
 // most keys), and the Hq / Hkv query heads that read one KV head run back to
 // back on one XCD (workgroups are dealt to the 8 XCDs round-robin) so that
 // their K/V tiles are shared through that XCD's L2.
+#include <cstdlib>
+#include <cstring>
+
 #include "attn_tiles.h"
 #include "usp_internal.h"
 
@@ -65,16 +68,65 @@ using namespace tiles;
 
 constexpr float TAU = 8.0f;  // log2 headroom before the running max must move
 
+// K and V tiles of TB keys in LDS (TB = 32 or 64).
+template <int D, int TB>
+struct KvLds {
+  static constexpr int ROW = D * 2;                 // bytes per key row
+  static constexpr int CH = D / 8;                  // 16-byte chunks per row
+  static constexpr int TILE = TB * ROW;             // one K or V tile
+  static constexpr int STAGE = 2 * TILE;            // K then V
+  static constexpr int KEYS_PER_KIB = 1024 / ROW;   // rows one wave-wide direct load fills
+  static constexpr int KIB_PER_TILE = TILE / 1024;
+};
+
+// Issue one TB-key tile of a KV block (K or V) into LDS with buffer loads
+// straight to LDS.  Wave w fills KiB blocks w, w + NW, ...; the rows of
+// block i are those of block 0 plus a multiple of 16, which the XOR swizzle
+// (row bits 0..3) does not see, so one per-lane offset `voff0` (the logical
+// chunk that the swizzle places at the lane's 16 bytes) serves every block
+// and the rest of the address is a scalar.  The descriptor is bounded to the
+// block's extent.  When the share ends inside the tile, rows past it repeat
+// the last row (their logits are masked, probabilities zero).
+template <int D, int TB, int NW>
+__device__ inline void issue_kv_tile(char *tile, const char *blk, uint32_t extent, int64_t rowbytes, int k0, int L,
+                                     int wave, int lane, uint32_t voff0) {
+  using G = KvLds<D, TB>;
+  constexpr int NBLK = G::KIB_PER_TILE / NW;
+  constexpr int RSTEP = NW * G::KEYS_PER_KIB;
+  static_assert(G::KIB_PER_TILE % NW == 0 && RSTEP % 16 == 0, "every wave fills whole 16-row swizzle periods");
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(blk), 0, extent, RSRC_WORD3);
+  if (k0 + TB <= L) {
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(tile + (wave + NW * i) * 1024), 16, voff0,
+                                               (uint32_t)((k0 + RSTEP * i) * rowbytes), 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i) {
+      const int row = (wave + NW * i) * G::KEYS_PER_KIB + lane / G::CH;
+      const int lch = swz<D>(row, lane % G::CH);
+      const int key = min(k0 + row, L - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(tile + (wave + NW * i) * 1024), 16,
+                                               (uint32_t)(key * rowbytes + lch * 16), 0, 0, 0);
+    }
+  }
+}
+
 // PS: built for the per-sample split (the other build serves the split of the
-// whole stream and holds no per-sample state)
-template <int D, bool PARTIAL, int NW, bool PS>
-__global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
+// whole stream and holds no per-sample state).  TB: keys per tile, 64 (two
+// workgroups per CU: 64 KiB of LDS and up to 256 registers each) or 32
+// (three: 32 KiB and at most 168 registers, one logit accumulator and half
+// the probabilities live), so that three waves share each SIMD.
+template <int D, bool PARTIAL, int NW, bool PS, int TB>
+__global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int BM = 32 * NW;
+  constexpr int NBK = TB / 32;   // 32-key logit blocks per tile
+  using KL = KvLds<D, TB>;
   // one array per stage: reads of one stage and the direct loads filling the
   // other are then provably disjoint, and the compiler does not make the
   // reads wait for those loads
-  __shared__ __attribute__((aligned(1024))) char smem0[Lds<D>::STAGE];
-  __shared__ __attribute__((aligned(1024))) char smem1[Lds<D>::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem0[KL::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem1[KL::STAGE];
 
   // ---------------------------------------------------------- work item --
   const int bid = blockIdx.x;
@@ -105,7 +157,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
   const bool causal = a.causal != 0, packed = sm.packed();
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hh = lane >> 5;
   const int q0 = lt * BM;
   const int qrow = q0 + wave * 32 + n;
@@ -143,8 +195,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
     if (hi <= lo) {
       r.kt = r.ke = 0;
     } else {
-      r.kt = lo / BN;
-      r.ke = (hi + BN - 1) / BN;
+      r.kt = lo / TB;
+      r.ke = (hi + TB - 1) / TB;
     }
     // a key row i of block j is at or before position p iff i < count_le(j, p),
     // so "every key <= the first query" and "every key in the last query's
@@ -161,16 +213,13 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
 
   // ------------------------------------------------ global -> LDS tiles --
   // per-lane byte offsets (within a tile) of the direct loads; see issue_kv_tile
-  constexpr int CH = Lds<D>::CH;
-  constexpr int NBLK = Lds<D>::KIB_PER_TILE / NW;  // KiB blocks per wave per tile
   const int64_t kbytes = a.k_ss * 2, vbytes = a.v_ss * 2;
-  uint32_t kvoff[NBLK], vvoff[NBLK];
-#pragma unroll
-  for (int i = 0; i < NBLK; ++i) {
-    const int row = (wave + NW * i) * Lds<D>::KEYS_PER_KIB + lane / CH;
-    const int lch = swz<D>(row, lane % CH);
-    kvoff[i] = (uint32_t)(row * kbytes + lch * 16);
-    vvoff[i] = (uint32_t)(row * vbytes + lch * 16);
+  uint32_t kvoff0, vvoff0;
+  {
+    const int row = wave * KL::KEYS_PER_KIB + lane / KL::CH;
+    const int lch = swz<D>(row, lane % KL::CH);
+    kvoff0 = (uint32_t)(row * kbytes + lch * 16);
+    vvoff0 = (uint32_t)(row * vbytes + lch * 16);
   }
   const char *const kbase = static_cast<const char *>(a.k) + 2 * (b * a.k_sb + kvh * a.k_sh);
   const char *const vbase = static_cast<const char *>(a.v) + 2 * (b * a.v_sb + kvh * a.v_sh);
@@ -178,8 +227,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
   const uint32_t v_extent = (uint32_t)((L - 1) * vbytes + 2 * D);
   auto issue_tile = [&](int j, int k0, int stg) {
     char *const st = stg == 0 ? smem0 : smem1;
-    issue_tile_lds<D, NW>(st, kbase + 2 * j * a.kv_blk, k_extent, kbytes, k0, L, wave, lane, kvoff);
-    issue_tile_lds<D, NW>(st + Lds<D>::TILE, vbase + 2 * j * a.kv_blk, v_extent, vbytes, k0, L, wave, lane, vvoff);
+    issue_kv_tile<D, TB, NW>(st, kbase + 2 * j * a.kv_blk, k_extent, kbytes, k0, L, wave, lane, kvoff0);
+    issue_kv_tile<D, TB, NW>(st + KL::TILE, vbase + 2 * j * a.kv_blk, v_extent, vbytes, k0, L, wave, lane, vvoff0);
   };
   auto wait_tiles = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
@@ -191,7 +240,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
   const int sig = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
   int koff[D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = sig * Lds<D>::ROW + swz<D>(sig, 2 * ks + hh) * 16;
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = sig * KL::ROW + swz<D>(sig, 2 * ks + hh) * 16;
   const int tg = lane >> 4, tr = (lane >> 2) & 3, tq = lane & 3;
   int voff[D / 32][2];
 #pragma unroll
@@ -199,7 +248,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int row = 8 * (tg >> 1) + 4 * e + tr;
-      voff[mb][e] = row * Lds<D>::ROW + swz<D>(row, 4 * mb + 2 * (tg & 1) + (tq >> 1)) * 16 + (tq & 1) * 8;
+      voff[mb][e] = row * KL::ROW + swz<D>(row, 4 * mb + 2 * (tg & 1) + (tq >> 1)) * 16 + (tq & 1) * 8;
     }
   }
 
@@ -224,44 +273,50 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
     int t_nxt = t;
     StepRange nxt = cur;
     advance(t_nxt, nxt);
-    if (t_nxt < a.t_hi) issue_tile(nxt.j, nxt.kt * BN, STG ^ 1);
+    if (t_nxt < a.t_hi) issue_tile(nxt.j, nxt.kt * TB, STG ^ 1);
 
     const char *const sK = STG == 0 ? smem0 : smem1;
-    const char *const sV = sK + Lds<D>::TILE;
-    const int k0 = cur.kt * BN;
+    const char *const sV = sK + KL::TILE;
+    const int k0 = cur.kt * TB;
     // tile class: every (query, key) pair of the workgroup visible?
-    const bool full = __builtin_amdgcn_readfirstlane((k0 >= cur.flo) & (k0 + BN <= cur.fhi));
+    const bool full = __builtin_amdgcn_readfirstlane((k0 >= cur.flo) & (k0 + TB <= cur.fhi));
 
-    // S^T = K Q^T for two 32-key blocks.  The K rows of k-step ks + AH are
-    // read while k-step ks's two products run, and the products alternate
-    // between the two accumulators, so neither chain waits on the other.
-    f32x16 S0 = f32x16{}, S1 = f32x16{};
-    __builtin_amdgcn_s_setprio(1);  // keep the matrix core fed while the SIMD's other wave runs softmax
+    // S^T = K Q^T for the tile's NBK 32-key blocks.  The K rows of k-step
+    // ks + AH are read while k-step ks's products run, and the products
+    // alternate between the blocks' accumulators, so no chain waits on
+    // another.
+    f32x16 S[NBK];
+#pragma unroll
+    for (int kb = 0; kb < NBK; ++kb) S[kb] = f32x16{};
+    __builtin_amdgcn_s_setprio(1);  // keep the matrix core fed while the SIMD's other waves run softmax
     {
       constexpr int NKS = D / 16, AH = 3;
-      bf16x8 kr[AH + 1][2];
+      bf16x8 kr[AH + 1][NBK];
 #pragma unroll
       for (int i = 0; i < AH; ++i) {
-        kr[i][0] = *reinterpret_cast<const bf16x8 *>(sK + koff[i]);
-        kr[i][1] = *reinterpret_cast<const bf16x8 *>(sK + koff[i] + 32 * Lds<D>::ROW);
+#pragma unroll
+        for (int kb = 0; kb < NBK; ++kb)
+          kr[i][kb] = *reinterpret_cast<const bf16x8 *>(sK + koff[i] + 32 * kb * KL::ROW);
       }
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         if (ks + AH < NKS) {
-          kr[(ks + AH) % (AH + 1)][0] = *reinterpret_cast<const bf16x8 *>(sK + koff[ks + AH]);
-          kr[(ks + AH) % (AH + 1)][1] = *reinterpret_cast<const bf16x8 *>(sK + koff[ks + AH] + 32 * Lds<D>::ROW);
+#pragma unroll
+          for (int kb = 0; kb < NBK; ++kb)
+            kr[(ks + AH) % (AH + 1)][kb] = *reinterpret_cast<const bf16x8 *>(sK + koff[ks + AH] + 32 * kb * KL::ROW);
         }
-        S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[ks % (AH + 1)][0], qf[ks], S0, 0, 0, 0);
-        S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[ks % (AH + 1)][1], qf[ks], S1, 0, 0, 0);
+#pragma unroll
+        for (int kb = 0; kb < NBK; ++kb)
+          S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[ks % (AH + 1)][kb], qf[ks], S[kb], 0, 0, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * AH, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, NBK * AH, 0);
 #pragma unroll
       for (int i = 0; i < NKS - AH; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NBK, 0);
+        if (NBK == 2) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * AH, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NBK * AH, 0);
     }
     __builtin_amdgcn_s_setprio(0);
 
@@ -273,32 +328,38 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kc = 16 * (r / 8) + (r % 8);
-        S0[r] = ((kc >= vlo) & (kc < vhi)) ? S0[r] : -INFINITY;
-        S1[r] = ((kc + 32 >= vlo) & (kc + 32 < vhi)) ? S1[r] : -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NBK; ++kb)
+          S[kb][r] = ((kc + 32 * kb >= vlo) & (kc + 32 * kb < vhi)) ? S[kb][r] : -INFINITY;
       }
     }
 
     // online softmax (base 2, scale folded in) against the running reference
     // m_run.  The tile's row max is only taken when some row has no reference
-    // yet or when a probability left the safe range (a lane's sum of 32 is
-    // not below 2^64, which also catches inf); otherwise the probabilities of
-    // the stale reference are used as they are, which changes nothing but
-    // the reference point of the final division.  When the max is taken, the
-    // reference only moves if the tile max exceeds it by more than 2^TAU.
-    bf16x8 pf[4];
+    // yet or when a probability left the safe range (a lane's sum of its
+    // probabilities is not below 2^64, which also catches inf); otherwise the
+    // probabilities of the stale reference are used as they are, which
+    // changes nothing but the reference point of the final division.  When
+    // the max is taken, the reference only moves if the tile max exceeds it
+    // by more than 2^TAU.
+    bf16x8 pf[2 * NBK];
     float ps;
     auto probs = [&](float m_use) {
       // the row sum takes the unrounded probabilities: lse is exact to fp32
-      // rounding, while O's weights are their bf16 roundings
+      // rounding, while O's weights are their bf16 roundings.  Two partial
+      // sums keep two add chains.
       float ps0 = 0.0f, ps1 = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[r], sl2, -m_use));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[r], sl2, -m_use));
-        ps0 += p0;
-        ps1 += p1;
-        pf[r / 8][r % 8] = (__bf16)p0;
-        pf[2 + r / 8][r % 8] = (__bf16)p1;
+      for (int kb = 0; kb < NBK; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], sl2, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r + 1], sl2, -m_use));
+          ps0 += p0;
+          ps1 += p1;
+          pf[2 * kb + r / 8][r % 8] = (__bf16)p0;
+          pf[2 * kb + r / 8][r % 8 + 1] = (__bf16)p1;
+        }
       }
       ps = ps0 + ps1;
     };
@@ -308,11 +369,12 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
       need_max = __builtin_amdgcn_ballot_w64(!(ps < 0x1p64f)) != 0;
     }
     if (need_max) {  // wave-uniform
-      float mx = S0[0];
+      float mx = S[0][0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S0[r]);
+      for (int kb = 0; kb < NBK; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S1[r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
+      }
       mx = partner_max(mx) * sl2;
       if (__builtin_amdgcn_ballot_w64(mx > m_run + TAU) != 0) {  // some row's reference moves: rescale
         const float m_new = fmaxf(m_run, mx);
@@ -332,17 +394,17 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
     // chains interleave); the next group's V operands are read meanwhile
     auto read_v = [&](int mb, int p) {
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4 *)(const_cast<char *>(sV) + voff[mb][0] + p * 16 * Lds<D>::ROW));
+          (__attribute__((address_space(3))) s16x4 *)(const_cast<char *>(sV) + voff[mb][0] + p * 16 * KL::ROW));
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4 *)(const_cast<char *>(sV) + voff[mb][1] + p * 16 * Lds<D>::ROW));
+          (__attribute__((address_space(3))) s16x4 *)(const_cast<char *>(sV) + voff[mb][1] + p * 16 * KL::ROW));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     bf16x8 vt[2][D / 32];
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) vt[0][mb] = read_v(mb, 0);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      if (p + 1 < 4) {
+    for (int p = 0; p < 2 * NBK; ++p) {
+      if (p + 1 < 2 * NBK) {
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb) vt[(p + 1) & 1][mb] = read_v(mb, p + 1);
       }
@@ -350,7 +412,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
       for (int mb = 0; mb < D / 32; ++mb)
         O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[p & 1][mb], pf[p], O[mb], 0, 0, 0);
     }
-    schedule_tr_products<4 * (D / 32), D / 32>();
+    schedule_tr_products<2 * NBK * (D / 32), D / 32>();
     __builtin_amdgcn_s_setprio(0);
     wait_tiles();
     __syncthreads();
@@ -359,7 +421,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
   };
 
   // prologue: tile 0 into stage 0
-  if (t < a.t_hi) issue_tile(cur.j, cur.kt * BN, 0);
+  if (t < a.t_hi) issue_tile(cur.j, cur.kt * TB, 0);
   wait_tiles();
   __syncthreads();
   while (t < a.t_hi) {
@@ -412,12 +474,34 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a) {
 
 }  // namespace
 
-template <int D, int NW, bool PS>
+template <int D, int NW, bool PS, int TB>
 void launch_one(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t stream) {
   if (a.partial)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, true, NW, PS>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, true, NW, PS, TB>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, false, NW, PS>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, false, NW, PS, TB>), grid, block, 0, stream, a);
+}
+
+template <int D, int NW, bool PS>
+void launch_tb(const AttnArgs &a, int tile, dim3 grid, dim3 block, hipStream_t stream) {
+  if (tile == 32)
+    launch_one<D, NW, PS, 32>(a, grid, block, stream);
+  else
+    launch_one<D, NW, PS, 64>(a, grid, block, stream);
+}
+
+// Keys per tile: 64, or 32 with USP_WALK_TILE=32 in the environment (the
+// tests run both tilings).  32-key tiles put three workgroups on a CU
+// instead of two.  They ran the whole 16-head block of the 128K-token hybrid
+// share 0.5-1.3% faster, but a 4096-token share 2.5-5% slower, and the same
+// share in head chunks 3-15% slower: each launch's last round of
+// workgroups, three times as long-lived per slot, leaves more CUs idle at
+// its tail.  The tiling sets where the running max moves, so the two give
+// results that differ by rounding; the variable is read at each launch, and
+// head-chunked and whole-block runs are bitwise equal under one setting.
+int walk_tile() {
+  const char *e = std::getenv("USP_WALK_TILE");
+  return e && std::strcmp(e, "32") == 0 ? 32 : 64;
 }
 
 template <int NW>
@@ -430,10 +514,11 @@ hipError_t launch_nw(AttnArgs a, int head_dim, hipStream_t stream) {
   if (blocks == 0) return hipSuccess;
   const dim3 grid((uint32_t)blocks), block(64 * NW);
   const bool ps = a.sm.per_sample != 0;
+  const int tile = walk_tile();
   if (head_dim == 128)
-    ps ? launch_one<128, NW, true>(a, grid, block, stream) : launch_one<128, NW, false>(a, grid, block, stream);
+    ps ? launch_tb<128, NW, true>(a, tile, grid, block, stream) : launch_tb<128, NW, false>(a, tile, grid, block, stream);
   else
-    ps ? launch_one<64, NW, true>(a, grid, block, stream) : launch_one<64, NW, false>(a, grid, block, stream);
+    ps ? launch_tb<64, NW, true>(a, tile, grid, block, stream) : launch_tb<64, NW, false>(a, tile, grid, block, stream);
   return hipGetLastError();
 }
 
