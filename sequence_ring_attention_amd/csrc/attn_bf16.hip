@@ -159,10 +159,29 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hh = lane >> 5;
-  const int q0 = lt * BM;
+  // Rows [q0, qend) of the share.  Under the per-sample split the share is a
+  // run of pieces, two per sample (its chunks r and 2 cp - 1 - r, m rows
+  // each), and tiles are cut at piece starts, so a tile's rows lie in one
+  // sample and one chunk and its key range holds no other sample's keys.
+  int q0, qend;
+  if (PS) {
+    int lo = 0, hi = a.sm.nseq;  // the sample n with ps_tiles[n] <= lt < ps_tiles[n + 1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.ps_tiles[mid] <= lt) lo = mid; else hi = mid;
+    }
+    const int s0 = a.sm.cu[lo], m = (a.sm.cu[lo + 1] - s0) / (2 * a.cp);
+    const int tp = (m + BM - 1) / BM, k = lt - a.ps_tiles[lo], piece = k >= tp ? 1 : 0;
+    const int pstart = s0 / a.cp + piece * m;
+    q0 = pstart + (k - piece * tp) * BM;
+    qend = min(q0 + BM, pstart + m);
+  } else {
+    q0 = lt * BM;
+    qend = min(q0 + BM, L);
+  }
   const int qrow = q0 + wave * 32 + n;
-  const bool qvalid = qrow < L;
-  const int qlast = min(q0 + BM, L) - 1;
+  const bool qvalid = qrow < qend;
+  const int qlast = qend - 1;
   const int qpos_min = sm.pos(rank, q0);
   const int qpos_max = sm.pos(rank, qlast);
   const int my_qpos = qvalid ? sm.pos(rank, qrow) : -1;
@@ -494,8 +513,8 @@ void launch_tb(const AttnArgs &a, int tile, dim3 grid, dim3 block, hipStream_t s
 // tests run both tilings).  32-key tiles put three workgroups on a CU
 // instead of two.  They ran the whole 16-head block of the 128K-token hybrid
 // share 0.5-1.3% faster, but a 4096-token share 2.5-5% slower, and the same
-// share in head chunks 3-15% slower: each launch's last round of
-// workgroups, three times as long-lived per slot, leaves more CUs idle at
+// share in head chunks 3-15% slower: a workgroup lives about 1.5 times as
+// long, so each launch's last, partly filled round leaves more CUs idle at
 // its tail.  The tiling sets where the running max moves, so the two give
 // results that differ by rounding; the variable is read at each launch, and
 // head-chunked and whole-block runs are bitwise equal under one setting.
@@ -508,6 +527,14 @@ template <int NW>
 hipError_t launch_nw(AttnArgs a, int head_dim, hipStream_t stream) {
   constexpr int BM = 32 * NW;
   a.n_qtiles = (a.L + BM - 1) / BM;
+  if (a.sm.per_sample) {  // tiles of each sample's two chunk pieces (m rows each)
+    a.ps_tiles[0] = 0;
+    for (int n = 0; n < a.sm.nseq; ++n) {
+      const int m = (a.sm.cu[n + 1] - a.sm.cu[n]) / (2 * a.cp);
+      a.ps_tiles[n + 1] = a.ps_tiles[n] + 2 * ((m + BM - 1) / BM);
+    }
+    a.n_qtiles = a.ps_tiles[a.sm.nseq];
+  }
   const int64_t groups = (int64_t)a.n_ranks * a.n_qtiles * a.B * a.Hkv;
   a.xcd_remap = groups % 8 == 0;
   const int64_t blocks = groups * a.G;

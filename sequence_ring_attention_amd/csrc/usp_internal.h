@@ -107,7 +107,11 @@ struct AttnArgs {
   int32_t n_ranks;    // ranks in this launch (1 or cp)
   int32_t xcd_remap;  // 1: group blocks sharing a KV head on one XCD
   Samples sm;         // packed samples and the split of the shares
+  // Per-sample split, bf16 walk: query tiles before sample n's rows (each
+  // sample's two chunk pieces cut into tiles of their own); set at launch.
+  int32_t ps_tiles[kMaxSeqs + 1];
 };
+static_assert(sizeof(AttnArgs) <= 4096, "kernel arguments above 4 KiB");
 
 hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t stream);
 hipError_t launch_attn_fp32(const AttnArgs &a, int head_dim, hipStream_t stream);
