@@ -165,16 +165,7 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
   // sample and one chunk and its key range holds no other sample's keys.
   int q0, qend;
   if (PS) {
-    int lo = 0, hi = a.sm.nseq;  // the sample n with ps_tiles[n] <= lt < ps_tiles[n + 1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.ps_tiles[mid] <= lt) lo = mid; else hi = mid;
-    }
-    const int s0 = a.sm.cu[lo], m = (a.sm.cu[lo + 1] - s0) / (2 * a.cp);
-    const int tp = (m + BM - 1) / BM, k = lt - a.ps_tiles[lo], piece = k >= tp ? 1 : 0;
-    const int pstart = s0 / a.cp + piece * m;
-    q0 = pstart + (k - piece * tp) * BM;
-    qend = min(q0 + BM, pstart + m);
+    piece_tile(a.sm, a.ps_tiles, a.cp, BM, lt, q0, qend);
   } else {
     q0 = lt * BM;
     qend = min(q0 + BM, L);
@@ -527,14 +518,7 @@ template <int NW>
 hipError_t launch_nw(AttnArgs a, int head_dim, hipStream_t stream) {
   constexpr int BM = 32 * NW;
   a.n_qtiles = (a.L + BM - 1) / BM;
-  if (a.sm.per_sample) {  // tiles of each sample's two chunk pieces (m rows each)
-    a.ps_tiles[0] = 0;
-    for (int n = 0; n < a.sm.nseq; ++n) {
-      const int m = (a.sm.cu[n + 1] - a.sm.cu[n]) / (2 * a.cp);
-      a.ps_tiles[n + 1] = a.ps_tiles[n] + 2 * ((m + BM - 1) / BM);
-    }
-    a.n_qtiles = a.ps_tiles[a.sm.nseq];
-  }
+  if (a.sm.per_sample) a.n_qtiles = fill_piece_tiles(a.sm, a.cp, BM, a.ps_tiles);
   const int64_t groups = (int64_t)a.n_ranks * a.n_qtiles * a.B * a.Hkv;
   a.xcd_remap = groups % 8 == 0;
   const int64_t blocks = groups * a.G;

@@ -170,10 +170,17 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, hh = lane >> 5;
-  const int q0 = lt * BM;
+  // rows [q0, qend); per-sample shares take tiles cut at their pieces
+  int q0, qend;
+  if (PS) {
+    piece_tile(a.sm, a.ps_tiles, a.cp, BM, lt, q0, qend);
+  } else {
+    q0 = lt * BM;
+    qend = min(q0 + BM, L);
+  }
   const int qrow = q0 + wave * 32 + n;
-  const bool qvalid = qrow < L;
-  const int qlast = min(q0 + BM, L) - 1;
+  const bool qvalid = qrow < qend;
+  const int qlast = qend - 1;
   const int qpos_min = sm.pos(rank, q0);
   const int qpos_max = sm.pos(rank, qlast);
   const int my_qpos = qvalid ? sm.pos(rank, qrow) : -1;
@@ -741,6 +748,7 @@ template <int D>
 hipError_t launch_d(BwdArgs a, hipStream_t stream) {
   // dQ pass
   a.n_tiles = (a.L + BM - 1) / BM;
+  if (a.sm.per_sample) a.n_tiles = fill_piece_tiles(a.sm, a.cp, BM, a.ps_tiles);
   const int64_t groups = (int64_t)a.n_ranks * a.n_tiles * a.B * a.Hkv;
   a.xcd_remap = groups % 8 == 0;
   const int64_t q_blocks = groups * a.G;

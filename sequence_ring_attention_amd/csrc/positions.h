@@ -84,4 +84,33 @@ struct ShareMap {
   __device__ int seg_end(int p) const { return sm->cu[sample_of(p) + 1]; }
 };
 
+// Query tiles of a per-sample share cut at its pieces: the share holds two
+// pieces per sample (its chunks r and 2 cp - 1 - r, m = length / (2 cp)
+// rows each), and each piece is cut into tiles of at most `rows` rows, so a
+// tile's rows lie in one sample and one chunk.  tiles[n] = the tiles before
+// sample n; returns their total.  Host side, at launch.
+inline int fill_piece_tiles(const Samples &s, int cp, int rows, int32_t *tiles) {
+  tiles[0] = 0;
+  for (int n = 0; n < s.nseq; ++n) {
+    const int m = (s.cu[n + 1] - s.cu[n]) / (2 * cp);
+    tiles[n + 1] = tiles[n] + 2 * ((m + rows - 1) / rows);
+  }
+  return tiles[s.nseq];
+}
+
+// Rows [q0, qend) of tile lt under the cut above (0 <= lt < tiles[nseq]).
+__device__ inline void piece_tile(const Samples &s, const int32_t *tiles, int cp, int rows, int lt, int &q0,
+                                  int &qend) {
+  int lo = 0, hi = s.nseq;  // the sample n with tiles[n] <= lt < tiles[n + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tiles[mid] <= lt) lo = mid; else hi = mid;
+  }
+  const int s0 = s.cu[lo], m = (s.cu[lo + 1] - s0) / (2 * cp);
+  const int tp = (m + rows - 1) / rows, k = lt - tiles[lo], piece = k >= tp ? 1 : 0;
+  const int pstart = s0 / cp + piece * m;
+  q0 = pstart + (k - piece * tp) * rows;
+  qend = min(q0 + rows, pstart + m);
+}
+
 }  // namespace usp

@@ -107,9 +107,7 @@ struct AttnArgs {
   int32_t n_ranks;    // ranks in this launch (1 or cp)
   int32_t xcd_remap;  // 1: group blocks sharing a KV head on one XCD
   Samples sm;         // packed samples and the split of the shares
-  // Per-sample split, bf16 walk: query tiles before sample n's rows (each
-  // sample's two chunk pieces cut into tiles of their own); set at launch.
-  int32_t ps_tiles[kMaxSeqs + 1];
+  int32_t ps_tiles[kMaxSeqs + 1];  // per-sample split, bf16: fill_piece_tiles at launch
 };
 static_assert(sizeof(AttnArgs) <= 4096, "kernel arguments above 4 KiB");
 
@@ -145,7 +143,9 @@ struct BwdArgs {
   int32_t n_tiles;    // set by the launchers
   int32_t xcd_remap;  // set by the launchers
   Samples sm;         // packed samples and the split of the shares
+  int32_t ps_tiles[kMaxSeqs + 1];  // per-sample split, dQ pass: fill_piece_tiles at launch
 };
+static_assert(sizeof(BwdArgs) <= 4096, "kernel arguments above 4 KiB");
 
 struct PrepArgs {
   const void *o;
