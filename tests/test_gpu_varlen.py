@@ -81,11 +81,22 @@ ATTN_CASES = {  # name: B, S, H, Hkv, D, cp, cu, dtype
     "bf16_cp4_gqa": (1, 2048, 4, 2, 128, 4, [0, 64, 72, 512, 1024, 1032, 2048], "bf16"),
     "bf16_cp3_d64_mqa_b2": (2, 1536, 4, 1, 64, 3, [0, 6, 600, 606, 1536], "bf16"),
     "fp32_cp2": (1, 96, 2, 2, 64, 2, [0, 4, 28, 96], "fp32"),
+    # 108 samples: pieces of 1, 65, 128 and 129 rows among many short ones,
+    # so the query tiles cut at pieces take every shape
+    "bf16_cp2_108_samples": (1, None, 2, 1, 64, 2, "many", "bf16"),
 }
+
+
+def _many_samples_cu():
+    lens = [4, 512, 516, 260, 8, 132, 4, 1028] + [4 * (1 + (7 * i) % 23) for i in range(100)]
+    return [0] + np.cumsum(lens).tolist()
 
 
 def _prepare(name):
     Bn, S, H, Hkv, D, cp, cu, dt = ATTN_CASES[name]
+    if cu == "many":
+        cu = _many_samples_cu()
+        S = cu[-1]
     dev = device()
     seed = 800 + sorted(ATTN_CASES).index(name) * 10
     q, k, v = inputs.qkv(Bn, S, H, Hkv, D, dt, seed)
