@@ -99,8 +99,9 @@ inline int fill_piece_tiles(const Samples &s, int cp, int rows, int32_t *tiles) 
 }
 
 // Rows [q0, qend) of tile lt under the cut above (0 <= lt < tiles[nseq]).
-__device__ inline void piece_tile(const Samples &s, const int32_t *tiles, int cp, int rows, int lt, int &q0,
-                                  int &qend) {
+// Host-callable too, for the CPU test of the map.
+__host__ __device__ inline void piece_tile(const Samples &s, const int32_t *tiles, int cp, int rows, int lt, int &q0,
+                                           int &qend) {
   int lo = 0, hi = s.nseq;  // the sample n with tiles[n] <= lt < tiles[n + 1]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -110,7 +111,7 @@ __device__ inline void piece_tile(const Samples &s, const int32_t *tiles, int cp
   const int tp = (m + rows - 1) / rows, k = lt - tiles[lo], piece = k >= tp ? 1 : 0;
   const int pstart = s0 / cp + piece * m;
   q0 = pstart + (k - piece * tp) * rows;
-  qend = min(q0 + rows, pstart + m);
+  qend = q0 + rows < pstart + m ? q0 + rows : pstart + m;
 }
 
 }  // namespace usp
