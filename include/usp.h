@@ -290,10 +290,6 @@ usp_status usp_lse_merge(float *o_acc, float *lse_acc, const float *o_step,
  * ring_rank = -1 runs every rank in one launch: rank r's query share starts
  * r * desc->q_rank_stride elements after q, its output r * desc->o_rank_stride
  * after o, and lse becomes (cp, Hq, B, 2c).
- * Tiling (bf16): 64-key K/V tiles; the environment variable USP_WALK_TILE=32,
- * read at each call, selects 32-key tiles (three workgroups per CU instead
- * of two).  The two tilings agree within rounding, not bitwise.  This also
- * holds for usp_ring_attn_step_fwd.
  * Errors: as usp_ring_attn_step_fwd, and ring_rank outside [-1, cp).
  */
 usp_status usp_attn_fwd(const void *q, const void *k_all, const void *v_all, void *o,

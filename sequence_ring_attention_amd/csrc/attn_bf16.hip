@@ -52,9 +52,6 @@
 // most keys), and the Hq / Hkv query heads that read one KV head run back to
 // back on one XCD (workgroups are dealt to the 8 XCDs round-robin) so that
 // their K/V tiles are shared through that XCD's L2.
-#include <cstdlib>
-#include <cstring>
-
 #include "attn_tiles.h"
 #include "usp_internal.h"
 
@@ -492,27 +489,14 @@ void launch_one(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t stream) {
     hipLaunchKernelGGL((attn_bf16_kernel<D, false, NW, PS, TB>), grid, block, 0, stream, a);
 }
 
-template <int D, int NW, bool PS>
-void launch_tb(const AttnArgs &a, int tile, dim3 grid, dim3 block, hipStream_t stream) {
-  if (tile == 32)
-    launch_one<D, NW, PS, 32>(a, grid, block, stream);
-  else
-    launch_one<D, NW, PS, 64>(a, grid, block, stream);
-}
-
-// Keys per tile: 64, or 32 with USP_WALK_TILE=32 in the environment (the
-// tests run both tilings).  32-key tiles put three workgroups on a CU
-// instead of two.  They ran the whole 16-head block of the 128K-token hybrid
-// share 0.5-1.3% faster, but a 4096-token share 2.5-5% slower, and the same
-// share in head chunks 3-15% slower: a workgroup lives about 1.5 times as
-// long, so each launch's last, partly filled round leaves more CUs idle at
-// its tail.  The tiling sets where the running max moves, so the two give
-// results that differ by rounding; the variable is read at each launch, and
-// head-chunked and whole-block runs are bitwise equal under one setting.
-int walk_tile() {
-  const char *e = std::getenv("USP_WALK_TILE");
-  return e && std::strcmp(e, "32") == 0 ? 32 : 64;
-}
+// Keys per tile: 64.  The kernel also builds with 32-key tiles (TB = 32:
+// 168 registers and 32 KiB of LDS, three workgroups per CU instead of two).
+// Measured, those ran the whole 16-head block of the 128K-token hybrid share
+// 0.5-1.3% faster but a 4096-token share 2.5-5% slower and the share in head
+// chunks 3-15% slower (a workgroup lives about 1.5 times as long, so each
+// launch's last, partly filled round idles more of the chip), and they are
+// not used.
+constexpr int kWalkTile = 64;
 
 template <int NW>
 hipError_t launch_nw(AttnArgs a, int head_dim, hipStream_t stream) {
@@ -525,11 +509,12 @@ hipError_t launch_nw(AttnArgs a, int head_dim, hipStream_t stream) {
   if (blocks == 0) return hipSuccess;
   const dim3 grid((uint32_t)blocks), block(64 * NW);
   const bool ps = a.sm.per_sample != 0;
-  const int tile = walk_tile();
   if (head_dim == 128)
-    ps ? launch_tb<128, NW, true>(a, tile, grid, block, stream) : launch_tb<128, NW, false>(a, tile, grid, block, stream);
+    ps ? launch_one<128, NW, true, kWalkTile>(a, grid, block, stream)
+       : launch_one<128, NW, false, kWalkTile>(a, grid, block, stream);
   else
-    ps ? launch_tb<64, NW, true>(a, tile, grid, block, stream) : launch_tb<64, NW, false>(a, tile, grid, block, stream);
+    ps ? launch_one<64, NW, true, kWalkTile>(a, grid, block, stream)
+       : launch_one<64, NW, false, kWalkTile>(a, grid, block, stream);
   return hipGetLastError();
 }
 

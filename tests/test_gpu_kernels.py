@@ -292,19 +292,8 @@ def _out(P, shape, dt, dev):
     return big[..., 1:1 + H, :], ok
 
 
-# The bf16 walk takes 64-key tiles, or 32-key tiles under USP_WALK_TILE=32:
-# every small case runs both tilings.
-WALK_TILES = ["32", "64"]
-
-
-@pytest.fixture(params=WALK_TILES, ids=lambda t: f"tile{t}")
-def walk_tile(request, monkeypatch):
-    monkeypatch.setenv("USP_WALK_TILE", request.param)
-    return request.param
-
-
 @pytest.mark.parametrize("name", sorted(ATTN_CASES))
-def test_ring_steps_and_merge(name, walk_tile):
+def test_ring_steps_and_merge(name):
     P = _prepare(name)
     dev, cp, H, Bn, L, D = P["dev"], P["cp"], P["H"], P["Bn"], P["L"], P["D"]
     desc = B.attn_desc(P["S"], cp, P["qs"][0], P["ks"], P["vs"], layout=_layout(P), causal=P["causal"],
@@ -331,7 +320,7 @@ def test_ring_steps_and_merge(name, walk_tile):
 
 
 @pytest.mark.parametrize("name", sorted(ATTN_CASES))
-def test_ring_walk_per_rank_and_all_ranks(name, walk_tile):
+def test_ring_walk_per_rank_and_all_ranks(name):
     P = _prepare(name)
     dev, cp, H, Bn, L, D = P["dev"], P["cp"], P["H"], P["Bn"], P["L"], P["D"]
     dt = torch.float32 if P["dt"] == "fp32" else torch.bfloat16
@@ -361,7 +350,7 @@ def test_ring_walk_per_rank_and_all_ranks(name, walk_tile):
                     f"{name} all-ranks r{r}", out_bf16=P["dt"] == "bf16")
 
 
-def test_first_row_is_exactly_v0(walk_tile):
+def test_first_row_is_exactly_v0():
     """Position 0 sees only itself: o = v_0 exactly (after bf16 rounding of an
     exact value) and lse = scale * q0.k0."""
     dev = device()
