@@ -14,26 +14,22 @@ import numpy as np
 # Algorithm 2 ([USP review] section 三, "Algorithm 2: 负载均衡序列分段")
 # --------------------------------------------------------------------------
 
-def _chunk(seq, n):
-    """``seq.chunk(n)`` for a length divisible by n (sizes that do not divide
-    are rejected, as no page says how to pad)."""
-    if len(seq) % n != 0:
-        raise ValueError(f"length {len(seq)} does not split into {n} equal chunks")
-    return np.split(seq, n)
-
-
 def zigzag_local_positions(S, rd, ud, ring_rank, ulysses_rank):
     """Global token positions held by ring rank ``ring_rank`` / Ulysses rank
     ``ulysses_rank``, in local order.
 
-    Follows Algorithm 2 step by step on the position sequence 0..S-1:
-    split into 2*rd chunks, concatenate chunk r with chunk 2*rd-1-r, split that
-    into ud equal parts and keep part u.
+    The split of Algorithm 2 written as a position formula: with chunk length
+    c = S / (2 rd), local row i of ring rank r's share is the token at
+    r c + i for i < c and at (2 rd - 1 - r) c + (i - c) for c <= i < 2c; the
+    Ulysses rank u keeps rows u T .. (u + 1) T - 1 of that share, T = 2c / ud.
+    Lengths that do not divide are rejected (no page says how to pad).
     """
-    seq = np.arange(S, dtype=np.int64)
-    seq_chunks = _chunk(seq, 2 * rd)
-    reorder_seq = np.concatenate([seq_chunks[ring_rank], seq_chunks[2 * rd - ring_rank - 1]])
-    return _chunk(reorder_seq, ud)[ulysses_rank]
+    if S % (2 * rd) != 0 or (S // rd) % ud != 0:
+        raise ValueError(f"S = {S} does not split into 2*{rd} chunks and {ud} equal parts of a share")
+    c = S // (2 * rd)
+    rows_per_rank = 2 * c // ud
+    i = np.arange(ulysses_rank * rows_per_rank, (ulysses_rank + 1) * rows_per_rank, dtype=np.int64)
+    return np.where(i < c, ring_rank * c + i, (2 * rd - 1 - ring_rank) * c + (i - c))
 
 
 def zigzag_share_positions(S, rd, ring_rank):
@@ -44,22 +40,30 @@ def zigzag_share_positions(S, rd, ring_rank):
 def zigzag_per_sample_positions(cu_seqlens, rd, ring_rank):
     """Positions held by ring rank r when Algorithm 2's split is applied to
     every packed sample on its own ([USP review] section 三, Algorithm 2, with
-    the packing of [ByteScale notes]): sample n, whose length must divide by
-    2*rd, is cut into 2*rd chunks and the rank takes chunks r and 2*rd-1-r;
-    the share is these pieces in sample order.  With one sample this is
-    :func:`zigzag_share_positions`."""
+    the packing of [ByteScale notes]): a sample starting at b with length n
+    (a multiple of 2 rd) has chunks of m = n / (2 rd) tokens, and the rank
+    holds b + r m .. b + (r + 1) m - 1 followed by
+    b + (2 rd - 1 - r) m .. b + (2 rd - r) m - 1; the share is these runs in
+    sample order.  With one sample this is :func:`zigzag_share_positions`."""
     cu = np.asarray(cu_seqlens, dtype=np.int64)
-    parts = []
-    for n in range(len(cu) - 1):
-        chunks = _chunk(np.arange(cu[n], cu[n + 1], dtype=np.int64), 2 * rd)
-        parts += [chunks[ring_rank], chunks[2 * rd - ring_rank - 1]]
-    return np.concatenate(parts)
+    runs = []
+    for b, e in zip(cu[:-1], cu[1:]):
+        if (e - b) % (2 * rd) != 0:
+            raise ValueError(f"sample of length {e - b} does not split into 2*{rd} chunks")
+        m = (e - b) // (2 * rd)
+        runs.append(b + ring_rank * m + np.arange(m, dtype=np.int64))
+        runs.append(b + (2 * rd - 1 - ring_rank) * m + np.arange(m, dtype=np.int64))
+    return np.concatenate(runs)
 
 
 def zigzag_per_sample_local_positions(cu_seqlens, rd, ud, ring_rank, ulysses_rank):
     """Per-sample zigzag share of ring rank r, then Algorithm 2's Ulysses
-    split: the u-th of ud equal parts."""
-    return _chunk(zigzag_per_sample_positions(cu_seqlens, rd, ring_rank), ud)[ulysses_rank]
+    split: rows u T .. (u + 1) T - 1 of the share, T = share length / ud."""
+    share = zigzag_per_sample_positions(cu_seqlens, rd, ring_rank)
+    if len(share) % ud != 0:
+        raise ValueError(f"share of {len(share)} tokens does not split into {ud} equal parts")
+    n = len(share) // ud
+    return share[ulysses_rank * n:(ulysses_rank + 1) * n]
 
 
 def zigzag_extract(x, rd, ud, ring_rank, ulysses_rank):

@@ -290,7 +290,7 @@ def check_zigzag(S=48, rd=3, ud=2):
                                 np.arange((2 * rd - 1 - r) * c, (2 * rd - r) * c)])
         assert np.array_equal(ix.zigzag_share_positions(S, rd, r), share)
         parts = [ix.zigzag_local_positions(S, rd, ud, r, u) for u in range(ud)]
-        assert np.array_equal(np.concatenate(parts), share)             # .chunk(ud) of reorder_seq
+        assert np.array_equal(np.concatenate(parts), share)             # the ud parts of the share, in order
         assert all(len(p) == 2 * c // ud for p in parts)
     x = _rand((2, S, 3, 4), 1)
     assert np.array_equal(ix.zigzag_scatter_all(ix.zigzag_extract_all(x, rd, ud), S), x)
@@ -367,7 +367,7 @@ def test_p7_ulysses_n1_is_transpose():
     assert np.array_equal(ix.ulysses_fwd([x], 0), np.transpose(x, (2, 0, 1, 3)))
 
 
-def test_p7_gather_reproduces_reorder_seq():
+def test_p7_gather_reproduces_the_share():
     S, rd, ud = 64, 2, 4
     x = _rand((1, S, 8, 2), 2)
     for r in range(rd):
