@@ -46,7 +46,11 @@
 //     on the first tiles of a row or when that check fails, and the reference
 //     then moves (and O is rescaled) only if the tile max exceeds it by more
 //     than 2^8.  This changes nothing but the reference point of the final
-//     division (o = O / l and lse = m + log l stay exact).
+//     division: lse = m + log l stays exact (l sums the fp32 probabilities),
+//     and O is divided by the sum of the bf16-rounded probabilities, the
+//     weights the PV product applied, so that o's weights add up to one and a
+//     dominant key's rounding (its P is not 1 under a stale reference)
+//     cancels.
 //
 // Grid order: heaviest query tiles first (the last rows of a share see the
 // most keys), and the Hq / Hkv query heads that read one KV head run back to
@@ -64,6 +68,9 @@ using namespace tiles;
 // 64 NW threads per workgroup.
 
 constexpr float TAU = 8.0f;  // log2 headroom before the running max must move
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 // K and V tiles of TB keys in LDS (TB = 32 or 64).
 template <int D, int TB>
@@ -263,7 +270,7 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
   f32x16 O[D / 32];
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) O[mb] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f, lr_run = 0.0f;
   const float sl2 = a.scale_log2;
 
   // next tile of the walk after `x` (workgroup-uniform); `tx` is its step
@@ -350,11 +357,15 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
     // the max is taken, the reference only moves if the tile max exceeds it
     // by more than 2^TAU.
     bf16x8 pf[2 * NBK];
-    float ps;
+    float ps, pr;
     auto probs = [&](float m_use) {
-      // the row sum takes the unrounded probabilities: lse is exact to fp32
-      // rounding, while O's weights are their bf16 roundings.  Two partial
-      // sums keep two add chains.
+      // Two row sums.  lse takes the unrounded probabilities, so it is exact
+      // to fp32 rounding.  O is divided by the sum of their bf16 roundings,
+      // the weights the PV product actually applied: the weights of the
+      // final o then add up to one, and a key that dominates its row (P far
+      // above the others, not 1 under the lazy reference) contributes its
+      // value with no error from the rounding of its P.  Two partial sums
+      // keep two add chains.
       float ps0 = 0.0f, ps1 = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < NBK; ++kb) {
@@ -369,6 +380,16 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
         }
       }
       ps = ps0 + ps1;
+      float pr0 = 0.0f, pr1 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 2 * NBK; ++i) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 4) {
+          pr0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[i][e], pf[i][e + 1]}, kOnes2, pr0, false);
+          pr1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[i][e + 2], pf[i][e + 3]}, kOnes2, pr1, false);
+        }
+      }
+      pr = pr0 + pr1;
     };
     bool need_max = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
     if (!need_max) {
@@ -387,6 +408,7 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
         const float m_new = fmaxf(m_run, mx);
         const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
+        lr_run *= alpha;
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb) O[mb] *= alpha;
         m_run = m_new;
@@ -394,6 +416,7 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
       probs(m_run == -INFINITY ? 0.0f : m_run);
     }
     l_run += ps;
+    lr_run += pr;
 
     // O^T += V^T P^T, 16 keys per MFMA; V^T read transposed from row-major V
     __builtin_amdgcn_s_setprio(1);
@@ -438,9 +461,9 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
   }
 
   // ---------------------------------------------------------- epilogue --
-  const float l = partner_sum(l_run);
+  const float l = partner_sum(l_run), lr = partner_sum(lr_run);
   const bool empty = !(l > 0.0f);
-  const float inv = empty ? 0.0f : 1.0f / l;
+  const float inv = empty || !(lr > 0.0f) ? 0.0f : 1.0f / lr;
   const float lse = empty ? -INFINITY : (m_run + __log2f(l)) * 0.69314718055994530942f;
   if (!qvalid) return;
   if (PARTIAL) {

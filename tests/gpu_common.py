@@ -6,6 +6,8 @@ Tolerances (floating point): bf16 inputs -- o max-abs <= 1e-2, o mean-abs <=
 1e-6, lse max-abs <= 1e-6.  Rows with no visible key must carry lse = -inf
 on both sides.  Index and layout work must be bit-exact.
 """
+import json
+import os
 import sys
 
 import numpy as np
@@ -62,15 +64,28 @@ def bf16_rounding_floor(o_ref):
     return float((ulp / 4).mean()) if a.size else 0.0
 
 
+def log_stats(kind, what, stats):
+    """Append one JSON line per check to $USP_PARITY_LOG (when set), so a GPU
+    run leaves the raw errors of every case beside the pass/fail verdict."""
+    path = os.environ.get("USP_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"kind": kind, "case": what, **stats}) + "\n")
+
+
 def check_close(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what="", out_bf16=False):
     """o arrays in the same layout; lse arrays in the same layout.
 
-    ``out_bf16``: o was rounded to bf16 by the kernel; the mean-abs bar then
-    adds the expected error of that rounding (negligible where |o| << 1, as
-    in the long-sequence workloads; about 1e-3 where rows average only a few
-    values and |o| ~ 1), and the max-abs bar, element by element, half a bf16
-    spacing of the exact value (what rounding the exact o alone may cost:
-    0.0078 at |o| in [2, 4), more than the bar itself above 4)."""
+    ``out_bf16``: o was rounded to bf16 by the kernel.  The max-abs bar stays
+    the flat 1e-2 wherever |o_ref| < 2, where a correctly rounded output
+    misses the exact value by at most 2^-8 (0.0039) and the bar is left to
+    the kernel's own error.  Only where |o_ref| >= 2 does it add half a bf16
+    spacing of the exact value, which rounding alone may cost there (0.0078
+    in [2, 4), more than the bar itself from 4 on).  The mean-abs bar adds
+    the expected error of that rounding, a quarter spacing averaged
+    (negligible where |o| << 1, as in the long-sequence workloads; about 1e-3
+    on rows that average only a few values and |o| ~ 1).  The raw errors are
+    returned (and logged) whatever the bars."""
     omax_tol, omean_tol, lse_tol = TOL[dtype]
     o_gpu = np.asarray(o_gpu, dtype=np.float64)
     o_ref = np.asarray(o_ref, dtype=np.float64)
@@ -78,7 +93,8 @@ def check_close(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what="", out_bf16=False):
     if out_bf16:
         omean_tol = omean_tol + bf16_rounding_floor(o_ref)
         a = np.abs(o_ref)
-        omax_bar = omax_bar + np.where(a > 0, 2.0 ** (np.floor(np.log2(np.where(a > 0, a, 1.0))) - 8), 0.0)
+        big = a >= 2.0
+        omax_bar = np.where(big, omax_tol + 2.0 ** (np.floor(np.log2(np.where(big, a, 1.0))) - 8), omax_tol)
     lse_gpu = np.asarray(lse_gpu, dtype=np.float64)
     lse_ref = np.asarray(lse_ref, dtype=np.float64)
     assert o_gpu.shape == o_ref.shape and lse_gpu.shape == lse_ref.shape
@@ -88,7 +104,11 @@ def check_close(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what="", out_bf16=False):
     assert not np.any(np.isnan(lse_gpu)), f"{what}: NaN lse"
     d = np.abs(o_gpu - o_ref)
     dl = np.abs(np.where(ninf_r, 0.0, lse_gpu - np.where(ninf_r, 0.0, lse_ref)))
-    stats = dict(o_max=float(d.max()), o_mean=float(d.mean()), lse_max=float(dl.max()) if dl.size else 0.0)
+    stats = dict(o_max=float(d.max()) if d.size else 0.0, o_mean=float(d.mean()) if d.size else 0.0,
+                 lse_max=float(dl.max()) if dl.size else 0.0,
+                 o_max_below2=float(d[np.abs(o_ref) < 2].max()) if np.any(np.abs(o_ref) < 2) else 0.0,
+                 o_frac_of_bar=float((d / omax_bar).max()) if d.size else 0.0, o_mean_bar=float(omean_tol))
+    log_stats("fwd", what, stats)
     assert np.all(d <= omax_bar), f"{what}: {stats}"
     assert stats["o_mean"] <= omean_tol, f"{what}: {stats}"
     assert stats["lse_max"] <= lse_tol, f"{what}: {stats}"
@@ -138,5 +158,6 @@ def check_grad(g_gpu, g_ref, dtype, what=""):
         return dict(norm=0.0, max=0.0)
     d = g - r
     stats = dict(norm=float(np.linalg.norm(d) / np.linalg.norm(r)), max=float(np.abs(d).max() / scale))
+    log_stats("grad_" + dtype, what, stats)
     assert stats["norm"] <= nrm_tol and stats["max"] <= max_tol, f"{what}: {stats}"
     return stats

@@ -89,3 +89,91 @@ def test_usp_hybrid_s128k_backward_share(r, u):
     ref = do64.sum(axis=(1, 3))
     assert np.all(np.abs(dv_sum - ref) <= 1e-3 * np.abs(do64).sum(axis=(1, 3))), \
         float(np.abs(dv_sum - ref).max())
+
+
+def test_packed_varlen_s32k_per_sample_backward_all_ranks():
+    """The per-sample split of the packed 32K workload (lengths rounded to
+    multiples of 2 cp), each rank's usp_attn_bwd after its forward as the
+    benchmark launches them: dQ on every piece's first and last rows and a
+    seeded random set, dK and dV on the last three chunks of the shortest
+    samples (few queries see them, so the oracle takes those queries exactly),
+    and the whole-walk identities."""
+    w = inputs.WORKLOADS["packed_varlen_s32k_cp4"]
+    dev = device()
+    q, k, v = inputs.workload_qkv(w)
+    cu = inputs.workload_cu_seqlens(w, multiple=2 * w.rd)
+    rd, S, L = w.rd, w.S, w.share
+
+    def ps(x):
+        out = torch.empty((rd, 1, w.B, L) + tuple(x.shape[2:]), dtype=x.dtype, device=dev)
+        B.usp_zigzag_extract_varlen(x.to(dev), out, rd, 1, -1, -1, cu)
+        return out[:, 0]
+
+    say(w.name, "per-sample backward: extract")
+    qs, ks, vs = ps(q), ps(k), ps(v)
+    pos = [ix.zigzag_per_sample_positions(cu, rd, r) for r in range(rd)]
+    owner = np.empty(S, dtype=np.int64)
+    local = np.empty(S, dtype=np.int64)
+    for j in range(rd):
+        owner[pos[j]] = j
+        local[pos[j]] = np.arange(L)
+    qn, kn, vn = f64(q), f64(k), f64(v)
+    all_pos = np.arange(S)
+    lens = np.diff(cu)
+    short = np.argsort(lens, kind="stable")[:2]
+    for r in range(rd):
+        qr = qs[r].contiguous()
+        o = torch.empty_like(qr)
+        lse = torch.empty(w.H, w.B, L, dtype=torch.float32, device=dev)
+        desc = B.attn_desc(S, rd, qr, ks, vs, o=o, cu_seqlens=cu, zigzag_per_sample=True)
+        say(w.name, "per-sample backward rank", r)
+        B.usp_attn_fwd(qr, ks, vs, o, lse, desc, r)
+        d_o = inputs.randn(tuple(qr.shape), 99, "bf16").to(dev)
+        dq = torch.empty_like(qr)
+        dk = torch.zeros(ks.shape, dtype=torch.float32, device=dev)
+        dv = torch.zeros(vs.shape, dtype=torch.float32, device=dev)
+        stats = torch.empty(2 * lse.numel(), dtype=torch.float32, device=dev)
+        B.usp_attn_bwd(qr, ks, vs, o, d_o, lse, dq, dk, dv, stats, desc, r)
+        torch.cuda.synchronize()
+        assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
+        don = f64(d_o)
+
+        # dQ rows: every piece's edges and random rows
+        edges, off = [], 0
+        for b, e in zip(cu[:-1], cu[1:]):
+            m = (e - b) // (2 * rd)
+            edges += [off, off + m - 1, off + m, off + 2 * m - 1]
+            off += 2 * m
+        rows = sample_rows(L, w.chunk, 16, 80 + r, extra=sorted(set(edges)))
+        qp = pos[r][rows]
+        gq, _, _ = ob.attention_backward(qn[:, qp], kn, vn, don[:, rows], w.scale, q_pos=qp, k_pos=all_pos,
+                                         q_seg_start=ix.segment_start(cu, qp))
+        check_grad(f64(dq[:, rows]), gq, "bf16", f"{w.name} per-sample r{r} dq rows")
+
+        # dK, dV: keys of the last three chunks of the two shortest samples
+        for n in short:
+            b, e = int(cu[n]), int(cu[n + 1])
+            m = (e - b) // (2 * rd)
+            kp = np.arange(e - 3 * m, e)
+            vis_rows = np.nonzero((pos[r] >= kp[0]) & (pos[r] < e))[0]
+            if vis_rows.size == 0:
+                continue
+            vq = pos[r][vis_rows]
+            seg = ix.segment_start(cu, vq)
+            o_v, lse_v = oa.masked_attention(qn[:, vq], kn, vn, w.scale, q_pos=vq, k_pos=all_pos, q_seg_start=seg)
+            do_v = don[:, vis_rows]
+            _, gk, gv = ob.ring_step_backward(qn[:, vq], kn[:, kp], vn[:, kp], do_v, lse_v, ob.delta_rows(o_v, do_v),
+                                              w.scale, vq, kp, q_seg_start=seg)
+            got_k = np.stack([f64(dk[owner[p]][:, local[p]]) for p in kp], axis=1)
+            got_v = np.stack([f64(dv[owner[p]][:, local[p]]) for p in kp], axis=1)
+            check_grad(got_k, gk, "bf16", f"{w.name} per-sample r{r} dk sample {n}")
+            check_grad(got_v, gv, "bf16", f"{w.name} per-sample r{r} dv sample {n}")
+
+        # whole-walk identities: every dS row sums to zero, every softmax row to one
+        dk64, dv64 = f64(dk), f64(dv)                                  # (rd, B, L, Hkv, D)
+        dk_sum = dk64.sum(axis=(0, 2))
+        assert np.all(np.abs(dk_sum) <= 1e-2 * np.abs(dk64).sum(axis=(0, 2))), "sum of dK"
+        G = w.H // w.Hkv
+        ref = don.reshape(w.B, L, w.Hkv, G, w.D).sum(axis=(1, 3))
+        scale_v = np.abs(don).reshape(w.B, L, w.Hkv, G, w.D).sum(axis=(1, 3))
+        assert np.all(np.abs(dv64.sum(axis=(0, 2)) - ref) <= 1e-3 * scale_v), "sum of dV"

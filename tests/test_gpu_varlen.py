@@ -84,6 +84,9 @@ ATTN_CASES = {  # name: B, S, H, Hkv, D, cp, cu, dtype
     # 108 samples: pieces of 1, 65, 128 and 129 rows among many short ones,
     # so the query tiles cut at pieces take every shape
     "bf16_cp2_108_samples": (1, None, 2, 1, 64, 2, "many", "bf16"),
+    # D = 128 with pieces of 257, 129, 513 and 1 rows: query tiles cut at
+    # pieces longer than one 128-row tile, in the walk and the dQ pass
+    "bf16_cp2_d128_long_pieces": (1, 3600, 4, 2, 128, 2, [0, 1028, 1544, 3596, 3600], "bf16"),
 }
 
 

@@ -133,6 +133,83 @@ def test_packed_varlen_s32k_all_ranks():
         check_close(f64(o[:, rows]), f64(lse[:, :, rows]), o_ref, l_ref, "bf16", f"{w.name} r{r}")
 
 
+def _piece_edges(cu, cp):
+    """Local rows of each ring rank's per-sample share at the first and last
+    row of each of its pieces: a sample of length n contributes its chunks r
+    and 2 cp - 1 - r, m = n / (2 cp) rows each, in sample order."""
+    out = []
+    for r in range(cp):
+        rows, off = [], 0
+        for b, e in zip(cu[:-1], cu[1:]):
+            m = (e - b) // (2 * cp)
+            rows += [off, off + m - 1, off + m, off + 2 * m - 1]
+            off += 2 * m
+        out.append(sorted(set(rows)))
+    return out
+
+
+def _per_sample_shares(x, w, cu, dev):
+    """Every rank's per-sample share (rd, B, S/rd, H, D) by the library's
+    extract, as the benchmark makes them."""
+    out = torch.empty((w.rd, 1, w.B, w.share) + tuple(x.shape[2:]), dtype=x.dtype, device=dev)
+    B.usp_zigzag_extract_varlen(x.to(dev), out, w.rd, 1, -1, -1, cu)
+    return out[:, 0]
+
+
+def test_packed_varlen_s32k_per_sample_all_ranks():
+    """The per-sample split of the packed 32K workload (lengths rounded to
+    multiples of 2 cp), each rank's walk as the benchmark launches it; every
+    piece's first and last rows and a seeded random set against the oracle."""
+    w = W["packed_varlen_s32k_cp4"]
+    dev = device()
+    q, k, v, kn, vn = _load(w)
+    cu = inputs.workload_cu_seqlens(w, multiple=2 * w.rd)
+    say(w.name, "per-sample extract")
+    qs, ks, vs = (_per_sample_shares(x, w, cu, dev) for x in (q, k, v))
+    pos = [ix.zigzag_per_sample_positions(cu, w.rd, r) for r in range(w.rd)]
+    for r in range(w.rd):
+        assert torch.equal(qs[r].cpu(), q[:, pos[r]]) and torch.equal(ks[r].cpu(), k[:, pos[r]])
+    edges = _piece_edges(cu, w.rd)
+    qn = f64(q)
+    for r in range(w.rd):
+        qr = qs[r].contiguous()
+        o = torch.empty_like(qr)
+        lse = torch.empty(w.H, w.B, w.share, dtype=torch.float32, device=dev)
+        desc = B.attn_desc(w.S, w.rd, qr, ks, vs, o=o, cu_seqlens=cu, zigzag_per_sample=True)
+        say(w.name, "per-sample walk rank", r)
+        B.usp_attn_fwd(qr, ks, vs, o, lse, desc, r)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+        rows = sample_rows(w.share, w.chunk, 24, 50 + r, extra=edges[r])
+        o_ref, l_ref = _oracle_rows(qn, kn, vn, pos[r][rows], w.scale, cu)
+        check_close(f64(o[:, rows]), f64(lse[:, :, rows]), o_ref, l_ref, "bf16", f"{w.name} per-sample r{r}")
+
+
+def test_usp_hybrid_s128k_share_384_rows():
+    """The benchmark's own comparison as a test: 384 seeded rows of the
+    share's head-major output (all 16 heads of the Ulysses rank, both
+    Ulysses halves of the ring share) after OneGpuShare.step, against the
+    oracle over all 131072 keys."""
+    w = W["usp_hybrid_s128k_ud2_rd4"]
+    r, u = 0, 0
+    dev = device()
+    q, k, v, kn, vn = _load(w)
+    say(w.name, "share", r, u, "384 rows")
+    share = OneGpuShare(q.to(dev), k.to(dev), v.to(dev), w.rd, w.ud, r, u)
+    share.prepare_peers()
+    share.step()
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(1234).choice(w.share, size=384, replace=False))
+    hb, kb = w.H // w.ud, w.Hkv // w.ud
+    rt = torch.from_numpy(rows).to(dev)
+    o = np.transpose(f64(share.oh[u].index_select(2, rt)), (1, 2, 0, 3))        # (B, n, hb, D)
+    lse = f64(share.lse[u].index_select(2, rt))
+    qp = ix.zigzag_share_positions(w.S, w.rd, r)[rows]
+    o_ref, l_ref = oa.masked_attention(f64(q[:, :, u * hb:(u + 1) * hb])[:, qp], kn[:, :, u * kb:(u + 1) * kb],
+                                       vn[:, :, u * kb:(u + 1) * kb], w.scale, q_pos=qp)
+    check_close(o, lse, o_ref, l_ref, "bf16", f"{w.name} share ({r},{u}) 384 rows x {hb} heads")
+
+
 def test_tiny_fp32_workload_all_ranks():
     w = W["tiny_causal_mha_fp32_s256_cp4"]
     dev = device()
