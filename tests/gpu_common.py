@@ -139,11 +139,13 @@ def sample_rows(L, c, n_random, seed, extra=()):
 
 # Gradient bar (the backward): normwise relative error and worst element
 # relative to the largest reference magnitude, per tensor.  bf16 -- the
-# kernels round P and dS to bf16 (relative 2^-9) before the fp32-accumulated
-# products and take delta from the bf16 O, so errors of a few 2^-9 of the
-# gradient's scale are expected; fp32 -- double internally, with lse and
-# delta passed as fp32 (relative 2^-24 of |lse| on P), a few 1e-7.
-GTOL = {"bf16": (1e-2, 5e-2), "fp32": (1e-5, 1e-4)}
+# kernels round P and dS to bf16 (relative error up to 2^-8) before the
+# fp32-accumulated products and take delta from the bf16 O, so errors of one
+# to two 2^-8 of the gradient's scale are expected where rows see few keys
+# (measured at worst: 5.9e-3 normwise, 8.9e-3 worst element); fp32 -- double
+# internally, with lse and delta passed as fp32 (relative 2^-24 of |lse| on
+# P), a few 1e-7 (measured at worst: 3.7e-7 and 4.6e-7).
+GTOL = {"bf16": (1e-2, 2e-2), "fp32": (1e-6, 2e-6)}
 
 
 def check_grad(g_gpu, g_ref, dtype, what=""):
