@@ -20,9 +20,11 @@
  *
  * Conventions shared by every entry point:
  *   - Every buffer is device memory owned by the caller.  The library
- *     allocates nothing, keeps no device state between calls and never
- *     synchronises: work is enqueued on `stream` (a hipStream_t; NULL is the
- *     default stream) and results are valid once that stream has completed.
+ *     allocates nothing, keeps no device state between calls (except the
+ *     statistics array of usp_attn_bwd_noalloc, a static device symbol) and
+ *     never synchronises: work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the default stream) and results are valid once that stream has
+ *     completed.
  *   - Element strides count elements, not bytes; head_dim is always the
  *     contiguous (stride 1) dimension.
  *   - Validation is synchronous and happens before any launch.  A non-OK
@@ -45,7 +47,7 @@
 extern "C" {
 #endif
 
-#define USP_ABI_VERSION 5
+#define USP_ABI_VERSION 6
 
 /* Most packed samples one call takes (their boundaries travel by value). */
 #define USP_MAX_SEQS 256
@@ -365,6 +367,32 @@ usp_status usp_attn_bwd(const void *q, const void *k_all, const void *v_all, con
                         const void *d_o, const float *lse, void *dq, float *dk_all,
                         float *dv_all, float *stats, const usp_attn_desc *desc,
                         int32_t ring_rank, void *stream);
+
+/*
+ * The ring backward without a caller-provided statistics buffer -- for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight training or serving loops, harnesses that forbid hipMalloc).  It is
+ * usp_attn_bwd with the same arguments except `stats`: the per-row
+ * statistics (delta and lse * log2(e), 2 floats per row) live in a
+ * library-owned device array of USP_NOALLOC_MAX_STATS_ROWS rows (16 MiB)
+ * that each GPU the library runs on holds until the process ends.  The call
+ * allocates nothing.  The array is resolved once per device, on the first
+ * call with that device current.  Every call on a GPU uses that GPU's one
+ * array: calls that overlap on one GPU (other streams, other threads) race
+ * on it and must be ordered by the caller.  Every row the passes read is
+ * written by the call first, so nothing carries over between calls.
+ * Outputs are bitwise those of usp_attn_bwd.
+ * Errors: as usp_attn_bwd, plus USP_ERR_INVALID_ARG when the call needs more
+ *   than USP_NOALLOC_MAX_STATS_ROWS statistics rows ((cp for ring_rank = -1,
+ *   else 1) * num_q_heads * batch * seq_len / cp); this is checked before
+ *   anything touches the GPU.  USP_ERR_HIP if the array's device address
+ *   cannot be obtained.
+ */
+#define USP_NOALLOC_MAX_STATS_ROWS (1 << 21)
+
+usp_status usp_attn_bwd_noalloc(const void *q, const void *k_all, const void *v_all, const void *o,
+                                const void *d_o, const float *lse, void *dq, float *dk_all, float *dv_all,
+                                const usp_attn_desc *desc, int32_t ring_rank, void *stream);
 
 /* Name of a status code (static storage). */
 const char *usp_status_string(usp_status status);

@@ -21,7 +21,9 @@ USP_DTYPE_BF16, USP_DTYPE_FP32 = 0, 1
 EXPORTED = ["usp_zigzag_extract", "usp_zigzag_extract_n", "usp_zigzag_extract_varlen", "usp_ulysses_a2a_layout",
             "usp_ulysses_a2a_layout_n", "usp_ulysses_a2a_layout_heads", "usp_ring_attn_step_fwd",
             "usp_lse_merge", "usp_attn_fwd", "usp_attn_bwd_prep", "usp_ring_attn_step_bwd", "usp_attn_bwd",
-            "usp_status_string", "usp_last_error_detail", "usp_abi_version"]
+            "usp_attn_bwd_noalloc", "usp_status_string", "usp_last_error_detail", "usp_abi_version"]
+
+NOALLOC_MAX_STATS_ROWS = 1 << 21
 
 
 class UspError(RuntimeError):
@@ -73,11 +75,12 @@ def lib():
         L.usp_ring_attn_step_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc),
                                              i32, i32, vp]
         L.usp_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, vp]
+        L.usp_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, vp]
         for f in ("usp_zigzag_extract", "usp_zigzag_extract_n", "usp_zigzag_extract_varlen", "usp_ulysses_a2a_layout",
                   "usp_ulysses_a2a_layout_n",
                   "usp_ulysses_a2a_layout_heads", "usp_ring_attn_step_fwd",
                   "usp_lse_merge", "usp_attn_fwd", "usp_attn_bwd_prep", "usp_ring_attn_step_bwd",
-                  "usp_attn_bwd"):
+                  "usp_attn_bwd", "usp_attn_bwd_noalloc"):
             getattr(L, f).restype = st
         L.usp_status_string.argtypes = [st]
         L.usp_status_string.restype = ctypes.c_char_p
@@ -377,6 +380,23 @@ def usp_attn_bwd(q, k_all, v_all, o, d_o, lse, dq, dk_all, dv_all, stats, desc, 
     check(lib().usp_attn_bwd(q.data_ptr(), k_all.data_ptr(), v_all.data_ptr(), o.data_ptr(), d_o.data_ptr(),
                              lse.data_ptr(), dq.data_ptr(), dk_all.data_ptr(), dv_all.data_ptr(),
                              stats.data_ptr(), ctypes.byref(desc), ring_rank, _stream(stream)))
+    return dq, dk_all, dv_all
+
+
+def usp_attn_bwd_noalloc(q, k_all, v_all, o, d_o, lse, dq, dk_all, dv_all, desc, ring_rank, stream=None):
+    """usp_attn_bwd with its statistics rows in the library's own device array
+    (no caller buffer, nothing allocated); at most NOALLOC_MAX_STATS_ROWS rows."""
+    _dev(q, k_all, v_all, o, d_o, lse, dq, dk_all, dv_all)
+    n = desc.cp if ring_rank < 0 else 1
+    _check_attn(k_all, v_all, lse, desc, n)
+    _check_dkv(k_all, v_all, dk_all, dv_all)
+    if dq.dtype != q.dtype or not _same_layout(dq, q):
+        raise ValueError("dq must have q's dtype, shape and strides")
+    if d_o.dtype != o.dtype or not _same_layout(d_o, o):
+        raise ValueError("d_o must have o's dtype, shape and strides")
+    check(lib().usp_attn_bwd_noalloc(q.data_ptr(), k_all.data_ptr(), v_all.data_ptr(), o.data_ptr(),
+                                     d_o.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk_all.data_ptr(),
+                                     dv_all.data_ptr(), ctypes.byref(desc), ring_rank, _stream(stream)))
     return dq, dk_all, dv_all
 
 

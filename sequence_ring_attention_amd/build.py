@@ -14,7 +14,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libusp.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "copy_kernels.hip", "merge_kernel.hip", "attn_fp32.hip", "attn_bf16.hip", "bwd_prep.hip",
+SOURCES = ["api.cpp", "noalloc.hip", "copy_kernels.hip", "merge_kernel.hip", "attn_fp32.hip", "attn_bf16.hip", "bwd_prep.hip",
            "attn_bwd_fp32.hip", "attn_bwd_bf16.hip"]
 
 # Packed fp32 VALU ops are switched off: the kernels use scalar and vector

@@ -676,7 +676,21 @@ usp_status usp_ring_attn_step_bwd(const void *q, const void *k_all, const void *
 usp_status usp_attn_bwd(const void *q, const void *k_all, const void *v_all, const void *o, const void *d_o,
                         const float *lse, void *dq, float *dk_all, float *dv_all, float *stats,
                         const usp_attn_desc *desc, int32_t ring_rank, void *stream) {
-  const char *who = "attn_bwd";
+  return usp::attn_bwd_with_stats(q, k_all, v_all, o, d_o, lse, dq, dk_all, dv_all, stats, desc, ring_rank, stream,
+                                  "attn_bwd");
+}
+
+}  // extern "C"
+
+namespace usp {
+
+usp_status report(usp_status s, const char *msg) { return s == USP_OK ? ok() : fail(s, "%s", msg); }
+
+int64_t bwd_stats_rows(const usp_attn_desc *d, int32_t ring_rank) { return stats_rows(d, ring_rank); }
+
+usp_status attn_bwd_with_stats(const void *q, const void *k_all, const void *v_all, const void *o, const void *d_o,
+                               const float *lse, void *dq, float *dk_all, float *dv_all, float *stats,
+                               const usp_attn_desc *desc, int32_t ring_rank, void *stream, const char *who) {
   usp::BwdArgs b;
   usp_status s = bwd_prepare(q, k_all, v_all, d_o, stats, desc, ring_rank, true, b, who);
   if (s != USP_OK) return s;
@@ -695,4 +709,4 @@ usp_status usp_attn_bwd(const void *q, const void *k_all, const void *v_all, con
   return bwd_launch(b, desc, stream, "attn_bwd launch");
 }
 
-}  // extern "C"
+}  // namespace usp

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/usp.h"
 #include "positions.h"
 
 namespace usp {
@@ -160,6 +161,21 @@ struct PrepArgs {
 };
 
 hipError_t launch_bwd_prep(const PrepArgs &p, int head_dim, bool bf16, hipStream_t stream);
+
+// ------------------------------------------ entry-point pieces (api.cpp) --
+
+// Sets the calling thread's error detail to `msg` (cleared for USP_OK) and
+// returns `s`.
+usp_status report(usp_status s, const char *msg);
+
+// Statistics rows of the backward for ring_rank (every rank for -1); the
+// descriptor's sizes must be >= 1.
+int64_t bwd_stats_rows(const usp_attn_desc *d, int32_t ring_rank);
+
+// usp_attn_bwd with the statistics rows at `stats` (validation, prep, passes).
+usp_status attn_bwd_with_stats(const void *q, const void *k_all, const void *v_all, const void *o, const void *d_o,
+                               const float *lse, void *dq, float *dk_all, float *dv_all, float *stats,
+                               const usp_attn_desc *desc, int32_t ring_rank, void *stream, const char *who);
 hipError_t launch_attn_bwd_bf16(const BwdArgs &a, int head_dim, hipStream_t stream);
 hipError_t launch_attn_bwd_fp32(const BwdArgs &a, int head_dim, hipStream_t stream);
 

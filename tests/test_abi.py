@@ -27,7 +27,7 @@ def declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     lib = B.lib()
     for name in names:
         assert hasattr(lib, name), name
@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = B.lib()
-    assert lib.usp_abi_version() == 5
+    assert lib.usp_abi_version() == 6
     assert lib.usp_status_string(0) == b"USP_OK"
     assert lib.usp_status_string(2) == b"USP_ERR_UNSUPPORTED"
     assert lib.usp_status_string(99) == b"USP_ERR_UNKNOWN"
@@ -406,3 +406,17 @@ def test_zigzag_varlen_rejects(cu, kw, status):
     n = 0 if arr is None else arr.size - 1
     assert B.lib().usp_zigzag_extract_varlen(a["x"], a["out"], a["dtype"], a["B"], a["S"], a["H"], a["D"], a["rd"],
                                              a["ud"], a["r"], a["u"], a["inv"], ptr, n, None) == status
+
+
+def test_noalloc_backward_rejects_more_rows_than_its_array():
+    """usp_attn_bwd_noalloc refuses a call whose statistics rows exceed the
+    library's array before anything touches the GPU (fake pointers)."""
+    lib = B.lib()
+    args = (FAKE, FAKE2, FAKE3, FAKE4, FAKE5, FAKE6, FAKE7, 0x80000, 0x90000)
+    big = _desc(num_q_heads=64, num_kv_heads=8, seq_len=4 * 65536)            # 64 x 65536 rows for one rank
+    assert lib.usp_attn_bwd_noalloc(*args, ctypes.byref(big), 0, None) == 1
+    assert b"statistics rows" in lib.usp_last_error_detail()
+    every = _desc(num_q_heads=32, num_kv_heads=8, seq_len=131072)              # 4 ranks x 32 x 32768 rows
+    assert lib.usp_attn_bwd_noalloc(*args, ctypes.byref(every), -1, None) == 1
+    assert lib.usp_attn_bwd_noalloc(*args, None, 0, None) == 1
+    assert B.NOALLOC_MAX_STATS_ROWS == 1 << 21
