@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=384, help="query rows of the oracle sample")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB (for scaling HBM byte counters)")
+    p.add_argument("--only-workloads", action="store_true",
+                   help="only the other configurations' launches (for profiling them), no oracle")
     return p.parse_args()
 
 
@@ -108,8 +110,9 @@ def plain_copy_reference(nbytes):
             "frac_hbm": 2 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
-def _time(fn, reps=5):
-    """Median HIP-event time (ms) of fn() on the current stream."""
+def _timed(fn, reps=20):
+    """HIP-event times (ms) of fn() on the current stream after one untimed
+    call: median, min and max of ``reps`` repetitions."""
     import torch
     fn()
     torch.cuda.synchronize()
@@ -121,7 +124,151 @@ def _time(fn, reps=5):
         b.record()
         torch.cuda.synchronize()
         out.append(a.elapsed_time(b))
-    return sorted(out)[len(out) // 2]
+    out.sort()
+    return {"ms": out[len(out) // 2], "ms_min": out[0], "ms_max": out[-1], "reps": reps}
+
+
+def _time(fn, reps=20):
+    """Median HIP-event time (ms) of fn() on the current stream."""
+    return _timed(fn, reps)["ms"]
+
+
+def _rate(t, flops):
+    """A timing dict from _timed with the causal-effective rate of `flops`."""
+    t = dict(t)
+    t["TFLOP/s"] = flops / (t["ms"] * 1e-3) / 1e12
+    t["frac_mfma"] = t["TFLOP/s"] / PEAK_BF16_TFLOPS
+    return t
+
+
+def clock_during(fn, seconds=1.0):
+    """The shader clock while fn() runs back to back for about `seconds`:
+    the firmware's gfx clock (amdsmi gpu metrics: the mean over XCDs of
+    current_gfxclks, MHz) sampled every 5 ms from a second thread.  Median,
+    min and max of the samples, or the reason it could not be read."""
+    import threading
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[torch.cuda.current_device()]
+        amdsmi.amdsmi_get_gpu_metrics_info(h)
+    except Exception as e:                      # no amdsmi or no access: say so
+        return {"mhz": None, "error": repr(e)[:200]}
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                xs = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+                if xs:
+                    samples.append(sum(xs) / len(xs))
+                elif isinstance(m.get("current_gfxclk"), (int, float)):
+                    samples.append(float(m["current_gfxclk"]))
+            except Exception:
+                pass
+            time.sleep(0.005)
+
+    fn()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=poll, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    if not samples:
+        return {"mhz": None, "error": "no clock samples"}
+    xs = sorted(samples)
+    # the first samples can predate the launches reaching the GPU
+    body = xs if len(xs) < 10 else sorted(samples[len(samples) // 10:])
+    return {"mhz": body[len(body) // 2], "mhz_min": body[0], "mhz_max": body[-1], "samples": len(body),
+            "source": "amdsmi gpu metrics current_gfxclks, mean over XCDs", "launches": n}
+
+
+def host_cores():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return os.cpu_count()
+
+
+def oracle_rows(w, q, k, v, rows_pos, cu=None, heads=None):
+    """The fp64 oracle on query positions `rows_pos` against the whole
+    sequence, timed on the host: (o, lse, seconds, causal-effective flops)."""
+    import numpy as np
+    import torch
+    from oracle import attention as oa
+    from oracle import index as ix
+    h0, h1 = heads if heads else (0, w.H)
+    g = w.H // w.Hkv
+    qn = q[:, :, h0:h1].to(torch.float64).numpy()
+    kn = k[:, :, h0 // g:h1 // g].to(torch.float64).numpy()
+    vn = v[:, :, h0 // g:h1 // g].to(torch.float64).numpy()
+    seg = None if cu is None else ix.segment_start(cu, rows_pos)
+    t0 = time.perf_counter()
+    o, lse = oa.masked_attention(qn[:, rows_pos], kn, vn, w.scale, q_pos=rows_pos, q_seg_start=seg)
+    dt = time.perf_counter() - t0
+    start = np.zeros_like(rows_pos) if cu is None else seg
+    pairs = int((np.asarray(rows_pos) - start + 1).sum())
+    return o, lse, dt, 4.0 * w.D * (h1 - h0) * w.B * pairs
+
+
+def baseline_entry(dt, flops, unit_flops, what, errors=None):
+    """One cpu_baseline object: the oracle's rate on its sample and the
+    sample time scaled to the configuration's whole unit (labelled as an
+    extrapolation)."""
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": host_cores(), "kind": "oracle",
+            "sample": what, "seconds": dt, "sample_tflop": flops / 1e12,
+            "extrapolated_unit_seconds": dt * unit_flops / flops, "extrapolation": "sample time x unit/sample flops",
+            "host_cpu_count": os.cpu_count(), "affinity_cores": len(os.sched_getaffinity(0)),
+            "gpu_vs_oracle": errors}
+
+
+def compare(o_gpu, lse_gpu, o_ref, lse_ref):
+    import numpy as np
+    eo, el = np.abs(o_gpu - o_ref), np.abs(lse_gpu - lse_ref)
+    return {"o_max_abs": float(eo.max()), "o_mean_abs": float(eo.mean()), "lse_max_abs": float(el.max()),
+            "bars": {"o_max_abs": 1e-2, "o_mean_abs": 1e-3, "lse_max_abs": 1e-3}}
+
+
+def index_oracle_copies():
+    """The CPU index oracle's copies timed on the host (bytes read + written
+    per second): the zigzag split of every rank of the 32K GQA workload's Q
+    (256 MiB) and the Ulysses layout of the 128K share's Q shards (256 MiB),
+    NumPy gathers of the bf16 bits."""
+    import numpy as np
+    from oracle import index as ix
+    rng = np.random.default_rng(7)
+    out = {}
+    x = rng.integers(-32768, 32767, size=(1, 32768, 32, 128), dtype=np.int16)
+    t0 = time.perf_counter()
+    ix.zigzag_extract_all(x, 8, 1)
+    dt = time.perf_counter() - t0
+    out["zigzag_extract_all_ranks_q_gqa_s32k_cp8"] = {"bytes": 2 * x.nbytes, "seconds": dt,
+                                                      "GB/s": 2 * x.nbytes / dt / 1e9}
+    shards = [rng.integers(-32768, 32767, size=(1, 16384, 32, 128), dtype=np.int16) for _ in range(2)]
+    t0 = time.perf_counter()
+    ix.ulysses_fwd(shards, 0)
+    ix.ulysses_fwd(shards, 1)
+    dt = time.perf_counter() - t0
+    nb = 2 * sum(s.nbytes for s in shards)
+    out["ulysses_layout_fwd_q_usp_hybrid_s128k"] = {"bytes": nb, "seconds": dt, "GB/s": nb / dt / 1e9}
+    out["kind"] = "oracle"
+    out["cores"] = 1
+    return out
 
 
 _FLUSH = []
@@ -202,7 +349,7 @@ def copy_launches(share, w):
     return res
 
 
-def other_share_walk(Q, K, V, w, r, u, flops, steps=5):
+def other_share_walk(Q, K, V, w, r, u, flops, steps=20):
     """The walk of another ring rank's share of the same grid (every share
     holds the same causal work under the zigzag split)."""
     import torch
@@ -222,7 +369,7 @@ def other_share_walk(Q, K, V, w, r, u, flops, steps=5):
             "frac_mfma": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
-def head_chunk_steps(Q, K, V, w, r, u, flops, whole_ms, whole_bytes, chunks=(8, 4, 2), overlapped=(4, 2), steps=5):
+def head_chunk_steps(Q, K, V, w, r, u, flops, whole_ms, whole_bytes, chunks=(8, 4, 2), overlapped=(4, 2), steps=20):
     """The share stepped with its head block pushed through in chunks
     (headwise chunking): step time and the head-major bytes the chunks in
     flight work on, beside the whole block's; chunks run one after another,
@@ -260,15 +407,19 @@ def packed_pairs(cu, pos):
     return int((np.asarray(pos) - start + 1).sum())
 
 
-def extra_workloads():
-    """The other configurations' launches, each timed on its own: the 8K MHA
-    walk of every rank in one launch, the 32K GQA walk of ranks 0 and 7 (zigzag
-    balance) with its per-step launches and merges, and the packed 32K walk
-    of each rank."""
+def extra_workloads(cpu=True):
+    """The other configurations, each launch timed on its own (20 reps: median,
+    min, max): the tiny fp32 workload's walk of every rank, the 8K MHA walk of
+    every rank in one launch, the 32K GQA walk of ranks 0 and 7 (zigzag
+    balance) with rank 0's per-step launches and merges, and the packed 32K
+    walk of each rank.  With ``cpu``, each configuration's unit is also run
+    through the fp64 oracle on a seeded row sample (the tiny workload whole),
+    timed on the host and compared with the GPU's rows."""
     import numpy as np
     import torch
     from sequence_ring_attention_amd import binding as B
     from sequence_ring_attention_amd import inputs
+    from oracle import index as ix
     dev = torch.device("cuda:0")
     res = {}
 
@@ -277,25 +428,81 @@ def extra_workloads():
         B.usp_zigzag_extract(x, out, rd, 1, -1, -1)
         return out[:, 0]                                       # (rd, B, 2c, H, D)
 
-    # 8K causal MHA, cp = 4, every rank in one launch
-    w = inputs.WORKLOADS["causal_mha_s8k_cp4"]
-    q, k, v = (t.to(dev) for t in inputs.workload_qkv(w))
-    qs, ks, vs = zig_shares(q, w.rd), zig_shares(k, w.rd), zig_shares(v, w.rd)
+    def gpu_rows(o, lse, rows):
+        """(B, n, H, D) o and (H, B, n) lse of local rows of one rank, as float64 numpy."""
+        rt = torch.from_numpy(np.asarray(rows)).to(dev)
+        return (o.index_select(1, rt).double().cpu().numpy(), lse.index_select(2, rt).double().cpu().numpy())
+
+    def pick(w, r, n, seed, extra=()):
+        rng = np.random.default_rng(seed)
+        c = w.chunk
+        base = {0, c - 1, c, 2 * c - 1, *extra} | set(rng.choice(w.share, size=n, replace=False).tolist())
+        return np.array(sorted(i for i in base if 0 <= i < w.share))
+
+    print("[bench] workload:tiny causal MHA", file=sys.stderr, flush=True)
+    # tiny causal MHA, fp32, cp = 4: every rank in one launch; the oracle runs the whole unit
+    w = inputs.WORKLOADS["tiny_causal_mha_fp32_s256_cp4"]
+    q, k, v = inputs.workload_qkv(w)
+    qs, ks, vs = zig_shares(q.to(dev), w.rd), zig_shares(k.to(dev), w.rd), zig_shares(v.to(dev), w.rd)
     o = torch.empty_like(qs)
     lse = torch.empty(w.rd, w.H, w.B, w.share, dtype=torch.float32, device=dev)
     d = B.attn_desc(w.S, w.rd, qs, ks, vs, o=o, all_ranks=True)
-    ms = _time(lambda: B.usp_attn_fwd(qs, ks, vs, o, lse, d, -1))
     fl = 2.0 * w.B * w.H * w.S * w.S * w.D
-    res[w.name] = {"all_ranks_walk_ms": ms, "TFLOP": fl / 1e12, "TFLOP/s": fl / (ms * 1e-3) / 1e12}
+    entry = {"all_ranks_walk": _rate(_timed(lambda: B.usp_attn_fwd(qs, ks, vs, o, lse, d, -1)), fl),
+             "TFLOP": fl / 1e12, "note": "latency-bound, not rated against the roofline"}
+    if cpu:
+        from oracle import attention as oa
+        t0 = time.perf_counter()
+        o_ref, l_ref = oa.attention_full(q.double().numpy(), k.double().numpy(), v.double().numpy(), w.scale)
+        dt = time.perf_counter() - t0
+        err = []
+        for r in range(w.rd):
+            p = ix.zigzag_share_positions(w.S, w.rd, r)
+            err.append(compare(o[r].double().cpu().numpy(), lse[r].double().cpu().numpy(), o_ref[:, p],
+                               l_ref[:, :, p]))
+        worst = {kk: max(e[kk] for e in err) for kk in ("o_max_abs", "o_mean_abs", "lse_max_abs")}
+        worst["bars"] = {"o_max_abs": 2e-5, "o_mean_abs": 1e-6, "lse_max_abs": 1e-6}
+        exact = 4.0 * w.D * w.H * w.B * (w.S * (w.S + 1) // 2)
+        entry["cpu_baseline"] = baseline_entry(dt, exact, exact, "the whole unit: one-shot fp64 attention of all "
+                                               f"{w.S} tokens (every rank and step), {dt * 1e3:.1f} ms", worst)
+    res[w.name] = entry
 
+    print("[bench] workload:8K causal MHA", file=sys.stderr, flush=True)
+    # 8K causal MHA, cp = 4, every rank in one launch
+    w = inputs.WORKLOADS["causal_mha_s8k_cp4"]
+    q, k, v = inputs.workload_qkv(w)
+    qs, ks, vs = zig_shares(q.to(dev), w.rd), zig_shares(k.to(dev), w.rd), zig_shares(v.to(dev), w.rd)
+    o = torch.empty_like(qs)
+    lse = torch.empty(w.rd, w.H, w.B, w.share, dtype=torch.float32, device=dev)
+    d = B.attn_desc(w.S, w.rd, qs, ks, vs, o=o, all_ranks=True)
+    fl = 2.0 * w.B * w.H * w.S * w.S * w.D
+    t = _rate(_timed(lambda: B.usp_attn_fwd(qs, ks, vs, o, lse, d, -1)), fl)
+    entry = {"all_ranks_walk": t, "all_ranks_walk_ms": t["ms"], "TFLOP": fl / 1e12, "TFLOP/s": t["TFLOP/s"]}
+    if cpu:
+        dt = fls = 0.0
+        err = []
+        for r in range(w.rd):
+            rows = pick(w, r, 24, 60 + r)
+            pos = ix.zigzag_share_positions(w.S, w.rd, r)[rows]
+            o_ref, l_ref, dtr, flr = oracle_rows(w, q, k, v, pos)
+            dt, fls = dt + dtr, fls + flr
+            err.append(compare(*gpu_rows(o[r], lse[r], rows), o_ref, l_ref))
+        worst = {kk: max(e[kk] for e in err) for kk in ("o_max_abs", "o_mean_abs", "lse_max_abs")}
+        worst["bars"] = err[0]["bars"]
+        entry["cpu_baseline"] = baseline_entry(dt, fls, fl, f"about 28 seeded rows (chunk edges included) of every "
+                                               f"rank x {w.H} heads vs all {w.S} keys, fp64 numpy", worst)
+    res[w.name] = entry
+
+    print("[bench] workload:32K causal GQA", file=sys.stderr, flush=True)
     # 32K causal GQA, cp = 8: ranks 0 and 7 (walk), rank 0 step by step + merges
     w = inputs.WORKLOADS["causal_gqa_s32k_cp8"]
-    q, k, v = (t.to(dev) for t in inputs.workload_qkv(w))
-    qs, ks, vs = zig_shares(q, w.rd), zig_shares(k, w.rd), zig_shares(v, w.rd)
+    q, k, v = inputs.workload_qkv(w)
+    qd = q.to(dev)
+    qs, ks, vs = zig_shares(qd, w.rd), zig_shares(k.to(dev), w.rd), zig_shares(v.to(dev), w.rd)
     fl_rank = 4.0 * w.D * w.H * w.B * 2 * w.rd * w.chunk * w.chunk
     entry = {"TFLOP_per_rank": fl_rank / 1e12}
     qz = torch.empty((w.rd, 1) + tuple(qs.shape[1:]), dtype=q.dtype, device=dev)
-    entry["zigzag_extract_all_ranks_q"] = _time_flushed(lambda: B.usp_zigzag_extract(q, qz, w.rd, 1, -1, -1),
+    entry["zigzag_extract_all_ranks_q"] = _time_flushed(lambda: B.usp_zigzag_extract(qd, qz, w.rd, 1, -1, -1),
                                                         2 * q.numel() * q.element_size())
     del qz
     for r in (0, w.rd - 1):
@@ -303,43 +510,71 @@ def extra_workloads():
         o = torch.empty_like(qr)
         lse = torch.empty(w.H, w.B, w.share, dtype=torch.float32, device=dev)
         d = B.attn_desc(w.S, w.rd, qr, ks, vs, o=o)
-        ms = _time(lambda: B.usp_attn_fwd(qr, ks, vs, o, lse, d, r))
-        entry[f"rank{r}_walk_ms"] = ms
-        entry[f"rank{r}_TFLOP/s"] = fl_rank / (ms * 1e-3) / 1e12
+        t = _rate(_timed(lambda: B.usp_attn_fwd(qr, ks, vs, o, lse, d, r)), fl_rank)
+        entry[f"rank{r}_walk"] = t
+        entry[f"rank{r}_walk_ms"] = t["ms"]
+        entry[f"rank{r}_TFLOP/s"] = t["TFLOP/s"]
+        if cpu:
+            rows = pick(w, r, 32, 70 + r)
+            pos = ix.zigzag_share_positions(w.S, w.rd, r)[rows]
+            o_ref, l_ref, dt, fls = oracle_rows(w, q, k, v, pos)
+            entry[f"rank{r}_cpu_baseline"] = baseline_entry(
+                dt, fls, fl_rank, f"{len(rows)} seeded rows (chunk edges included) of rank {r} x {w.H} heads vs "
+                f"all {w.S} keys, fp64 numpy", compare(*gpu_rows(o, lse, rows), o_ref, l_ref))
     qr = qs[0].contiguous()
     acc = torch.zeros(w.H, w.B, w.share, w.D, dtype=torch.float32, device=dev)
     lacc = torch.zeros(w.H, w.B, w.share, dtype=torch.float32, device=dev)
     ost, lst = torch.empty_like(acc), torch.empty_like(lacc)
     d = B.attn_desc(w.S, w.rd, qr, ks, vs)
-    step_ms = [_time(lambda t=t: B.usp_ring_attn_step_fwd(qr, ks, vs, ost, lst, d, 0, t)) for t in range(w.rd)]
+    steps = [_rate(_timed(lambda t=t: B.usp_ring_attn_step_fwd(qr, ks, vs, ost, lst, d, 0, t)), fl_rank / w.rd)
+             for t in range(w.rd)]
     rows = w.H * w.B * w.share
     merge = _time_flushed(lambda: B.usp_lse_merge(acc, lacc, ost, lst), 3 * rows * w.D * 4 + 3 * rows * 4)
-    entry["rank0_step_ms"] = step_ms
-    entry["rank0_step_TFLOP/s"] = [fl_rank / w.rd / (m * 1e-3) / 1e12 for m in step_ms]
+    entry["rank0_steps"] = steps
+    entry["rank0_step_ms"] = [x["ms"] for x in steps]
+    entry["rank0_step_TFLOP/s"] = [x["TFLOP/s"] for x in steps]
+    entry["merge"] = merge
     entry["merge_ms"] = merge["ms"]
     entry["merge_GB/s"] = merge["GB/s"]
     entry["merge_frac_hbm"] = merge["frac_hbm"]
     res[w.name] = entry
+    del qs, ks, vs, acc, lacc, ost, lst, qd
 
+    print("[bench] workload:packed variable-length 32K", file=sys.stderr, flush=True)
     # packed variable-length 32K, cp = 4: each rank
     w = inputs.WORKLOADS["packed_varlen_s32k_cp4"]
-    q, k, v = (t.to(dev) for t in inputs.workload_qkv(w))
+    q, k, v = inputs.workload_qkv(w)
     cu = inputs.workload_cu_seqlens(w)
     cu_t = torch.from_numpy(cu).to(dev)
-    qs, ks, vs = zig_shares(q, w.rd), zig_shares(k, w.rd), zig_shares(v, w.rd)
+    qs, ks, vs = zig_shares(q.to(dev), w.rd), zig_shares(k.to(dev), w.rd), zig_shares(v.to(dev), w.rd)
     entry = {"num_samples": len(cu) - 1}
     c = w.chunk
+    cpu_dt = cpu_fl = unit_fl = 0.0
+    errs = []
     for r in range(w.rd):
-        pos = np.concatenate([np.arange(r * c, (r + 1) * c), np.arange((2 * w.rd - 1 - r) * c, (2 * w.rd - r) * c)])
-        fl = 4.0 * w.D * w.H * w.B * packed_pairs(cu, pos)
+        share_pos = np.concatenate([np.arange(r * c, (r + 1) * c), np.arange((2 * w.rd - 1 - r) * c, (2 * w.rd - r) * c)])
+        fl = 4.0 * w.D * w.H * w.B * packed_pairs(cu, share_pos)
+        unit_fl += fl
         qr = qs[r].contiguous()
         o = torch.empty_like(qr)
         lse = torch.empty(w.H, w.B, w.share, dtype=torch.float32, device=dev)
         d = B.attn_desc(w.S, w.rd, qr, ks, vs, o=o, cu_seqlens=cu_t)
-        ms = _time(lambda: B.usp_attn_fwd(qr, ks, vs, o, lse, d, r))
-        entry[f"rank{r}"] = {"TFLOP": fl / 1e12, "ms": ms, "TFLOP/s": fl / (ms * 1e-3) / 1e12}
+        t = _rate(_timed(lambda: B.usp_attn_fwd(qr, ks, vs, o, lse, d, r)), fl)
+        entry[f"rank{r}"] = {"TFLOP": fl / 1e12, **t}
+        if cpu:
+            edges = [int(i) for b in cu[1:-1] for i in np.nonzero(np.abs(share_pos - b) <= 1)[0]]
+            rows = pick(w, r, 16, 80 + r, extra=edges)
+            o_ref, l_ref, dt, fls = oracle_rows(w, q, k, v, share_pos[rows], cu=cu)
+            cpu_dt, cpu_fl = cpu_dt + dt, cpu_fl + fls
+            errs.append(compare(*gpu_rows(o, lse, rows), o_ref, l_ref))
+    if cpu:
+        worst = {kk: max(e[kk] for e in errs) for kk in ("o_max_abs", "o_mean_abs", "lse_max_abs")}
+        worst["bars"] = errs[0]["bars"]
+        entry["cpu_baseline"] = baseline_entry(cpu_dt, cpu_fl, unit_fl, f"about 22 seeded rows (sample and chunk "
+                                               f"edges included) of every rank x {w.H} heads, fp64 numpy", worst)
     res[w.name] = entry
-    res[w.name + "_split_balance"] = split_balance(w, q, k, v, zig_shares)
+    print("[bench] workload: packed 32K, both splits", file=sys.stderr, flush=True)
+    res[w.name + "_split_balance"] = split_balance(w, q.to(dev), k.to(dev), v.to(dev), zig_shares)
     return res
 
 
@@ -390,12 +625,9 @@ def cpu_baseline(w, r, u, n_rows, gpu=None):
                   "lse_max_abs": float(el.max()), "bars": {"o_max_abs": 1e-2, "o_mean_abs": 1e-3, "lse_max_abs": 1e-3}}
     pairs = int((qp + 1).sum())                       # causal: position p sees p + 1 keys
     flops = 4.0 * w.D * hb * w.B * pairs
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count()
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    share_flops = 4.0 * w.D * hb * w.B * 2 * w.rd * w.chunk * w.chunk
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": host_cores(), "kind": "oracle",
+            "extrapolated_unit_seconds": dt * share_flops / flops,
             "sample": f"{n_rows} random query rows of share (r={r}, u={u}) x {hb} heads vs all "
                       f"{w.S} keys, fp64 numpy, {dt:.2f} s, {flops / 1e9:.1f} GFLOP causal-effective",
             "seconds": dt, "host_cpu_count": os.cpu_count(),
@@ -483,7 +715,7 @@ def ring_steps(share, flops):
             "work_per_step_tflop": per_step / 1e12, "merge": merge}
 
 
-def backward_walk(share, fwd_flops, reps=5):
+def backward_walk(share, fwd_flops, reps=20):
     """The ring backward of the same share (usp_attn_bwd: per-row statistics,
     dQ pass, dK/dV pass) after its forward, with a seeded upstream gradient.
     Algorithmic work: five products of the forward's shape (S, dP, dV, dK,
@@ -520,6 +752,12 @@ def main():
         copy_calibration(args.copy_calibration_mib)
         return
     import torch
+    if args.only_workloads:
+        if not torch.cuda.is_available():
+            print("no GPU visible", file=sys.stderr)
+            sys.exit(1)
+        print(json.dumps({"workloads": extra_workloads(cpu=False)}), flush=True)
+        return
     from sequence_ring_attention_amd import inputs
     from sequence_ring_attention_amd.pipeline import OneGpuShare
 
@@ -613,6 +851,14 @@ def main():
     walks = sorted(marks[s][2].elapsed_time(marks[s][3]) for s in range(args.steps))
     result["kernels"]["ring_walk_attention"].update(
         {"ms_median": walks[len(walks) // 2], "ms_min": walks[0], "ms_max": walks[-1]})
+    print("[bench] clock during the walk", file=sys.stderr, flush=True)
+    clk = clock_during(lambda: share._walk(u), 1.0)
+    result["roofline"]["clock"] = clk
+    if clk.get("mhz"):
+        # the same walk rated against the peak at the clock it ran at (256 CUs x 4096 bf16 FLOP/clk)
+        at_clock = 256 * 4096 * clk["mhz"] * 1e6 / 1e12
+        result["roofline"]["peak_at_measured_clock"] = at_clock
+        result["roofline"]["frac_at_measured_clock"] = walk_tflops / at_clock
     if not args.no_backward:
         print("[bench] backward of the same share", file=sys.stderr, flush=True)
         result["backward"] = backward_walk(share, flops)
@@ -630,10 +876,11 @@ def main():
         print("[bench] other workloads", file=sys.stderr, flush=True)
         del share, Q, K, V
         torch.cuda.empty_cache()
-        result["workloads"] = extra_workloads()
+        result["workloads"] = extra_workloads(cpu=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, r, u, args.cpu_rows, sample)
+        result["cpu_baseline"]["index_oracle_copies"] = index_oracle_copies()
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -55,19 +55,22 @@ __device__ inline float4 blend(double a1, float4 x, double a2, float4 y) {
   return r;
 }
 
-// Rows of 2^d4_shift float4 (at most 64): a wavefront takes 64 rows, each
-// lane computing the weights of one of them, then streams the rows' vectors
-// (64 consecutive per load, kUnroll loads in flight) and takes each vector's
-// row weights from the lane that computed them.  Each row's lse is read and
-// written by its own lane only.
+// Rows of 2^d4_shift float4 (at most 64): a workgroup of four wavefronts
+// takes 64 rows.  Every wavefront computes the weights of the 64 rows (lane i
+// those of row i) and streams its quarter of the rows' vectors (64
+// consecutive per load, kUnroll loads in flight), taking each vector's row
+// weights from the lane that computed them.  All four waves read the rows'
+// lse before the barrier; after it, wave 0 writes the merged lse.  Four waves
+// per 64 rows keep four times as many loads in flight as one wave would at
+// sizes that give each CU only a few 64-row groups.
 __global__ __launch_bounds__(kThreads) void lse_merge_rows64_kernel(float *o_acc, float *lse_acc,
                                                                     const float *o_step, const float *lse_step,
                                                                     int64_t rows, int32_t d4_shift) {
   const int lane = threadIdx.x & 63;
-  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-  const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
+  const int wave = threadIdx.x >> 6;
   const int d4 = 1 << d4_shift;
-  for (int64_t row0 = wave * 64; row0 < rows; row0 += nwaves * 64) {
+  const int per_wave = d4 * 16;  // vectors of one wave: a quarter of 64 rows x d4
+  for (int64_t row0 = (int64_t)blockIdx.x * 64; row0 < rows; row0 += (int64_t)gridDim.x * 64) {
     const int64_t my_row = row0 + lane;
     const bool live = my_row < rows;
     double a1 = 0.0, a2 = 0.0, lse = -INFINITY;
@@ -76,26 +79,28 @@ __global__ __launch_bounds__(kThreads) void lse_merge_rows64_kernel(float *o_acc
     float4 *acc = reinterpret_cast<float4 *>(o_acc) + row0 * d4;
     const float4 *stp = reinterpret_cast<const float4 *>(o_step) + row0 * d4;
     const int64_t nvec = (rows - row0 < 64 ? rows - row0 : 64) * d4;  // vectors of the rows in range
-    for (int it0 = 0; it0 < d4; it0 += kUnroll) {
+    const int v0 = wave * per_wave;
+    for (int it0 = 0; it0 < per_wave; it0 += kUnroll * 64) {
       float4 x[kUnroll], y[kUnroll];
 #pragma unroll
       for (int k = 0; k < kUnroll; ++k) {
-        const int v = (it0 + k) * 64 + lane;
-        if (it0 + k < d4 && v < nvec) {
+        const int v = v0 + it0 + k * 64 + lane;
+        if (it0 + k * 64 + lane < per_wave && v < nvec) {
           x[k] = as_float4(__builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(acc + v)));
           y[k] = as_float4(__builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(stp + v)));
         }
       }
 #pragma unroll
       for (int k = 0; k < kUnroll; ++k) {
-        const int v = (it0 + k) * 64 + lane;
-        const int src = v >> d4_shift;  // the vector's row within the 64
+        const int v = v0 + it0 + k * 64 + lane;
+        const int src = (v >> d4_shift) & 63;  // the vector's row within the 64
         const double b1 = __shfl(a1, src), b2 = __shfl(a2, src);
-        if (it0 + k < d4 && v < nvec)
+        if (it0 + k * 64 + lane < per_wave && v < nvec)
           __builtin_nontemporal_store(as_f32x4(blend(b1, x[k], b2, y[k])), reinterpret_cast<f32x4 *>(acc + v));
       }
     }
-    if (live) lse_acc[my_row] = (float)lse;
+    __syncthreads();  // every wave has read lse_acc of these rows
+    if (wave == 0 && live) lse_acc[my_row] = (float)lse;
   }
 }
 
@@ -140,8 +145,8 @@ hipError_t launch_lse_merge(float *o_acc, float *lse_acc, const float *o_step,
   if (d4 <= 64 && (d4 & (d4 - 1)) == 0) {
     int32_t shift = 0;
     while ((1 << shift) < d4) ++shift;
-    int64_t blocks = (rows + 4 * 64 - 1) / (4 * 64);  // 4 waves per block, 64 rows each
-    if (blocks > 8192) blocks = 8192;
+    int64_t blocks = (rows + 63) / 64;  // one 64-row group per block (4 waves)
+    if (blocks > 16384) blocks = 16384;
     hipLaunchKernelGGL(lse_merge_rows64_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, o_acc, lse_acc,
                        o_step, lse_step, rows, shift);
     return hipGetLastError();
