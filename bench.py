@@ -439,7 +439,7 @@ def extra_workloads(cpu=True):
         base = {0, c - 1, c, 2 * c - 1, *extra} | set(rng.choice(w.share, size=n, replace=False).tolist())
         return np.array(sorted(i for i in base if 0 <= i < w.share))
 
-    print("[bench] workload:tiny causal MHA", file=sys.stderr, flush=True)
+    print("[bench] workload: tiny causal MHA", file=sys.stderr, flush=True)
     # tiny causal MHA, fp32, cp = 4: every rank in one launch; the oracle runs the whole unit
     w = inputs.WORKLOADS["tiny_causal_mha_fp32_s256_cp4"]
     q, k, v = inputs.workload_qkv(w)
@@ -467,7 +467,7 @@ def extra_workloads(cpu=True):
                                                f"{w.S} tokens (every rank and step), {dt * 1e3:.1f} ms", worst)
     res[w.name] = entry
 
-    print("[bench] workload:8K causal MHA", file=sys.stderr, flush=True)
+    print("[bench] workload: 8K causal MHA", file=sys.stderr, flush=True)
     # 8K causal MHA, cp = 4, every rank in one launch
     w = inputs.WORKLOADS["causal_mha_s8k_cp4"]
     q, k, v = inputs.workload_qkv(w)
@@ -493,7 +493,7 @@ def extra_workloads(cpu=True):
                                                f"rank x {w.H} heads vs all {w.S} keys, fp64 numpy", worst)
     res[w.name] = entry
 
-    print("[bench] workload:32K causal GQA", file=sys.stderr, flush=True)
+    print("[bench] workload: 32K causal GQA", file=sys.stderr, flush=True)
     # 32K causal GQA, cp = 8: ranks 0 and 7 (walk), rank 0 step by step + merges
     w = inputs.WORKLOADS["causal_gqa_s32k_cp8"]
     q, k, v = inputs.workload_qkv(w)
@@ -540,7 +540,7 @@ def extra_workloads(cpu=True):
     res[w.name] = entry
     del qs, ks, vs, acc, lacc, ost, lst, qd
 
-    print("[bench] workload:packed variable-length 32K", file=sys.stderr, flush=True)
+    print("[bench] workload: packed variable-length 32K", file=sys.stderr, flush=True)
     # packed variable-length 32K, cp = 4: each rank
     w = inputs.WORKLOADS["packed_varlen_s32k_cp4"]
     q, k, v = inputs.workload_qkv(w)
