@@ -46,11 +46,12 @@
 //     on the first tiles of a row or when that check fails, and the reference
 //     then moves (and O is rescaled) only if the tile max exceeds it by more
 //     than 2^8.  This changes nothing but the reference point of the final
-//     division: lse = m + log l stays exact (l sums the fp32 probabilities),
-//     and O is divided by the sum of the bf16-rounded probabilities, the
-//     weights the PV product applied, so that o's weights add up to one and a
-//     dominant key's rounding (its P is not 1 under a stale reference)
-//     cancels.
+//     division: lse = m + log l stays exact (l sums the fp32 probabilities).
+//     Wavefronts holding a row that sees at most kRoundedSumKeys keys divide
+//     O by the sum of the bf16-rounded probabilities, the weights the PV
+//     product applied, so that o's weights add up to one and a dominant key's
+//     rounding (its P is not 1 under a stale reference) cancels; on longer
+//     rows O is divided by l, the rounding of each P averaging out.
 //
 // Grid order: heaviest query tiles first (the last rows of a share see the
 // most keys), and the Hq / Hkv query heads that read one KV head run back to
@@ -68,6 +69,11 @@ using namespace tiles;
 // 64 NW threads per workgroup.
 
 constexpr float TAU = 8.0f;  // log2 headroom before the running max must move
+
+// Rows that see at most this many keys in all divide O by the sum of the
+// bf16-rounded probabilities (see the softmax below); longer rows by the fp32
+// sum, where the rounding of each P averages out over the keys.
+constexpr int kRoundedSumKeys = 2048;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
@@ -186,6 +192,10 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
     sst_max = sm.seg_start(qpos_max);
     my_sst = qvalid ? sm.seg_start(my_qpos) : 0x7fffffff;
   }
+  // keys this lane's query sees over the whole walk: its position's distance
+  // from the start of its sample, or every key without the causal mask
+  const int my_keys = causal ? my_qpos - (packed ? my_sst : 0) + 1 : cp * L;
+  const bool rounded_sum = __builtin_amdgcn_ballot_w64(qvalid && my_keys <= kRoundedSumKeys) != 0;
 
   // ------------------------------------------------------- Q fragments --
   const __bf16 *qbase = static_cast<const __bf16 *>(a.q) + (a.ring_rank < 0 ? rank * a.q_rank : 0) +
@@ -360,12 +370,12 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
     float ps, pr;
     auto probs = [&](float m_use) {
       // Two row sums.  lse takes the unrounded probabilities, so it is exact
-      // to fp32 rounding.  O is divided by the sum of their bf16 roundings,
-      // the weights the PV product actually applied: the weights of the
-      // final o then add up to one, and a key that dominates its row (P far
-      // above the others, not 1 under the lazy reference) contributes its
-      // value with no error from the rounding of its P.  Two partial sums
-      // keep two add chains.
+      // to fp32 rounding.  On waves holding a row with few keys O is divided
+      // by the sum of their bf16 roundings, the weights the PV product
+      // actually applied: the weights of the final o then add up to one, and
+      // a key that dominates its row (P far above the others, not 1 under
+      // the lazy reference) contributes its value with no error from the
+      // rounding of its P.  Two partial sums keep two add chains.
       float ps0 = 0.0f, ps1 = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < NBK; ++kb) {
@@ -373,23 +383,27 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
         for (int r = 0; r < 16; r += 2) {
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], sl2, -m_use));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r + 1], sl2, -m_use));
-          ps0 += p0;
-          ps1 += p1;
+          ps0 = kb == 0 && r == 0 ? p0 : ps0 + p0;
+          ps1 = kb == 0 && r == 0 ? p1 : ps1 + p1;
           pf[2 * kb + r / 8][r % 8] = (__bf16)p0;
           pf[2 * kb + r / 8][r % 8 + 1] = (__bf16)p1;
         }
       }
       ps = ps0 + ps1;
-      float pr0 = 0.0f, pr1 = 0.0f;
+      if (rounded_sum) {  // wave-uniform
+        float pr0 = 0.0f, pr1 = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 2 * NBK; ++i) {
+        for (int i = 0; i < 2 * NBK; ++i) {
 #pragma unroll
-        for (int e = 0; e < 8; e += 4) {
-          pr0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[i][e], pf[i][e + 1]}, kOnes2, pr0, false);
-          pr1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[i][e + 2], pf[i][e + 3]}, kOnes2, pr1, false);
+          for (int e = 0; e < 8; e += 4) {
+            pr0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[i][e], pf[i][e + 1]}, kOnes2, pr0, false);
+            pr1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[i][e + 2], pf[i][e + 3]}, kOnes2, pr1, false);
+          }
         }
+        pr = pr0 + pr1;
+      } else {
+        pr = ps;
       }
-      pr = pr0 + pr1;
     };
     bool need_max = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
     if (!need_max) {
@@ -541,10 +555,13 @@ hipError_t launch_nw(AttnArgs a, int head_dim, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Four wavefronts (128 query rows) per workgroup: eight measured the same at
-// the 128K-token share, and four gives twice as many workgroups for balance.
+// Eight wavefronts (256 query rows) per workgroup share each K/V tile, which
+// halves the tile loads per query row: alternating on one box, 2.8% faster on
+// the 128K-token share and 4.2% on a 4096-token GQA share than four.  Packed
+// samples keep four wavefronts (128 rows): their query tiles are cut at
+// samples or pieces, and 256-row tiles ran the packed 32K ranks 16% slower.
 hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t stream) {
-  return launch_nw<4>(a, head_dim, stream);
+  return a.sm.nseq > 0 ? launch_nw<4>(a, head_dim, stream) : launch_nw<8>(a, head_dim, stream);
 }
 
 }  // namespace usp
