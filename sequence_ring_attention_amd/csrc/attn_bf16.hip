@@ -289,66 +289,58 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
     while (x.kt >= x.ke && ++tx < a.t_hi) x = step_range(tx);
   };
 
-  // One tile on LDS stage STG (a compile-time constant, so every operand
-  // read below is a per-lane base plus an immediate offset).
-  auto body = [&](auto stage_tag) {
-    constexpr int STG = decltype(stage_tag)::value;
-    // the next tile goes into the other stage while this one is computed
-    int t_nxt = t;
-    StepRange nxt = cur;
-    advance(t_nxt, nxt);
-    if (t_nxt < a.t_hi) issue_tile(nxt.j, nxt.kt * TB, STG ^ 1);
+  // The pieces of one tile.  Every LDS operand read below is a per-lane base
+  // plus an immediate offset when the tile's stage is a compile-time
+  // constant at the call.
+  f32x16 S[NBK];
+  bf16x8 pf[2 * NBK];
 
-    const char *const sK = STG == 0 ? smem0 : smem1;
-    const char *const sV = sK + KL::TILE;
-    const int k0 = cur.kt * TB;
-    // tile class: every (query, key) pair of the workgroup visible?
-    const bool full = __builtin_amdgcn_readfirstlane((k0 >= cur.flo) & (k0 + TB <= cur.fhi));
-
-    // S^T = K Q^T for the tile's NBK 32-key blocks.  The K rows of k-step
-    // ks + AH are read while k-step ks's products run, and the products
-    // alternate between the blocks' accumulators, so no chain waits on
-    // another.
-    f32x16 S[NBK];
+  // S^T = K Q^T for the tile's NBK 32-key blocks.  The K rows of k-step
+  // ks + AH are read while k-step ks's products run, and the products
+  // alternate between the blocks' accumulators, so no chain waits on
+  // another.
+  auto qk = [&](const char *sK) {
 #pragma unroll
     for (int kb = 0; kb < NBK; ++kb) S[kb] = f32x16{};
-    __builtin_amdgcn_s_setprio(1);  // keep the matrix core fed while the SIMD's other waves run softmax
-    {
-      constexpr int NKS = D / 16, AH = 3;
-      bf16x8 kr[AH + 1][NBK];
+    constexpr int NKS = D / 16, AH = 3;
+    bf16x8 kr[AH + 1][NBK];
 #pragma unroll
-      for (int i = 0; i < AH; ++i) {
+    for (int i = 0; i < AH; ++i) {
 #pragma unroll
-        for (int kb = 0; kb < NBK; ++kb)
-          kr[i][kb] = *reinterpret_cast<const bf16x8 *>(sK + koff[i] + 32 * kb * KL::ROW);
-      }
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        if (ks + AH < NKS) {
-#pragma unroll
-          for (int kb = 0; kb < NBK; ++kb)
-            kr[(ks + AH) % (AH + 1)][kb] = *reinterpret_cast<const bf16x8 *>(sK + koff[ks + AH] + 32 * kb * KL::ROW);
-        }
-#pragma unroll
-        for (int kb = 0; kb < NBK; ++kb)
-          S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[ks % (AH + 1)][kb], qf[ks], S[kb], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, NBK * AH, 0);
-#pragma unroll
-      for (int i = 0; i < NKS - AH; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, NBK, 0);
-        if (NBK == 2) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, NBK * AH, 0);
+      for (int kb = 0; kb < NBK; ++kb)
+        kr[i][kb] = *reinterpret_cast<const bf16x8 *>(sK + koff[i] + 32 * kb * KL::ROW);
     }
-    __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (ks + AH < NKS) {
+#pragma unroll
+        for (int kb = 0; kb < NBK; ++kb)
+          kr[(ks + AH) % (AH + 1)][kb] = *reinterpret_cast<const bf16x8 *>(sK + koff[ks + AH] + 32 * kb * KL::ROW);
+      }
+#pragma unroll
+      for (int kb = 0; kb < NBK; ++kb)
+        S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[ks % (AH + 1)][kb], qf[ks], S[kb], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, NBK * AH, 0);
+#pragma unroll
+    for (int i = 0; i < NKS - AH; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, NBK, 0);
+      if (NBK == 2) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NBK * AH, 0);
+  };
 
-    if (!full) {  // diagonal, sample-boundary or ragged tile: elementwise mask
-      // positions grow with the local row, so the keys of block j this lane's
-      // query sees are one local range; as offsets from the lane's first key
-      // row in the tile, [vlo, vhi)
-      const int vlo = cur.llo - k0 - 8 * hh, vhi = cur.lhi - k0 - 8 * hh;
+  // A tile that straddles the diagonal, a sample boundary or the ragged end
+  // (not every pair of the workgroup visible) takes the elementwise mask.
+  // Positions grow with the local row, so the keys of block j this lane's
+  // query sees are one local range; as offsets from the lane's first key row
+  // in the tile, [vlo, vhi).
+  auto mask = [&](const StepRange &x) {
+    const int k0 = x.kt * TB;
+    const bool full = __builtin_amdgcn_readfirstlane((k0 >= x.flo) & (k0 + TB <= x.fhi));
+    if (!full) {
+      const int vlo = x.llo - k0 - 8 * hh, vhi = x.lhi - k0 - 8 * hh;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kc = 16 * (r / 8) + (r % 8);
@@ -357,16 +349,17 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
           S[kb][r] = ((kc + 32 * kb >= vlo) & (kc + 32 * kb < vhi)) ? S[kb][r] : -INFINITY;
       }
     }
+  };
 
-    // online softmax (base 2, scale folded in) against the running reference
-    // m_run.  The tile's row max is only taken when some row has no reference
-    // yet or when a probability left the safe range (a lane's sum of its
-    // probabilities is not below 2^64, which also catches inf); otherwise the
-    // probabilities of the stale reference are used as they are, which
-    // changes nothing but the reference point of the final division.  When
-    // the max is taken, the reference only moves if the tile max exceeds it
-    // by more than 2^TAU.
-    bf16x8 pf[2 * NBK];
+  // online softmax (base 2, scale folded in) against the running reference
+  // m_run.  The tile's row max is only taken when some row has no reference
+  // yet or when a probability left the safe range (a lane's sum of its
+  // probabilities is not below 2^64, which also catches inf); otherwise the
+  // probabilities of the stale reference are used as they are, which
+  // changes nothing but the reference point of the final division.  When
+  // the max is taken, the reference only moves if the tile max exceeds it
+  // by more than 2^TAU.
+  auto softmax = [&]() {
     float ps, pr;
     auto probs = [&](float m_use) {
       // Two row sums.  lse takes the unrounded probabilities, so it is exact
@@ -431,11 +424,12 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
     }
     l_run += ps;
     lr_run += pr;
+  };
 
-    // O^T += V^T P^T, 16 keys per MFMA; V^T read transposed from row-major V
-    __builtin_amdgcn_s_setprio(1);
-    // one 16-key group of P at a time across all D / 32 accumulators (the
-    // chains interleave); the next group's V operands are read meanwhile
+  // O^T += V^T P^T, 16 keys per MFMA; V^T read transposed from row-major V.
+  // One 16-key group of P at a time across all D / 32 accumulators (the
+  // chains interleave); the next group's V operands are read meanwhile.
+  auto pv = [&](const char *sV) {
     auto read_v = [&](int mb, int p) {
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) s16x4 *)(const_cast<char *>(sV) + voff[mb][0] + p * 16 * KL::ROW));
@@ -457,6 +451,24 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
         O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[p & 1][mb], pf[p], O[mb], 0, 0, 0);
     }
     schedule_tr_products<2 * NBK * (D / 32), D / 32>();
+  };
+
+  // One tile on LDS stage STG: the next tile goes into the other stage
+  // while this one is computed.
+  auto body = [&](auto stage_tag) {
+    constexpr int STG = decltype(stage_tag)::value;
+    int t_nxt = t;
+    StepRange nxt = cur;
+    advance(t_nxt, nxt);
+    if (t_nxt < a.t_hi) issue_tile(nxt.j, nxt.kt * TB, STG ^ 1);
+    const char *const sK = STG == 0 ? smem0 : smem1;
+    __builtin_amdgcn_s_setprio(1);  // keep the matrix core fed while the SIMD's other waves run softmax
+    qk(sK);
+    __builtin_amdgcn_s_setprio(0);
+    mask(cur);
+    softmax();
+    __builtin_amdgcn_s_setprio(1);
+    pv(sK + KL::TILE);
     __builtin_amdgcn_s_setprio(0);
     wait_tiles();
     __syncthreads();
@@ -545,13 +557,20 @@ hipError_t launch_nw(AttnArgs a, int head_dim, hipStream_t stream) {
   const int64_t blocks = groups * a.G;
   if (blocks == 0) return hipSuccess;
   const dim3 grid((uint32_t)blocks), block(64 * NW);
-  const bool ps = a.sm.per_sample != 0;
-  if (head_dim == 128)
-    ps ? launch_one<128, NW, true, kWalkTile>(a, grid, block, stream)
-       : launch_one<128, NW, false, kWalkTile>(a, grid, block, stream);
-  else
-    ps ? launch_one<64, NW, true, kWalkTile>(a, grid, block, stream)
-       : launch_one<64, NW, false, kWalkTile>(a, grid, block, stream);
+  if constexpr (NW == 8) {  // unpacked launches only: no per-sample split
+    if (head_dim == 128)
+      launch_one<128, NW, false, kWalkTile>(a, grid, block, stream);
+    else
+      launch_one<64, NW, false, kWalkTile>(a, grid, block, stream);
+  } else {
+    const bool ps = a.sm.per_sample != 0;
+    if (head_dim == 128)
+      ps ? launch_one<128, NW, true, kWalkTile>(a, grid, block, stream)
+         : launch_one<128, NW, false, kWalkTile>(a, grid, block, stream);
+    else
+      ps ? launch_one<64, NW, true, kWalkTile>(a, grid, block, stream)
+         : launch_one<64, NW, false, kWalkTile>(a, grid, block, stream);
+  }
   return hipGetLastError();
 }
 
