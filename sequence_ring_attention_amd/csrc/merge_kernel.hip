@@ -15,7 +15,7 @@ namespace usp {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;  // vector loads per lane in flight (64-row path): 4 ran at 5.6 TB/s, 2 and 8 at 5.5 and 5.3
+constexpr int kUnroll = 4;  // vector loads per lane in flight (64-row path): 4 measured faster than 8
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ inline float4 as_float4(f32x4 v) { return make_float4(v.x, v.y, v.z, v.w); }
@@ -62,26 +62,32 @@ __device__ inline float4 blend(double a1, float4 x, double a2, float4 y) {
 // weights from the lane that computed them.  All four waves read the rows'
 // lse before the barrier; after it, wave 0 writes the merged lse.  Four waves
 // per 64 rows keep four times as many loads in flight as one wave would at
-// sizes that give each CU only a few 64-row groups.
+// sizes that give each CU only a few 64-row groups, and each wave requests
+// its first vectors before the weights' double-precision exp and log1p.
+// Measured with the cache flushed, against one wave per 64 rows: 5.29
+// against 4.87 TB/s for 131072 rows of 128 (one step of a 4096-token GQA
+// share), 6.01 against 5.63 TB/s for 524288 rows; 128- and 512-thread
+// workgroups were slower.
 __global__ __launch_bounds__(kThreads) void lse_merge_rows64_kernel(float *o_acc, float *lse_acc,
                                                                     const float *o_step, const float *lse_step,
                                                                     int64_t rows, int32_t d4_shift) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int d4 = 1 << d4_shift;
-  const int per_wave = d4 * 16;  // vectors of one wave: a quarter of 64 rows x d4
+  constexpr int kWaves = kThreads / 64;
+  const int per_wave = d4 * 64 / kWaves;  // vectors of one wave: its share of 64 rows x d4
   for (int64_t row0 = (int64_t)blockIdx.x * 64; row0 < rows; row0 += (int64_t)gridDim.x * 64) {
     const int64_t my_row = row0 + lane;
     const bool live = my_row < rows;
-    double a1 = 0.0, a2 = 0.0, lse = -INFINITY;
-    merge_weights(live ? (double)lse_acc[my_row] : -INFINITY, live ? (double)lse_step[my_row] : -INFINITY, a1,
-                  a2, lse);
     float4 *acc = reinterpret_cast<float4 *>(o_acc) + row0 * d4;
     const float4 *stp = reinterpret_cast<const float4 *>(o_step) + row0 * d4;
     const int64_t nvec = (rows - row0 < 64 ? rows - row0 : 64) * d4;  // vectors of the rows in range
     const int v0 = wave * per_wave;
-    for (int it0 = 0; it0 < per_wave; it0 += kUnroll * 64) {
-      float4 x[kUnroll], y[kUnroll];
+    // the first kUnroll vectors of both partials are requested before the
+    // weights are computed, so their latency overlaps the double-precision
+    // exp and log1p
+    float4 x[kUnroll], y[kUnroll];
+    auto load = [&](int it0) {
 #pragma unroll
       for (int k = 0; k < kUnroll; ++k) {
         const int v = v0 + it0 + k * 64 + lane;
@@ -90,6 +96,13 @@ __global__ __launch_bounds__(kThreads) void lse_merge_rows64_kernel(float *o_acc
           y[k] = as_float4(__builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(stp + v)));
         }
       }
+    };
+    load(0);
+    double a1 = 0.0, a2 = 0.0, lse = -INFINITY;
+    merge_weights(live ? (double)lse_acc[my_row] : -INFINITY, live ? (double)lse_step[my_row] : -INFINITY, a1,
+                  a2, lse);
+    for (int it0 = 0; it0 < per_wave; it0 += kUnroll * 64) {
+      if (it0 > 0) load(it0);
 #pragma unroll
       for (int k = 0; k < kUnroll; ++k) {
         const int v = v0 + it0 + k * 64 + lane;
