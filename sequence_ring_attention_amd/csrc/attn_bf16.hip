@@ -57,6 +57,8 @@
 // most keys), and the Hq / Hkv query heads that read one KV head run back to
 // back on one XCD (workgroups are dealt to the 8 XCDs round-robin) so that
 // their K/V tiles are shared through that XCD's L2.
+#include <algorithm>
+
 #include "attn_tiles.h"
 #include "usp_internal.h"
 
@@ -154,7 +156,11 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
   const int b = rest % a.B;
   const int order = rest / a.B;
   int rank, lt;
-  if (a.ring_rank >= 0) {
+  if (a.n_order > 0) {  // packed samples: the launch's heaviest-first order
+    const int idx = a.tile_order[order];
+    rank = a.ring_rank >= 0 ? a.ring_rank : idx / a.n_qtiles;
+    lt = idx % a.n_qtiles;
+  } else if (a.ring_rank >= 0) {
     rank = a.ring_rank;
     lt = a.n_qtiles - 1 - order;
   } else {
@@ -547,11 +553,50 @@ void launch_one(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t stream) {
 // not used.
 constexpr int kWalkTile = 64;
 
+// Key tiles a query tile of `rank` visits over the launch's ring steps: the
+// kernel's per-step tile range, computed on the host.
+int tile_work(const AttnArgs &a, int BM, int rank, int lt) {
+  const ShareMap sm(a.c, a.cp, a.L, a.sm);
+  int q0, qend;
+  if (a.sm.per_sample) {
+    piece_tile(a.sm, a.ps_tiles, a.cp, BM, lt, q0, qend);
+  } else {
+    q0 = lt * BM;
+    qend = q0 + BM < a.L ? q0 + BM : a.L;
+  }
+  const int pmin = sm.pos(rank, q0), pmax = sm.pos(rank, qend - 1), smin = sm.seg_start(pmin);
+  int work = 0;
+  for (int t = a.t_lo; t < a.t_hi; ++t) {
+    const int j = ((rank - t) % a.cp + a.cp) % a.cp;
+    const int hi = a.causal ? sm.count_le(j, pmax) : a.L, lo = sm.count_le(j, smin - 1);
+    if (hi > lo) work += (hi + kWalkTile - 1) / kWalkTile - lo / kWalkTile;
+  }
+  return work;
+}
+
+// Packed samples: the workgroups of a launch in decreasing order of work, so
+// that long ones start first and short ones fill the last round (the tile
+// index orders work only for one sequence, whose later rows see more keys).
+void order_tiles(AttnArgs &a, int BM) {
+  a.n_order = 0;
+  const int n = a.n_ranks * a.n_qtiles;
+  if (a.sm.nseq == 0 || n > kMaxTileOrder) return;
+  int work[kMaxTileOrder], idx[kMaxTileOrder];
+  for (int i = 0; i < n; ++i) {
+    idx[i] = i;
+    work[i] = tile_work(a, BM, a.ring_rank >= 0 ? a.ring_rank : i / a.n_qtiles, i % a.n_qtiles);
+  }
+  std::stable_sort(idx, idx + n, [&](int x, int y) { return work[x] > work[y]; });
+  for (int i = 0; i < n; ++i) a.tile_order[i] = (uint16_t)idx[i];
+  a.n_order = n;
+}
+
 template <int NW>
 hipError_t launch_nw(AttnArgs a, int head_dim, hipStream_t stream) {
   constexpr int BM = 32 * NW;
   a.n_qtiles = (a.L + BM - 1) / BM;
   if (a.sm.per_sample) a.n_qtiles = fill_piece_tiles(a.sm, a.cp, BM, a.ps_tiles);
+  order_tiles(a, BM);
   const int64_t groups = (int64_t)a.n_ranks * a.n_qtiles * a.B * a.Hkv;
   a.xcd_remap = groups % 8 == 0;
   const int64_t blocks = groups * a.G;

@@ -19,6 +19,8 @@ namespace usp {
 
 constexpr int kMaxSeqs = 256;
 
+__host__ __device__ inline int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
 // Packed samples and the split, passed by value with the kernel arguments.
 struct Samples {
   int32_t nseq;        // 0: one sequence, no sample mask
@@ -33,13 +35,13 @@ struct ShareMap {
 
   // A kernel built for the whole-stream split only passes per_sample_ok =
   // false, which removes the per-sample branches at compile time.
-  __device__ ShareMap(int c_, int cp_, int L_, const Samples &s, bool per_sample_ok = true)
+  __host__ __device__ ShareMap(int c_, int cp_, int L_, const Samples &s, bool per_sample_ok = true)
       : c(c_), cp(cp_), L(L_), sm(&s), ps(per_sample_ok && s.per_sample) {}
 
-  __device__ bool packed() const { return sm->nseq > 0; }
+  __host__ __device__ bool packed() const { return sm->nseq > 0; }
 
   // Sample n holding global position p: cu[n] <= p < cu[n + 1].
-  __device__ int sample_of(int p) const {
+  __host__ __device__ int sample_of(int p) const {
     int lo = 0, hi = sm->nseq;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -49,7 +51,7 @@ struct ShareMap {
   }
 
   // Global position of local row i of `rank`'s share.
-  __device__ int pos(int rank, int i) const {
+  __host__ __device__ int pos(int rank, int i) const {
     if (!ps) return i < c ? rank * c + i : (2 * cp - 1 - rank) * c + (i - c);
     const int n = sample_of(i * cp);  // the sample's rows start at local row cu[n] / cp
     const int b = sm->cu[n], m = (sm->cu[n + 1] - b) / (2 * cp), o = i - b / cp;
@@ -57,31 +59,31 @@ struct ShareMap {
   }
 
   // Number of local rows of `rank`'s share at positions <= p (a prefix).
-  __device__ int count_le(int rank, int p) const {
+  __host__ __device__ int count_le(int rank, int p) const {
     if (!ps) {
-      const int a = min(max(p - rank * c + 1, 0), c);
-      const int b = min(max(p - (2 * cp - 1 - rank) * c + 1, 0), c);
+      const int a = clampi(p - rank * c + 1, 0, c);
+      const int b = clampi(p - (2 * cp - 1 - rank) * c + 1, 0, c);
       return a + b;
     }
     if (p < 0) return 0;
     if (p >= cp * L) return L;
     const int n = sample_of(p);
     const int b = sm->cu[n], m = (sm->cu[n + 1] - b) / (2 * cp), q = p - b;
-    return b / cp + min(max(q - rank * m + 1, 0), m) + min(max(q - (2 * cp - 1 - rank) * m + 1, 0), m);
+    return b / cp + clampi(q - rank * m + 1, 0, m) + clampi(q - (2 * cp - 1 - rank) * m + 1, 0, m);
   }
 
   // count_le(rank, p) for s0 - 1 <= p < s1, where [s0, s1) is a sample: the
   // per-sample split then needs no search (the samples before it put s0 / cp
   // rows in every share).
-  __device__ int count_le_in(int rank, int p, int s0, int s1) const {
+  __host__ __device__ int count_le_in(int rank, int p, int s0, int s1) const {
     if (!ps) return count_le(rank, p);
     const int m = (s1 - s0) / (2 * cp), q = p - s0;
-    return s0 / cp + min(max(q - rank * m + 1, 0), m) + min(max(q - (2 * cp - 1 - rank) * m + 1, 0), m);
+    return s0 / cp + clampi(q - rank * m + 1, 0, m) + clampi(q - (2 * cp - 1 - rank) * m + 1, 0, m);
   }
 
   // First position of the sample holding p, and the first position after it.
-  __device__ int seg_start(int p) const { return sm->cu[sample_of(p)]; }
-  __device__ int seg_end(int p) const { return sm->cu[sample_of(p) + 1]; }
+  __host__ __device__ int seg_start(int p) const { return sm->cu[sample_of(p)]; }
+  __host__ __device__ int seg_end(int p) const { return sm->cu[sample_of(p) + 1]; }
 };
 
 // Query tiles of a per-sample share cut at its pieces: the share holds two

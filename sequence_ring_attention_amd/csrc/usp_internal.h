@@ -82,6 +82,8 @@ hipError_t launch_lse_merge(float *o_acc, float *lse_acc, const float *o_step,
 
 // ------------------------------------------------------------- attention --
 
+constexpr int kMaxTileOrder = 640;
+
 struct AttnArgs {
   const void *q;
   const void *k;
@@ -109,6 +111,11 @@ struct AttnArgs {
   int32_t xcd_remap;  // 1: group blocks sharing a KV head on one XCD
   Samples sm;         // packed samples and the split of the shares
   int32_t ps_tiles[kMaxSeqs + 1];  // per-sample split, bf16: fill_piece_tiles at launch
+  // bf16 walk of packed samples: the (rank, query tile) pairs, rank *
+  // n_qtiles + tile, heaviest first (set at launch; n_order = 0: the tile
+  // index gives the order)
+  int32_t n_order;
+  uint16_t tile_order[kMaxTileOrder];
 };
 static_assert(sizeof(AttnArgs) <= 4096, "kernel arguments above 4 KiB");
 
