@@ -619,13 +619,30 @@ hipError_t launch_nw(AttnArgs a, int head_dim, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cus[dev];
+}
+
 // Eight wavefronts (256 query rows) per workgroup share each K/V tile, which
 // halves the tile loads per query row: alternating on one box, 2.8% faster on
 // the 128K-token share and 4.2% on a 4096-token GQA share than four.  Packed
 // samples keep four wavefronts (128 rows): their query tiles are cut at
 // samples or pieces, and 256-row tiles ran the packed 32K ranks 16% slower.
+// So do launches that would give fewer than two eight-wave workgroups per CU
+// (one round of tiles of unequal work, e.g. two query heads of the 128K
+// share): four-wave workgroups run two per CU and halve each tile's work.
 hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t stream) {
-  return a.sm.nseq > 0 ? launch_nw<4>(a, head_dim, stream) : launch_nw<8>(a, head_dim, stream);
+  if (a.sm.nseq > 0) return launch_nw<4>(a, head_dim, stream);
+  const int64_t blocks8 = (int64_t)a.n_ranks * ((a.L + 255) / 256) * a.B * a.Hkv * a.G;
+  return blocks8 < 2 * (int64_t)device_cus() ? launch_nw<4>(a, head_dim, stream) : launch_nw<8>(a, head_dim, stream);
 }
 
 }  // namespace usp

@@ -225,3 +225,43 @@ def test_tiny_fp32_workload_all_ranks():
     for r in range(w.rd):
         p = ix.zigzag_share_positions(w.S, w.rd, r)
         check_close(f64(o[r]), f64(lse[r]), o_ref[:, p], l_ref[:, :, p], "fp32", f"{w.name} r{r}")
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,c", [(64, 64, 8, 1000), (128, 64, 16, 1100)])
+def test_eight_wave_walk_ragged(D, Hq, Hkv, c):
+    """Launches large enough for eight-wave workgroups (at least two per CU)
+    whose shares do not divide into 256-row query tiles: the walk of every
+    rank in one launch and rank 1's ring steps (fp32 partials, merged), on
+    sampled rows including the ragged tail, against the oracle."""
+    cp = 2
+    S = 2 * cp * c
+    dev = device()
+    q, k, v = inputs.qkv(1, S, Hq, Hkv, D, "bf16", 9300 + D)
+    kn, vn, qn = f64(k), f64(v), f64(q)
+    qs, ks, vs = shares(q.to(dev), cp), shares(k.to(dev), cp), shares(v.to(dev), cp)
+    L = S // cp
+    o = torch.empty_like(qs)
+    lse = torch.empty(cp, Hq, 1, L, dtype=torch.float32, device=dev)
+    desc = B.attn_desc(S, cp, qs, ks, vs, o=o, all_ranks=True)
+    say("eight-wave walk", D, Hq, Hkv, c)
+    B.usp_attn_fwd(qs, ks, vs, o, lse, desc, -1)
+    r = 1
+    qr = qs[r].contiguous()
+    d1 = B.attn_desc(S, cp, qr, ks, vs)
+    acc = torch.empty(Hq, 1, L, D, dtype=torch.float32, device=dev)
+    lacc = torch.empty(Hq, 1, L, dtype=torch.float32, device=dev)
+    o_st, l_st = torch.empty_like(acc), torch.empty_like(lacc)
+    for t in range(cp):
+        B.usp_ring_attn_step_fwd(qr, ks, vs, acc if t == 0 else o_st, lacc if t == 0 else l_st, d1, r, t)
+        if t:
+            B.usp_lse_merge(acc, lacc, o_st, l_st)
+    torch.cuda.synchronize()
+    tail = list(range(L - 210, L))   # the last, partial 256-row tile and the one before
+    for rr in range(cp):
+        rows = sample_rows(L, c, 24, 60 + rr, extra=tail[::7] + [L - 1])
+        pos = ix.zigzag_share_positions(S, cp, rr)[rows]
+        o_ref, l_ref = _oracle_rows(qn, kn, vn, pos, D ** -0.5)
+        check_close(f64(o[rr][:, rows]), f64(lse[rr][:, :, rows]), o_ref, l_ref, "bf16", f"eight-wave walk D{D} r{rr}")
+        if rr == r:
+            check_close(np.transpose(f64(acc[:, :, rows]), (1, 2, 0, 3)), f64(lacc[:, :, rows]), o_ref, l_ref, "bf16",
+                        f"eight-wave steps D{D} r{rr}")
