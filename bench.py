@@ -110,22 +110,32 @@ def plain_copy_reference(nbytes):
             "frac_hbm": 2 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
-def _timed(fn, reps=20):
+def _timed(fn, reps=20, batch_ms=2.0):
     """HIP-event times (ms) of fn() on the current stream after one untimed
-    call: median, min and max of ``reps`` repetitions."""
+    call: median, min and max over ``reps`` repetitions of the time per call.
+    A call shorter than ``batch_ms`` is timed as a run of back-to-back calls
+    between one pair of events (as a ring loop issues its launches), so that
+    the events' own latency, tens of microseconds, does not count against a
+    kernel that runs for a fraction of a millisecond."""
     import torch
-    fn()
-    torch.cuda.synchronize()
-    out = []
-    for _ in range(reps):
+
+    def run(n):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        fn()
+        for _ in range(n):
+            fn()
         b.record()
         torch.cuda.synchronize()
-        out.append(a.elapsed_time(b))
-    out.sort()
-    return {"ms": out[len(out) // 2], "ms_min": out[0], "ms_max": out[-1], "reps": reps}
+        return a.elapsed_time(b) / n
+
+    fn()
+    torch.cuda.synchronize()
+    per = 1
+    est = run(1)
+    if est < batch_ms:
+        per = min(16, max(1, int(batch_ms / max(est, 1e-3))))
+    out = sorted(run(per) for _ in range(reps))
+    return {"ms": out[len(out) // 2], "ms_min": out[0], "ms_max": out[-1], "reps": reps, "calls_per_rep": per}
 
 
 def _time(fn, reps=20):

@@ -156,7 +156,7 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
   const int b = rest % a.B;
   const int order = rest / a.B;
   int rank, lt;
-  if (a.n_order > 0) {  // packed samples: the launch's heaviest-first order
+  if (a.n_order > 0) {  // the launch's heaviest-first order
     const int idx = a.tile_order[order];
     rank = a.ring_rank >= 0 ? a.ring_rank : idx / a.n_qtiles;
     lt = idx % a.n_qtiles;
@@ -574,13 +574,15 @@ int tile_work(const AttnArgs &a, int BM, int rank, int lt) {
   return work;
 }
 
-// Packed samples: the workgroups of a launch in decreasing order of work, so
-// that long ones start first and short ones fill the last round (the tile
-// index orders work only for one sequence, whose later rows see more keys).
+// The workgroups of a launch in decreasing order of work, so that long ones
+// start first and short ones fill the last round.  The tile index alone
+// orders work only within one zigzag chunk of one rank: across the ranks of
+// an all-ranks launch the first chunk's tiles grow with the rank and the
+// second chunk's shrink, and packed samples restart at every sample.
 void order_tiles(AttnArgs &a, int BM) {
   a.n_order = 0;
   const int n = a.n_ranks * a.n_qtiles;
-  if (a.sm.nseq == 0 || n > kMaxTileOrder) return;
+  if (n > kMaxTileOrder) return;
   int work[kMaxTileOrder], idx[kMaxTileOrder];
   for (int i = 0; i < n; ++i) {
     idx[i] = i;

@@ -111,9 +111,9 @@ struct AttnArgs {
   int32_t xcd_remap;  // 1: group blocks sharing a KV head on one XCD
   Samples sm;         // packed samples and the split of the shares
   int32_t ps_tiles[kMaxSeqs + 1];  // per-sample split, bf16: fill_piece_tiles at launch
-  // bf16 walk of packed samples: the (rank, query tile) pairs, rank *
-  // n_qtiles + tile, heaviest first (set at launch; n_order = 0: the tile
-  // index gives the order)
+  // bf16 walk: the (rank, query tile) pairs, rank * n_qtiles + tile,
+  // heaviest first (set at launch when there are at most kMaxTileOrder;
+  // n_order = 0: the tile index gives the order)
   int32_t n_order;
   uint16_t tile_order[kMaxTileOrder];
 };
