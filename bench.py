@@ -747,8 +747,8 @@ def backward_walk(share, fwd_flops, reps=20):
     prep_bytes = 2 * o.numel() * o.element_size() + 3 * lse.numel() * 4
     return {"entry": "usp_attn_bwd", "ms": bwd_ms, "TFLOP/s": flops / (bwd_ms * 1e-3) / 1e12,
             "frac_mfma": flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-            "work_per_launch_tflop": flops / 1e12, "executed_products": 8, "algorithmic_products": 5,
-            "executed_by_pass": {"dQ": "S, dP, dQ", "dV": "S, dV", "dK": "S, dP, dK"},
+            "work_per_launch_tflop": flops / 1e12, "executed_products": 7, "algorithmic_products": 5,
+            "executed_by_pass": {"dQ": "S, dP, dQ", "dK/dV": "S, dP, dV, dK"},
             "prep": {"ms": prep_ms, "bytes": prep_bytes, "GB/s": prep_bytes / (prep_ms * 1e-3) / 1e9}}
 
 

@@ -12,7 +12,7 @@
 // tiles above the diagonal are never visited and only tiles that straddle it
 // evaluate the elementwise mask.
 //
-// Three passes, each the single owner of what it writes (no atomics, results
+// Two passes, each the single owner of what it writes (no atomics, results
 // independent of scheduling):
 //   * dQ pass -- a workgroup of 4 wavefronts owns 128 query rows of one
 //     (rank, query head, batch), walks the steps' 64-key tiles like the
@@ -22,18 +22,16 @@
 //     wave's Q and dO rows in registers; dQ^T += K^T dS^T reads K transposed
 //     from the same row-major LDS tile (ds_read_b64_tr_b16) and takes dS^T
 //     straight from the registers.
-//   * dV pass and dK pass -- a workgroup of 4 wavefronts owns 128 keys of
-//     one (KV block, KV head, batch); each wavefront holds its 32 keys' K
-//     (and, for dK, V) rows in registers and keeps one accumulator, dV^T or
-//     dK^T.  For every rank that reaches the block and every query head
-//     reading the KV head, the visible 64-row query tiles of Q and dO stream
-//     through LDS (double buffered, buffer loads straight to LDS, the
-//     forward's swizzle) with the tile's delta and lse2.  S = Q K^T and
+//   * dK/dV pass -- a workgroup of 8 wavefronts owns 256 keys of one (KV
+//     block, KV head, batch); each wavefront holds its 32 keys' K rows and
+//     both accumulators, dV^T and dK^T, in registers, and its V rows in a
+//     private LDS area.  For every rank that reaches the block and every
+//     query head reading the KV head, the visible 64-row query tiles of Q and
+//     dO stream through LDS (double buffered, buffer loads straight to LDS,
+//     the forward's swizzle) with the tile's delta and lse2.  S = Q K^T and
 //     dP = dO V^T take Q and dO rows as the M operand; dV^T += dO^T P and
-//     dK^T += Q^T dS read dO and Q transposed.  One pass holding both
-//     accumulators needs about 480 registers per lane, one wavefront per
-//     SIMD; split, each pass fits two, and the pair runs faster although S
-//     is computed twice.
+//     dK^T += Q^T dS read dO and Q transposed.  S is computed once for both
+//     gradients: four products per tile.
 // The scale is applied once, to the final dQ and dK.
 #include "attn_tiles.h"
 #include "usp_internal.h"
@@ -46,7 +44,6 @@ using namespace tiles;
 constexpr int NW = 4;          // wavefronts per workgroup
 constexpr int BM = 32 * NW;    // query rows per dQ workgroup
 constexpr int KW = 8;          // wavefronts per dK/dV workgroup (32 keys each)
-constexpr int NS = 3;          // dK/dV pipeline stages (query tiles in flight + 1): 2, 3 or 4
 constexpr int STATS = 512;     // bytes of one tile's delta[64] and lse2[64]
 
 __device__ inline int mod_cp(int x, int cp) {
@@ -387,37 +384,27 @@ struct QRange {
   int flo, fhi;
 };
 
-// DV: the dV pass (S, then dV^T += dO^T P); otherwise the dK pass (S and dP,
-// then dK^T += Q^T dS).  Each keeps one accumulator set, which leaves room
-// for two wavefronts per SIMD.
-//
-// Query tiles stream through an NS-stage ring in LDS, issued NS - 1 tiles
-// ahead: a Q and a dO tile (direct buffer loads, the forward's swizzle) and
-// the tile's delta and lse2 (dword direct loads by wavefronts 0 and 1).  Each
-// wavefront waits with a count of its own loads still allowed in flight, and
-// one barrier per tile both publishes the tile and frees the stage read in
-// the previous tile for the next issue.  PS as in the dQ pass.
-template <int D, bool DV, int KW, int NS, bool PS>
+// Both key-side gradients in one pass: S = Q K^T and dP = dO V^T once per
+// query tile, then dV^T += dO^T P and dK^T += Q^T dS.  Each wavefront holds
+// its 32 keys' K rows and both accumulators in registers (160 of them) and
+// keeps its V rows in a private LDS area (written once, read back as the dP
+// operand), so that the pass fits two wavefronts per SIMD; the V rows in
+// registers as well would spill.  Query tiles stream through a two-stage
+// ring (the V areas take the LDS a third stage would need).  Measured on the
+// 128K-token share's backward against separate dV and dK passes (which
+// computed S twice): 60.1 against 69.7 ms for the whole backward.
+template <int D, bool PS>
 __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
-  static_assert(NS >= 2 && NS <= 4, "two to four pipeline stages");
-  constexpr int BK = 32 * KW;  // keys per workgroup
+  constexpr int BK = 32 * KW;
   constexpr int TILE = Lds<D>::TILE;
-  constexpr int STAGE = 2 * TILE;                        // Q tile, then dO tile
-  constexpr int NBLK = Lds<D>::KIB_PER_TILE / KW;        // direct loads per wavefront per tile
-  constexpr int OPS = 2 * NBLK;                          // vector memory ops per wavefront per tile
-  // one array per stage (tiles, then the tile's delta[64] and lse2[64]):
-  // the reads of one stage are then provably disjoint from the direct loads
-  // filling the others, and the compiler does not make them wait for those
-  constexpr int X2 = NS >= 3 ? STAGE + STATS : 16, X3 = NS == 4 ? STAGE + STATS : 16;  // stages in use
+  constexpr int STAGE = 2 * TILE;
+  constexpr int NBLK = Lds<D>::KIB_PER_TILE / KW;
+  constexpr int OPS = 2 * NBLK;
+  constexpr int VROWS = 32 * Lds<D>::ROW;  // one wavefront's V rows
   __shared__ __attribute__((aligned(1024))) char ring0[STAGE + STATS];
   __shared__ __attribute__((aligned(1024))) char ring1[STAGE + STATS];
-  __shared__ __attribute__((aligned(1024))) char ring2[X2];
-  __shared__ __attribute__((aligned(1024))) char ring3[X3];
-  // every stage index below is a compile-time constant after unrolling
-  auto stage_base = [&](int stg) -> char * { return stg == 0 ? ring0 : stg == 1 ? ring1 : stg == 2 ? ring2 : ring3; };
+  __shared__ __attribute__((aligned(1024))) char vrows[KW * VROWS];
 
-  // work item: key tiles in order of local index (the first chunk of a
-  // share holds the earliest positions, which the most queries see)
   const int n_slots = a.ring_rank >= 0 ? a.t_hi - a.t_lo : a.cp;
   int rest = blockIdx.x;
   const int g = rest % a.Hkv;
@@ -460,13 +447,10 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
       x.qt = lo / BN;
       x.qe = (hi + BN - 1) / BN;
     }
-    // query row i of rank r is at or before position p iff i < count_le(r, p)
     x.flo = causal ? sm.count_le(r, kpos_max - 1) : 0;
     x.fhi = packed ? sm.count_le(r, kend_min - 1) : L;
     return x;
   };
-  // tile iterator: rank r, query head offset h in the group, tile range;
-  // exhausted when r > r_last
   struct It {
     int r, h;
     QRange x;
@@ -486,26 +470,28 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
   };
   It cur{r_first, 0, q_range(r_first)};
   normalise(cur);
-  // this lane's key's visible query rows of rank lane_r, [lane_lo, lane_hi)
   int lane_r = -1, lane_lo = 0, lane_hi = 0;
-  if (cur.r > r_last) return;  // no query sees these keys: nothing to add (uniform)
+  if (cur.r > r_last) return;  // no query sees these keys (uniform)
 
-  bf16x8 kf[D / 16], vf[DV ? 1 : D / 16];
+  const TileOffsets<D> off(lane);
+  bf16x8 kf[D / 16];
   const int64_t kvo = j * a.kv_blk;
   load_row_frags<D>(kf, static_cast<const __bf16 *>(a.k) + kvo + b * a.k_sb + g * a.k_sh + (int64_t)krow * a.k_ss,
                     kvalid, hh);
-  if (!DV)
+  // this wavefront's V rows, key n stored at row sig(n) of its area so that
+  // the tile-row offsets read them back as the N operand
+  char *const myv = vrows + wave * VROWS;
+  {
+    bf16x8 vf[D / 16];
     load_row_frags<D>(vf, static_cast<const __bf16 *>(a.v) + kvo + b * a.v_sb + g * a.v_sh + (int64_t)krow * a.v_ss,
                       kvalid, hh);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) *reinterpret_cast<bf16x8 *>(myv + off.row[ks]) = vf[ks];
+  }
 
   const int64_t qbytes = a.q_ss * 2, dbytes = a.do_ss * 2;
-  uint32_t qvoff[NBLK], dvoff[NBLK];
-  tile_load_offsets<D, KW>(qvoff, qbytes, wave, lane);
-  tile_load_offsets<D, KW>(dvoff, dbytes, wave, lane);
   const uint32_t q_extent = (uint32_t)((L - 1) * qbytes + 2 * D);
   const uint32_t d_extent = (uint32_t)((L - 1) * dbytes + 2 * D);
-  // delta and lse2 as two bounded arrays: a read past a tile's last row
-  // returns a neighbour's statistics or 0, both harmless on masked rows
   const __amdgpu_buffer_rsrc_t delta_rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.stats), 0, (uint32_t)(a.rows * 4), RSRC_WORD3);
   const __amdgpu_buffer_rsrc_t lse2_rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -516,9 +502,16 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
                      2 * ((a.ring_rank < 0 ? it.r * a.q_rank : 0) + b * a.q_sb + hq * a.q_sh);
     const char *db = static_cast<const char *>(a.dout) +
                      2 * ((a.ring_rank < 0 ? it.r * a.do_rank : 0) + b * a.do_sb + hq * a.do_sh);
-    char *const st = stage_base(stg);
-    issue_tile_lds<D, KW>(st, qb, q_extent, qbytes, it.x.qt * BN, L, wave, lane, qvoff);
-    issue_tile_lds<D, KW>(st + TILE, db, d_extent, dbytes, it.x.qt * BN, L, wave, lane, dvoff);
+    char *const st = stg == 0 ? ring0 : ring1;
+    // the per-lane load offsets are recomputed here (a few integer ops): kept
+    // across the loop they would be spilled
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    uint32_t qvoff[NBLK], dvoff[NBLK];
+    tile_load_offsets<D, KW>(qvoff, qbytes, wave, ln);
+    tile_load_offsets<D, KW>(dvoff, dbytes, wave, ln);
+    issue_tile_lds<D, KW>(st, qb, q_extent, qbytes, it.x.qt * BN, L, wave, ln, qvoff);
+    issue_tile_lds<D, KW>(st + TILE, db, d_extent, dbytes, it.x.qt * BN, L, wave, ln, dvoff);
     if (wave < 2) {
       const int rs = a.ring_rank >= 0 ? 0 : it.r;
       const int64_t srow = (((int64_t)rs * a.Hq + hq) * a.B + b) * L + it.x.qt * BN;
@@ -527,64 +520,49 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
                                                (uint32_t)((srow + lane) * 4), 0, 0, 0);
     }
   };
-  // wait until the tile `after` tiles before the newest one has landed
   auto wait_tile = [&](int after) {
     if (wave < 2) {
-      if (after >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (OPS + 1)) : "memory");
-      else if (after == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(OPS + 1) : "memory");
+      if (after >= 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(OPS + 1) : "memory");
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
-      if (after >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * OPS) : "memory");
-      else if (after == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(OPS) : "memory");
+      if (after >= 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(OPS) : "memory");
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
   };
-  // wait_tile covers up to two younger tiles in flight (NS - 2)
-  const TileOffsets<D> off(lane);
 
-  f32x16 acc[D / 32];  // dV^T or dK^T
+  f32x16 accv[D / 32], acck[D / 32];  // dV^T and dK^T
 #pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb) acc[mb] = f32x16{};
+  for (int mb = 0; mb < D / 32; ++mb) {
+    accv[mb] = f32x16{};
+    acck[mb] = f32x16{};
+  }
   const float sl2 = a.scale_log2;
 
-  // prologue: the first NS - 1 tiles
   It ld = cur;
-  int pending = 0;  // tiles issued and not yet computed (uniform)
-#pragma unroll
-  for (int k = 0; k < NS - 1; ++k) {
-    if (ld.r <= r_last) {
-      issue(ld, k);
-      ++pending;
-      advance(ld);
-    }
-  }
+  int pending = 0;
+  issue(ld, 0);
+  ++pending;
+  advance(ld);
 
   auto body = [&](auto stage_tag) {
     constexpr int STG = decltype(stage_tag)::value;
     wait_tile(pending - 1);
-    // tile ready for every wavefront; the previous stage is free.  All LDS
-    // writes here are direct loads each wavefront has just waited for, so a
-    // plain barrier suffices: a workgroup fence would also drain the loads
-    // still in flight for the next stages
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (ld.r <= r_last) {
-      issue(ld, (STG + NS - 1) % NS);
+      issue(ld, STG ^ 1);
       ++pending;
       advance(ld);
     }
-
-    const char *const sQ = stage_base(STG);
+    const char *const sQ = STG == 0 ? ring0 : ring1;
     const char *const sD = sQ + TILE;
     const float *const sst = reinterpret_cast<const float *>(sQ + STAGE);
     const int r = cur.r;
     const int q0 = cur.x.qt * BN;
     const bool full =
         __builtin_amdgcn_readfirstlane((k0 + BK <= L) & (q0 >= cur.x.flo) & (q0 + BN <= cur.x.fhi));
-    // the queries of rank r that see this lane's key are one local range; as
-    // offsets from the lane's first query row in the tile, [vlo, vhi)
     int vlo = 0, vhi = BN;
     if (!full) {
-      if (r != lane_r) {  // uniform: the range moves with the rank only
+      if (r != lane_r) {
         lane_r = r;
         lane_lo = causal ? sm.count_le(r, my_kpos - 1) : 0;
         lane_hi = kvalid ? (packed ? sm.count_le(r, my_kend - 1) : L) : 0;
@@ -592,119 +570,90 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
       vlo = lane_lo - q0 - 8 * hh;
       vhi = lane_hi - q0 - 8 * hh;
     }
-
-    if (DV) {
-      // S = Q K^T for the tile's two 32-query blocks as two interleaved
-      // accumulator chains, then P and dV^T += dO^T P
-      f32x16 S2[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      // S = Q K^T, then P (kept in fp32 for dS, rounded for dV), dV^T +=
+      // dO^T P, then dP = dO V^T, dS and dK^T += Q^T dS: P's rounding and
+      // the dV products are done before dP takes its registers
+      f32x16 S = f32x16{};
       __builtin_amdgcn_s_setprio(1);
-      bf16x8 qa[D / 16], qb[D / 16];
+      {
+        bf16x8 qa[2];
+        qa[0] = *reinterpret_cast<const bf16x8 *>(sQ + off.row[0] + blk * 32 * Lds<D>::ROW);
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        qa[ks] = *reinterpret_cast<const bf16x8 *>(sQ + off.row[ks]);
-        qb[ks] = *reinterpret_cast<const bf16x8 *>(sQ + off.row[ks] + 32 * Lds<D>::ROW);
-      }
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        S2[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], S2[0], 0, 0, 0);
-        S2[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[ks], kf[ks], S2[1], 0, 0, 0);
-      }
-      schedule_products<D / 8, D / 16>();
-      __builtin_amdgcn_s_setprio(0);
-      bf16x8 pf[4];
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        // this lane's queries: 32 blk + 16 (r / 8) + 8 hh + r % 8
-        const float4 *l4 = reinterpret_cast<const float4 *>(sst + 64 + 32 * blk + 8 * hh);
-        const float4 ll[4] = {l4[0], l4[1], l4[4], l4[5]};
-        if (!full) {
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int qc = 32 * blk + 16 * (rr / 8) + (rr % 8);
-            S2[blk][rr] = ((qc >= vlo) & (qc < vhi)) ? S2[blk][rr] : -INFINITY;
-          }
+        for (int ks = 0; ks < D / 16; ++ks) {
+          if (ks + 1 < D / 16)
+            qa[(ks + 1) & 1] = *reinterpret_cast<const bf16x8 *>(sQ + off.row[ks + 1] + blk * 32 * Lds<D>::ROW);
+          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks & 1], kf[ks], S, 0, 0, 0);
         }
+      }
+      __builtin_amdgcn_s_setprio(0);
+      const float4 *d4 = reinterpret_cast<const float4 *>(sst + 32 * blk + 8 * hh);
+      const float4 *l4 = reinterpret_cast<const float4 *>(sst + 64 + 32 * blk + 8 * hh);
+      if (!full) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-          const float4 lq4 = ll[rr / 4];
-          const float ls = (rr % 4 == 0) ? lq4.x : (rr % 4 == 1) ? lq4.y : (rr % 4 == 2) ? lq4.z : lq4.w;
-          pf[2 * blk + rr / 8][rr % 8] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(S2[blk][rr], sl2, -ls));
+          const int qc = 32 * blk + 16 * (rr / 8) + (rr % 8);
+          S[rr] = ((qc >= vlo) & (qc < vhi)) ? S[rr] : -INFINITY;
+        }
+      }
+      bf16x8 pf[2];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 lq4 = l4[(q4 / 2) * 4 + (q4 % 2)];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rr = 4 * q4 + e;
+          const float ls = e == 0 ? lq4.x : e == 1 ? lq4.y : e == 2 ? lq4.z : lq4.w;
+          S[rr] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[rr], sl2, -ls));
+          pf[rr / 8][rr % 8] = (__bf16)S[rr];
         }
       }
       __builtin_amdgcn_s_setprio(1);
-      // operands of the next accumulator are read while this one's products run
-      bf16x8 vt[2][4];
-#pragma unroll
-      for (int sl = 0; sl < 4; ++sl) vt[0][sl] = read_tr<D>(sD, off, 0, sl);
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) {
-        if (mb + 1 < D / 32) {
 #pragma unroll
-          for (int sl = 0; sl < 4; ++sl) vt[(mb + 1) & 1][sl] = read_tr<D>(sD, off, mb + 1, sl);
+        for (int sl = 0; sl < 2; ++sl) {
+          const bf16x8 dt = read_tr<D>(sD, off, mb, 2 * blk + sl);
+          accv[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dt, pf[sl], accv[mb], 0, 0, 0);
         }
-#pragma unroll
-        for (int sl = 0; sl < 4; ++sl)
-          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[mb & 1][sl], pf[sl], acc[mb], 0, 0, 0);
       }
-      schedule_tr_products<4 * (D / 32), 4>();
+      f32x16 P = f32x16{};
+      {
+        bf16x8 da[2], va[2];
+        da[0] = *reinterpret_cast<const bf16x8 *>(sD + off.row[0] + blk * 32 * Lds<D>::ROW);
+        va[0] = *reinterpret_cast<const bf16x8 *>(myv + off.row[0]);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          if (ks + 1 < D / 16) {
+            da[(ks + 1) & 1] = *reinterpret_cast<const bf16x8 *>(sD + off.row[ks + 1] + blk * 32 * Lds<D>::ROW);
+            va[(ks + 1) & 1] = *reinterpret_cast<const bf16x8 *>(myv + off.row[ks + 1]);
+          }
+          P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ks & 1], va[ks & 1], P, 0, 0, 0);
+        }
+      }
       __builtin_amdgcn_s_setprio(0);
-    } else {
+      bf16x8 dsf[2];
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        // S = Q K^T and dP = dO V^T for 32 queries x the wave's 32 keys
-        f32x16 S = f32x16{}, P = f32x16{};
-        __builtin_amdgcn_s_setprio(1);
-        bf16x8 qa[D / 16], da[D / 16];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 dq4 = d4[(q4 / 2) * 4 + (q4 % 2)];
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          qa[ks] = *reinterpret_cast<const bf16x8 *>(sQ + off.row[ks] + blk * 32 * Lds<D>::ROW);
-          da[ks] = *reinterpret_cast<const bf16x8 *>(sD + off.row[ks] + blk * 32 * Lds<D>::ROW);
+        for (int e = 0; e < 4; ++e) {
+          const int rr = 4 * q4 + e;
+          const float dlt = e == 0 ? dq4.x : e == 1 ? dq4.y : e == 2 ? dq4.z : dq4.w;
+          dsf[rr / 8][rr % 8] = (__bf16)(S[rr] * (P[rr] - dlt));
         }
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], S, 0, 0, 0);
-          P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ks], vf[ks], P, 0, 0, 0);
-        }
-        schedule_products<D / 8, D / 16>();
-        __builtin_amdgcn_s_setprio(0);
-        const float4 *d4 = reinterpret_cast<const float4 *>(sst + 32 * blk + 8 * hh);
-        const float4 *l4 = reinterpret_cast<const float4 *>(sst + 64 + 32 * blk + 8 * hh);
-        const float4 dl[4] = {d4[0], d4[1], d4[4], d4[5]};
-        const float4 ll[4] = {l4[0], l4[1], l4[4], l4[5]};
-        if (!full) {
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int qc = 32 * blk + 16 * (rr / 8) + (rr % 8);
-            S[rr] = ((qc >= vlo) & (qc < vhi)) ? S[rr] : -INFINITY;
-          }
-        }
-        bf16x8 dsf[2];
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const float4 dq4 = dl[rr / 4], lq4 = ll[rr / 4];
-          const float dlt = (rr % 4 == 0) ? dq4.x : (rr % 4 == 1) ? dq4.y : (rr % 4 == 2) ? dq4.z : dq4.w;
-          const float ls = (rr % 4 == 0) ? lq4.x : (rr % 4 == 1) ? lq4.y : (rr % 4 == 2) ? lq4.z : lq4.w;
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[rr], sl2, -ls));
-          dsf[rr / 8][rr % 8] = (__bf16)(p * (P[rr] - dlt));
-        }
-        // dK^T += Q^T dS over this block's two 16-query slabs
-        __builtin_amdgcn_s_setprio(1);
-        bf16x8 qt[2][2];
-#pragma unroll
-        for (int sl = 0; sl < 2; ++sl) qt[0][sl] = read_tr<D>(sQ, off, 0, 2 * blk + sl);
-#pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb) {
-          if (mb + 1 < D / 32) {
-#pragma unroll
-            for (int sl = 0; sl < 2; ++sl) qt[(mb + 1) & 1][sl] = read_tr<D>(sQ, off, mb + 1, 2 * blk + sl);
-          }
-#pragma unroll
-          for (int sl = 0; sl < 2; ++sl)
-            acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[mb & 1][sl], dsf[sl], acc[mb], 0, 0, 0);
-        }
-        schedule_tr_products<2 * (D / 32), 4>();
-        __builtin_amdgcn_s_setprio(0);
       }
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb) {
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+          const bf16x8 qt = read_tr<D>(sQ, off, mb, 2 * blk + sl);
+          acck[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dsf[sl], acck[mb], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
     }
     --pending;
     advance(cur);
@@ -715,31 +664,29 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
     if (pending == 0) break;
     body(StageTag<1>{});
     if (pending == 0) break;
-    if constexpr (NS >= 3) {
-      body(StageTag<2>{});
-      if (pending == 0) break;
-    }
-    if constexpr (NS == 4) {
-      body(StageTag<3>{});
-      if (pending == 0) break;
-    }
   }
 
   if (!kvalid) return;
-  float *dst = DV ? a.dv + kvo + b * a.v_sb + g * a.v_sh + (int64_t)krow * a.v_ss
-                  : a.dk + kvo + b * a.k_sb + g * a.k_sh + (int64_t)krow * a.k_ss;
-  const float mul = DV ? 1.0f : a.scale;
+  float *dv = a.dv + kvo + b * a.v_sb + g * a.v_sh + (int64_t)krow * a.v_ss;
+  float *dk = a.dk + kvo + b * a.k_sb + g * a.k_sh + (int64_t)krow * a.k_ss;
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      float4 *pd = reinterpret_cast<float4 *>(dst + 32 * mb + 8 * r4 + 4 * hh);
-      float4 val = *pd;
-      val.x += acc[mb][4 * r4 + 0] * mul;
-      val.y += acc[mb][4 * r4 + 1] * mul;
-      val.z += acc[mb][4 * r4 + 2] * mul;
-      val.w += acc[mb][4 * r4 + 3] * mul;
-      *pd = val;
+      float4 *pv = reinterpret_cast<float4 *>(dv + 32 * mb + 8 * r4 + 4 * hh);
+      float4 v = *pv;
+      v.x += accv[mb][4 * r4 + 0];
+      v.y += accv[mb][4 * r4 + 1];
+      v.z += accv[mb][4 * r4 + 2];
+      v.w += accv[mb][4 * r4 + 3];
+      *pv = v;
+      float4 *pk = reinterpret_cast<float4 *>(dk + 32 * mb + 8 * r4 + 4 * hh);
+      float4 k = *pk;
+      k.x += acck[mb][4 * r4 + 0] * a.scale;
+      k.y += acck[mb][4 * r4 + 1] * a.scale;
+      k.z += acck[mb][4 * r4 + 2] * a.scale;
+      k.w += acck[mb][4 * r4 + 3] * a.scale;
+      *pk = k;
     }
   }
 }
@@ -766,20 +713,17 @@ hipError_t launch_d(BwdArgs a, hipStream_t stream) {
         hipLaunchKernelGGL((dq_bf16_kernel<D, false, false>), grid, block, 0, stream, a);
     }
   }
-  // dV and dK passes
+  // dK/dV pass
   a.n_tiles = (a.L + 32 * KW - 1) / (32 * KW);
   a.xcd_remap = 0;
   const int n_slots = a.ring_rank >= 0 ? a.t_hi - a.t_lo : a.cp;
   const int64_t k_blocks = (int64_t)a.n_tiles * n_slots * a.B * a.Hkv;
   if (k_blocks > 0) {
     const dim3 grid((uint32_t)k_blocks), block(64 * KW);
-    if (a.sm.per_sample) {
-      hipLaunchKernelGGL((dkdv_bf16_kernel<D, true, KW, NS, true>), grid, block, 0, stream, a);
-      hipLaunchKernelGGL((dkdv_bf16_kernel<D, false, KW, NS, true>), grid, block, 0, stream, a);
-    } else {
-      hipLaunchKernelGGL((dkdv_bf16_kernel<D, true, KW, NS, false>), grid, block, 0, stream, a);
-      hipLaunchKernelGGL((dkdv_bf16_kernel<D, false, KW, NS, false>), grid, block, 0, stream, a);
-    }
+    if (a.sm.per_sample)
+      hipLaunchKernelGGL((dkdv_bf16_kernel<D, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((dkdv_bf16_kernel<D, false>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }
