@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=384, help="query rows of the oracle sample")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB (for scaling HBM byte counters)")
+    p.add_argument("--calls-per-rep", type=int, default=0,
+                   help="calls per timed repetition of a short launch (0: enough for about 2 ms); a fixed count "
+                        "gives counter runs the same dispatch sequence")
     p.add_argument("--only-workloads", action="store_true",
                    help="only the other configurations' launches (for profiling them), no oracle")
     return p.parse_args()
@@ -110,6 +113,9 @@ def plain_copy_reference(nbytes):
             "frac_hbm": 2 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
+_CALLS_PER_REP = [0]
+
+
 def _timed(fn, reps=20, batch_ms=2.0):
     """HIP-event times (ms) of fn() on the current stream after one untimed
     call: median, min and max over ``reps`` repetitions of the time per call.
@@ -132,7 +138,9 @@ def _timed(fn, reps=20, batch_ms=2.0):
     torch.cuda.synchronize()
     per = 1
     est = run(1)
-    if est < batch_ms:
+    if _CALLS_PER_REP[0] > 0:
+        per = _CALLS_PER_REP[0]
+    elif est < batch_ms:
         per = min(16, max(1, int(batch_ms / max(est, 1e-3))))
     out = sorted(run(per) for _ in range(reps))
     return {"ms": out[len(out) // 2], "ms_min": out[0], "ms_max": out[-1], "reps": reps, "calls_per_rep": per}
@@ -684,16 +692,19 @@ def split_balance(w, q, k, v, zig_shares):
             o = torch.empty_like(qr)
             lse = torch.empty(w.H, w.B, w.share, dtype=torch.float32, device=dev)
             d = B.attn_desc(w.S, w.rd, qr, ks, vs, o=o, cu_seqlens=cu, zigzag_per_sample=split == "per_sample")
-            ms = _time(lambda: B.usp_attn_fwd(qr, ks, vs, o, lse, d, r))
+            tf = _timed(lambda: B.usp_attn_fwd(qr, ks, vs, o, lse, d, r))
+            ms = tf["ms"]
             # the rank's backward from this forward (2.5 times its work: S, dP, dV, dK, dQ)
             d_o = inputs.randn(tuple(qr.shape), 99, "bf16").to(dev)
             dq = torch.empty_like(qr)
             dk = torch.zeros(ks.shape, dtype=torch.float32, device=dev)
             dv = torch.zeros(vs.shape, dtype=torch.float32, device=dev)
             stats = torch.empty(2 * lse.numel(), dtype=torch.float32, device=dev)
-            bms = _time(lambda: B.usp_attn_bwd(qr, ks, vs, o, d_o, lse, dq, dk, dv, stats, d, r))
+            tb = _timed(lambda: B.usp_attn_bwd(qr, ks, vs, o, d_o, lse, dq, dk, dv, stats, d, r))
+            bms = tb["ms"]
             ranks.append({"TFLOP": fl / 1e12, "ms": ms, "TFLOP/s": fl / (ms * 1e-3) / 1e12,
-                          "bwd_ms": bms, "bwd_TFLOP/s": 2.5 * fl / (bms * 1e-3) / 1e12})
+                          "bwd_ms": bms, "bwd_TFLOP/s": 2.5 * fl / (bms * 1e-3) / 1e12,
+                          "calls_per_rep": tf["calls_per_rep"], "bwd_calls_per_rep": tb["calls_per_rep"]})
         times = [x["ms"] for x in ranks]
         btimes = [x["bwd_ms"] for x in ranks]
         out[split] = {"ranks": ranks, "slowest_ms": max(times), "mean_ms": sum(times) / len(times),
@@ -754,6 +765,7 @@ def backward_walk(share, fwd_flops, reps=20):
 
 def main():
     args = parse()
+    _CALLS_PER_REP[0] = max(0, args.calls_per_rep)
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share on a single MI355X; --gpus {args.gpus} is not "
               "supported: the library runs one GPU's share and has no multi-GPU path.", file=sys.stderr)
