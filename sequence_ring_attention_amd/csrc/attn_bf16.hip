@@ -574,12 +574,32 @@ int tile_work(const AttnArgs &a, int BM, int rank, int lt) {
   return work;
 }
 
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cus[dev];
+}
+
+// Eight wavefronts (256 query rows) per workgroup share each K/V tile, which
+// halves the tile loads per query row: alternating on one box, 2.8% faster on
+// the 128K-token share and 4.2% on a 4096-token GQA share than four.  Packed
+// samples keep four wavefronts (128 rows): their query tiles are cut at
+// samples or pieces, and 256-row tiles ran the packed 32K ranks 16% slower.
+// So do launches that would give fewer than two eight-wave workgroups per CU
+// (one round of tiles of unequal work, e.g. two query heads of the 128K
+// share): four-wave workgroups run two per CU and halve each tile's work.
 // The workgroups of a launch in decreasing order of work, so that long ones
 // start first and short ones fill the last round.  The tile index alone
 // orders work only within one zigzag chunk of one rank: across the ranks of
 // an all-ranks launch the first chunk's tiles grow with the rank and the
 // second chunk's shrink, and packed samples restart at every sample.
-void order_tiles(AttnArgs &a, int BM) {
+void order_tiles(AttnArgs &a, int BM, int per_cu) {
   a.n_order = 0;
   const int n = a.n_ranks * a.n_qtiles;
   if (n > kMaxTileOrder) return;
@@ -589,6 +609,13 @@ void order_tiles(AttnArgs &a, int BM) {
     work[i] = tile_work(a, BM, a.ring_rank >= 0 ? a.ring_rank : i / a.n_qtiles, i % a.n_qtiles);
   }
   std::stable_sort(idx, idx + n, [&](int x, int y) { return work[x] > work[y]; });
+  // A launch whose workgroups are all resident at once (one round at two
+  // workgroups per CU) takes the second half in increasing order, so that
+  // the CU given the heaviest tile of the first half gets the lightest of the
+  // second (the 128K-token share in chunks of two query heads: 19.88 ->
+  // 19.41 ms per step).
+  const int64_t wgs = (int64_t)n * a.B * a.Hkv * a.G;
+  if (per_cu == 2 && wgs <= 2 * (int64_t)device_cus()) std::reverse(idx + n / 2, idx + n);
   for (int i = 0; i < n; ++i) a.tile_order[i] = (uint16_t)idx[i];
   a.n_order = n;
 }
@@ -598,7 +625,7 @@ hipError_t launch_nw(AttnArgs a, int head_dim, hipStream_t stream) {
   constexpr int BM = 32 * NW;
   a.n_qtiles = (a.L + BM - 1) / BM;
   if (a.sm.per_sample) a.n_qtiles = fill_piece_tiles(a.sm, a.cp, BM, a.ps_tiles);
-  order_tiles(a, BM);
+  order_tiles(a, BM, NW == 4 ? 2 : 1);
   const int64_t groups = (int64_t)a.n_ranks * a.n_qtiles * a.B * a.Hkv;
   a.xcd_remap = groups % 8 == 0;
   const int64_t blocks = groups * a.G;
@@ -621,26 +648,6 @@ hipError_t launch_nw(AttnArgs a, int head_dim, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Compute units of the current device (queried once per device).
-int device_cus() {
-  static int cus[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
-  }
-  return cus[dev];
-}
-
-// Eight wavefronts (256 query rows) per workgroup share each K/V tile, which
-// halves the tile loads per query row: alternating on one box, 2.8% faster on
-// the 128K-token share and 4.2% on a 4096-token GQA share than four.  Packed
-// samples keep four wavefronts (128 rows): their query tiles are cut at
-// samples or pieces, and 256-row tiles ran the packed 32K ranks 16% slower.
-// So do launches that would give fewer than two eight-wave workgroups per CU
-// (one round of tiles of unequal work, e.g. two query heads of the 128K
-// share): four-wave workgroups run two per CU and halve each tile's work.
 hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t stream) {
   if (a.sm.nseq > 0) return launch_nw<4>(a, head_dim, stream);
   const int64_t blocks8 = (int64_t)a.n_ranks * ((a.L + 255) / 256) * a.B * a.Hkv * a.G;
