@@ -387,17 +387,21 @@ def other_share_walk(Q, K, V, w, r, u, flops, steps=20):
             "frac_mfma": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
-def head_chunk_steps(Q, K, V, w, r, u, flops, whole_ms, whole_bytes, chunks=(8, 4, 2), overlapped=(4, 2), steps=20):
+def head_chunk_steps(Q, K, V, w, r, u, flops, whole_ms, whole_bytes, chunks=(8, 4, 2), overlapped=(4, 2), split=(2,),
+                     steps=20):
     """The share stepped with its head block pushed through in chunks
     (headwise chunking): step time and the head-major bytes the chunks in
     flight work on, beside the whole block's; chunks run one after another,
-    and for ``overlapped`` also alternating between two streams."""
+    and for ``overlapped`` also alternating between two streams; for
+    ``split`` on one stream with the split walk."""
     import torch
     from sequence_ring_attention_amd.pipeline import OneGpuShare
     res = {"whole_block": {"heads": w.H // w.ud, "ms": whole_ms, "TFLOP/s": flops / (whole_ms * 1e-3) / 1e12,
                            "head_major_bytes": whole_bytes}}
-    for nh, ov in [(nh, False) for nh in chunks] + [(nh, True) for nh in overlapped]:
-        sh = OneGpuShare(Q, K, V, w.rd, w.ud, r, u, head_chunk=nh, overlap_chunks=ov)
+    runs = [(nh, False, False) for nh in chunks] + [(nh, True, False) for nh in overlapped] + \
+           [(nh, False, True) for nh in split]
+    for nh, ov, sp in runs:
+        sh = OneGpuShare(Q, K, V, w.rd, w.ud, r, u, head_chunk=nh, overlap_chunks=ov, split_walk=sp)
         sh.prepare_peers()
         sh.step()
         torch.cuda.synchronize()
@@ -408,10 +412,13 @@ def head_chunk_steps(Q, K, V, w, r, u, flops, whole_ms, whole_bytes, chunks=(8, 
         b.record()
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / steps
-        res[f"chunks_of_{nh}" + ("_two_streams" if ov else "")] = {"heads": nh, "ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+        res[f"chunks_of_{nh}" + ("_two_streams" if ov else "") + ("_split_walk" if sp else "")] = {
+                                  "heads": nh, "ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
                                   "head_major_bytes": sh.head_major_bytes(),
                                   "head_major_fraction": sh.head_major_bytes() / whole_bytes,
                                   "step_time_ratio": ms / whole_ms}
+        if sp:
+            res[f"chunks_of_{nh}_split_walk"]["split_workspace_bytes"] = sum(t.numel() for t in sh._ws.values())
         del sh
         torch.cuda.empty_cache()
     return res

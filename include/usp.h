@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define USP_ABI_VERSION 6
+#define USP_ABI_VERSION 7
 
 /* Most packed samples one call takes (their boundaries travel by value). */
 #define USP_MAX_SEQS 256
@@ -296,6 +296,35 @@ usp_status usp_lse_merge(float *o_acc, float *lse_acc, const float *o_step,
  */
 usp_status usp_attn_fwd(const void *q, const void *k_all, const void *v_all, void *o,
                         float *lse, const usp_attn_desc *desc, int32_t ring_rank, void *stream);
+
+/*
+ * usp_attn_fwd for launches too small to fill the GPU twice over (a few query
+ * heads of a share, e.g. headwise chunks): a causal query tile whose work is
+ * above the launch's mean has its ring steps walked by two workgroups, steps
+ * [0, t_mid) and [t_mid, cp), each into an fp32 partial (o, lse) in
+ * `workspace`; a finalize kernel merges the two partials by the LSE rule of
+ * [CP vs Ulysses], concepts section (the same rule usp_lse_merge applies),
+ * rounds o once to `dtype` and writes o and lse exactly where usp_attn_fwd
+ * does.  Results equal usp_attn_fwd's to rounding (the merge replaces part of
+ * the in-kernel running fold).  Launches that fill the GPU, packed samples,
+ * fp32, cp = 1 and cp > 15 run usp_attn_fwd's walk and leave the workspace
+ * untouched.
+ *   workspace:       device memory owned by the caller, 256-byte aligned, at
+ *                    least usp_attn_fwd_split_workspace(desc, ring_rank)
+ *                    bytes; overwritten.  Calls that may overlap on the GPU
+ *                    need separate workspaces.
+ * Errors: as usp_attn_fwd, plus USP_ERR_INVALID_ARG for a null, misaligned
+ *   or too small workspace.
+ */
+usp_status usp_attn_fwd_split(const void *q, const void *k_all, const void *v_all, void *o,
+                              float *lse, const usp_attn_desc *desc, int32_t ring_rank,
+                              void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Bytes of workspace usp_attn_fwd_split needs for this descriptor and
+ * ring_rank: two fp32 partials (head_dim + 1 floats) of every query row the
+ * call covers.  Host-only; -1 for a null descriptor or ring_rank out of
+ * range. */
+int64_t usp_attn_fwd_split_workspace(const usp_attn_desc *desc, int32_t ring_rank);
 
 /*
  * ---------------------------------------------------------------- backward

@@ -20,8 +20,9 @@ USP_DTYPE_BF16, USP_DTYPE_FP32 = 0, 1
 
 EXPORTED = ["usp_zigzag_extract", "usp_zigzag_extract_n", "usp_zigzag_extract_varlen", "usp_ulysses_a2a_layout",
             "usp_ulysses_a2a_layout_n", "usp_ulysses_a2a_layout_heads", "usp_ring_attn_step_fwd",
-            "usp_lse_merge", "usp_attn_fwd", "usp_attn_bwd_prep", "usp_ring_attn_step_bwd", "usp_attn_bwd",
-            "usp_attn_bwd_noalloc", "usp_status_string", "usp_last_error_detail", "usp_abi_version"]
+            "usp_lse_merge", "usp_attn_fwd", "usp_attn_fwd_split", "usp_attn_fwd_split_workspace",
+            "usp_attn_bwd_prep", "usp_ring_attn_step_bwd", "usp_attn_bwd", "usp_attn_bwd_noalloc",
+            "usp_status_string", "usp_last_error_detail", "usp_abi_version"]
 
 NOALLOC_MAX_STATS_ROWS = 1 << 21
 
@@ -71,6 +72,9 @@ def lib():
         L.usp_ring_attn_step_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, i32, vp]
         L.usp_lse_merge.argtypes = [vp, vp, vp, vp, i64, i64, vp]
         L.usp_attn_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, vp]
+        L.usp_attn_fwd_split.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, vp, i64, vp]
+        L.usp_attn_fwd_split_workspace.argtypes = [ctypes.POINTER(UspAttnDesc), i32]
+        L.usp_attn_fwd_split_workspace.restype = i64
         L.usp_attn_bwd_prep.argtypes = [vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, vp]
         L.usp_ring_attn_step_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc),
                                              i32, i32, vp]
@@ -79,7 +83,7 @@ def lib():
         for f in ("usp_zigzag_extract", "usp_zigzag_extract_n", "usp_zigzag_extract_varlen", "usp_ulysses_a2a_layout",
                   "usp_ulysses_a2a_layout_n",
                   "usp_ulysses_a2a_layout_heads", "usp_ring_attn_step_fwd",
-                  "usp_lse_merge", "usp_attn_fwd", "usp_attn_bwd_prep", "usp_ring_attn_step_bwd",
+                  "usp_lse_merge", "usp_attn_fwd", "usp_attn_fwd_split", "usp_attn_bwd_prep", "usp_ring_attn_step_bwd",
                   "usp_attn_bwd", "usp_attn_bwd_noalloc"):
             getattr(L, f).restype = st
         L.usp_status_string.argtypes = [st]
@@ -314,6 +318,27 @@ def usp_attn_fwd(q, k_all, v_all, o, lse, desc, ring_rank, stream=None):
     _check_attn(k_all, v_all, lse, desc, desc.cp if ring_rank < 0 else 1)
     check(lib().usp_attn_fwd(q.data_ptr(), k_all.data_ptr(), v_all.data_ptr(), o.data_ptr(),
                              lse.data_ptr(), ctypes.byref(desc), ring_rank, _stream(stream)))
+    return o, lse
+
+
+def usp_attn_fwd_split_workspace(desc, ring_rank):
+    """Bytes of workspace usp_attn_fwd_split needs (host only)."""
+    n = lib().usp_attn_fwd_split_workspace(ctypes.byref(desc), ring_rank)
+    if n < 0:
+        raise ValueError("bad descriptor or ring_rank")
+    return n
+
+
+def usp_attn_fwd_split(q, k_all, v_all, o, lse, desc, ring_rank, workspace, stream=None):
+    """usp_attn_fwd with heavy query tiles' ring steps split over two
+    workgroups when the launch is small; `workspace` is a contiguous GPU tensor
+    of at least usp_attn_fwd_split_workspace(desc, ring_rank) bytes."""
+    _dev(q, k_all, v_all, o, lse, workspace)
+    _contig(workspace)
+    _check_attn(k_all, v_all, lse, desc, desc.cp if ring_rank < 0 else 1)
+    check(lib().usp_attn_fwd_split(q.data_ptr(), k_all.data_ptr(), v_all.data_ptr(), o.data_ptr(),
+                                   lse.data_ptr(), ctypes.byref(desc), ring_rank, workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
     return o, lse
 
 

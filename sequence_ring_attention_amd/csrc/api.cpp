@@ -635,6 +635,72 @@ usp_status usp_attn_fwd(const void *q, const void *k_all, const void *v_all, voi
   return attn_launch(a, desc, stream, "attn_fwd launch");
 }
 
+int64_t usp_attn_fwd_split_workspace(const usp_attn_desc *desc, int32_t ring_rank) {
+  if (!desc || desc->cp < 1 || desc->seq_len < 1 || desc->batch < 1 || desc->num_q_heads < 1 || desc->head_dim < 1 ||
+      ring_rank < -1 || ring_rank >= desc->cp)
+    return -1;
+  const int64_t rows = stats_rows(desc, ring_rank);
+  return 2 * rows * (desc->head_dim + 1) * 4;
+}
+
+usp_status usp_attn_fwd_split(const void *q, const void *k_all, const void *v_all, void *o, float *lse,
+                              const usp_attn_desc *desc, int32_t ring_rank, void *workspace,
+                              int64_t workspace_bytes, void *stream) {
+  const char *who = "attn_fwd_split";
+  usp::AttnArgs a;
+  usp_status s = attn_prepare(q, k_all, v_all, o, lse, desc, ring_rank, true, a, who);
+  if (s != USP_OK) return s;
+  const int64_t e = elem_bytes(desc->dtype);
+  const int64_t ostr[] = {desc->o.b, desc->o.s, desc->o.h, desc->q_rank_stride, desc->o_rank_stride};
+  for (int64_t st : ostr)
+    if (st < 0 || (st * e) % 8 != 0)
+      return fail(USP_ERR_INVALID_ARG, "%s: o and rank strides must be >= 0 and keep 8-byte alignment", who);
+  if (ring_rank < 0 && (desc->q_rank_stride * e) % 16 != 0)
+    return fail(USP_ERR_INVALID_ARG, "%s: q_rank_stride must keep 16-byte alignment", who);
+  const int64_t need = usp_attn_fwd_split_workspace(desc, ring_rank);
+  if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(USP_ERR_INVALID_ARG, "%s: workspace must be non-null and 256-byte aligned", who);
+  if (workspace_bytes < need)
+    return fail(USP_ERR_INVALID_ARG, "%s: workspace of %lld bytes, %lld needed", who, (long long)workspace_bytes,
+                (long long)need);
+  a.t_lo = 0;
+  a.t_hi = desc->cp;
+  a.partial = 0;
+  if (desc->dtype != USP_DTYPE_BF16) return attn_launch(a, desc, stream, "attn_fwd_split launch");
+  const int64_t rows = stats_rows(desc, ring_rank);
+  usp::SplitPlan plan{};
+  plan.po = static_cast<float *>(workspace);
+  plan.slot_o = rows * desc->head_dim;
+  plan.pl = plan.po + 2 * plan.slot_o;
+  plan.slot_lse = rows;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((s = hip_result(usp::launch_attn_bf16_split(a, (int)desc->head_dim, plan, st), "attn_fwd_split walk")) !=
+      USP_OK)
+    return s;
+  if (!plan.split) return USP_OK;
+  usp::FinalizeArgs f{};
+  f.po = plan.po;
+  f.pl = plan.pl;
+  f.slot_o = plan.slot_o;
+  f.slot_lse = plan.slot_lse;
+  f.o = o;
+  f.lse = lse;
+  f.o_sb = desc->o.b;
+  f.o_ss = desc->o.s;
+  f.o_sh = desc->o.h;
+  f.o_rank = ring_rank < 0 ? desc->o_rank_stride : 0;
+  f.rows = rows;
+  f.B = a.B;
+  f.Hq = a.Hq;
+  f.L = a.L;
+  f.d4 = (int32_t)(desc->head_dim / 4);
+  f.ring_rank = ring_rank;
+  f.bm = plan.bm;
+  f.n_qtiles = plan.n_qtiles;
+  for (int i = 0; i < usp::kMaxTileOrder / 32; ++i) f.mask[i] = plan.mask[i];
+  return hip_result(usp::launch_split_finalize(f, st), "attn_fwd_split finalize");
+}
+
 usp_status usp_attn_bwd_prep(const void *o, const void *d_o, const float *lse, float *stats,
                              const usp_attn_desc *desc, int32_t ring_rank, void *stream) {
   const char *who = "attn_bwd_prep";

@@ -156,10 +156,21 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
   const int b = rest % a.B;
   const int order = rest / a.B;
   int rank, lt;
+  // ring steps [t_begin, t_end) of this workgroup and its partial's slot
+  int t_begin = a.t_lo, t_end = a.t_hi, slot = 0;
   if (a.n_order > 0) {  // the launch's heaviest-first order
-    const int idx = a.tile_order[order];
+    const int e = a.tile_order[order];
+    const int idx = e & kOrderTile;
     rank = a.ring_rank >= 0 ? a.ring_rank : idx / a.n_qtiles;
     lt = idx % a.n_qtiles;
+    if (PARTIAL && a.split) {  // a split tile: its first or second run of steps
+      const int part = (e >> kOrderPartShift) & 3, t_mid = e >> kOrderMidShift;
+      if (part == 1) t_end = t_mid;
+      if (part == 2) {
+        t_begin = t_mid;
+        slot = 1;
+      }
+    }
   } else if (a.ring_rank >= 0) {
     rank = a.ring_rank;
     lt = a.n_qtiles - 1 - order;
@@ -237,9 +248,9 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
     r.llo = packed ? sm.count_le(r.j, my_sst - 1) : 0;
     return r;
   };
-  int t = a.t_lo;
+  int t = t_begin;
   StepRange cur = step_range(t);
-  while (cur.kt >= cur.ke && ++t < a.t_hi) cur = step_range(t);
+  while (cur.kt >= cur.ke && ++t < t_end) cur = step_range(t);
 
   // ------------------------------------------------ global -> LDS tiles --
   // per-lane byte offsets (within a tile) of the direct loads; see issue_kv_tile
@@ -292,7 +303,7 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
   // next tile of the walk after `x` (workgroup-uniform); `tx` is its step
   auto advance = [&](int &tx, StepRange &x) {
     ++x.kt;
-    while (x.kt >= x.ke && ++tx < a.t_hi) x = step_range(tx);
+    while (x.kt >= x.ke && ++tx < t_end) x = step_range(tx);
   };
 
   // The pieces of one tile.  Every LDS operand read below is a per-lane base
@@ -466,7 +477,7 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
     int t_nxt = t;
     StepRange nxt = cur;
     advance(t_nxt, nxt);
-    if (t_nxt < a.t_hi) issue_tile(nxt.j, nxt.kt * TB, STG ^ 1);
+    if (t_nxt < t_end) issue_tile(nxt.j, nxt.kt * TB, STG ^ 1);
     const char *const sK = STG == 0 ? smem0 : smem1;
     __builtin_amdgcn_s_setprio(1);  // keep the matrix core fed while the SIMD's other waves run softmax
     qk(sK);
@@ -483,12 +494,12 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
   };
 
   // prologue: tile 0 into stage 0
-  if (t < a.t_hi) issue_tile(cur.j, cur.kt * TB, 0);
+  if (t < t_end) issue_tile(cur.j, cur.kt * TB, 0);
   wait_tiles();
   __syncthreads();
-  while (t < a.t_hi) {
+  while (t < t_end) {
     body(StageTag<0>{});
-    if (t >= a.t_hi) break;
+    if (t >= t_end) break;
     body(StageTag<1>{});
   }
 
@@ -499,7 +510,8 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
   const float lse = empty ? -INFINITY : (m_run + __log2f(l)) * 0.69314718055994530942f;
   if (!qvalid) return;
   if (PARTIAL) {
-    float *o = static_cast<float *>(a.o) + (((int64_t)hq * a.B + b) * L + qrow) * D;
+    const int64_t prow = (((a.ring_rank < 0 ? (int64_t)rank * a.Hq : 0) + hq) * a.B + b) * L + qrow;
+    float *o = static_cast<float *>(a.o) + slot * a.slot_o + prow * D;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
 #pragma unroll
@@ -530,7 +542,7 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
   }
   if (hh == 0) {
     const int64_t li = (((a.ring_rank < 0 ? (int64_t)rank * a.Hq : 0) + hq) * a.B + b) * L + qrow;
-    a.lse[li] = lse;
+    a.lse[li + slot * a.slot_lse] = lse;
   }
 }
 
@@ -553,9 +565,9 @@ void launch_one(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t stream) {
 // not used.
 constexpr int kWalkTile = 64;
 
-// Key tiles a query tile of `rank` visits over the launch's ring steps: the
+// Key tiles a query tile of `rank` visits over ring steps [t0, t1): the
 // kernel's per-step tile range, computed on the host.
-int tile_work(const AttnArgs &a, int BM, int rank, int lt) {
+int tile_work(const AttnArgs &a, int BM, int rank, int lt, int t0, int t1) {
   const ShareMap sm(a.c, a.cp, a.L, a.sm);
   int q0, qend;
   if (a.sm.per_sample) {
@@ -566,7 +578,7 @@ int tile_work(const AttnArgs &a, int BM, int rank, int lt) {
   }
   const int pmin = sm.pos(rank, q0), pmax = sm.pos(rank, qend - 1), smin = sm.seg_start(pmin);
   int work = 0;
-  for (int t = a.t_lo; t < a.t_hi; ++t) {
+  for (int t = t0; t < t1; ++t) {
     const int j = ((rank - t) % a.cp + a.cp) % a.cp;
     const int hi = a.causal ? sm.count_le(j, pmax) : a.L, lo = sm.count_le(j, smin - 1);
     if (hi > lo) work += (hi + kWalkTile - 1) / kWalkTile - lo / kWalkTile;
@@ -586,47 +598,105 @@ int device_cus() {
   return cus[dev];
 }
 
-// Eight wavefronts (256 query rows) per workgroup share each K/V tile, which
-// halves the tile loads per query row: alternating on one box, 2.8% faster on
-// the 128K-token share and 4.2% on a 4096-token GQA share than four.  Packed
-// samples keep four wavefronts (128 rows): their query tiles are cut at
-// samples or pieces, and 256-row tiles ran the packed 32K ranks 16% slower.
-// So do launches that would give fewer than two eight-wave workgroups per CU
-// (one round of tiles of unequal work, e.g. two query heads of the 128K
-// share): four-wave workgroups run two per CU and halve each tile's work.
 // The workgroups of a launch in decreasing order of work, so that long ones
 // start first and short ones fill the last round.  The tile index alone
 // orders work only within one zigzag chunk of one rank: across the ranks of
 // an all-ranks launch the first chunk's tiles grow with the rank and the
 // second chunk's shrink, and packed samples restart at every sample.
+// A launch whose workgroups are all resident at once (one round at two
+// workgroups per CU) takes the second half in increasing order, so that the
+// CU given the heaviest tile of the first half gets the lightest of the
+// second (the 128K-token share in chunks of two query heads: 19.88 -> 19.41
+// ms per step).
+void order_items(AttnArgs &a, const uint16_t *item, const int *work, int m, int per_cu) {
+  int idx[kMaxTileOrder];
+  for (int i = 0; i < m; ++i) idx[i] = i;
+  std::stable_sort(idx, idx + m, [&](int x, int y) { return work[x] > work[y]; });
+  const int64_t wgs = (int64_t)m * a.B * a.Hkv * a.G;
+  if (per_cu == 2 && wgs <= 2 * (int64_t)device_cus()) std::reverse(idx + m / 2, idx + m);
+  for (int i = 0; i < m; ++i) a.tile_order[i] = item[idx[i]];
+  a.n_order = m;
+}
+
 void order_tiles(AttnArgs &a, int BM, int per_cu) {
   a.n_order = 0;
   const int n = a.n_ranks * a.n_qtiles;
   if (n > kMaxTileOrder) return;
-  int work[kMaxTileOrder], idx[kMaxTileOrder];
+  uint16_t item[kMaxTileOrder];
+  int work[kMaxTileOrder];
   for (int i = 0; i < n; ++i) {
-    idx[i] = i;
-    work[i] = tile_work(a, BM, a.ring_rank >= 0 ? a.ring_rank : i / a.n_qtiles, i % a.n_qtiles);
+    item[i] = (uint16_t)i;
+    work[i] = tile_work(a, BM, a.ring_rank >= 0 ? a.ring_rank : i / a.n_qtiles, i % a.n_qtiles, a.t_lo, a.t_hi);
   }
-  std::stable_sort(idx, idx + n, [&](int x, int y) { return work[x] > work[y]; });
-  // A launch whose workgroups are all resident at once (one round at two
-  // workgroups per CU) takes the second half in increasing order, so that
-  // the CU given the heaviest tile of the first half gets the lightest of the
-  // second (the 128K-token share in chunks of two query heads: 19.88 ->
-  // 19.41 ms per step).
-  const int64_t wgs = (int64_t)n * a.B * a.Hkv * a.G;
-  if (per_cu == 2 && wgs <= 2 * (int64_t)device_cus()) std::reverse(idx + n / 2, idx + n);
-  for (int i = 0; i < n; ++i) a.tile_order[i] = (uint16_t)idx[i];
-  a.n_order = n;
+  order_items(a, item, work, n, per_cu);
+}
+
+// Split walk: every tile whose work is above the launch's mean is walked by
+// two workgroups, one over the ring steps before t_mid and one from t_mid,
+// with t_mid the step boundary that halves its work best; each writes an
+// fp32 partial (o, lse) into its own slot, and the finalize kernel merges
+// the two by the LSE rule.  For launches of at most one round of workgroups,
+// where a heavy tile would otherwise run alone at the tail.  False when no
+// tile is split (the caller then runs the plain walk).
+bool split_tiles(AttnArgs &a, int BM, uint32_t *mask) {
+  const int n = a.n_ranks * a.n_qtiles;
+  if (a.cp < 2 || a.cp > kMaxSplitCp || a.sm.nseq > 0 || n > kMaxTileOrder) return false;
+  int work[kMaxTileOrder];
+  int64_t total = 0;
+  for (int i = 0; i < n; ++i) {
+    work[i] = tile_work(a, BM, a.ring_rank >= 0 ? a.ring_rank : i / a.n_qtiles, i % a.n_qtiles, a.t_lo, a.t_hi);
+    total += work[i];
+  }
+  for (int w = 0; w < kMaxTileOrder / 32; ++w) mask[w] = 0;
+  uint16_t item[kMaxTileOrder];
+  int iw[kMaxTileOrder];
+  int m = 0;
+  bool any = false;
+  for (int i = 0; i < n; ++i) {
+    const int rank = a.ring_rank >= 0 ? a.ring_rank : i / a.n_qtiles, lt = i % a.n_qtiles;
+    int best = -1, best_w = 0, best_d = 0;
+    if ((int64_t)work[i] * n > total) {
+      int acc = 0;
+      for (int t = a.t_lo + 1; t < a.t_hi; ++t) {
+        acc += tile_work(a, BM, rank, lt, t - 1, t);
+        const int d = std::abs(2 * acc - work[i]);
+        if (best < 0 || d < best_d) {
+          best = t;
+          best_w = acc;
+          best_d = d;
+        }
+      }
+    }
+    // both parts need work, and the items must fit the table
+    if (best > 0 && best_w > 0 && best_w < work[i] && m + 2 + (n - 1 - i) <= kMaxTileOrder) {
+      item[m] = (uint16_t)(i | 1 << kOrderPartShift | best << kOrderMidShift);
+      iw[m++] = best_w;
+      item[m] = (uint16_t)(i | 2 << kOrderPartShift | best << kOrderMidShift);
+      iw[m++] = work[i] - best_w;
+      mask[i >> 5] |= 1u << (i & 31);
+      any = true;
+    } else {
+      item[m] = (uint16_t)i;
+      iw[m++] = work[i];
+    }
+  }
+  if (!any) return false;
+  order_items(a, item, iw, m, 2);
+  a.split = 1;
+  return true;
 }
 
 template <int NW>
-hipError_t launch_nw(AttnArgs a, int head_dim, hipStream_t stream) {
+hipError_t launch_nw(AttnArgs a, int head_dim, hipStream_t stream, bool ordered = false) {
   constexpr int BM = 32 * NW;
-  a.n_qtiles = (a.L + BM - 1) / BM;
-  if (a.sm.per_sample) a.n_qtiles = fill_piece_tiles(a.sm, a.cp, BM, a.ps_tiles);
-  order_tiles(a, BM, NW == 4 ? 2 : 1);
-  const int64_t groups = (int64_t)a.n_ranks * a.n_qtiles * a.B * a.Hkv;
+  if (!ordered) {
+    a.n_qtiles = (a.L + BM - 1) / BM;
+    if (a.sm.per_sample) a.n_qtiles = fill_piece_tiles(a.sm, a.cp, BM, a.ps_tiles);
+    order_tiles(a, BM, NW == 4 ? 2 : 1);
+  }
+  // the grid: one workgroup per (order item, batch, KV head, query head of the group)
+  const int64_t items = a.n_order > 0 ? a.n_order : (int64_t)a.n_ranks * a.n_qtiles;
+  const int64_t groups = items * a.B * a.Hkv;
   a.xcd_remap = groups % 8 == 0;
   const int64_t blocks = groups * a.G;
   if (blocks == 0) return hipSuccess;
@@ -648,10 +718,40 @@ hipError_t launch_nw(AttnArgs a, int head_dim, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t stream) {
-  if (a.sm.nseq > 0) return launch_nw<4>(a, head_dim, stream);
+// Eight wavefronts (256 query rows) per workgroup share each K/V tile, which
+// halves the tile loads per query row: alternating on one box, 2.8% faster on
+// the 128K-token share and 4.2% on a 4096-token GQA share than four.  Packed
+// samples keep four wavefronts (128 rows): their query tiles are cut at
+// samples or pieces, and 256-row tiles ran the packed 32K ranks 16% slower.
+// So do launches that would give fewer than two eight-wave workgroups per CU
+// (one round of tiles of unequal work, e.g. two query heads of the 128K
+// share): four-wave workgroups run two per CU and halve each tile's work.
+bool four_waves(const AttnArgs &a) {
   const int64_t blocks8 = (int64_t)a.n_ranks * ((a.L + 255) / 256) * a.B * a.Hkv * a.G;
-  return blocks8 < 2 * (int64_t)device_cus() ? launch_nw<4>(a, head_dim, stream) : launch_nw<8>(a, head_dim, stream);
+  return a.sm.nseq > 0 || blocks8 < 2 * (int64_t)device_cus();
+}
+
+hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t stream) {
+  return four_waves(a) ? launch_nw<4>(a, head_dim, stream) : launch_nw<8>(a, head_dim, stream);
+}
+
+hipError_t launch_attn_bf16_split(const AttnArgs &a0, int head_dim, SplitPlan &plan, hipStream_t stream) {
+  plan.split = 0;
+  if (!four_waves(a0) || a0.sm.nseq > 0) return launch_attn_bf16(a0, head_dim, stream);
+  constexpr int BM = 128;
+  AttnArgs a = a0;
+  a.n_qtiles = (a.L + BM - 1) / BM;
+  const int64_t wgs = (int64_t)a.n_ranks * a.n_qtiles * a.B * a.Hkv * a.G;
+  if (wgs > 2 * (int64_t)device_cus() || !split_tiles(a, BM, plan.mask)) return launch_attn_bf16(a0, head_dim, stream);
+  a.o = plan.po;
+  a.lse = plan.pl;
+  a.slot_o = plan.slot_o;
+  a.slot_lse = plan.slot_lse;
+  a.partial = 1;
+  plan.split = 1;
+  plan.bm = BM;
+  plan.n_qtiles = a.n_qtiles;
+  return launch_nw<4>(a, head_dim, stream, true);
 }
 
 }  // namespace usp

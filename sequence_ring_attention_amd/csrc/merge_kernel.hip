@@ -148,7 +148,54 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(float *o_acc, float
   }
 }
 
+// The split walk's finalize: per row, slot 0's partial alone, or merged with
+// slot 1's when the row's tile was split; rounded once to bf16 (nearest even)
+// into the caller's layout, with the merged lse.  One thread per four
+// elements of a row; every thread of a split row evaluates the row's weights.
+__global__ __launch_bounds__(kThreads) void split_finalize_kernel(FinalizeArgs f) {
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t row = gid / f.d4;
+  const int c4 = (int)(gid - row * f.d4);
+  if (row >= f.rows) return;
+  const int qrow = (int)(row % f.L);
+  int64_t rest = row / f.L;
+  const int b = (int)(rest % f.B);
+  rest /= f.B;
+  const int hq = (int)(rest % f.Hq);
+  const int rank = (int)(rest / f.Hq);
+  const int tile = rank * f.n_qtiles + qrow / f.bm;
+  const bool split = (f.mask[tile >> 5] >> (tile & 31)) & 1u;
+  const float4 x = reinterpret_cast<const float4 *>(f.po)[row * f.d4 + c4];
+  float4 r = x;
+  float lse = f.pl[row];
+  if (split) {
+    const float4 y = reinterpret_cast<const float4 *>(f.po + f.slot_o)[row * f.d4 + c4];
+    double a1, a2, l;
+    merge_weights((double)lse, (double)f.pl[f.slot_lse + row], a1, a2, l);
+    r = blend(a1, x, a2, y);
+    lse = (float)l;
+  }
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 v;
+  v[0] = (__bf16)r.x;
+  v[1] = (__bf16)r.y;
+  v[2] = (__bf16)r.z;
+  v[3] = (__bf16)r.w;
+  __bf16 *o = static_cast<__bf16 *>(f.o) + (f.ring_rank < 0 ? rank * f.o_rank : 0) + b * f.o_sb + qrow * f.o_ss +
+              hq * f.o_sh + 4 * c4;
+  *reinterpret_cast<bf16x4 *>(o) = v;
+  if (c4 == 0) f.lse[row] = lse;
+}
+
 }  // namespace
+
+hipError_t launch_split_finalize(const FinalizeArgs &f, hipStream_t stream) {
+  const int64_t threads = f.rows * f.d4;
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(split_finalize_kernel, dim3((uint32_t)((threads + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     stream, f);
+  return hipGetLastError();
+}
 
 hipError_t launch_lse_merge(float *o_acc, float *lse_acc, const float *o_step,
                             const float *lse_step, int64_t rows, int64_t head_dim,

@@ -83,12 +83,17 @@ hipError_t launch_lse_merge(float *o_acc, float *lse_acc, const float *o_step,
 // ------------------------------------------------------------- attention --
 
 constexpr int kMaxTileOrder = 640;
+// A tile_order entry: the tile index in bits 0-9; under a split walk the
+// part in bits 10-11 (0: every step, 1: steps before t_mid, 2: from t_mid)
+// and t_mid in bits 12-15.
+constexpr int kOrderTile = 1023, kOrderPartShift = 10, kOrderMidShift = 12;
+constexpr int kMaxSplitCp = 15;
 
 struct AttnArgs {
   const void *q;
   const void *k;
   const void *v;
-  void *o;       // fp32 partial (Hq,B,L,D) or final in dtype with strides
+  void *o;       // fp32 partial (Hq,B,L,D) [(cp,Hq,B,L,D) for every rank] or final in dtype with strides
   float *lse;    // (Hq,B,L), or (cp,Hq,B,L) for every rank
   int32_t B, Hq, Hkv, G;
   int32_t L;     // share length 2c
@@ -116,11 +121,40 @@ struct AttnArgs {
   // n_order = 0: the tile index gives the order)
   int32_t n_order;
   uint16_t tile_order[kMaxTileOrder];
+  // split walk (partial output only): the entries carry parts; part 2 writes
+  // its partial slot_o / slot_lse elements after part 1's
+  int32_t split;
+  int64_t slot_o, slot_lse;
 };
 static_assert(sizeof(AttnArgs) <= 4096, "kernel arguments above 4 KiB");
 
 hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t stream);
 hipError_t launch_attn_fp32(const AttnArgs &a, int head_dim, hipStream_t stream);
+
+// Split walk of a bf16 launch of at most one round of workgroups: heavy
+// tiles' ring steps over two workgroups, fp32 partials in the caller's
+// workspace, then a finalize that merges them.
+struct SplitPlan {
+  float *po, *pl;            // partial o (two slots of rows x D) and lse (two slots of rows)
+  int64_t slot_o, slot_lse;  // elements from slot 0 to slot 1
+  int32_t split;             // set by the launch: 1 if tiles were split (finalize needed)
+  int32_t bm, n_qtiles;      // query rows per tile and tiles per share of the split launch
+  uint32_t mask[kMaxTileOrder / 32];  // the tiles (rank * n_qtiles + tile) that were split
+};
+hipError_t launch_attn_bf16_split(const AttnArgs &a, int head_dim, SplitPlan &plan, hipStream_t stream);
+
+struct FinalizeArgs {
+  const float *po, *pl;
+  int64_t slot_o, slot_lse;
+  void *o;                   // bf16, the caller's strides
+  float *lse;                // (Hq,B,L), or (cp,Hq,B,L) for every rank
+  int64_t o_sb, o_ss, o_sh, o_rank;
+  int64_t rows;              // ranks x Hq x B x L
+  int32_t B, Hq, L, d4;      // d4 = head_dim / 4
+  int32_t ring_rank, bm, n_qtiles;
+  uint32_t mask[kMaxTileOrder / 32];
+};
+hipError_t launch_split_finalize(const FinalizeArgs &f, hipStream_t stream);
 
 // -------------------------------------------------------------- backward --
 

@@ -32,14 +32,17 @@ from . import binding as B
 
 class OneGpuShare:
     def __init__(self, Q, K, V, rd, ud, ring_rank, ulysses_rank, causal=True, cu_seqlens=None, per_sample=False,
-                 head_chunk=None, overlap_chunks=False):
+                 head_chunk=None, overlap_chunks=False, split_walk=False):
         """Q (B, S, H, D), K/V (B, S, Hkv, D): global tensors on the GPU.
         ``cu_seqlens``: packed-sample boundaries; ``per_sample``: the shares
         are the per-sample zigzag split (Algorithm 2 on every sample) instead
         of the split of the whole packed stream.  ``head_chunk``: query heads
         per chunk (dividing H / ud, a multiple or a divisor of H / Hkv), or
         None for the whole head block at once.  ``overlap_chunks``: run
-        consecutive chunks on two streams (needs ``head_chunk``)."""
+        consecutive chunks on two streams (needs ``head_chunk``).
+        ``split_walk``: chunks walk with usp_attn_fwd_split (a chunk's heavy
+        query tiles split over two workgroups when the chunk's launch is too
+        small to fill the GPU), with one workspace per query buffer."""
         self.Q, self.K, self.V = Q, K, V
         self.rd, self.ud, self.r, self.u = rd, ud, ring_rank, ulysses_rank
         Bn, S, H, D = Q.shape
@@ -82,6 +85,8 @@ class OneGpuShare:
             raise ValueError("overlap_chunks needs head_chunk")
         self.overlap = bool(overlap_chunks)
         self._side = torch.cuda.Stream(device=dev) if self.overlap else None
+        self.split_walk = bool(split_walk)
+        self._ws = {}
         self.lse = torch.empty(ud, hb, Bn, L, dtype=torch.float32, device=dev)
         self.out = e(Bn, T, H, D)     # this GPU's output shard after the inverse layout
         self._descs = {}
@@ -130,8 +135,17 @@ class OneGpuShare:
     def _walk_chunk(self, u, c, qc=None):
         """Ulysses rank u's walk over chunk c's heads, its query heads in qc."""
         h0, nh, k0, nk = self._chunk_heads(c)
-        B.usp_attn_fwd(self.qc if qc is None else qc, self.kh[u][:, k0:k0 + nk], self.vh[u][:, k0:k0 + nk],
-                       self.ohc[c, u], self.lse[u, h0:h0 + nh], self._chunk_desc(), self.r)
+        q = self.qc if qc is None else qc
+        args = (q, self.kh[u][:, k0:k0 + nk], self.vh[u][:, k0:k0 + nk], self.ohc[c, u], self.lse[u, h0:h0 + nh],
+                self._chunk_desc(), self.r)
+        if self.split_walk:
+            i = 0 if q is self.qcs[0] else 1     # the walks of one query buffer run in order on one stream
+            if i not in self._ws:
+                n = B.usp_attn_fwd_split_workspace(self._chunk_desc(), self.r)
+                self._ws[i] = torch.empty(n, dtype=torch.uint8, device=q.device)
+            B.usp_attn_fwd_split(*args, self._ws[i])
+        else:
+            B.usp_attn_fwd(*args)
 
     def _chunks(self):
         return range(self.H // self.ud // self.chunk)

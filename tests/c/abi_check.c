@@ -64,6 +64,11 @@ int main(void) {
     expect(usp_attn_fwd(a, b, a, b, (float *)a, &d, 0, NULL) == USP_ERR_UNSUPPORTED, "attn_fwd rejects head_dim 96");
     expect(strstr(usp_last_error_detail(), "head_dim") != NULL, "the message names head_dim");
     d.head_dim = 64;
+    expect(usp_attn_fwd_split_workspace(&d, 0) == 2 * 2 * 64 * (d.head_dim + 1) * 4,
+           "split walk workspace: two partials of every row");
+    expect(usp_attn_fwd_split_workspace(NULL, 0) == -1, "split walk workspace rejects a null descriptor");
+    expect(usp_attn_fwd_split(a, b, a, b, (float *)a, &d, 0, NULL, 1 << 20, NULL) == USP_ERR_INVALID_ARG,
+           "attn_fwd_split rejects a null workspace");
     expect(usp_attn_fwd(a, b, a, b, (float *)a, &d, 4, NULL) == USP_ERR_INVALID_ARG,
            "attn_fwd rejects ring_rank = cp");
     expect(strstr(usp_last_error_detail(), "ring_rank") != NULL, "the message names ring_rank");

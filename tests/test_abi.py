@@ -22,12 +22,12 @@ no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="fake-pointer erro
 
 def declared_symbols():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:usp_status|const char \*|int32_t)\s*(usp_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:usp_status|const char \*|int32_t|int64_t)\s*(usp_\w+)\s*\(", text, re.M)))
 
 
 def test_library_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     lib = B.lib()
     for name in names:
         assert hasattr(lib, name), name
@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = B.lib()
-    assert lib.usp_abi_version() == 6
+    assert lib.usp_abi_version() == 7
     assert lib.usp_status_string(0) == b"USP_OK"
     assert lib.usp_status_string(2) == b"USP_ERR_UNSUPPORTED"
     assert lib.usp_status_string(99) == b"USP_ERR_UNKNOWN"
@@ -148,6 +148,30 @@ def test_attention_rank_and_step_ranges():
     assert walk(4) == 1 and walk(-2) == 1
     assert lib.usp_attn_fwd(FAKE, FAKE2, FAKE3, FAKE, FAKE2, None, 0, None) == 1
     assert lib.usp_attn_fwd(None, FAKE2, FAKE3, FAKE, FAKE2, ctypes.byref(d), 0, None) == 1
+
+
+def test_split_walk_workspace_size():
+    lib = B.lib()
+    d = _desc()
+    rows = d.num_q_heads * d.batch * (d.seq_len // d.cp)
+    assert lib.usp_attn_fwd_split_workspace(ctypes.byref(d), 0) == 2 * rows * (d.head_dim + 1) * 4
+    assert lib.usp_attn_fwd_split_workspace(ctypes.byref(d), -1) == 2 * d.cp * rows * (d.head_dim + 1) * 4
+    assert lib.usp_attn_fwd_split_workspace(ctypes.byref(d), d.cp) == -1
+    assert lib.usp_attn_fwd_split_workspace(None, 0) == -1
+
+
+@no_gpu
+def test_split_walk_rejects_bad_workspace():
+    lib = B.lib()
+    d = _desc()
+    need = lib.usp_attn_fwd_split_workspace(ctypes.byref(d), 0)
+    ws = 0x1000000
+    call = lambda w, n, **kw: lib.usp_attn_fwd_split(FAKE, FAKE2, FAKE3, FAKE, FAKE2, ctypes.byref(_desc(**kw)), 0,
+                                                     w, n, None)
+    assert call(None, need) == 1
+    assert call(ws + 16, need) == 1
+    assert call(ws, need - 1) == 1
+    assert call(ws, need, head_dim=96) == 2
 
 
 def _arrays(xs, outs, heads):

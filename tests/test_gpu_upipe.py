@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import attention as oa
 from oracle import index as ix
 from oracle import usp as ou
 from sequence_ring_attention_amd import binding as B
@@ -87,9 +88,9 @@ def _case(name):
     return c + ("bf16", True) if len(c) == 10 else c
 
 
-def _run_share(q, k, v, rd, ud, r, u, chunk, cu, ps, causal=True, overlap=False):
+def _run_share(q, k, v, rd, ud, r, u, chunk, cu, ps, causal=True, overlap=False, split=False):
     share = OneGpuShare(q, k, v, rd, ud, r, u, causal=causal, cu_seqlens=cu, per_sample=ps, head_chunk=chunk,
-                        overlap_chunks=overlap)
+                        overlap_chunks=overlap, split_walk=split)
     share.prepare_peers()
     out = share.step().clone()
     torch.cuda.synchronize()
@@ -117,6 +118,11 @@ def test_chunked_share_equals_unchunked_and_oracle(name):
                else ix.zigzag_local_positions(S, rd, ud, r, u))
         check_close(f64(o_ch), f64(l_ch[:, :, u * T:(u + 1) * T]), o_ref[:, pos],
                     lse_ref[u * hb:(u + 1) * hb][:, :, pos], dt, f"{name} ({r},{u})", out_bf16=dt == "bf16")
+        say("share", name, r, u, "chunks of", nh, "with the split walk")
+        o_sp, l_sp = _run_share(qd, kd, vd, rd, ud, r, u, nh, cu, ps, causal, split=True)
+        check_close(f64(o_sp), f64(l_sp[:, :, u * T:(u + 1) * T]), o_ref[:, pos],
+                    lse_ref[u * hb:(u + 1) * hb][:, :, pos], dt, f"{name} ({r},{u}) split walk",
+                    out_bf16=dt == "bf16")
 
 
 def test_chunked_share_rejects_bad_chunks():
@@ -145,3 +151,27 @@ def test_usp_hybrid_s128k_share_in_head_chunks_is_bitwise_the_same():
     say(w.name, "share (0,0) chunks of 2 heads on two streams")
     o_ov, l_ov = _run_share(q, k, v, w.rd, w.ud, 0, 0, 2, None, False, overlap=True)
     assert torch.equal(o_ov, o_full) and torch.equal(l_ov, l_full)
+
+
+def test_usp_hybrid_s128k_share_in_head_chunks_with_the_split_walk():
+    """The benchmark's share in 8 chunks of 2 query heads with the split walk
+    (each chunk's launch is a single round, so its heavy query tiles walk
+    their ring steps in two workgroups): within one bf16 spacing of the
+    whole block's output, and 128 seeded rows of the shard (all 32 heads)
+    against the oracle over all 131072 keys."""
+    w = inputs.WORKLOADS["usp_hybrid_s128k_ud2_rd4"]
+    dev = device()
+    q, k, v = inputs.workload_qkv(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    say(w.name, "share (0,0) whole head block")
+    o_full, l_full = _run_share(qd, kd, vd, w.rd, w.ud, 0, 0, None, None, False)
+    say(w.name, "share (0,0) chunks of 2 heads, split walk")
+    o_sp, l_sp = _run_share(qd, kd, vd, w.rd, w.ud, 0, 0, 2, None, False, split=True)
+    assert bool(((o_sp.float() - o_full.float()).abs() <= 1e-2 + o_full.float().abs() * 2.0 ** -7).all())
+    assert float((l_sp - l_full).abs().max()) <= 1e-5
+    T, hb = w.S // (w.rd * w.ud), w.H // w.ud
+    rows = np.sort(np.random.default_rng(4321).choice(T, size=128, replace=False))
+    p = ix.zigzag_local_positions(w.S, w.rd, w.ud, 0, 0)[rows]
+    o_ref, l_ref = oa.masked_attention(f64(q[:, p]), f64(k), f64(v), w.scale, q_pos=p)   # (B, n, H, D), (H, B, n)
+    check_close(f64(o_sp)[:, rows], f64(l_sp)[:, :, rows], o_ref, l_ref[:hb], "bf16",
+                f"{w.name} (0,0) split walk 128 rows x {w.H} heads", out_bf16=True)
