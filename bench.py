@@ -556,6 +556,10 @@ def extra_workloads(cpu=True):
     rows = w.H * w.B * w.share
     merge = _time_flushed(lambda: B.usp_lse_merge(acc, lacc, ost, lst), 3 * rows * w.D * 4 + 3 * rows * 4)
     entry["rank0_steps"] = steps
+    entry["rank0_whole_ring"] = ring_forms(
+        lambda t, o_, l_: B.usp_ring_attn_step_fwd(qr, ks, vs, o_, l_, d, 0, t),
+        lambda t, o_, l_: B.usp_ring_attn_step_fwd_merge(qr, ks, vs, o_, l_, d, 0, t),
+        lambda: B.usp_lse_merge(acc, lacc, ost, lst), w.rd, acc, lacc, ost, lst, fl_rank)
     entry["rank0_step_ms"] = [x["ms"] for x in steps]
     entry["rank0_step_TFLOP/s"] = [x["TFLOP/s"] for x in steps]
     entry["merge"] = merge
@@ -738,9 +742,33 @@ def ring_steps(share, flops):
     rows = lst.numel()
     merge = _time_flushed(lambda: B.usp_lse_merge(acc, lacc, ost, lst), 3 * rows * q.shape[-1] * 4 + 3 * rows * 4)
     per_step = flops / share.rd
+    ring = ring_forms(lambda t, o_, l_: B.usp_ring_attn_step_fwd(q, k, v, o_, l_, desc, r, t),
+                      lambda t, o_, l_: B.usp_ring_attn_step_fwd_merge(q, k, v, o_, l_, desc, r, t),
+                      lambda: B.usp_lse_merge(acc, lacc, ost, lst), share.rd, acc, lacc, ost, lst, flops)
     return {"step_ms": step_ms, "step_TFLOP/s": [per_step / (m * 1e-3) / 1e12 for m in step_ms],
             "step_frac_mfma": [per_step / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS for m in step_ms],
-            "work_per_step_tflop": per_step / 1e12, "merge": merge}
+            "work_per_step_tflop": per_step / 1e12, "merge": merge, "whole_ring": ring}
+
+
+def ring_forms(step, step_merge, merge, cp, acc, lacc, ost, lst, flops):
+    """A rank's whole ring in its two step-wise forms, each timed as one
+    sequence of launches: step 0 into the accumulator, then every later step
+    as a partial plus usp_lse_merge, or as usp_ring_attn_step_fwd_merge (the
+    merge in the step kernel's epilogue, no partial in HBM)."""
+    def two_launch():
+        step(0, acc, lacc)
+        for t in range(1, cp):
+            step(t, ost, lst)
+            merge()
+
+    def fused():
+        step(0, acc, lacc)
+        for t in range(1, cp):
+            step_merge(t, acc, lacc)
+    a, b = _timed(two_launch), _timed(fused)
+    return {"two_launch": {**a, "TFLOP/s": flops / (a["ms"] * 1e-3) / 1e12},
+            "merge_fused": {**b, "TFLOP/s": flops / (b["ms"] * 1e-3) / 1e12},
+            "launches": {"two_launch": 2 * cp - 1, "merge_fused": cp}}
 
 
 def backward_walk(share, fwd_flops, reps=20):

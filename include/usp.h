@@ -267,6 +267,24 @@ usp_status usp_ring_attn_step_fwd(const void *q, const void *k_all, const void *
  * zigzag_per_sample, every length a multiple of 2 cp.) */
 
 /*
+ * One ring step merged into a running accumulator in the same launch:
+ * usp_ring_attn_step_fwd of rank r at step t (block j = (r - t) mod cp)
+ * followed by usp_lse_merge, with the merge ([CP vs Ulysses], concepts
+ * section) done in the step kernel's epilogue, so the step's partial never
+ * reaches HBM.  Results are bitwise those of the two calls on an accumulator
+ * whose empty rows hold o = 0.
+ *   o_acc (Hq, B, 2c, D), lse_acc (Hq, B, 2c): fp32, contiguous, read and
+ *                    written in place.  A row whose lse_acc is -inf takes the
+ *                    step's partial as it is and its o_acc is not read, so a
+ *                    ring starts from lse_acc = -inf with o_acc left as it is.
+ *                    A row with no visible key in the step is left alone.
+ * Errors: as usp_ring_attn_step_fwd.
+ */
+usp_status usp_ring_attn_step_fwd_merge(const void *q, const void *k_all, const void *v_all,
+                                        float *o_acc, float *lse_acc, const usp_attn_desc *desc,
+                                        int32_t ring_rank, int32_t step, void *stream);
+
+/*
  * LSE merge, in place on the accumulator -- [CP vs Ulysses], concepts
  * section: lse = log(e^lse1 + e^lse2), o = e^(lse1 - lse) o1 + e^(lse2 - lse)
  * o2, evaluated as M + log(e^(lse1-M) + e^(lse2-M)) with M = max(lse1, lse2).

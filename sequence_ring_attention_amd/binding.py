@@ -20,6 +20,7 @@ USP_DTYPE_BF16, USP_DTYPE_FP32 = 0, 1
 
 EXPORTED = ["usp_zigzag_extract", "usp_zigzag_extract_n", "usp_zigzag_extract_varlen", "usp_ulysses_a2a_layout",
             "usp_ulysses_a2a_layout_n", "usp_ulysses_a2a_layout_heads", "usp_ring_attn_step_fwd",
+            "usp_ring_attn_step_fwd_merge",
             "usp_lse_merge", "usp_attn_fwd", "usp_attn_fwd_split", "usp_attn_fwd_split_workspace",
             "usp_attn_bwd_prep", "usp_ring_attn_step_bwd", "usp_attn_bwd", "usp_attn_bwd_noalloc",
             "usp_status_string", "usp_last_error_detail", "usp_abi_version"]
@@ -70,6 +71,7 @@ def lib():
         L.usp_zigzag_extract_n.argtypes = [i32, vp, vp, vp, st, i64, i64, i64, i32, i32, i32, i32, i32, vp]
         L.usp_ulysses_a2a_layout_n.argtypes = [i32, vp, vp, vp, st, i64, i64, i64, i32, i32, i32, vp]
         L.usp_ring_attn_step_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, i32, vp]
+        L.usp_ring_attn_step_fwd_merge.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, i32, vp]
         L.usp_lse_merge.argtypes = [vp, vp, vp, vp, i64, i64, vp]
         L.usp_attn_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, vp]
         L.usp_attn_fwd_split.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, vp, i64, vp]
@@ -82,7 +84,7 @@ def lib():
         L.usp_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(UspAttnDesc), i32, vp]
         for f in ("usp_zigzag_extract", "usp_zigzag_extract_n", "usp_zigzag_extract_varlen", "usp_ulysses_a2a_layout",
                   "usp_ulysses_a2a_layout_n",
-                  "usp_ulysses_a2a_layout_heads", "usp_ring_attn_step_fwd",
+                  "usp_ulysses_a2a_layout_heads", "usp_ring_attn_step_fwd", "usp_ring_attn_step_fwd_merge",
                   "usp_lse_merge", "usp_attn_fwd", "usp_attn_fwd_split", "usp_attn_bwd_prep", "usp_ring_attn_step_bwd",
                   "usp_attn_bwd", "usp_attn_bwd_noalloc"):
             getattr(L, f).restype = st
@@ -298,6 +300,19 @@ def usp_ring_attn_step_fwd(q, k_all, v_all, o_step, lse_step, desc, ring_rank, s
                                        o_step.data_ptr(), lse_step.data_ptr(), ctypes.byref(desc),
                                        ring_rank, step, _stream(stream)))
     return o_step, lse_step
+
+
+def usp_ring_attn_step_fwd_merge(q, k_all, v_all, o_acc, lse_acc, desc, ring_rank, step, stream=None):
+    """One ring step merged into (o_acc, lse_acc) in place (layouts of usp_ring_attn_step_fwd's partial)."""
+    _dev(q, k_all, v_all, o_acc, lse_acc)
+    _check_attn(k_all, v_all, lse_acc, desc, 1)
+    if o_acc.dtype != torch.float32 or not o_acc.is_contiguous() or \
+            o_acc.numel() != lse_acc.numel() * desc.head_dim:
+        raise ValueError("o_acc must be contiguous fp32 (Hq, B, 2c, D)")
+    check(lib().usp_ring_attn_step_fwd_merge(q.data_ptr(), k_all.data_ptr(), v_all.data_ptr(),
+                                             o_acc.data_ptr(), lse_acc.data_ptr(), ctypes.byref(desc),
+                                             ring_rank, step, _stream(stream)))
+    return o_acc, lse_acc
 
 
 def usp_lse_merge(o_acc, lse_acc, o_step, lse_step, stream=None):

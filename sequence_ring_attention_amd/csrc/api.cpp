@@ -617,6 +617,21 @@ usp_status usp_ring_attn_step_fwd(const void *q, const void *k_all, const void *
   return attn_launch(a, desc, stream, "ring_attn_step_fwd launch");
 }
 
+usp_status usp_ring_attn_step_fwd_merge(const void *q, const void *k_all, const void *v_all, float *o_acc,
+                                        float *lse_acc, const usp_attn_desc *desc, int32_t ring_rank,
+                                        int32_t step, void *stream) {
+  const char *who = "ring_attn_step_fwd_merge";
+  usp::AttnArgs a;
+  usp_status s = attn_prepare(q, k_all, v_all, o_acc, lse_acc, desc, ring_rank, false, a, who);
+  if (s != USP_OK) return s;
+  if (step < 0 || step >= desc->cp) return fail(USP_ERR_INVALID_ARG, "%s: step %d out of range", who, (int)step);
+  a.t_lo = step;
+  a.t_hi = step + 1;
+  a.partial = 1;
+  a.merge = 1;
+  return attn_launch(a, desc, stream, "ring_attn_step_fwd_merge launch");
+}
+
 usp_status usp_attn_fwd(const void *q, const void *k_all, const void *v_all, void *o, float *lse,
                         const usp_attn_desc *desc, int32_t ring_rank, void *stream) {
   usp::AttnArgs a;

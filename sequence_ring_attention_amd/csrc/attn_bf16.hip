@@ -60,6 +60,7 @@
 #include <algorithm>
 
 #include "attn_tiles.h"
+#include "lse_rule.h"
 #include "usp_internal.h"
 
 namespace usp {
@@ -509,6 +510,36 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
   const float inv = empty || !(lr > 0.0f) ? 0.0f : 1.0f / lr;
   const float lse = empty ? -INFINITY : (m_run + __log2f(l)) * 0.69314718055994530942f;
   if (!qvalid) return;
+  if (PARTIAL && a.merge) {
+    // the step's partial folded into the accumulator by the LSE rule: a row
+    // whose accumulator is empty (lse -inf) takes the partial as it is, a row
+    // with no key in this step leaves it alone.  Both lanes of a row read the
+    // accumulator's lse before the row's writer lane (hh = 0) stores the new
+    // one: one instruction each, in program order within the wavefront.
+    const int64_t prow = (((a.ring_rank < 0 ? (int64_t)rank * a.Hq : 0) + hq) * a.B + b) * L + qrow;
+    float *o = static_cast<float *>(a.o) + prow * D;
+    const float la = a.lse[prow];
+    double w1, w2, lm;
+    merge_weights((double)la, (double)lse, w1, w2, lm);
+    const bool take = la == -INFINITY, keep = !take && empty;
+    if (!keep) {
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          float4 y;
+          y.x = O[mb][4 * r4 + 0] * inv;
+          y.y = O[mb][4 * r4 + 1] * inv;
+          y.z = O[mb][4 * r4 + 2] * inv;
+          y.w = O[mb][4 * r4 + 3] * inv;
+          float4 *po = reinterpret_cast<float4 *>(o + 32 * mb + 8 * r4 + 4 * hh);
+          *po = take ? y : blend(w1, *po, w2, y);
+        }
+      }
+    }
+    if (hh == 0 && !keep) a.lse[prow] = take ? lse : (float)lm;
+    return;
+  }
   if (PARTIAL) {
     const int64_t prow = (((a.ring_rank < 0 ? (int64_t)rank * a.Hq : 0) + hq) * a.B + b) * L + qrow;
     float *o = static_cast<float *>(a.o) + slot * a.slot_o + prow * D;

@@ -11,6 +11,7 @@
 // Figure 1); a key is visible iff its global position is <= the query's
 // (causal) and, for packed samples, inside the query's sample.  The fold over
 // steps is the online form of the LSE merge of the same page.
+#include "lse_rule.h"
 #include "usp_internal.h"
 
 namespace usp {
@@ -79,6 +80,25 @@ __global__ __launch_bounds__(kThreads) void attn_fp32_kernel(AttnArgs a) {
   const bool empty = l == 0.0;
   const double inv = empty ? 0.0 : 1.0 / l;
   const float lse = empty ? -INFINITY : (float)(m + log(l));
+  if (a.partial && a.merge) {
+    // the step's partial folded into the accumulator by the LSE rule (see the
+    // bf16 kernel); every lane reads the row's lse before lane 0 stores it
+    const int64_t prow = ((int64_t)hq * a.B + b) * a.L + qrow;
+    float *o = static_cast<float *>(a.o) + prow * D;
+    const float la = a.lse[prow];
+    double w1, w2, lm;
+    merge_weights((double)la, (double)lse, w1, w2, lm);
+    const bool take = la == -INFINITY, keep = !take && empty;
+    if (!keep) {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const float y = (float)(acc[e] * inv);
+        o[lane + 64 * e] = take ? y : blend1(w1, o[lane + 64 * e], w2, y);
+      }
+      if (lane == 0) a.lse[prow] = take ? lse : (float)lm;
+    }
+    return;
+  }
   if (a.partial) {
     float *o = static_cast<float *>(a.o) + (((int64_t)hq * a.B + b) * a.L + qrow) * D;
 #pragma unroll

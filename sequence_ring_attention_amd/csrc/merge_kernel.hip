@@ -1,14 +1,9 @@
-// LSE merge of a step's partial result into an accumulator, in place.
-//
-// "Context Parallel 与 Ulysses" (ml-interview blog), concepts section: two
-// partials combine as lse = log(e^lse1 + e^lse2) and
-// o = e^(lse1 - lse) o1 + e^(lse2 - lse) o2.  Evaluated in the shifted form
-// lse = M + log1p(e^(m - M)) with M the larger and m the smaller input, in
-// double precision, so the fp32 result is rounded once.  A partial with
-// lse = -inf (no visible key) is the identity; two of them give (0, -inf).
+// LSE merge of a step's partial result into an accumulator, in place, by the
+// rule of lse_rule.h ("Context Parallel 与 Ulysses", concepts section).
 //
 // All lanes that touch one row live in the same wavefront, so every lane has
 // read lse_acc[row] before the row's writer lane stores the new value.
+#include "lse_rule.h"
 #include "usp_internal.h"
 
 namespace usp {
@@ -20,40 +15,6 @@ constexpr int kUnroll = 4;  // vector loads per lane in flight (64-row path): 4 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ inline float4 as_float4(f32x4 v) { return make_float4(v.x, v.y, v.z, v.w); }
 __device__ inline f32x4 as_f32x4(float4 v) { return f32x4{v.x, v.y, v.z, v.w}; }
-
-// The weights of the two partials and the merged lse of one row.
-__device__ inline void merge_weights(double l1, double l2, double &a1, double &a2, double &lse) {
-  const bool e1 = l1 == -INFINITY, e2 = l2 == -INFINITY;
-  if (e1 && e2) {
-    a1 = 0.0;
-    a2 = 0.0;
-    lse = -INFINITY;
-  } else if (e2) {
-    a1 = 1.0;
-    a2 = 0.0;
-    lse = l1;
-  } else if (e1) {
-    a1 = 0.0;
-    a2 = 1.0;
-    lse = l2;
-  } else {
-    const double M = l1 > l2 ? l1 : l2;
-    const double w = exp((l1 > l2 ? l2 : l1) - M);  // in (0, 1]
-    lse = M + log1p(w);
-    const double big = 1.0 / (1.0 + w), small = w / (1.0 + w);
-    a1 = l1 > l2 ? big : small;
-    a2 = l1 > l2 ? small : big;
-  }
-}
-
-__device__ inline float4 blend(double a1, float4 x, double a2, float4 y) {
-  float4 r;
-  r.x = (float)(a1 * (double)x.x + a2 * (double)y.x);
-  r.y = (float)(a1 * (double)x.y + a2 * (double)y.y);
-  r.z = (float)(a1 * (double)x.z + a2 * (double)y.z);
-  r.w = (float)(a1 * (double)x.w + a2 * (double)y.w);
-  return r;
-}
 
 // Rows of 2^d4_shift float4 (at most 64): a workgroup of four wavefronts
 // takes 64 rows.  Every wavefront computes the weights of the 64 rows (lane i

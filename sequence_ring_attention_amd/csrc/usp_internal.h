@@ -111,6 +111,7 @@ struct AttnArgs {
   int32_t ring_rank; // >= 0, or -1 for every rank
   int32_t t_lo, t_hi; // ring steps to walk
   int32_t partial;    // 1: write fp32 partial (o_step, lse_step)
+  int32_t merge;      // with partial: merge it into (o, lse) by the LSE rule instead of writing it
   int32_t n_qtiles;   // query tiles per share
   int32_t n_ranks;    // ranks in this launch (1 or cp)
   int32_t xcd_remap;  // 1: group blocks sharing a KV head on one XCD

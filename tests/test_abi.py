@@ -27,7 +27,7 @@ def declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     lib = B.lib()
     for name in names:
         assert hasattr(lib, name), name
@@ -135,6 +135,7 @@ def test_attention_descriptor_rejects(kw, status):
     lib = B.lib()
     d = _desc(**kw)
     assert lib.usp_ring_attn_step_fwd(FAKE, FAKE2, FAKE3, FAKE, FAKE2, ctypes.byref(d), 0, 0, None) == status
+    assert lib.usp_ring_attn_step_fwd_merge(FAKE, FAKE2, FAKE3, FAKE, FAKE2, ctypes.byref(d), 0, 0, None) == status
     assert lib.usp_attn_fwd(FAKE, FAKE2, FAKE3, FAKE, FAKE2, ctypes.byref(d), 0, None) == status
 
 
@@ -144,6 +145,9 @@ def test_attention_rank_and_step_ranges():
     d = _desc()
     step = lambda r, t: lib.usp_ring_attn_step_fwd(FAKE, FAKE2, FAKE3, FAKE, FAKE2, ctypes.byref(d), r, t, None)
     assert step(4, 0) == 1 and step(-1, 0) == 1 and step(0, 4) == 1 and step(0, -1) == 1
+    merged = lambda r, t: lib.usp_ring_attn_step_fwd_merge(FAKE, FAKE2, FAKE3, FAKE, FAKE2, ctypes.byref(d), r, t,
+                                                           None)
+    assert merged(4, 0) == 1 and merged(-1, 0) == 1 and merged(0, 4) == 1 and merged(0, -1) == 1
     walk = lambda r: lib.usp_attn_fwd(FAKE, FAKE2, FAKE3, FAKE, FAKE2, ctypes.byref(d), r, None)
     assert walk(4) == 1 and walk(-2) == 1
     assert lib.usp_attn_fwd(FAKE, FAKE2, FAKE3, FAKE, FAKE2, None, 0, None) == 1

@@ -320,6 +320,38 @@ def test_ring_steps_and_merge(name):
 
 
 @pytest.mark.parametrize("name", sorted(ATTN_CASES))
+def test_ring_steps_merged_in_the_step_kernel(name):
+    """usp_ring_attn_step_fwd_merge step after step: bitwise the step-then-
+    usp_lse_merge chain on an accumulator starting at (0, -inf), from an
+    accumulator whose o starts as NaN (an empty row's o is not read), and
+    within the bars of the oracle."""
+    P = _prepare(name)
+    dev, cp, H, Bn, L, D = P["dev"], P["cp"], P["H"], P["Bn"], P["L"], P["D"]
+    desc = B.attn_desc(P["S"], cp, P["qs"][0], P["ks"], P["vs"], layout=_layout(P), causal=P["causal"],
+                       cu_seqlens=P["cu_t"])
+    for r in range(cp):
+        o_ref, lse_ref, _ = _oracle_rank(P, r)
+        acc = torch.zeros((H, Bn, L, D), dtype=torch.float32, device=dev)
+        lacc = torch.full((H, Bn, L), float("-inf"), dtype=torch.float32, device=dev)
+        facc, ok1 = guarded((H, Bn, L, D), torch.float32, dev, fill=float("nan"))
+        flacc, ok2 = guarded((H, Bn, L), torch.float32, dev, fill=float("-inf"))
+        o_st = torch.empty_like(acc)
+        l_st = torch.empty_like(lacc)
+        for t in range(cp):
+            say("merged step", name, "rank", r, "step", t)
+            B.usp_ring_attn_step_fwd(P["qs"][r], P["ks"], P["vs"], o_st, l_st, desc, r, t)
+            B.usp_lse_merge(acc, lacc, o_st, l_st)
+            B.usp_ring_attn_step_fwd_merge(P["qs"][r], P["ks"], P["vs"], facc, flacc, desc, r, t)
+        torch.cuda.synchronize()
+        assert ok1() and ok2()
+        assert np.array_equal(bits(flacc), bits(lacc)), f"{name} r{r} lse"
+        live = torch.isfinite(lacc)
+        assert np.array_equal(bits(facc[live]), bits(acc[live])), f"{name} r{r} o"
+        check_close(np.transpose(f64(facc), (1, 2, 0, 3)), f64(flacc), o_ref, lse_ref, P["dt"],
+                    f"{name} r{r} merged in the step kernel")
+
+
+@pytest.mark.parametrize("name", sorted(ATTN_CASES))
 def test_ring_walk_per_rank_and_all_ranks(name):
     P = _prepare(name)
     dev, cp, H, Bn, L, D = P["dev"], P["cp"], P["H"], P["Bn"], P["L"], P["D"]

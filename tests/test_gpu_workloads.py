@@ -69,8 +69,15 @@ def test_causal_gqa_s32k_cp8_rank(rank):
         B.usp_ring_attn_step_fwd(qr, ks, vs, acc if t == 0 else o_st, lacc if t == 0 else l_st, desc, rank, t)
         if t:
             B.usp_lse_merge(acc, lacc, o_st, l_st)
+    # the same steps with the merge fused into the step kernel: bitwise the chain above
+    facc = torch.empty_like(acc)
+    flacc = torch.full_like(lacc, float("-inf"))
+    for t in range(w.rd):
+        say(w.name, "merged step", t)
+        B.usp_ring_attn_step_fwd_merge(qr, ks, vs, facc, flacc, desc, rank, t)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all() and torch.isfinite(lse).all() and torch.isfinite(acc).all()
+    assert torch.equal(flacc, lacc) and torch.equal(facc, acc)
     rows = sample_rows(w.share, w.chunk, 32, 20 + rank)
     pos = ix.zigzag_share_positions(w.S, w.rd, rank)[rows]
     o_ref, l_ref = _oracle_rows(f64(q), kn, vn, pos, w.scale)
