@@ -33,6 +33,8 @@
 //     dK^T += Q^T dS read dO and Q transposed.  S is computed once for both
 //     gradients: four products per tile.
 // The scale is applied once, to the final dQ and dK.
+#include <algorithm>
+
 #include "attn_tiles.h"
 #include "usp_internal.h"
 
@@ -411,6 +413,7 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
   rest /= a.Hkv;
   const int b = rest % a.B;
   rest /= a.B;
+  if (a.n_korder > 0) rest = a.k_order[rest];
   const int slot = rest % n_slots;
   const int kt = rest / n_slots;
   const int j = a.ring_rank >= 0 ? mod_cp(a.ring_rank - (a.t_lo + slot), a.cp) : slot;
@@ -691,6 +694,45 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
   }
 }
 
+// Query tiles (of BN rows) that see key tile kt (BK keys) of block j, summed
+// over the ranks the launch covers: the dK/dV pass's per-tile range, computed
+// on the host.
+int key_tile_work(const BwdArgs &a, int BK, int j, int kt) {
+  const ShareMap sm(a.c, a.cp, a.L, a.sm);
+  const int k0 = kt * BK, klast = std::min(k0 + BK, a.L) - 1;
+  const int kpos_min = sm.pos(j, k0), kpos_max = sm.pos(j, klast);
+  const int kend_max = sm.packed() ? sm.seg_end(kpos_max) : 0x7fffffff;
+  const int r_first = a.ring_rank >= 0 ? a.ring_rank : 0, r_last = a.ring_rank >= 0 ? a.ring_rank : a.cp - 1;
+  int work = 0;
+  for (int r = r_first; r <= r_last; ++r) {
+    const int lo = a.causal ? sm.count_le(r, kpos_min - 1) : 0;
+    const int hi = sm.packed() ? sm.count_le(r, kend_max - 1) : a.L;
+    if (hi > lo) work += (hi + BN - 1) / BN - lo / BN;
+  }
+  return work;
+}
+
+// The dK/dV pass's workgroups heaviest first.  A key tile's work spans a
+// wide range (under causal zigzag shares the first key tiles of the rank's
+// own block see up to twice a full block's query tiles, the last ones a
+// handful), one workgroup fills a CU, and in grid order the heavy tiles were
+// spread over the launch, leaving some CUs a full tile behind at the end.
+void order_key_tiles(BwdArgs &a, int BK, int n_slots) {
+  a.n_korder = 0;
+  const int m = a.n_tiles * n_slots;
+  if (m > kMaxKeyOrder) return;
+  int work[kMaxKeyOrder], idx[kMaxKeyOrder];
+  for (int i = 0; i < m; ++i) {
+    const int slot = i % n_slots, kt = i / n_slots;
+    const int j = a.ring_rank >= 0 ? ((a.ring_rank - (a.t_lo + slot)) % a.cp + a.cp) % a.cp : slot;
+    work[i] = key_tile_work(a, BK, j, kt);
+    idx[i] = i;
+  }
+  std::stable_sort(idx, idx + m, [&](int x, int y) { return work[x] > work[y]; });
+  for (int i = 0; i < m; ++i) a.k_order[i] = (uint16_t)idx[i];
+  a.n_korder = m;
+}
+
 template <int D>
 hipError_t launch_d(BwdArgs a, hipStream_t stream) {
   // dQ pass
@@ -718,6 +760,7 @@ hipError_t launch_d(BwdArgs a, hipStream_t stream) {
   a.xcd_remap = 0;
   const int n_slots = a.ring_rank >= 0 ? a.t_hi - a.t_lo : a.cp;
   const int64_t k_blocks = (int64_t)a.n_tiles * n_slots * a.B * a.Hkv;
+  order_key_tiles(a, 32 * KW, n_slots);
   if (k_blocks > 0) {
     const dim3 grid((uint32_t)k_blocks), block(64 * KW);
     if (a.sm.per_sample)
