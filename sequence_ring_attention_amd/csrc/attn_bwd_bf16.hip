@@ -154,7 +154,11 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
   const int b = rest % a.B;
   const int order = rest / a.B;
   int rank, lt;
-  if (a.ring_rank >= 0) {
+  if (a.n_order > 0) {
+    const int item = a.order[order];
+    rank = a.ring_rank >= 0 ? a.ring_rank : item / a.n_tiles;
+    lt = item % a.n_tiles;
+  } else if (a.ring_rank >= 0) {
     rank = a.ring_rank;
     lt = a.n_tiles - 1 - order;
   } else {
@@ -413,7 +417,7 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
   rest /= a.Hkv;
   const int b = rest % a.B;
   rest /= a.B;
-  if (a.n_korder > 0) rest = a.k_order[rest];
+  if (a.n_order > 0) rest = a.order[rest];
   const int slot = rest % n_slots;
   const int kt = rest / n_slots;
   const int j = a.ring_rank >= 0 ? mod_cp(a.ring_rank - (a.t_lo + slot), a.cp) : slot;
@@ -694,6 +698,50 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
   }
 }
 
+// Key tiles (of BN keys) that query tile lt (BM rows) of `rank` visits over
+// the launch's ring steps: the dQ pass's per-step tile range, computed on the
+// host.
+int query_tile_work(const BwdArgs &a, int rank, int lt) {
+  const ShareMap sm(a.c, a.cp, a.L, a.sm);
+  int q0, qend;
+  if (a.sm.per_sample) {
+    piece_tile(a.sm, a.ps_tiles, a.cp, BM, lt, q0, qend);
+  } else {
+    q0 = lt * BM;
+    qend = std::min(q0 + BM, a.L);
+  }
+  const int pmax = sm.pos(rank, qend - 1), smin = sm.packed() ? sm.seg_start(sm.pos(rank, q0)) : 0;
+  int work = 0;
+  for (int t = a.t_lo; t < a.t_hi; ++t) {
+    const int j = ((rank - t) % a.cp + a.cp) % a.cp;
+    const int hi = a.causal ? sm.count_le(j, pmax) : a.L, lo = sm.packed() ? sm.count_le(j, smin - 1) : 0;
+    if (hi > lo) work += (hi + BN - 1) / BN - lo / BN;
+  }
+  return work;
+}
+
+// Sets a.order to items 0 .. m - 1 by decreasing work (stable).
+void order_by_work(BwdArgs &a, const int *work, int m) {
+  int idx[kMaxBwdOrder];
+  for (int i = 0; i < m; ++i) idx[i] = i;
+  std::stable_sort(idx, idx + m, [&](int x, int y) { return work[x] > work[y]; });
+  for (int i = 0; i < m; ++i) a.order[i] = (uint16_t)idx[i];
+  a.n_order = m;
+}
+
+// The dQ pass's query tiles heaviest first.  The tile index orders work only
+// within one zigzag chunk of one rank; across the ranks of an all-ranks launch
+// and across the pieces of per-sample shares it does not.
+void order_query_tiles(BwdArgs &a) {
+  a.n_order = 0;
+  const int m = a.n_ranks * a.n_tiles;
+  if (m > kMaxBwdOrder) return;
+  int work[kMaxBwdOrder];
+  for (int i = 0; i < m; ++i)
+    work[i] = query_tile_work(a, a.ring_rank >= 0 ? a.ring_rank : i / a.n_tiles, i % a.n_tiles);
+  order_by_work(a, work, m);
+}
+
 // Query tiles (of BN rows) that see key tile kt (BK keys) of block j, summed
 // over the ranks the launch covers: the dK/dV pass's per-tile range, computed
 // on the host.
@@ -718,19 +766,16 @@ int key_tile_work(const BwdArgs &a, int BK, int j, int kt) {
 // handful), one workgroup fills a CU, and in grid order the heavy tiles were
 // spread over the launch, leaving some CUs a full tile behind at the end.
 void order_key_tiles(BwdArgs &a, int BK, int n_slots) {
-  a.n_korder = 0;
+  a.n_order = 0;
   const int m = a.n_tiles * n_slots;
-  if (m > kMaxKeyOrder) return;
-  int work[kMaxKeyOrder], idx[kMaxKeyOrder];
+  if (m > kMaxBwdOrder) return;
+  int work[kMaxBwdOrder];
   for (int i = 0; i < m; ++i) {
     const int slot = i % n_slots, kt = i / n_slots;
     const int j = a.ring_rank >= 0 ? ((a.ring_rank - (a.t_lo + slot)) % a.cp + a.cp) % a.cp : slot;
     work[i] = key_tile_work(a, BK, j, kt);
-    idx[i] = i;
   }
-  std::stable_sort(idx, idx + m, [&](int x, int y) { return work[x] > work[y]; });
-  for (int i = 0; i < m; ++i) a.k_order[i] = (uint16_t)idx[i];
-  a.n_korder = m;
+  order_by_work(a, work, m);
 }
 
 template <int D>
@@ -740,6 +785,7 @@ hipError_t launch_d(BwdArgs a, hipStream_t stream) {
   if (a.sm.per_sample) a.n_tiles = fill_piece_tiles(a.sm, a.cp, BM, a.ps_tiles);
   const int64_t groups = (int64_t)a.n_ranks * a.n_tiles * a.B * a.Hkv;
   a.xcd_remap = groups % 8 == 0;
+  order_query_tiles(a);
   const int64_t q_blocks = groups * a.G;
   if (q_blocks > 0) {
     const dim3 grid((uint32_t)q_blocks), block(64 * NW);

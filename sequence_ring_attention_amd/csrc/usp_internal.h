@@ -83,7 +83,7 @@ hipError_t launch_lse_merge(float *o_acc, float *lse_acc, const float *o_step,
 // ------------------------------------------------------------- attention --
 
 constexpr int kMaxTileOrder = 640;
-constexpr int kMaxKeyOrder = 768;  // entries of the backward's dK/dV order
+constexpr int kMaxBwdOrder = 768;  // entries of a backward pass's work order
 // A tile_order entry: the tile index in bits 0-9; under a split walk the
 // part in bits 10-11 (0: every step, 1: steps before t_mid, 2: from t_mid)
 // and t_mid in bits 12-15.
@@ -188,10 +188,11 @@ struct BwdArgs {
   int32_t xcd_remap;  // set by the launchers
   Samples sm;         // packed samples and the split of the shares
   int32_t ps_tiles[kMaxSeqs + 1];  // per-sample split, dQ pass: fill_piece_tiles at launch
-  // dK/dV pass: its (key tile, block) items heaviest first, set at launch
-  // when there are at most kMaxKeyOrder (n_korder = 0: grid order)
-  int32_t n_korder;
-  uint16_t k_order[kMaxKeyOrder];
+  // each pass's work items heaviest first, set at its launch when there are
+  // at most kMaxBwdOrder (n_order = 0: grid order).  dQ pass: rank * n_tiles
+  // + query tile; dK/dV pass: key tile * blocks + block slot
+  int32_t n_order;
+  uint16_t order[kMaxBwdOrder];
 };
 static_assert(sizeof(BwdArgs) <= 4096, "kernel arguments above 4 KiB");
 
