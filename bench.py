@@ -159,11 +159,15 @@ def _rate(t, flops):
     return t
 
 
-def clock_during(fn, seconds=1.0):
-    """The shader clock while fn() runs back to back for about `seconds`:
-    the firmware's gfx clock (amdsmi gpu metrics: the mean over XCDs of
-    current_gfxclks, MHz) sampled every 5 ms from a second thread.  Median,
-    min and max of the samples, or the reason it could not be read."""
+def clock_during(fn, min_snapshots=3, max_seconds=8.0):
+    """The shader clock while fn() runs back to back: the firmware's gfx clock
+    (amdsmi gpu metrics: the mean over XCDs of current_gfxclks, MHz).  The
+    firmware refreshes that table about once a second (its
+    system_clock_counter moves in steps), so the table is polled every 10 ms
+    and each refresh counted once; the snapshot already there when the
+    launches start predates them and is dropped.  fn() runs until
+    `min_snapshots` refreshes were seen or `max_seconds` passed.  Median, min
+    and max of the snapshots, or the reason it could not be read."""
     import threading
     import torch
     try:
@@ -173,28 +177,43 @@ def clock_during(fn, seconds=1.0):
         amdsmi.amdsmi_get_gpu_metrics_info(h)
     except Exception as e:                      # no amdsmi or no access: say so
         return {"mhz": None, "error": repr(e)[:200]}
-    samples, stop = [], threading.Event()
+
+    def snapshot():
+        m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+        xs = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+        if xs:
+            mhz = sum(xs) / len(xs)
+        elif isinstance(m.get("current_gfxclk"), (int, float)):
+            mhz = float(m["current_gfxclk"])
+        else:
+            mhz = None
+        return m.get("system_clock_counter"), mhz
+
+    fn()
+    torch.cuda.synchronize()
+    seen, snaps, stop = set(), [], threading.Event()
+    try:
+        seen.add(snapshot()[0])                 # the refresh before the launches
+    except Exception:
+        pass
 
     def poll():
         while not stop.is_set():
             try:
-                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
-                xs = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
-                if xs:
-                    samples.append(sum(xs) / len(xs))
-                elif isinstance(m.get("current_gfxclk"), (int, float)):
-                    samples.append(float(m["current_gfxclk"]))
+                stamp, mhz = snapshot()
+                if stamp not in seen:
+                    seen.add(stamp)
+                    if mhz is not None:
+                        snaps.append(mhz)
             except Exception:
                 pass
-            time.sleep(0.005)
+            time.sleep(0.01)
 
-    fn()
-    torch.cuda.synchronize()
     th = threading.Thread(target=poll, daemon=True)
     t0 = time.perf_counter()
     th.start()
     n = 0
-    while time.perf_counter() - t0 < seconds:
+    while len(snaps) < min_snapshots and time.perf_counter() - t0 < max_seconds:
         fn()
         n += 1
         if n % 4 == 0:
@@ -206,13 +225,13 @@ def clock_during(fn, seconds=1.0):
         amdsmi.amdsmi_shut_down()
     except Exception:
         pass
-    if not samples:
-        return {"mhz": None, "error": "no clock samples"}
-    xs = sorted(samples)
-    # the first samples can predate the launches reaching the GPU
-    body = xs if len(xs) < 10 else sorted(samples[len(samples) // 10:])
-    return {"mhz": body[len(body) // 2], "mhz_min": body[0], "mhz_max": body[-1], "samples": len(body),
-            "source": "amdsmi gpu metrics current_gfxclks, mean over XCDs", "launches": n}
+    if not snaps:
+        return {"mhz": None, "error": "no refresh of the gpu metrics table while the launches ran"}
+    xs = sorted(snaps)
+    return {"mhz": xs[len(xs) // 2], "mhz_min": xs[0], "mhz_max": xs[-1], "snapshots": len(xs),
+            "seconds": time.perf_counter() - t0,
+            "source": "amdsmi gpu metrics current_gfxclks, mean over XCDs, one value per table refresh",
+            "launches": n}
 
 
 def host_cores():
@@ -909,7 +928,7 @@ def main():
     result["kernels"]["ring_walk_attention"].update(
         {"ms_median": walks[len(walks) // 2], "ms_min": walks[0], "ms_max": walks[-1]})
     print("[bench] clock during the walk", file=sys.stderr, flush=True)
-    clk = clock_during(lambda: share._walk(u), 1.0)
+    clk = clock_during(lambda: share._walk(u))
     result["roofline"]["clock"] = clk
     if clk.get("mhz"):
         # the same walk rated against the peak at the clock it ran at (256 CUs x 4096 bf16 FLOP/clk)
