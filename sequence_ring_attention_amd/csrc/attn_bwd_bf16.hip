@@ -417,9 +417,12 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
   rest /= a.Hkv;
   const int b = rest % a.B;
   rest /= a.B;
+  const int sub = rest % a.order_sub;
+  rest /= a.order_sub;
   if (a.n_order > 0) rest = a.order[rest];
   const int slot = rest % n_slots;
-  const int kt = rest / n_slots;
+  const int kt = (rest / n_slots) * a.order_sub + sub;
+  if (kt >= a.n_tiles) return;  // the last group's missing tiles (uniform)
   const int j = a.ring_rank >= 0 ? mod_cp(a.ring_rank - (a.t_lo + slot), a.cp) : slot;
   const int r_first = a.ring_rank >= 0 ? a.ring_rank : 0;
   const int r_last = a.ring_rank >= 0 ? a.ring_rank : a.cp - 1;
@@ -734,6 +737,7 @@ void order_by_work(BwdArgs &a, const int *work, int m) {
 // and across the pieces of per-sample shares it does not.
 void order_query_tiles(BwdArgs &a) {
   a.n_order = 0;
+  a.order_sub = 1;
   const int m = a.n_ranks * a.n_tiles;
   if (m > kMaxBwdOrder) return;
   int work[kMaxBwdOrder];
@@ -765,17 +769,27 @@ int key_tile_work(const BwdArgs &a, int BK, int j, int kt) {
 // own block see up to twice a full block's query tiles, the last ones a
 // handful), one workgroup fills a CU, and in grid order the heavy tiles were
 // spread over the launch, leaving some CUs a full tile behind at the end.
-void order_key_tiles(BwdArgs &a, int BK, int n_slots) {
+// Above kMaxBwdOrder (key tile, block) items the entries are groups of
+// order_sub consecutive key tiles of one block, whose work is alike; the
+// grid then has order_sub workgroups per entry.  Returns the entries' count.
+int order_key_tiles(BwdArgs &a, int BK, int n_slots) {
   a.n_order = 0;
-  const int m = a.n_tiles * n_slots;
-  if (m > kMaxBwdOrder) return;
+  a.order_sub = 1;
+  if (n_slots <= 0 || a.n_tiles <= 0) return 0;
+  if (n_slots > kMaxBwdOrder) return a.n_tiles * n_slots;
+  const int per_slot = kMaxBwdOrder / n_slots;
+  a.order_sub = (a.n_tiles + per_slot - 1) / per_slot;
+  const int groups = (a.n_tiles + a.order_sub - 1) / a.order_sub, m = groups * n_slots;
   int work[kMaxBwdOrder];
   for (int i = 0; i < m; ++i) {
-    const int slot = i % n_slots, kt = i / n_slots;
+    const int slot = i % n_slots, grp = i / n_slots;
     const int j = a.ring_rank >= 0 ? ((a.ring_rank - (a.t_lo + slot)) % a.cp + a.cp) % a.cp : slot;
-    work[i] = key_tile_work(a, BK, j, kt);
+    work[i] = 0;
+    for (int kt = grp * a.order_sub; kt < std::min((grp + 1) * a.order_sub, a.n_tiles); ++kt)
+      work[i] += key_tile_work(a, BK, j, kt);
   }
   order_by_work(a, work, m);
+  return m;
 }
 
 template <int D>
@@ -805,8 +819,8 @@ hipError_t launch_d(BwdArgs a, hipStream_t stream) {
   a.n_tiles = (a.L + 32 * KW - 1) / (32 * KW);
   a.xcd_remap = 0;
   const int n_slots = a.ring_rank >= 0 ? a.t_hi - a.t_lo : a.cp;
-  const int64_t k_blocks = (int64_t)a.n_tiles * n_slots * a.B * a.Hkv;
-  order_key_tiles(a, 32 * KW, n_slots);
+  const int64_t entries = order_key_tiles(a, 32 * KW, n_slots);
+  const int64_t k_blocks = entries * a.order_sub * a.B * a.Hkv;
   if (k_blocks > 0) {
     const dim3 grid((uint32_t)k_blocks), block(64 * KW);
     if (a.sm.per_sample)

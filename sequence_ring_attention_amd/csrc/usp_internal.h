@@ -188,10 +188,12 @@ struct BwdArgs {
   int32_t xcd_remap;  // set by the launchers
   Samples sm;         // packed samples and the split of the shares
   int32_t ps_tiles[kMaxSeqs + 1];  // per-sample split, dQ pass: fill_piece_tiles at launch
-  // each pass's work items heaviest first, set at its launch when there are
-  // at most kMaxBwdOrder (n_order = 0: grid order).  dQ pass: rank * n_tiles
-  // + query tile; dK/dV pass: key tile * blocks + block slot
+  // each pass's work items heaviest first, set at its launch (n_order = 0:
+  // grid order).  dQ pass: rank * n_tiles + query tile, when there are at
+  // most kMaxBwdOrder; dK/dV pass: key tile group * blocks + block slot, a
+  // group being order_sub consecutive key tiles (one workgroup each)
   int32_t n_order;
+  int32_t order_sub;
   uint16_t order[kMaxBwdOrder];
 };
 static_assert(sizeof(BwdArgs) <= 4096, "kernel arguments above 4 KiB");

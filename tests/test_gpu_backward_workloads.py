@@ -14,7 +14,7 @@ from oracle import index as ix
 from sequence_ring_attention_amd import binding as B
 from sequence_ring_attention_amd import inputs
 from sequence_ring_attention_amd.pipeline import OneGpuShare
-from tests.gpu_common import check_grad, device, f64, sample_rows, say
+from tests.gpu_common import check_grad, device, f64, sample_rows, say, shares
 
 pytestmark = pytest.mark.gpu
 
@@ -177,3 +177,44 @@ def test_packed_varlen_s32k_per_sample_backward_all_ranks():
         ref = don.reshape(w.B, L, w.Hkv, G, w.D).sum(axis=(1, 3))
         scale_v = np.abs(don).reshape(w.B, L, w.Hkv, G, w.D).sum(axis=(1, 3))
         assert np.all(np.abs(dv64.sum(axis=(0, 2)) - ref) <= 1e-3 * scale_v), "sum of dV"
+
+
+def test_backward_key_tile_groups_match_the_ring_steps():
+    """A 49900-row share at cp = 4 (2 query heads on 1 KV head, D = 128): its
+    195 key tiles x 4 blocks exceed the dK/dV pass's table of work items, so
+    the walk's entries group two consecutive key tiles (the last group one
+    tile short).  Each ring step alone orders its 195 tiles one by one.  Each
+    dK/dV workgroup owns its keys and accumulates in the same order either
+    way, so the walk's dK and dV must be bitwise those of the four steps
+    summed (a tile lost or doubled by the grouping would show); dQ (bf16,
+    from registers) against the steps' fp32 sum at the gradient bar."""
+    dev = device()
+    Bn, H, Hkv, D, cp, L = 1, 2, 1, 128, 4, 49900
+    S = cp * L
+    q, k, v = inputs.qkv(Bn, S, H, Hkv, D, "bf16", 990)
+    do = inputs.randn((Bn, S, H, D), 994, "bf16")
+    qs, ks, vs, dos = (shares(x.to(dev), cp) for x in (q, k, v, do))
+    r = 0
+    o = torch.empty_like(qs[r])
+    lse = torch.empty((H, Bn, L), dtype=torch.float32, device=dev)
+    desc = B.attn_desc(S, cp, qs[r], ks, vs, o=o)
+    say("key tile groups: forward", S)
+    B.usp_attn_fwd(qs[r], ks, vs, o, lse, desc, r)
+    stats = torch.empty(2 * H * Bn * L, dtype=torch.float32, device=dev)
+    dq = torch.empty_like(qs[r])
+    dk = torch.zeros(ks.shape, dtype=torch.float32, device=dev)
+    dv = torch.zeros(vs.shape, dtype=torch.float32, device=dev)
+    say("key tile groups: walk backward")
+    B.usp_attn_bwd(qs[r], ks, vs, o, dos[r], lse, dq, dk, dv, stats, desc, r)
+    stats2 = torch.empty_like(stats)
+    B.usp_attn_bwd_prep(o, dos[r], lse, stats2, desc, r)
+    dq_acc = torch.zeros((H, Bn, L, D), dtype=torch.float32, device=dev)
+    dk2, dv2 = torch.zeros_like(dk), torch.zeros_like(dv)
+    for t in range(cp):
+        say("key tile groups: step", t)
+        B.usp_ring_attn_step_bwd(qs[r], ks, vs, dos[r], stats2, dq_acc, dk2, dv2, desc, r, t)
+    torch.cuda.synchronize()
+    assert torch.equal(stats, stats2)
+    assert bool((dk.abs().sum(dim=(1, 2, 3, 4)) > 0).all()), "a block got no dK"
+    assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    check_grad(f64(dq), np.transpose(f64(dq_acc), (1, 2, 0, 3)), "bf16", "dq walk vs steps")
