@@ -267,11 +267,15 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
     // query sees are one local range; as offsets from the lane's first key
     // row in the tile, [vlo, vhi)
     int vlo = 0, vhi = BN;
+    bool seen = true;
     if (!full) {
       const int hi = qvalid ? (causal ? sm.count_le_in(cur.j, my_qpos, my_sst, my_send) : L) : 0;
       const int lo = packed ? sm.count_le_in(cur.j, my_sst - 1, my_sst, my_send) : 0;
       vlo = lo - k0 - 8 * hh;
       vhi = hi - k0 - 8 * hh;
+      // a wavefront none of whose queries sees this tile's keys skips its
+      // products, leaving the matrix core to the other wavefronts of its SIMD
+      seen = __builtin_amdgcn_ballot_w64((lo < hi) & (lo < k0 + BN) & (hi > k0)) != 0;
     }
 
     // per 32-key half: S^T = K Q^T and dP^T = V dO^T, then that half's
@@ -280,7 +284,7 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
     // read a half's K and V rows ahead of its products.
     bf16x8 dsf[4];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < 2 * seen; ++half) {
       f32x16 S = f32x16{}, P = f32x16{};
       // K and V rows of two k-steps in registers; the next two are read while
       // this pair's four products run
@@ -321,7 +325,7 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
     // dQ^T += K^T dS^T, 16 keys per product; K^T read transposed
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) {
+    for (int mb = 0; mb < D / 32 * seen; ++mb) {
 #pragma unroll
       for (int p = 0; p < 4; ++p)
         dQ[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(sK, off, mb, p), dsf[p], dQ[mb], 0, 0, 0);
@@ -571,6 +575,7 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
     const bool full =
         __builtin_amdgcn_readfirstlane((k0 + BK <= L) & (q0 >= cur.x.flo) & (q0 + BN <= cur.x.fhi));
     int vlo = 0, vhi = BN;
+    bool seen = true;
     if (!full) {
       if (r != lane_r) {
         lane_r = r;
@@ -579,9 +584,13 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
       }
       vlo = lane_lo - q0 - 8 * hh;
       vhi = lane_hi - q0 - 8 * hh;
+      // a wavefront none of whose keys this tile's queries see (keys past
+      // the tile's queries, or of other samples) skips the tile's products,
+      // leaving the matrix core to the other wavefront of its SIMD
+      seen = __builtin_amdgcn_ballot_w64((lane_lo < lane_hi) & (lane_lo < q0 + BN) & (lane_hi > q0)) != 0;
     }
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
+    for (int blk = 0; blk < 2 * seen; ++blk) {
       // S = Q K^T, then P (kept in fp32 for dS, rounded for dV), dV^T +=
       // dO^T P, then dP = dO V^T, dS and dK^T += Q^T dS: P's rounding and
       // the dV products are done before dP takes its registers
