@@ -32,6 +32,9 @@
 //     dP = dO V^T take Q and dO rows as the M operand; dV^T += dO^T P and
 //     dK^T += Q^T dS read dO and Q transposed.  S is computed once for both
 //     gradients: four products per tile.
+// Both passes deal their workgroups heaviest first (a host-side count of the
+// tiles each one visits), and on a masked tile a wavefront that sees nothing
+// of it skips the tile's products.
 // The scale is applied once, to the final dQ and dK.
 #include <algorithm>
 
