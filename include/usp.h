@@ -316,16 +316,17 @@ usp_status usp_attn_fwd(const void *q, const void *k_all, const void *v_all, voi
                         float *lse, const usp_attn_desc *desc, int32_t ring_rank, void *stream);
 
 /*
- * usp_attn_fwd for launches too small to fill the GPU twice over (a few query
- * heads of a share, e.g. headwise chunks): a causal query tile whose work is
+ * usp_attn_fwd for launches too small to fill the GPU once (at most one
+ * 256-row query tile per CU: a few query heads of a share, e.g. headwise
+ * chunks): a causal query tile whose work is
  * above the launch's mean has its ring steps walked by two workgroups, steps
  * [0, t_mid) and [t_mid, cp), each into an fp32 partial (o, lse) in
  * `workspace`; a finalize kernel merges the two partials by the LSE rule of
  * [CP vs Ulysses], concepts section (the same rule usp_lse_merge applies),
  * rounds o once to `dtype` and writes o and lse exactly where usp_attn_fwd
  * does.  Results equal usp_attn_fwd's to rounding (the merge replaces part of
- * the in-kernel running fold).  Launches that fill the GPU, packed samples,
- * fp32, cp = 1 and cp > 15 run usp_attn_fwd's walk and leave the workspace
+ * the in-kernel running fold).  Larger launches, packed samples, fp32,
+ * cp = 1 and cp > 15 run usp_attn_fwd's walk and leave the workspace
  * untouched.
  *   workspace:       device memory owned by the caller, 256-byte aligned, at
  *                    least usp_attn_fwd_split_workspace(desc, ring_rank)
