@@ -18,11 +18,14 @@ namespace usp {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int KB = 16;  // keys per group
 
-__device__ inline double wave_sum(double x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-  return x;
+// Lane i's value of x, in every lane.
+__device__ inline double read_lane(double x, int i) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(x);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, i);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), i);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
 template <int D>
@@ -59,21 +62,60 @@ __global__ __launch_bounds__(kThreads) void attn_fp32_kernel(AttnArgs a) {
     if (j < 0) j += a.cp;
     const float *kb = static_cast<const float *>(a.k) + j * a.kv_blk + b * a.k_sb + kvh * a.k_sh;
     const float *vb = static_cast<const float *>(a.v) + j * a.kv_blk + b * a.v_sb + kvh * a.v_sh;
-    for (int kk = 0; kk < a.L; ++kk) {
-      const int kpos = sm.pos(j, kk);
-      if (a.causal && kpos > qpos) continue;
-      if (kpos < sst) continue;  // another packed sample (sst = 0 for one sequence)
-      double part = 0.0;
+    // positions grow with the local row, so the keys of block j this row
+    // sees are the local rows [lo, hi): at or before the query (causal) and
+    // not before its sample's start (sst = 0 for one sequence)
+    const int hi = a.causal ? sm.count_le(j, qpos) : a.L;
+    const int lo = sst > 0 ? sm.count_le(j, sst - 1) : 0;
+    // KB keys at a time: their partial dot products are summed across the
+    // wavefront in one pass of independent shuffles, and the running max,
+    // sum and output are rescaled once per group
+    for (int k0 = lo; k0 < hi; k0 += KB) {
+      const int n = hi - k0 < KB ? hi - k0 : KB;
+      // the group's K and V elements are requested together: one memory
+      // latency per group
+      double part[KB];
+      float vv[KB][PER];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) part += qv[e] * (double)kb[(int64_t)kk * a.k_ss + lane + 64 * e];
-      const double s = wave_sum(part) * scale;
-      const double m_new = s > m ? s : m;
-      const double alpha = exp(m - m_new);  // m = -inf on the first key: alpha = 0
-      const double p = exp(s - m_new);
-      l = l * alpha + p;
+      for (int i = 0; i < KB; ++i) {
+        part[i] = 0.0;
 #pragma unroll
-      for (int e = 0; e < PER; ++e)
-        acc[e] = acc[e] * alpha + p * (double)vb[(int64_t)kk * a.v_ss + lane + 64 * e];
+        for (int e = 0; e < PER; ++e) vv[i][e] = i < n ? vb[(int64_t)(k0 + i) * a.v_ss + lane + 64 * e] : 0.0f;
+        if (i < n) {
+#pragma unroll
+          for (int e = 0; e < PER; ++e) part[i] += qv[e] * (double)kb[(int64_t)(k0 + i) * a.k_ss + lane + 64 * e];
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+#pragma unroll
+        for (int i = 0; i < KB; ++i) part[i] += __shfl_xor(part[i], off);
+      }
+      double m_new = m;
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        part[i] *= scale;
+        if (i < n) m_new = part[i] > m_new ? part[i] : m_new;
+      }
+      const double alpha = exp(m - m_new);  // m = -inf before the first key: alpha = 0
+      l *= alpha;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] *= alpha;
+      // lane i < n takes key k0 + i's probability (one exp per lane instead
+      // of every lane evaluating all of them), read back lane by lane
+      double mine = part[0];
+#pragma unroll
+      for (int i = 1; i < KB; ++i) mine = lane == i ? part[i] : mine;
+      const double pl = lane < n ? exp(mine - m_new) : 0.0;
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        if (i < n) {
+          const double p = read_lane(pl, i);
+          l += p;
+#pragma unroll
+          for (int e = 0; e < PER; ++e) acc[e] += p * (double)vv[i][e];
+        }
+      }
       m = m_new;
     }
   }
