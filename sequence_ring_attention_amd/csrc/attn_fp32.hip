@@ -1,9 +1,12 @@
 // Ring-step / ring-walk attention for fp32 inputs (small problems).
 //
-// One wavefront per (rank, query head, batch, query row); the 64 lanes split
-// head_dim.  Logits, the running max/sum and the output accumulator are kept
-// in double: a product of two floats is exact in double, so the only
-// rounding that reaches the fp32 outputs is the final one.
+// One workgroup of four wavefronts per (rank, query head, batch, query row):
+// the wavefronts take turns over the row's visible keys in groups of 16 and
+// each keeps its own running max, sum and output, merged at the end by the
+// LSE rule; the 64 lanes of a wavefront split head_dim.  Logits, the running
+// max/sum and the output accumulator are kept in double: a product of two
+// floats is exact in double, so the only rounding that reaches the fp32
+// outputs is the final one.
 //
 // Semantics as the bf16 kernel (positions from the share map of either
 // split): ring rank r at step t reads KV block
@@ -31,11 +34,14 @@ __device__ inline double read_lane(double x, int i) {
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_fp32_kernel(AttnArgs a) {
   constexpr int PER = D / 64;  // elements per lane (1 or 2)
+  constexpr int NWV = kThreads / 64;
+  // the four wavefronts of a workgroup share one query row: wavefront w
+  // takes key groups w, w + 4, ... of the row's walk, and wavefront 0 merges
+  // the four partial results by the LSE rule
+  __shared__ double part_m[NWV], part_l[NWV], part_acc[NWV][D];
   const int lane = threadIdx.x & 63;
-  const int64_t w = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-  const int64_t rows_per_rank = (int64_t)a.Hq * a.B * a.L;
-  if (w >= rows_per_rank * a.n_ranks) return;  // whole wavefront exits together
-  int64_t rest = w;
+  const int wv = threadIdx.x >> 6;
+  int64_t rest = blockIdx.x;
   const int qrow = (int)(rest % a.L);
   rest /= a.L;
   const int b = (int)(rest % a.B);
@@ -57,6 +63,7 @@ __global__ __launch_bounds__(kThreads) void attn_fp32_kernel(AttnArgs a) {
   }
   const double scale = (double)a.scale;
   double m = -INFINITY, l = 0.0;
+  int grp = 0;  // key groups of the row's walk so far
   for (int t = a.t_lo; t < a.t_hi; ++t) {
     int j = (rank - t) % a.cp;
     if (j < 0) j += a.cp;
@@ -65,12 +72,13 @@ __global__ __launch_bounds__(kThreads) void attn_fp32_kernel(AttnArgs a) {
     // positions grow with the local row, so the keys of block j this row
     // sees are the local rows [lo, hi): at or before the query (causal) and
     // not before its sample's start (sst = 0 for one sequence)
-    const int hi = a.causal ? sm.count_le(j, qpos) : a.L;
-    const int lo = sst > 0 ? sm.count_le(j, sst - 1) : 0;
+    const int hi = __builtin_amdgcn_readfirstlane(a.causal ? sm.count_le(j, qpos) : a.L);
+    const int lo = __builtin_amdgcn_readfirstlane(sst > 0 ? sm.count_le(j, sst - 1) : 0);
     // KB keys at a time: their partial dot products are summed across the
     // wavefront in one pass of independent shuffles, and the running max,
     // sum and output are rescaled once per group
-    for (int k0 = lo; k0 < hi; k0 += KB) {
+    for (int k0 = lo; k0 < hi; k0 += KB, ++grp) {
+      if (grp % NWV != wv) continue;
       const int n = hi - k0 < KB ? hi - k0 : KB;
       // the group's K and V elements are requested together: one memory
       // latency per group
@@ -119,6 +127,33 @@ __global__ __launch_bounds__(kThreads) void attn_fp32_kernel(AttnArgs a) {
       m = m_new;
     }
   }
+  // the four partials -> wavefront 0
+  if (lane == 0) {
+    part_m[wv] = m;
+    part_l[wv] = l;
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) part_acc[wv][lane + 64 * e] = acc[e];
+  __syncthreads();
+  if (wv != 0) return;
+  {
+    double mm = part_m[0];
+#pragma unroll
+    for (int i = 1; i < NWV; ++i) mm = part_m[i] > mm ? part_m[i] : mm;
+    l = 0.0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = 0.0;
+    if (mm != -INFINITY) {
+#pragma unroll
+      for (int i = 0; i < NWV; ++i) {
+        const double f = exp(part_m[i] - mm);  // 0 for a wavefront that saw no key
+        l += part_l[i] * f;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] += part_acc[i][lane + 64 * e] * f;
+      }
+    }
+    m = mm;
+  }
   const bool empty = l == 0.0;
   const double inv = empty ? 0.0 : 1.0 / l;
   const float lse = empty ? -INFINITY : (float)(m + log(l));
@@ -160,8 +195,7 @@ __global__ __launch_bounds__(kThreads) void attn_fp32_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attn_fp32(const AttnArgs &a, int head_dim, hipStream_t stream) {
-  const int64_t waves = (int64_t)a.Hq * a.B * a.L * a.n_ranks;
-  const int64_t blocks = (waves + 3) / 4;
+  const int64_t blocks = (int64_t)a.Hq * a.B * a.L * a.n_ranks;  // one workgroup per query row
   if (blocks == 0) return hipSuccess;
   if (head_dim == 64)
     hipLaunchKernelGGL(attn_fp32_kernel<64>, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, a);
