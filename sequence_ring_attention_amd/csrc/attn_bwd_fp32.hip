@@ -8,25 +8,53 @@
 // and lse2 = lse log2(e) taken from the statistics buffer.
 //
 // Two passes, each owning its outputs so that no two lanes write one value:
-//   * dQ: one wavefront per (rank, query head, batch, query row) walks the
+//   * dQ: one workgroup per (rank, query head, batch, query row) walks the
 //     steps' KV blocks, like the forward;
-//   * dK, dV: one wavefront per (KV block, KV head, batch, key row) walks the
+//   * dK, dV: one workgroup per (KV block, KV head, batch, key row) walks the
 //     query rows of every rank that reaches the block, over the query heads
 //     that read the KV head, and adds its sums into the fp32 accumulators.
-// The 64 lanes split head_dim; dot products and sums are in double (fp32
-// products are exact there), so the outputs see one final rounding.
+// Each wavefront is one of four that share the row, taking its groups of 16
+// keys (queries) in turn; a group's dot products are summed across the
+// wavefront in one pass of independent shuffles, and the four wavefronts'
+// sums are added in a fixed order at the end.  The 64 lanes split head_dim;
+// dot products and sums are in double (fp32 products are exact there), so
+// the outputs see one final rounding.
 #include "usp_internal.h"
 
 namespace usp {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int NWV = kThreads / 64;  // wavefronts sharing one row
+constexpr int KB = 16;              // keys (queries) per group
 constexpr double kLog2e = 1.4426950408889634074;
 
-__device__ inline double wave_sum(double x) {
+// Sums x[0 .. N) across the wavefront, every lane getting every sum: one
+// pass of N independent shuffles per step.
+template <int N>
+__device__ inline void wave_sums(double *x) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-  return x;
+  for (int off = 32; off >= 1; off >>= 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += __shfl_xor(x[i], off);
+  }
+}
+
+// Lane i's value of x, in every lane.
+__device__ inline double read_lane(double x, int i) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(x);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, i);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), i);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// x[i] for i = lane (lanes 0 .. N - 1), by selects (no dynamic indexing).
+template <int N>
+__device__ inline double pick_lane(const double *x, int lane) {
+  double r = x[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) r = lane == i ? x[i] : r;
+  return r;
 }
 
 __device__ inline int mod_cp(int x, int cp) {
@@ -37,11 +65,10 @@ __device__ inline int mod_cp(int x, int cp) {
 template <int D>
 __global__ __launch_bounds__(kThreads) void dq_fp32_kernel(BwdArgs a) {
   constexpr int PER = D / 64;
+  __shared__ double part[NWV][D];
   const int lane = threadIdx.x & 63;
-  const int64_t w = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-  const int64_t rows_per_rank = (int64_t)a.Hq * a.B * a.L;
-  if (w >= rows_per_rank * a.n_ranks) return;  // whole wavefront exits together
-  int64_t rest = w;
+  const int wv = threadIdx.x >> 6;
+  int64_t rest = blockIdx.x;
   const int qrow = (int)(rest % a.L);
   rest /= a.L;
   const int b = (int)(rest % a.B);
@@ -69,27 +96,59 @@ __global__ __launch_bounds__(kThreads) void dq_fp32_kernel(BwdArgs a) {
     acc[e] = 0.0;
   }
   const double sl2 = (double)a.scale * kLog2e;
+  int grp = 0;  // key groups of the row's walk so far
   for (int t = a.t_lo; t < a.t_hi; ++t) {
     const int j = mod_cp(rank - t, a.cp);
     const float *kb = static_cast<const float *>(a.k) + j * a.kv_blk + b * a.k_sb + kvh * a.k_sh;
     const float *vb = static_cast<const float *>(a.v) + j * a.kv_blk + b * a.v_sb + kvh * a.v_sh;
-    for (int kk = 0; kk < a.L; ++kk) {
-      const int kpos = sm.pos(j, kk);
-      if (a.causal && kpos > qpos) continue;
-      if (kpos < sst) continue;  // another packed sample (sst = 0 for one sequence)
-      double s = 0.0, g = 0.0;
+    // positions grow with the local row: the keys this row sees are the
+    // local rows [lo, hi) of block j (sst = 0 for one sequence)
+    const int hi = __builtin_amdgcn_readfirstlane(a.causal ? sm.count_le(j, qpos) : a.L);
+    const int lo = __builtin_amdgcn_readfirstlane(sst > 0 ? sm.count_le(j, sst - 1) : 0);
+    for (int k0 = lo; k0 < hi; k0 += KB, ++grp) {
+      if (grp % NWV != wv) continue;
+      const int n = hi - k0 < KB ? hi - k0 : KB;
+      double sg[2 * KB];  // logits, then dO . V
+      float kk[KB][PER];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        s += qv[e] * (double)kb[(int64_t)kk * a.k_ss + lane + 64 * e];
-        g += dov[e] * (double)vb[(int64_t)kk * a.v_ss + lane + 64 * e];
+      for (int i = 0; i < KB; ++i) {
+        sg[i] = 0.0;
+        sg[KB + i] = 0.0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) kk[i][e] = 0.0f;
+        if (i < n) {
+#pragma unroll
+          for (int e = 0; e < PER; ++e) {
+            kk[i][e] = kb[(int64_t)(k0 + i) * a.k_ss + lane + 64 * e];
+            sg[i] += qv[e] * (double)kk[i][e];
+            sg[KB + i] += dov[e] * (double)vb[(int64_t)(k0 + i) * a.v_ss + lane + 64 * e];
+          }
+        }
       }
-      s = wave_sum(s);
-      g = wave_sum(g);
-      const double p = exp2(s * sl2 - lse2);  // lse2 = +inf for a row with no key: p = 0
-      const double ds = p * (g - delta);
+      wave_sums<2 * KB>(sg);
+      // lane i < n evaluates key k0 + i's dS
+      const double si = pick_lane<KB>(sg, lane), gi = pick_lane<KB>(sg + KB, lane);
+      const double dsl = lane < n ? exp2(si * sl2 - lse2) * (gi - delta) : 0.0;  // lse2 = +inf: p = 0
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] += ds * (double)kb[(int64_t)kk * a.k_ss + lane + 64 * e];
+      for (int i = 0; i < KB; ++i) {
+        if (i < n) {
+          const double ds = read_lane(dsl, i);
+#pragma unroll
+          for (int e = 0; e < PER; ++e) acc[e] += ds * (double)kk[i][e];
+        }
+      }
     }
+  }
+  // the four wavefronts' sums, added in a fixed order by wavefront 0
+#pragma unroll
+  for (int e = 0; e < PER; ++e) part[wv][lane + 64 * e] = acc[e];
+  __syncthreads();
+  if (wv != 0) return;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    acc[e] = part[0][lane + 64 * e];
+#pragma unroll
+    for (int i = 1; i < NWV; ++i) acc[e] += part[i][lane + 64 * e];
   }
   const double scale = (double)a.scale;
   if (a.dq_acc) {
@@ -107,11 +166,10 @@ __global__ __launch_bounds__(kThreads) void dq_fp32_kernel(BwdArgs a) {
 template <int D>
 __global__ __launch_bounds__(kThreads) void dkdv_fp32_kernel(BwdArgs a) {
   constexpr int PER = D / 64;
+  __shared__ double part[NWV][2][D];
   const int lane = threadIdx.x & 63;
-  const int64_t w = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-  const int n_slots = a.ring_rank >= 0 ? a.t_hi - a.t_lo : a.cp;
-  if (w >= (int64_t)n_slots * a.Hkv * a.B * a.L) return;  // whole wavefront exits together
-  int64_t rest = w;
+  const int wv = threadIdx.x >> 6;
+  int64_t rest = blockIdx.x;
   const int krow = (int)(rest % a.L);
   rest /= a.L;
   const int b = (int)(rest % a.B);
@@ -138,37 +196,81 @@ __global__ __launch_bounds__(kThreads) void dkdv_fp32_kernel(BwdArgs a) {
     dv[e] = 0.0;
   }
   const double sl2 = (double)a.scale * kLog2e;
+  int grp = 0;  // query groups so far
   for (int r = r_first; r <= r_last; ++r) {
     const int rs = a.ring_rank >= 0 ? 0 : r;
+    // the query rows of rank r that see this key: [lo, hi) (causal: at or
+    // after the key; packed: before the end of its sample)
+    const int lo = __builtin_amdgcn_readfirstlane(a.causal ? sm.count_le(r, kpos - 1) : 0);
+    const int hi = __builtin_amdgcn_readfirstlane(sm.packed() ? sm.count_le(r, kend - 1) : a.L);
     for (int hq = g * a.G; hq < (g + 1) * a.G; ++hq) {
       const float *qb = static_cast<const float *>(a.q) + (a.ring_rank < 0 ? r * a.q_rank : 0) + b * a.q_sb +
                         hq * a.q_sh;
       const float *db = static_cast<const float *>(a.dout) + (a.ring_rank < 0 ? r * a.do_rank : 0) +
                         b * a.do_sb + hq * a.do_sh;
       const int64_t srow0 = (((int64_t)rs * a.Hq + hq) * a.B + b) * a.L;
-      for (int i = 0; i < a.L; ++i) {
-        const int qpos = sm.pos(r, i);
-        if (a.causal && qpos < kpos) continue;
-        if (qpos >= kend) continue;  // another packed sample
-        double s = 0.0, gd = 0.0;
-        double qe[PER], de[PER];
+      for (int i0 = lo; i0 < hi; i0 += KB, ++grp) {
+        if (grp % NWV != wv) continue;
+        const int n = hi - i0 < KB ? hi - i0 : KB;
+        double sg[2 * KB];  // logits, then dO . V
+        float qe[KB][PER], de[KB][PER];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) {
-          qe[e] = (double)qb[(int64_t)i * a.q_ss + lane + 64 * e];
-          de[e] = (double)db[(int64_t)i * a.do_ss + lane + 64 * e];
-          s += qe[e] * kv[e];
-          gd += de[e] * vv[e];
+        for (int i = 0; i < KB; ++i) {
+          sg[i] = 0.0;
+          sg[KB + i] = 0.0;
+#pragma unroll
+          for (int e = 0; e < PER; ++e) {
+            qe[i][e] = 0.0f;
+            de[i][e] = 0.0f;
+          }
+          if (i < n) {
+#pragma unroll
+            for (int e = 0; e < PER; ++e) {
+              qe[i][e] = qb[(int64_t)(i0 + i) * a.q_ss + lane + 64 * e];
+              de[i][e] = db[(int64_t)(i0 + i) * a.do_ss + lane + 64 * e];
+              sg[i] += (double)qe[i][e] * kv[e];
+              sg[KB + i] += (double)de[i][e] * vv[e];
+            }
+          }
         }
-        s = wave_sum(s);
-        gd = wave_sum(gd);
-        const double p = exp2(s * sl2 - (double)a.stats[a.rows + srow0 + i]);
-        const double ds = p * (gd - (double)a.stats[srow0 + i]);
+        wave_sums<2 * KB>(sg);
+        // lane i < n evaluates query i0 + i's P and dS
+        const double si = pick_lane<KB>(sg, lane), gi = pick_lane<KB>(sg + KB, lane);
+        double pl = 0.0, dsl = 0.0;
+        if (lane < n) {
+          pl = exp2(si * sl2 - (double)a.stats[a.rows + srow0 + i0 + lane]);
+          dsl = pl * (gi - (double)a.stats[srow0 + i0 + lane]);
+        }
 #pragma unroll
-        for (int e = 0; e < PER; ++e) {
-          dv[e] += p * de[e];
-          dk[e] += ds * qe[e];
+        for (int i = 0; i < KB; ++i) {
+          if (i < n) {
+            const double p = read_lane(pl, i), ds = read_lane(dsl, i);
+#pragma unroll
+            for (int e = 0; e < PER; ++e) {
+              dv[e] += p * (double)de[i][e];
+              dk[e] += ds * (double)qe[i][e];
+            }
+          }
         }
       }
+    }
+  }
+  // the four wavefronts' sums, added in a fixed order by wavefront 0
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    part[wv][0][lane + 64 * e] = dk[e];
+    part[wv][1][lane + 64 * e] = dv[e];
+  }
+  __syncthreads();
+  if (wv != 0) return;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    dk[e] = part[0][0][lane + 64 * e];
+    dv[e] = part[0][1][lane + 64 * e];
+#pragma unroll
+    for (int i = 1; i < NWV; ++i) {
+      dk[e] += part[i][0][lane + 64 * e];
+      dv[e] += part[i][1][lane + 64 * e];
     }
   }
   float *dkp = a.dk + kvo + b * a.k_sb + (int64_t)krow * a.k_ss + g * a.k_sh;
@@ -183,13 +285,11 @@ __global__ __launch_bounds__(kThreads) void dkdv_fp32_kernel(BwdArgs a) {
 
 template <int D>
 hipError_t launch_d(const BwdArgs &a, hipStream_t stream) {
-  const int64_t q_waves = (int64_t)a.Hq * a.B * a.L * a.n_ranks;
-  if (q_waves > 0)
-    hipLaunchKernelGGL(dq_fp32_kernel<D>, dim3((uint32_t)((q_waves + 3) / 4)), dim3(kThreads), 0, stream, a);
+  const int64_t q_rows = (int64_t)a.Hq * a.B * a.L * a.n_ranks;  // one workgroup each
+  if (q_rows > 0) hipLaunchKernelGGL(dq_fp32_kernel<D>, dim3((uint32_t)q_rows), dim3(kThreads), 0, stream, a);
   const int n_slots = a.ring_rank >= 0 ? a.t_hi - a.t_lo : a.cp;
-  const int64_t k_waves = (int64_t)n_slots * a.Hkv * a.B * a.L;
-  if (k_waves > 0)
-    hipLaunchKernelGGL(dkdv_fp32_kernel<D>, dim3((uint32_t)((k_waves + 3) / 4)), dim3(kThreads), 0, stream, a);
+  const int64_t k_rows = (int64_t)n_slots * a.Hkv * a.B * a.L;  // one workgroup each
+  if (k_rows > 0) hipLaunchKernelGGL(dkdv_fp32_kernel<D>, dim3((uint32_t)k_rows), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
