@@ -234,11 +234,14 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
     if (r.j < 0) r.j += cp;
     const int hi = a.causal ? sm.count_le(r.j, qpos_max) : L;
     const int lo = packed ? sm.count_le(r.j, sst_min - 1) : 0;
+    // the step's tiles start at lo (key row kt * TB + shift): in a packed
+    // stream the first tile then holds no key of an earlier sample
+    r.shift = lo % TB;
     if (hi <= lo) {
       r.kt = r.ke = 0;
     } else {
       r.kt = lo / TB;
-      r.ke = (hi + TB - 1) / TB;
+      r.ke = r.kt + (hi - lo + TB - 1) / TB;
     }
     // a key row i of block j is at or before position p iff i < count_le(j, p),
     // so "every key <= the first query" and "every key in the last query's
@@ -355,7 +358,7 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
   // query sees are one local range; as offsets from the lane's first key row
   // in the tile, [vlo, vhi).
   auto mask = [&](const StepRange &x) {
-    const int k0 = x.kt * TB;
+    const int k0 = x.kt * TB + x.shift;
     const bool full = __builtin_amdgcn_readfirstlane((k0 >= x.flo) & (k0 + TB <= x.fhi));
     if (!full) {
       const int vlo = x.llo - k0 - 8 * hh, vhi = x.lhi - k0 - 8 * hh;
@@ -478,7 +481,7 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
     int t_nxt = t;
     StepRange nxt = cur;
     advance(t_nxt, nxt);
-    if (t_nxt < t_end) issue_tile(nxt.j, nxt.kt * TB, STG ^ 1);
+    if (t_nxt < t_end) issue_tile(nxt.j, nxt.kt * TB + nxt.shift, STG ^ 1);
     const char *const sK = STG == 0 ? smem0 : smem1;
     __builtin_amdgcn_s_setprio(1);  // keep the matrix core fed while the SIMD's other waves run softmax
     qk(sK);
@@ -495,7 +498,7 @@ __global__ __launch_bounds__(64 * NW, TB == 32 ? 3 : 2) void attn_bf16_kernel(At
   };
 
   // prologue: tile 0 into stage 0
-  if (t < t_end) issue_tile(cur.j, cur.kt * TB, 0);
+  if (t < t_end) issue_tile(cur.j, cur.kt * TB + cur.shift, 0);
   wait_tiles();
   __syncthreads();
   while (t < t_end) {
@@ -612,7 +615,7 @@ int tile_work(const AttnArgs &a, int BM, int rank, int lt, int t0, int t1) {
   for (int t = t0; t < t1; ++t) {
     const int j = ((rank - t) % a.cp + a.cp) % a.cp;
     const int hi = a.causal ? sm.count_le(j, pmax) : a.L, lo = sm.count_le(j, smin - 1);
-    if (hi > lo) work += (hi + kWalkTile - 1) / kWalkTile - lo / kWalkTile;
+    if (hi > lo) work += (hi - lo + kWalkTile - 1) / kWalkTile;
   }
   return work;
 }

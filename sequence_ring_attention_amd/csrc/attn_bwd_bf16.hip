@@ -214,11 +214,14 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
     r.j = mod_cp(rank - t, cp);
     const int hi = causal ? sm.count_le(r.j, qpos_max) : L;
     const int lo = packed ? sm.count_le(r.j, sst_min - 1) : 0;
+    // the step's tiles start at lo (key row kt * BN + shift): in a packed
+    // stream the first tile then holds no key of an earlier sample
+    r.shift = lo % BN;
     if (hi <= lo) {
       r.kt = r.ke = 0;
     } else {
       r.kt = lo / BN;
-      r.ke = (hi + BN - 1) / BN;
+      r.ke = r.kt + (hi - lo + BN - 1) / BN;
     }
     // key row i of block j is at or before position p iff i < count_le(j, p)
     r.fhi = causal ? sm.count_le(r.j, qpos_min) : L;
@@ -260,11 +263,11 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
     int t_nxt = t;
     StepRange nxt = cur;
     advance(t_nxt, nxt);
-    if (t_nxt < a.t_hi) issue_tile(nxt.j, nxt.kt * BN, STG ^ 1);
+    if (t_nxt < a.t_hi) issue_tile(nxt.j, nxt.kt * BN + nxt.shift, STG ^ 1);
 
     const char *const sK = STG == 0 ? smem0 : smem1;
     const char *const sV = sK + Lds<D>::TILE;
-    const int k0 = cur.kt * BN;
+    const int k0 = cur.kt * BN + cur.shift;
     const bool full = __builtin_amdgcn_readfirstlane((k0 >= cur.flo) & (k0 + BN <= cur.fhi));
     // positions grow with the local index, so the keys of block j this lane's
     // query sees are one local range; as offsets from the lane's first key
@@ -340,7 +343,7 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
     cur = nxt;
   };
 
-  if (t < a.t_hi) issue_tile(cur.j, cur.kt * BN, 0);
+  if (t < a.t_hi) issue_tile(cur.j, cur.kt * BN + cur.shift, 0);
   wait_tiles();
   __syncthreads();
   while (t < a.t_hi) {
@@ -394,6 +397,7 @@ __global__ __launch_bounds__(64 * NW, 2) void dq_bf16_kernel(BwdArgs a) {
 // row <= fhi).
 struct QRange {
   int qt, qe;
+  int shift;  // the tiles start at query row qt * BN + shift
   int flo, fhi;
 };
 
@@ -458,11 +462,14 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
     QRange x;
     const int lo = causal ? sm.count_le(r, kpos_min - 1) : 0;
     const int hi = packed ? sm.count_le(r, kend_max - 1) : L;
+    // the tiles start at lo: the first one holds no query before the
+    // key tile's first position (or, packed, of an earlier sample)
+    x.shift = lo % BN;
     if (hi <= lo) {
       x.qt = x.qe = 0;
     } else {
       x.qt = lo / BN;
-      x.qe = (hi + BN - 1) / BN;
+      x.qe = x.qt + (hi - lo + BN - 1) / BN;
     }
     x.flo = causal ? sm.count_le(r, kpos_max - 1) : 0;
     x.fhi = packed ? sm.count_le(r, kend_min - 1) : L;
@@ -527,11 +534,11 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
     uint32_t qvoff[NBLK], dvoff[NBLK];
     tile_load_offsets<D, KW>(qvoff, qbytes, wave, ln);
     tile_load_offsets<D, KW>(dvoff, dbytes, wave, ln);
-    issue_tile_lds<D, KW>(st, qb, q_extent, qbytes, it.x.qt * BN, L, wave, ln, qvoff);
-    issue_tile_lds<D, KW>(st + TILE, db, d_extent, dbytes, it.x.qt * BN, L, wave, ln, dvoff);
+    issue_tile_lds<D, KW>(st, qb, q_extent, qbytes, it.x.qt * BN + it.x.shift, L, wave, ln, qvoff);
+    issue_tile_lds<D, KW>(st + TILE, db, d_extent, dbytes, it.x.qt * BN + it.x.shift, L, wave, ln, dvoff);
     if (wave < 2) {
       const int rs = a.ring_rank >= 0 ? 0 : it.r;
-      const int64_t srow = (((int64_t)rs * a.Hq + hq) * a.B + b) * L + it.x.qt * BN;
+      const int64_t srow = (((int64_t)rs * a.Hq + hq) * a.B + b) * L + it.x.qt * BN + it.x.shift;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wave == 0 ? delta_rsrc : lse2_rsrc,
                                                (lds_void *)(st + STAGE + wave * (STATS / 2)), 4,
                                                (uint32_t)((srow + lane) * 4), 0, 0, 0);
@@ -574,7 +581,7 @@ __global__ __launch_bounds__(64 * KW, 2) void dkdv_bf16_kernel(BwdArgs a) {
     const char *const sD = sQ + TILE;
     const float *const sst = reinterpret_cast<const float *>(sQ + STAGE);
     const int r = cur.r;
-    const int q0 = cur.x.qt * BN;
+    const int q0 = cur.x.qt * BN + cur.x.shift;
     const bool full =
         __builtin_amdgcn_readfirstlane((k0 + BK <= L) & (q0 >= cur.x.flo) & (q0 + BN <= cur.x.fhi));
     int vlo = 0, vhi = BN;
@@ -730,7 +737,7 @@ int query_tile_work(const BwdArgs &a, int rank, int lt) {
   for (int t = a.t_lo; t < a.t_hi; ++t) {
     const int j = ((rank - t) % a.cp + a.cp) % a.cp;
     const int hi = a.causal ? sm.count_le(j, pmax) : a.L, lo = sm.packed() ? sm.count_le(j, smin - 1) : 0;
-    if (hi > lo) work += (hi + BN - 1) / BN - lo / BN;
+    if (hi > lo) work += (hi - lo + BN - 1) / BN;
   }
   return work;
 }
@@ -771,7 +778,7 @@ int key_tile_work(const BwdArgs &a, int BK, int j, int kt) {
   for (int r = r_first; r <= r_last; ++r) {
     const int lo = a.causal ? sm.count_le(r, kpos_min - 1) : 0;
     const int hi = sm.packed() ? sm.count_le(r, kend_max - 1) : a.L;
-    if (hi > lo) work += (hi + BN - 1) / BN - lo / BN;
+    if (hi > lo) work += (hi - lo + BN - 1) / BN;
   }
   return work;
 }

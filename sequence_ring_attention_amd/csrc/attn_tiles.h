@@ -117,6 +117,7 @@ __device__ inline void schedule_tr_products() {
 // are local rows of the walked share, found once per step.
 struct StepRange {
   int j, kt, ke;
+  int shift;  // tiles of this step start at key row kt * tile + shift (forward walk)
   int flo, fhi;
   int llo, lhi;
 };
