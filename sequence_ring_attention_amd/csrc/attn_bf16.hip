@@ -58,6 +58,7 @@
 // back on one XCD (workgroups are dealt to the 8 XCDs round-robin) so that
 // their K/V tiles are shared through that XCD's L2.
 #include <algorithm>
+#include <atomic>
 
 #include "attn_tiles.h"
 #include "lse_rule.h"
@@ -620,16 +621,19 @@ int tile_work(const AttnArgs &a, int BM, int rank, int lt, int t0, int t1) {
   return work;
 }
 
-// Compute units of the current device (queried once per device).
+// Compute units of the current device (queried once per device; calls from
+// several host threads may query it concurrently and store the same value).
 int device_cus() {
-  static int cus[64] = {};
+  static std::atomic<int> cus[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
+  int c = cus[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
     int n = 0;
-    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+    c = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+    cus[dev].store(c, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return c;
 }
 
 // The workgroups of a launch in decreasing order of work, so that long ones
