@@ -54,6 +54,26 @@ def parse():
     return p.parse_args()
 
 
+def share_walk_flops(D, heads, B, rd, c):
+    """Work of one ring rank's walk over its zigzag share (chunks r and
+    2 rd - 1 - r of c rows each) against all 2 rd chunks of keys, at 4 D flops
+    per visible (query, key) pair: the half-diagonal convention counts
+    2 rd c^2 pairs per head (each chunk-pair cell c^2, the two diagonal cells
+    c^2 / 2 each), the exact count 2 rd c^2 + c (the diagonals' c (c + 1) / 2).
+    Returns (half-diagonal, exact) flops; the same on every rank."""
+    return 4.0 * D * heads * B * 2 * rd * c * c, 4.0 * D * heads * B * (2 * rd * c * c + c)
+
+
+def per_sample_pairs(cu, rd):
+    """Visible pairs of one rank's per-sample share (every sample of length
+    n = 2 rd m cut into 2 rd chunks, the rank holding chunks r and
+    2 rd - 1 - r of each), under the causal same-sample mask: per sample
+    (2 rd - 1) m^2 + m (m + 1), the same on every rank."""
+    import numpy as np
+    m = np.diff(np.asarray(cu)).astype(np.int64) // (2 * rd)
+    return int(((2 * rd - 1) * m * m + m * (m + 1)).sum())
+
+
 def copy_calibration(mib):
     """A plain torch device-to-device copy of known size, three times; its
     FETCH_SIZE / WRITE_SIZE counters give the factor between counted and
@@ -560,7 +580,7 @@ def extra_workloads(cpu=True):
     q, k, v = inputs.workload_qkv(w)
     qd = q.to(dev)
     qs, ks, vs = zig_shares(qd, w.rd), zig_shares(k.to(dev), w.rd), zig_shares(v.to(dev), w.rd)
-    fl_rank = 4.0 * w.D * w.H * w.B * 2 * w.rd * w.chunk * w.chunk
+    fl_rank = share_walk_flops(w.D, w.H, w.B, w.rd, w.chunk)[0]
     entry = {"TFLOP_per_rank": fl_rank / 1e12}
     qz = torch.empty((w.rd, 1) + tuple(qs.shape[1:]), dtype=q.dtype, device=dev)
     entry["zigzag_extract_all_ranks_q"] = _time_flushed(lambda: B.usp_zigzag_extract(qd, qz, w.rd, 1, -1, -1),
@@ -687,7 +707,7 @@ def cpu_baseline(w, r, u, n_rows, gpu=None):
         errors = {"rows": int(n_rows), "heads": hb, **compare(gpu[0], gpu[1], o_ref, l_ref)}
     pairs = int((qp + 1).sum())                       # causal: position p sees p + 1 keys
     flops = 4.0 * w.D * hb * w.B * pairs
-    share_flops = 4.0 * w.D * hb * w.B * 2 * w.rd * w.chunk * w.chunk
+    share_flops = share_walk_flops(w.D, hb, w.B, w.rd, w.chunk)[0]
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": host_cores(), "kind": "oracle",
             "extrapolated_unit_seconds": dt * share_flops / flops,
             "sample": f"{n_rows} random query rows of share (r={r}, u={u}) x {hb} heads vs all "
@@ -710,8 +730,7 @@ def split_balance(w, q, k, v, zig_shares):
     dev = q.device
     cu = inputs.workload_cu_seqlens(w, multiple=2 * w.rd)
     c = w.chunk
-    m = np.diff(cu).astype(np.int64) // (2 * w.rd)
-    per_sample_pairs = int(((2 * w.rd - 1) * m * m + m * (m + 1)).sum())   # the same on every rank
+    ps_pairs = per_sample_pairs(cu, w.rd)   # the same on every rank
     out = {"num_samples": len(cu) - 1, "lengths_multiple_of": 2 * w.rd}
     for split in ("stream", "per_sample"):
         if split == "stream":
@@ -730,7 +749,7 @@ def split_balance(w, q, k, v, zig_shares):
                                       np.arange((2 * w.rd - 1 - r) * c, (2 * w.rd - r) * c)])
                 pairs = packed_pairs(cu, pos)
             else:
-                pairs = per_sample_pairs
+                pairs = ps_pairs
             fl = 4.0 * w.D * w.H * w.B * pairs
             qr = qs[r].contiguous()
             o = torch.empty_like(qr)
@@ -869,9 +888,7 @@ def main():
     # algorithmic work per step
     hb = w.H // w.ud
     c = w.chunk
-    units = 2 * w.rd                                 # 2 chunk-pair cells per ring step
-    flops = 4.0 * w.D * hb * w.B * units * c * c      # half-diagonal convention
-    flops_exact = 4.0 * w.D * hb * w.B * (units * c * c + c)
+    flops, flops_exact = share_walk_flops(w.D, hb, w.B, w.rd, c)   # half-diagonal convention, exact
     zig_bytes, fwd_bytes, inv_bytes = share.copy_bytes()
 
     for _ in range(args.warmup):
